@@ -1,0 +1,178 @@
+/*
+ * mk.h -- C ABI of libmk.so: one GPU's share of a tile-granular fused
+ * GEMM+AllReduce on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the "GEMM + AllReduce (TP)" kernel of "mKernel: Fast
+ * Multi-GPU, Multi-Node Fused Kernels" (arXiv 2609.13585), thelatestinai.com
+ * page, Table 3: a compute -> communication kernel whose output tiles are
+ * reduced across the GPUs of a tensor-parallel group. With K split across P
+ * GPUs, the share computed here is
+ *
+ *     C[i,j] = sum_{k<K} A[i,k] * B[k,j]  +  sum_{p<P-1} peers[p][i,j]
+ *
+ * where peers[] stands for the P-1 partial products that the other GPUs would
+ * deliver (here: inputs already resident in device memory).
+ *
+ * The fused entry point runs one persistent kernel whose workgroups take one
+ * of two roles (same page, Figure 2, items 1 and 6, and the abstract):
+ *   - compute workgroups run the bf16 matrix-core GEMM of a tile, store its
+ *     fp32 partial to a library workspace and set that tile's readiness flag;
+ *   - reducer workgroups wait for a tile's flag, then add the peer partials and
+ *     write C.
+ * An on-GPU controller (Figure 2 caption, Figure 7) reads progress counters and
+ * publishes how many workgroups should be reducers.
+ *
+ * Layout of every tensor argument: dense, row-major, 16-byte aligned device
+ * memory owned by the caller:
+ *   A      [M, K]            bfloat16
+ *   B      [K, N]            bfloat16
+ *   peers  [n_peers, M, N]   peer_dtype (bfloat16 or float32), one contiguous block
+ *   C      [M, N]            c_dtype    (bfloat16 or float32)
+ * Accumulation is float32. Peer partials are added to the local fp32 partial in
+ * index order (local partial first, then peers[0], peers[1], ...); the sum is
+ * rounded once to c_dtype, round to nearest even. The result is bitwise
+ * identical for every reducer count, for the adaptive controller and for the
+ * two-kernel baseline.
+ *
+ * Supported shapes: M >= 0 (any), N and K multiples of 8 (16-byte rows).
+ * M == 0 or N == 0 is a no-op. K == 0 gives C = sum of peers. n_peers == 0
+ * gives C = A*B. 0 <= n_peers <= MK_MAX_PEERS.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream). No host<->device copy happens inside a call. The library keeps one
+ * workspace per (device, stream): the fp32 partial buffer, tile flags and
+ * counters. It is created on first use, grows as needed and lives until
+ * process exit or mk_workspace_reset(). Calls on one stream are ordered by the
+ * stream; calls on different streams use different workspaces.
+ *
+ * Errors: every function returns an mk_status_t. Argument validation never
+ * dereferences device pointers, so it runs without touching the GPU. Errors
+ * raised on the device (a reducer wait that exceeded its time limit) are
+ * reported by mk_stream_status(). mk_last_error() gives a thread-local text.
+ */
+#ifndef MK_H_
+#define MK_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad dtype, negative size, aliasing */
+  MK_ERR_UNSUPPORTED = 2, /* valid but outside the supported envelope (N or K not %8) */
+  MK_ERR_HIP = 3,         /* a HIP runtime call failed; see mk_last_error() */
+  MK_ERR_TIMEOUT = 4,     /* a reducer waited on a tile flag past its time limit */
+  MK_ERR_NO_DEVICE = 5,   /* no usable gfx950 device */
+  MK_ERR_WORKSPACE = 6    /* workspace allocation failed */
+} mk_status_t;
+
+typedef enum { MK_DT_BF16 = 0, MK_DT_F32 = 1 } mk_dtype_t;
+
+/* n_reduce_wg value that hands the reducer count to the on-GPU controller. */
+#define MK_ADAPTIVE (-1)
+#define MK_MAX_PEERS 64
+
+/* Telemetry written by the fused kernel when the caller passes a device buffer
+ * of sizeof(mk_telemetry_t) bytes (else NULL). Times are in ticks of the GPU's
+ * constant 100 MHz clock. The controller trace holds one entry per controller
+ * update (Figure 7 of the thelatestinai.com page plots the same quantity). */
+#define MK_TRACE_CAP 512
+typedef struct {
+  uint64_t t;         /* tick of the update */
+  int32_t computed;   /* tiles whose partial was published */
+  int32_t reduced;    /* tiles whose C was written */
+  int32_t target;     /* published reducer target */
+  int32_t spare;
+} mk_trace_entry_t;
+
+typedef struct {
+  uint64_t t_start;          /* first workgroup start */
+  uint64_t t_end;            /* last workgroup exit */
+  uint64_t busy_compute;     /* sum over compute tiles of their duration */
+  uint64_t busy_reduce;      /* sum over reduce tiles, excluding flag waits */
+  uint64_t wait_reduce;      /* sum of reducer flag waits */
+  int32_t tiles;             /* tile count of the call */
+  int32_t grid;              /* workgroups launched */
+  int32_t initial_target;
+  int32_t final_target;
+  int32_t n_updates;         /* controller updates that changed the target */
+  int32_t n_trace;           /* valid entries in trace[] (<= MK_TRACE_CAP) */
+  int32_t role_switches;     /* workgroup role changes, summed */
+  int32_t reduced_by_compute;/* tiles reduced by workgroups draining the queue */
+  mk_trace_entry_t trace[MK_TRACE_CAP];
+} mk_telemetry_t;
+
+/*
+ * mk_gemm_ar_local -- fused persistent kernel (one launch).
+ *   A, B, peers, C : device pointers, layout above. peers may be NULL iff
+ *                    n_peers == 0. C must not overlap A, B or peers.
+ *   n_peers        : P-1, the number of peer partials.
+ *   M, N, K        : K is this GPU's K-shard length.
+ *   peer_dtype     : MK_DT_BF16 or MK_DT_F32.
+ *   c_dtype        : MK_DT_BF16 or MK_DT_F32.
+ *   stream         : hipStream_t (NULL = default stream).
+ *   n_reduce_wg    : 0 .. G-1 dedicated reducer workgroups (G =
+ *                    mk_num_workgroups()), or MK_ADAPTIVE. With 0, compute
+ *                    workgroups reduce the tiles once no GEMM tile is left;
+ *                    the same draining applies in every mode.
+ *   telemetry      : NULL or a device buffer of sizeof(mk_telemetry_t).
+ * Returns MK_OK once the kernel is enqueued.
+ */
+mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, int n_peers,
+                             void* C, int64_t M, int64_t N, int64_t K, int peer_dtype,
+                             int c_dtype, void* stream, int n_reduce_wg, void* telemetry);
+
+/*
+ * mk_gemm_then_reduce_baseline -- the unfused schedule of Figure 1 on the
+ * thelatestinai.com page: a GEMM kernel that writes every fp32 partial tile,
+ * then a separate reduce kernel, in order on `stream`. Same arguments and
+ * result as mk_gemm_ar_local (bitwise).
+ */
+mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const void* peers,
+                                         int n_peers, void* C, int64_t M, int64_t N, int64_t K,
+                                         int peer_dtype, int c_dtype, void* stream);
+
+/* Synchronizes `stream`, then returns and clears the device error word of that
+ * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
+mk_status_t mk_stream_status(void* stream);
+
+/* Synchronizes the device and frees every workspace of `device`; the next call
+ * recreates them zeroed. Use after an error. */
+mk_status_t mk_workspace_reset(int device);
+
+/* G: workgroups of the fused kernel's persistent grid on `device` (one per
+ * compute unit). Returns a negative mk_status_t on failure. */
+int mk_num_workgroups(int device);
+
+/* Tunables and debug switches (process-wide; read at each call). */
+typedef enum {
+  MK_OPT_SPIN_TIMEOUT_US = 0,   /* reducer flag-wait limit, microseconds (default 2000000) */
+  MK_OPT_WITHHOLD_TILE = 1,     /* debug: compute skips publishing this tile (-1 = off) */
+  MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
+  MK_OPT_TILE_SHAPE = 3         /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
+} mk_option_t;
+mk_status_t mk_set_option(int option, int64_t value);
+int64_t mk_get_option(int option);
+
+/* Host copy of the controller rule that the fused kernel runs on the device;
+ * exported so that its behaviour can be simulated on the CPU.
+ *   G        workgroups, T tiles
+ *   computed/reduced   progress counters
+ *   busy_c   summed compute-tile time; busy_r summed reduce time without waits
+ *   seed_x   the host's initial reducer fraction in [0,1]
+ *   current  the target now in force
+ * Returns the new target. */
+int mk_controller_eval(int G, int T, int computed, int reduced, uint64_t busy_c,
+                       uint64_t busy_r, float seed_x, int current);
+
+const char* mk_status_string(int status);
+const char* mk_last_error(void);
+int mk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H_ */
