@@ -1,0 +1,176 @@
+"""Benchmark: fused GEMM+AllReduce (one GPU's share) on MI355X.
+
+A step is one call of the fused persistent kernel (mk_gemm_ar_local, adaptive
+reducer count) over one batch of synthetic inputs already resident in HBM:
+C = A*B + sum of 15 peer partials for the Llama-70B-like MLP down-projection
+shard (M=4096 tokens, N=8192, K=1792 = 28672/16, P=16; bf16 A/B/peers/C, fp32
+accumulation). The two-kernel baseline (GEMM kernel, then reduce kernel) is timed
+in the same process for the speedup.
+
+Prints ONE JSON line. `value` is effective TFLOP/s = 2*M*N*K / time. The
+roofline object prices the fused kernel against HBM (the workload's arithmetic
+intensity, 107.6 FLOP/byte, is below MI355X's ridge of about 315): achieved =
+compulsory bytes (A + B + peers + C) per launch / average launch time.
+cpu_baseline times the CPU oracle on a bounded sample of rows of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_mlp.json")
+KERNEL_SOURCES = ["tile_gemm_all_amd/csrc/mk_kernels.hip", "tile_gemm_all_amd/csrc/mk_device.h",
+                  "tile_gemm_all_amd/csrc/mk_controller.h"]
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
+    on the kernel source as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha() or t.get("workload") != workload:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, peers, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of rows of the workload."""
+    import numpy as np
+    import torch
+
+    import mk_inputs
+    import oracle
+
+    Bb = mk_inputs.bits(B)
+    threads = oracle.max_threads()
+
+    def run_rows(rows):
+        idx = torch.as_tensor(rows, device=A.device)
+        Ab = mk_inputs.bits(A[idx])
+        Pb = mk_inputs.bits(peers[:, idx, :])
+        t0 = time.perf_counter()
+        oracle.gemm_ar(Ab, Bb, Pb, w.c_dtype)
+        return time.perf_counter() - t0
+
+    probe = list(range(threads))
+    t = run_rows(probe)
+    n = int(max(threads, min(w.M, len(probe) * budget_s / max(t, 1e-3))))
+    n = max(threads, (n // threads) * threads)
+    rows = list(np.linspace(0, w.M - 1, n).astype(int))
+    t = run_rows(rows)
+    flops = 2.0 * len(rows) * w.N * w.K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {w.M} rows of the {w.name} workload (all N={w.N}, "
+                      f"K={w.K}, {w.n_peers} peers), fp64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp")
+    ap.add_argument("--n-reduce-wg", type=int, default=None,
+                    help="static reducer count (default: adaptive controller)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the fused kernel; runs on more than one "
+              "GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mk_inputs
+    import tile_gemm_all_amd as mk
+
+    w = mk_inputs.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if w.c_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=args.n_reduce_wg)
+
+    def two_kernel():
+        mk.gemm_then_reduce_baseline(A, B, peers, C)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        mk.stream_status()
+        return start.elapsed_time(stop) / steps  # ms per launch
+
+    base_ms = timed(two_kernel, args.steps, args.warmup)
+    t0 = time.perf_counter()
+    fused_ms = timed(fused, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+
+    tflops = w.flops / (fused_ms * 1e-3) / 1e12
+    bytes_ = w.compulsory_bytes()
+    gbps = bytes_ / (fused_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(w.name)}
+    out = {
+        "metric": "fused GEMM+reduce TFLOP/s, % MFMA/HBM roofline, speedup vs 2-kernel baseline",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fused_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "M": w.M, "N": w.N, "K_local": w.K,
+                   "P": w.P, "peer_dtype": w.peer_dtype, "c_dtype": w.c_dtype,
+                   "reducers": "adaptive" if args.n_reduce_wg is None else args.n_reduce_wg},
+        "roofline": roofline,
+        "effective_GBps": round(gbps, 1),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "two_kernel_ms": round(base_ms, 5),
+        "speedup_vs_two_kernel": round(base_ms / fused_ms, 4),
+        "timed_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, peers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

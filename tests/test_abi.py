@@ -1,0 +1,105 @@
+"""The C ABI library loads, exports every function include/mk.h declares, and
+rejects bad arguments before touching the GPU (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_gemm_all_amd as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(mk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mk.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert mk.library().mk_version() == 1
+
+
+def test_status_strings():
+    assert mk.status_string(0) == "MK_OK"
+    assert mk.status_string(4) == "MK_ERR_TIMEOUT"
+    assert mk.status_string(99) == "MK_ERR_UNKNOWN"
+
+
+A16 = 0x10000  # fake, 16-byte aligned addresses: validation never dereferences them
+B16 = 0x20000000
+P16 = 0x40000000
+C16 = 0x80000000
+
+
+def call(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt=0, nr=-1):
+    return mk.library().mk_gemm_ar_local(A, B, peers, n_peers, C, M, N, K, pdt, cdt, None, nr,
+                                         None)
+
+
+def base(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt=0):
+    return mk.library().mk_gemm_then_reduce_baseline(A, B, peers, n_peers, C, M, N, K, pdt, cdt,
+                                                     None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), mk.MK_ERR_INVALID_ARG),
+    (dict(B=None), mk.MK_ERR_INVALID_ARG),
+    (dict(C=None), mk.MK_ERR_INVALID_ARG),
+    (dict(peers=None), mk.MK_ERR_INVALID_ARG),
+    (dict(A=A16 + 2), mk.MK_ERR_INVALID_ARG),
+    (dict(C=C16 + 8), mk.MK_ERR_INVALID_ARG),
+    (dict(M=-1), mk.MK_ERR_INVALID_ARG),
+    (dict(K=-8), mk.MK_ERR_INVALID_ARG),
+    (dict(n_peers=-1), mk.MK_ERR_INVALID_ARG),
+    (dict(n_peers=65), mk.MK_ERR_INVALID_ARG),
+    (dict(pdt=2), mk.MK_ERR_INVALID_ARG),
+    (dict(cdt=-1), mk.MK_ERR_INVALID_ARG),
+    (dict(N=60), mk.MK_ERR_UNSUPPORTED),
+    (dict(K=12), mk.MK_ERR_UNSUPPORTED),
+    (dict(C=A16), mk.MK_ERR_INVALID_ARG),               # C aliases A
+    (dict(C=P16 + 64 * 64 * 2), mk.MK_ERR_INVALID_ARG),  # C inside peer 1
+    (dict(M=1 << 41), mk.MK_ERR_UNSUPPORTED),
+])
+def test_validation_rejects(kw, status):
+    assert call(**kw) == status, mk.last_error()
+    assert base(**kw) == status, mk.last_error()
+    assert mk.last_error()
+
+
+def test_reducer_count_below_adaptive_is_rejected():
+    assert call(nr=-2) == mk.MK_ERR_INVALID_ARG
+
+
+def test_peers_may_be_null_without_peers_and_inputs_without_size():
+    # valid arguments reach the device query; without a GPU that is the first failure
+    st = call(peers=None, n_peers=0)
+    assert st in (mk.MK_OK, mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP), mk.last_error()
+    st = call(A=None, B=None, K=0)
+    assert st in (mk.MK_OK, mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP), mk.last_error()
+
+
+def test_options_roundtrip():
+    old = mk.get_option(mk.OPT_CTRL_PERIOD)
+    mk.set_option(mk.OPT_CTRL_PERIOD, 4)
+    assert mk.get_option(mk.OPT_CTRL_PERIOD) == 4
+    mk.set_option(mk.OPT_CTRL_PERIOD, old)
+    with pytest.raises(mk.MkError):
+        mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 0)
+    with pytest.raises(mk.MkError):
+        mk.set_option(mk.OPT_TILE_SHAPE, 7)
+    with pytest.raises(mk.MkError):
+        mk.set_option(99, 1)
+
+
+def test_telemetry_struct_size():
+    # 5 u64 + 8 i32 + MK_TRACE_CAP entries of 24 bytes
+    assert mk.TELEMETRY_BYTES == 5 * 8 + 8 * 4 + mk.MK_TRACE_CAP * 24

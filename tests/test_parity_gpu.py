@@ -1,0 +1,246 @@
+"""GPU parity: libmk.so's fused kernel and two-kernel baseline against the CPU oracle.
+
+Operation: C = A*B + sum of the P-1 peer partials (GEMM + AllReduce row of Table 3,
+thelatestinai.com page). Bars:
+  - integer-valued inputs: bit-exact against the oracle;
+  - Gaussian inputs: tests/compare.py's rule (literal 2e-3*rms(C) bound for fp32 C;
+    that bound plus half a bfloat16 ulp for bf16 C);
+  - the output is bitwise identical for every reducer count, for the adaptive
+    controller and for the baseline (all reduce in the same order).
+Full-size workloads are checked on sampled rows (first, last and one random row of
+every 256-row band), with the oracle evaluating those rows only.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mk_inputs
+import oracle
+from tests.compare import check_exact, check_tolerance
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import tile_gemm_all_amd as mk
+else:  # collected on CPU-only machines, never run there
+    mk = None
+
+DEV = "cuda"
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def oracle_rows(A, B, peers, c_dtype, rows=None):
+    Ab = mk_inputs.bits(A if rows is None else A[torch.as_tensor(rows, device=A.device)])
+    Bb = mk_inputs.bits(B)
+    if peers is None or peers.numel() == 0:
+        Pb = None
+    elif rows is None:
+        Pb = mk_inputs.bits(peers)
+    else:
+        Pb = mk_inputs.bits(peers[:, torch.as_tensor(rows, device=peers.device), :])
+    return oracle.gemm_ar(Ab, Bb, Pb, c_dtype)
+
+
+def new_c(M, N, c_dtype):
+    # poison: NaN bit patterns everywhere, so an unwritten element cannot pass
+    C = torch.empty((M, N), dtype=TORCH_DT[c_dtype], device=DEV)
+    if c_dtype == "bf16":
+        C.view(torch.int16).fill_(0x7FC1)
+    else:
+        C.view(torch.int32).fill_(0x7FC00001)
+    return C
+
+
+def run(A, B, peers, c_dtype, mode):
+    M, N = A.shape[0], B.shape[1]
+    C = new_c(M, N, c_dtype)
+    if mode == "baseline":
+        mk.gemm_then_reduce_baseline(A, B, peers, C)
+    else:
+        mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=None if mode == "adaptive" else int(mode))
+    mk.stream_status()
+    return C
+
+
+def c_bits(C, rows=None):
+    if rows is not None:
+        C = C[torch.as_tensor(rows, device=C.device)]
+    return mk_inputs.bits(C)
+
+
+def sample_rows(M, band=256, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for m0 in range(0, M, band):
+        m1 = min(M, m0 + band)
+        rows.update({m0, m1 - 1, int(rng.integers(m0, m1))})
+    return sorted(rows)
+
+
+MODES = ["adaptive", "0", "3", "baseline"]
+
+SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
+    (256, 512, 512, 3, "f32", "f32"),
+    (300, 264, 200, 3, "bf16", "bf16"),      # ragged in M, N and K
+    (130, 136, 72, 15, "bf16", "bf16"),
+    (1, 8, 8, 0, "bf16", "bf16"),
+    (64, 64, 0, 2, "bf16", "f32"),           # K == 0: C is the peer sum
+    (257, 520, 264, 7, "f32", "bf16"),
+    (520, 776, 1032, 1, "bf16", "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}-{s[5]}")
+@pytest.mark.parametrize("mode", MODES)
+def test_small_integer_bit_exact(shape, mode):
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"integer {shape} {mode}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 7, device="cpu")
+    _, want = oracle_rows(A, B, peers, cdt)
+    C = run(A.to(DEV), B.to(DEV), peers.to(DEV), cdt, mode)
+    check_exact(c_bits(C), want, f"{shape} {mode}")
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}-{s[5]}")
+@pytest.mark.parametrize("mode", ["adaptive", "baseline"])
+def test_small_gaussian_tolerance(shape, mode):
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"gaussian {shape} {mode}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "gaussian", 11, device="cpu")
+    C64, _ = oracle_rows(A, B, peers, cdt)
+    C = run(A.to(DEV), B.to(DEV), peers.to(DEV), cdt, mode)
+    check_tolerance(c_bits(C), C64, cdt, f"{shape} {mode}")
+
+
+def test_empty_shapes_are_no_ops():
+    announce("empty shapes")
+    A = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    B = torch.zeros((64, 32), dtype=torch.bfloat16, device=DEV)
+    C = torch.zeros((0, 32), dtype=torch.bfloat16, device=DEV)
+    mk.gemm_ar_local(A, B, None, C)
+    mk.gemm_then_reduce_baseline(A, B, None, C)
+    A = torch.zeros((16, 64), dtype=torch.bfloat16, device=DEV)
+    B = torch.zeros((64, 0), dtype=torch.bfloat16, device=DEV)
+    C = torch.zeros((16, 0), dtype=torch.float32, device=DEV)
+    mk.gemm_ar_local(A, B, None, C)
+    mk.stream_status()
+
+
+@pytest.mark.parametrize("w", mk_inputs.WORKLOADS, ids=lambda w: w.name)
+@pytest.mark.parametrize("variant", ["integer", "gaussian", "zeropeer"])
+def test_workload_parity(w, variant):
+    """Every workload at full size, fused (adaptive) and baseline; sampled rows."""
+    announce(f"workload {w.name} {variant}")
+    A, B, peers = mk_inputs.workload_inputs(w, variant, device=DEV)
+    rows = None if w.M * w.N <= 1 << 20 else sample_rows(w.M, seed=w.index)
+    C64, want = oracle_rows(A, B, peers, w.c_dtype, rows)
+    rms = float(np.sqrt(np.mean(C64 * C64)))
+    for mode in ("adaptive", "baseline"):
+        C = run(A, B, peers, w.c_dtype, mode)
+        got = c_bits(C, rows)
+        if variant == "integer":
+            check_exact(got, want, f"{w.name} {mode}")
+        else:
+            check_tolerance(got, C64, w.c_dtype, f"{w.name} {variant} {mode}", rms_ref=rms)
+        del C
+    if variant == "gaussian" and w.c_dtype == "bf16":
+        # fp32 output of the same inputs meets the literal bound
+        C64f, _ = oracle_rows(A, B, peers, "f32", rows)
+        C = run(A, B, peers, "f32", "adaptive")
+        check_tolerance(c_bits(C, rows), C64f, "f32", f"{w.name} f32 output", rms_ref=rms)
+    del A, B, peers
+    torch.cuda.empty_cache()
+
+
+def test_bitwise_invariance_across_reducer_counts():
+    announce("invariance across reducer counts")
+    M, N, K, npeer = 1024, 2048, 576, 7
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "gaussian", 21, device=DEV)
+    G = mk.num_workgroups()
+    ref = c_bits(run(A, B, peers, "bf16", "baseline"))
+    for mode in ["adaptive", "0", "1", "4", "16", "64", str(G - 1)]:
+        check_exact(c_bits(run(A, B, peers, "bf16", mode)), ref, f"mode {mode}")
+
+
+def test_back_to_back_alternating_inputs():
+    """Reducers must never read a partial before its flag: alternate two input sets so
+    that any early read would pick up the other set's partial."""
+    announce("alternating inputs")
+    M, N, K, npeer = 768, 1024, 320, 3
+    sets = []
+    for s in (31, 32):
+        A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", s, device="cpu")
+        _, want = oracle_rows(A, B, peers, "bf16")
+        sets.append((A.to(DEV), B.to(DEV), peers.to(DEV), want))
+    G = mk.num_workgroups()
+    C = new_c(M, N, "bf16")
+    for i in range(60):
+        A, B, peers, want = sets[i % 2]
+        nr = [None, 0, G - 1, 8, 200][i % 5]
+        mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr)
+        if i % 2 == 1 or i > 50:
+            mk.stream_status()
+            check_exact(c_bits(C), want, f"call {i} reducers {nr}")
+    mk.stream_status()
+
+
+def test_withheld_flag_times_out_and_recovers():
+    """Failure injection from the host: one tile's flag is never published; reducers
+    give up after a short wait, the kernel exits normally, and the error is reported."""
+    announce("withheld flag")
+    M, N, K, npeer = 512, 512, 128, 2
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", 41, device="cpu")
+    _, want = oracle_rows(A, B, peers, "bf16")
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    C = new_c(M, N, "bf16")
+    old = mk.get_option(mk.OPT_SPIN_TIMEOUT_US)
+    try:
+        mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 20000)
+        mk.set_option(mk.OPT_WITHHOLD_TILE, 1)
+        mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=4)
+        with pytest.raises(mk.MkError) as ei:
+            mk.stream_status()
+        assert ei.value.status == mk.MK_ERR_TIMEOUT
+    finally:
+        mk.set_option(mk.OPT_WITHHOLD_TILE, -1)
+        mk.set_option(mk.OPT_SPIN_TIMEOUT_US, old)
+    mk.stream_status()  # error word was cleared
+    mk.gemm_ar_local(A, B, peers, C)
+    mk.stream_status()
+    check_exact(c_bits(C), want, "after recovery")
+    mk.workspace_reset()
+    C2 = new_c(M, N, "bf16")
+    mk.gemm_ar_local(A, B, peers, C2)
+    mk.stream_status()
+    check_exact(c_bits(C2), want, "after workspace reset")
+
+
+def test_telemetry_and_controller_trace():
+    announce("telemetry")
+    w = mk_inputs.BY_NAME["mlp"]
+    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device=DEV)
+    C = new_c(w.M, w.N, "bf16")
+    tel = mk.new_telemetry()
+    mk.gemm_ar_local(A, B, peers, C, telemetry=tel)
+    mk.stream_status()
+    t = mk.read_telemetry(tel)
+    G = mk.num_workgroups()
+    assert t.tiles == (w.M // 256) * (w.N // 256)
+    assert t.grid == G
+    assert 1 <= t.initial_target <= G - 1
+    assert 1 <= t.final_target <= G
+    assert 0 < t.n_trace <= mk.MK_TRACE_CAP
+    assert t.t_end > t.t_start
+    assert t.busy_compute > 0 and t.busy_reduce > 0
+    targets = [t.trace[i].target for i in range(t.n_trace)]
+    computed = [t.trace[i].computed for i in range(t.n_trace)]
+    assert all(a <= b for a, b in zip(computed, computed[1:]))
+    assert all(1 <= x <= G for x in targets)
+    # once every tile is computed the controller hands all workgroups to the reduce
+    assert all(t.trace[i].target == G for i in range(t.n_trace) if computed[i] == t.tiles)

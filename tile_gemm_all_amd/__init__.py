@@ -1,0 +1,206 @@
+"""Python binding of libmk.so: one GPU's share of a tile-granular fused GEMM+AllReduce
+on AMD Instinct MI355X (gfx950).
+
+The functions here only marshal torch tensors (device pointers, sizes, dtypes and
+the current HIP stream) into the C ABI declared in include/mk.h. Every step of
+the computation runs in the library's HIP kernels. There is no fallback: if
+libmk.so is missing or fails to load, importing this package raises.
+
+    import tile_gemm_all_amd as mk
+    mk.gemm_ar_local(A, B, peers, C)                  # adaptive reducer count
+    mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=16)  # static reducer count
+    mk.gemm_then_reduce_baseline(A, B, peers, C)      # two-kernel baseline
+    mk.stream_status()                                # sync + device error word
+
+Shapes: A [M,K] bf16, B [K,N] bf16, peers [P-1,M,N] bf16|fp32, C [M,N] bf16|fp32,
+all contiguous on the current CUDA (HIP) device.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_TIMEOUT = 0, 1, 2, 3, 4
+MK_ERR_NO_DEVICE, MK_ERR_WORKSPACE = 5, 6
+MK_DT_BF16, MK_DT_F32 = 0, 1
+MK_ADAPTIVE = -1
+MK_MAX_PEERS = 64
+MK_TRACE_CAP = 512
+OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
+
+EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_stream_status",
+           "mk_workspace_reset", "mk_num_workgroups", "mk_set_option", "mk_get_option",
+           "mk_controller_eval", "mk_status_string", "mk_last_error", "mk_version"]
+
+
+class MkError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run tile_gemm_all_amd/build.py "
+                      "(or __graft_entry__.build()) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_lib.mk_gemm_ar_local.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _int, _vp,
+                                  _int, _vp]
+_lib.mk_gemm_ar_local.restype = _int
+_lib.mk_gemm_then_reduce_baseline.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int,
+                                              _int, _vp]
+_lib.mk_gemm_then_reduce_baseline.restype = _int
+_lib.mk_stream_status.argtypes = [_vp]
+_lib.mk_stream_status.restype = _int
+_lib.mk_workspace_reset.argtypes = [_int]
+_lib.mk_workspace_reset.restype = _int
+_lib.mk_num_workgroups.argtypes = [_int]
+_lib.mk_num_workgroups.restype = _int
+_lib.mk_set_option.argtypes = [_int, _i64]
+_lib.mk_set_option.restype = _int
+_lib.mk_get_option.argtypes = [_int]
+_lib.mk_get_option.restype = _i64
+_lib.mk_controller_eval.argtypes = [_int, _int, _int, _int, ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.c_float, _int]
+_lib.mk_controller_eval.restype = _int
+_lib.mk_status_string.argtypes = [_int]
+_lib.mk_status_string.restype = ctypes.c_char_p
+_lib.mk_last_error.restype = ctypes.c_char_p
+_lib.mk_version.restype = _int
+
+
+class TraceEntry(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_uint64), ("computed", ctypes.c_int32),
+                ("reduced", ctypes.c_int32), ("target", ctypes.c_int32),
+                ("spare", ctypes.c_int32)]
+
+
+class Telemetry(ctypes.Structure):
+    """Host mirror of mk_telemetry_t."""
+    _fields_ = [("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64),
+                ("busy_compute", ctypes.c_uint64), ("busy_reduce", ctypes.c_uint64),
+                ("wait_reduce", ctypes.c_uint64), ("tiles", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("initial_target", ctypes.c_int32),
+                ("final_target", ctypes.c_int32), ("n_updates", ctypes.c_int32),
+                ("n_trace", ctypes.c_int32), ("role_switches", ctypes.c_int32),
+                ("reduced_by_compute", ctypes.c_int32), ("trace", TraceEntry * MK_TRACE_CAP)]
+
+
+TELEMETRY_BYTES = ctypes.sizeof(Telemetry)
+
+
+def library():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def last_error():
+    return _lib.mk_last_error().decode()
+
+
+def status_string(st):
+    return _lib.mk_status_string(st).decode()
+
+
+def _check(st):
+    if st != MK_OK:
+        raise MkError(st, f"{status_string(st)}: {last_error()}")
+
+
+_DT = {torch.bfloat16: MK_DT_BF16, torch.float32: MK_DT_F32}
+
+
+def _stream_ptr(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _args(A, B, peers, C):
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if C.dtype not in _DT:
+        raise TypeError("C must be bfloat16 or float32")
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    if peers is None or peers.numel() == 0:
+        n_peers, pdt, pptr = 0, MK_DT_BF16, None
+    else:
+        if peers.dtype not in _DT or not peers.is_cuda or not peers.is_contiguous():
+            raise ValueError("peers must be a contiguous bf16/fp32 GPU tensor")
+        if peers.dim() != 3 or tuple(peers.shape[1:]) != (M, N):
+            raise ValueError(f"peers must be [P-1, {M}, {N}], got {tuple(peers.shape)}")
+        n_peers, pdt, pptr = peers.shape[0], _DT[peers.dtype], peers.data_ptr()
+    return (A.data_ptr(), B.data_ptr(), pptr, n_peers, C.data_ptr(), M, N, K, pdt, _DT[C.dtype])
+
+
+def gemm_ar_local(A, B, peers, C, n_reduce_wg=None, telemetry=None, stream=None):
+    """C = A @ B + peers.sum(0) with the fused persistent kernel.
+
+    n_reduce_wg: None (adaptive controller) or a static reducer workgroup count in
+    [0, G-1]. telemetry: None or a uint8 GPU tensor of TELEMETRY_BYTES bytes."""
+    a = _args(A, B, peers, C)
+    nr = MK_ADAPTIVE if n_reduce_wg is None else int(n_reduce_wg)
+    tel = None
+    if telemetry is not None:
+        if telemetry.numel() * telemetry.element_size() < TELEMETRY_BYTES or not telemetry.is_cuda:
+            raise ValueError("telemetry buffer too small")
+        tel = telemetry.data_ptr()
+    _check(_lib.mk_gemm_ar_local(*a[:10], _stream_ptr(stream), nr, tel))
+    return C
+
+
+def gemm_then_reduce_baseline(A, B, peers, C, stream=None):
+    """Same result as gemm_ar_local, by a GEMM kernel followed by a reduce kernel."""
+    a = _args(A, B, peers, C)
+    _check(_lib.mk_gemm_then_reduce_baseline(*a[:10], _stream_ptr(stream)))
+    return C
+
+
+def stream_status(stream=None):
+    """Synchronizes the stream and raises MkError if a kernel reported an error."""
+    _check(_lib.mk_stream_status(_stream_ptr(stream)))
+
+
+def workspace_reset(device=None):
+    dev = torch.cuda.current_device() if device is None else int(device)
+    _check(_lib.mk_workspace_reset(dev))
+
+
+def num_workgroups(device=None):
+    dev = torch.cuda.current_device() if device is None else int(device)
+    g = _lib.mk_num_workgroups(dev)
+    if g < 0:
+        _check(-g)
+    return g
+
+
+def set_option(option, value):
+    _check(_lib.mk_set_option(int(option), int(value)))
+
+
+def get_option(option):
+    return int(_lib.mk_get_option(int(option)))
+
+
+def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current):
+    return int(_lib.mk_controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current))
+
+
+def read_telemetry(buf):
+    """Copies a telemetry GPU buffer to the host and returns a Telemetry structure."""
+    host = buf.detach().cpu().contiguous().numpy().tobytes()[:TELEMETRY_BYTES]
+    return Telemetry.from_buffer_copy(host)
+
+
+def new_telemetry(device=None):
+    return torch.zeros(TELEMETRY_BYTES, dtype=torch.uint8,
+                       device=device if device is not None else "cuda")

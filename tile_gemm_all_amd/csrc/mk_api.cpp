@@ -1,0 +1,465 @@
+// mk_api.cpp -- host side of libmk.so: argument validation, per-(device,
+// stream) workspaces, kernel selection and launch. See include/mk.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "mk.h"
+#include "mk_controller.h"
+#include "mk_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mk_status_t fail(mk_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mk_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------ options
+
+struct Options {
+  int64_t spin_timeout_us = 2000000;
+  int64_t withhold_tile = -1;
+  int64_t ctrl_period = 8;
+  int64_t tile_shape = mk::SHAPE_AUTO;
+};
+std::mutex g_opt_mu;
+Options g_opt;
+
+Options options() {
+  std::lock_guard<std::mutex> lk(g_opt_mu);
+  return g_opt;
+}
+
+// ------------------------------------------------------------ device info
+
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+  int occ[3][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU)
+};
+std::mutex g_dev_mu;
+std::map<int, DeviceInfo> g_dev;
+
+mk_status_t device_info(int dev, DeviceInfo& out) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev.find(dev);
+  if (it != g_dev.end()) {
+    out = it->second;
+    return MK_OK;
+  }
+  hipDeviceProp_t p;
+  hipError_t e = hipGetDeviceProperties(&p, dev);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+    return fail(MK_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950", dev,
+                p.gcnArchName);
+  DeviceInfo d;
+  d.cus = p.multiProcessorCount;
+  for (int s = 1; s <= 2; ++s)
+    for (int pt = 0; pt < 2; ++pt)
+      for (int ct = 0; ct < 2; ++ct) {
+        int n = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mk::fused_kernel_ptr(s, pt, ct),
+                                                         mk::kThreadsHost, 0);
+        if (e != hipSuccess || n < 1)
+          return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        d.occ[s][pt][ct] = n;
+      }
+  d.ok = true;
+  g_dev[dev] = d;
+  out = d;
+  return MK_OK;
+}
+
+// ------------------------------------------------------------ workspaces
+
+struct Workspace {
+  int device = 0;
+  float* P = nullptr;
+  size_t P_elems = 0;
+  int* flags = nullptr;
+  int flags_cap = 0;
+  unsigned long long* slots = nullptr;
+  int epoch = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
+
+void free_ws(Workspace* w) {
+  if (w->P) (void)hipFree(w->P);
+  if (w->flags) (void)hipFree(w->flags);
+  if (w->slots) (void)hipFree(w->slots);
+  delete w;
+}
+
+// Returns the workspace of (dev, stream) with room for P_elems partials and
+// n_tiles flags; caller holds g_ws_mu.
+mk_status_t get_ws(int dev, hipStream_t s, size_t P_elems, int n_tiles, Workspace** out) {
+  auto key = std::make_pair(dev, s);
+  Workspace* w;
+  auto it = g_ws.find(key);
+  if (it == g_ws.end()) {
+    w = new Workspace();
+    w->device = dev;
+    hipError_t e = hipMalloc(&w->slots, sizeof(unsigned long long) * mk::S_COUNT * mk::kSlotWords);
+    if (e != hipSuccess) {
+      delete w;
+      return fail(MK_ERR_WORKSPACE, "workspace control words: %s", hipGetErrorString(e));
+    }
+    e = mk::launch_ws_init(nullptr, 0, w->slots, s);
+    if (e != hipSuccess) {
+      free_ws(w);
+      return hip_fail(e, "workspace init");
+    }
+    g_ws[key] = w;
+  } else {
+    w = it->second;
+  }
+  if (n_tiles > w->flags_cap || P_elems > w->P_elems) {
+    // Growing: earlier calls on this stream may still use the old buffers.
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  }
+  if (n_tiles > w->flags_cap) {
+    if (w->flags) (void)hipFree(w->flags);
+    w->flags = nullptr;
+    w->flags_cap = 0;
+    int cap = n_tiles < 1024 ? 1024 : n_tiles;
+    hipError_t e = hipMalloc(&w->flags, sizeof(int) * (size_t)cap);
+    if (e != hipSuccess) return fail(MK_ERR_WORKSPACE, "tile flags: %s", hipGetErrorString(e));
+    e = mk::launch_ws_init(w->flags, cap, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "flag init");
+    w->flags_cap = cap;
+  }
+  if (P_elems > w->P_elems) {
+    if (w->P) (void)hipFree(w->P);
+    w->P = nullptr;
+    w->P_elems = 0;
+    hipError_t e = hipMalloc(&w->P, sizeof(float) * P_elems);
+    if (e != hipSuccess)
+      return fail(MK_ERR_WORKSPACE, "partial buffer of %zu floats: %s", P_elems, hipGetErrorString(e));
+    w->P_elems = P_elems;
+  }
+  *out = w;
+  return MK_OK;
+}
+
+// ------------------------------------------------------------ validation
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+size_t dt_size(int dt) { return dt == MK_DT_F32 ? 4 : 2; }
+
+// Checks everything that can be checked without the GPU.
+mk_status_t validate(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                     int64_t M, int64_t N, int64_t K, int peer_dtype, int c_dtype) {
+  if (M < 0 || N < 0 || K < 0) return fail(MK_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld",
+                                           (long long)M, (long long)N, (long long)K);
+  if (n_peers < 0 || n_peers > MK_MAX_PEERS)
+    return fail(MK_ERR_INVALID_ARG, "n_peers=%d outside [0, %d]", n_peers, MK_MAX_PEERS);
+  if (peer_dtype != MK_DT_BF16 && peer_dtype != MK_DT_F32)
+    return fail(MK_ERR_INVALID_ARG, "peer_dtype=%d", peer_dtype);
+  if (c_dtype != MK_DT_BF16 && c_dtype != MK_DT_F32)
+    return fail(MK_ERR_INVALID_ARG, "c_dtype=%d", c_dtype);
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(MK_ERR_UNSUPPORTED, "N=%lld and K=%lld must be multiples of 8", (long long)N,
+                (long long)K);
+  const int64_t lim = (int64_t)1 << 40;
+  if (M > lim || N > lim || K > lim || (M > 0 && N > lim / M) || (M > 0 && K > lim / M) ||
+      (N > 0 && K > lim / N) || (n_peers > 0 && M * N > lim / n_peers))
+    return fail(MK_ERR_UNSUPPORTED, "sizes too large");
+  const size_t a_bytes = (size_t)(M * K) * 2, b_bytes = (size_t)(K * N) * 2;
+  const size_t p_bytes = (size_t)n_peers * (size_t)(M * N) * dt_size(peer_dtype);
+  const size_t c_bytes = (size_t)(M * N) * dt_size(c_dtype);
+  if (a_bytes && !A) return fail(MK_ERR_INVALID_ARG, "A is NULL");
+  if (b_bytes && !B) return fail(MK_ERR_INVALID_ARG, "B is NULL");
+  if (p_bytes && !peers) return fail(MK_ERR_INVALID_ARG, "peers is NULL with n_peers=%d", n_peers);
+  if (c_bytes && !C) return fail(MK_ERR_INVALID_ARG, "C is NULL");
+  const void* ptrs[] = {A, B, peers, C};
+  const char* names[] = {"A", "B", "peers", "C"};
+  for (int i = 0; i < 4; ++i)
+    if (((uintptr_t)ptrs[i]) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes) ||
+      overlaps(C, c_bytes, peers, p_bytes))
+    return fail(MK_ERR_INVALID_ARG, "C overlaps an input");
+  return MK_OK;
+}
+
+int pick_shape(int64_t M, int64_t N, int cus) {
+  int64_t forced = options().tile_shape;
+  if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
+  int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  return t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
+}
+
+// Host roofline seed for the controller: the reducers' share of the work when
+// the reduce streams at HBM speed and the GEMM runs at matrix-core peak.
+float seed_share(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype) {
+  double flops = 2.0 * (double)M * (double)N * (double)K;
+  double red_bytes = (double)M * (double)N * (4.0 + n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
+  double t_mfma = flops / 2.5e15, t_hbm = red_bytes / 8.0e12;
+  if (t_mfma + t_hbm <= 0) return 0.5f;
+  return (float)(t_hbm / (t_hbm + t_mfma));
+}
+
+struct Launch {
+  int dev;
+  DeviceInfo info;
+  int shape;
+  int64_t tiles_m, tiles_n;
+};
+
+mk_status_t prepare(int64_t M, int64_t N, Launch& L) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  mk_status_t st = device_info(dev, L.info);
+  if (st != MK_OK) return st;
+  L.dev = dev;
+  L.shape = pick_shape(M, N, L.info.cus);
+  L.tiles_m = (M + mk::shape_bm(L.shape) - 1) / mk::shape_bm(L.shape);
+  L.tiles_n = (N + mk::shape_bn(L.shape) - 1) / mk::shape_bn(L.shape);
+  if (L.tiles_m * L.tiles_n > (1 << 30)) return fail(MK_ERR_UNSUPPORTED, "too many tiles");
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                             int64_t M, int64_t N, int64_t K, int peer_dtype, int c_dtype,
+                             void* stream, int n_reduce_wg, void* telemetry) {
+  mk_status_t st = validate(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype);
+  if (st != MK_OK) return st;
+  if (n_reduce_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d", n_reduce_wg);
+  if (((uintptr_t)telemetry) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "telemetry not 16-byte aligned");
+  Launch L;
+  st = prepare(M, N, L);
+  if (st != MK_OK) return st;
+  const int G = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  if (n_reduce_wg > G - 1)
+    return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
+  if (M == 0 || N == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const Options opt = options();
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  const int T = (int)(L.tiles_m * L.tiles_n);
+  st = get_ws(L.dev, s, (size_t)(M * N), T, &w);
+  if (st != MK_OK) return st;
+  if (++w->epoch >= 0x7FFFFFFF) {  // flags hold old epochs: restart them from zero
+    hipError_t e = mk::launch_ws_init(w->flags, w->flags_cap, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "flag reset");
+    w->epoch = 1;
+  }
+  mk::FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = (const uint16_t*)A;
+  a.B = (const uint16_t*)B;
+  a.peers = peers;
+  a.C = C;
+  a.P = w->P;
+  a.flags = w->flags;
+  a.slots = w->slots;
+  a.tel = (mk_telemetry_t*)telemetry;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.n_peers = n_peers;
+  a.tiles_m = (int)L.tiles_m;
+  a.tiles_n = (int)L.tiles_n;
+  a.T = T;
+  a.G = G;
+  a.epoch = w->epoch;
+  a.seed_x = seed_share(M, N, K, n_peers, peer_dtype, c_dtype);
+  if (n_reduce_wg == MK_ADAPTIVE) {
+    a.adaptive = 1;
+    int t0 = (int)lrintf(a.seed_x * (float)G);
+    a.init_target = t0 < 1 ? 1 : (t0 > G - 1 ? G - 1 : t0);
+  } else {
+    a.adaptive = 0;
+    a.init_target = n_reduce_wg;
+  }
+  a.ctrl_period = opt.ctrl_period < 1 ? 1 : (int)opt.ctrl_period;
+  a.withhold_tile = (int)opt.withhold_tile;
+  a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
+  hipError_t e = mk::launch_fused(L.shape, peer_dtype, c_dtype, a, s);
+  if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}
+
+mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const void* peers,
+                                         int n_peers, void* C, int64_t M, int64_t N, int64_t K,
+                                         int peer_dtype, int c_dtype, void* stream) {
+  mk_status_t st = validate(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype);
+  if (st != MK_OK) return st;
+  Launch L;
+  st = prepare(M, N, L);
+  if (st != MK_OK) return st;
+  if (M == 0 || N == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  const int T = (int)(L.tiles_m * L.tiles_n);
+  st = get_ws(L.dev, s, (size_t)(M * N), T, &w);
+  if (st != MK_OK) return st;
+  mk::GemmArgs g;
+  g.A = (const uint16_t*)A;
+  g.B = (const uint16_t*)B;
+  g.P = w->P;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tiles_m = (int)L.tiles_m;
+  g.tiles_n = (int)L.tiles_n;
+  hipError_t e = mk::launch_gemm(L.shape, g, s);
+  if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
+  mk::ReduceArgs r;
+  r.P = w->P;
+  r.peers = peers;
+  r.C = C;
+  r.M = M;
+  r.N = N;
+  r.n_peers = n_peers;
+  r.pad_ = 0;
+  int64_t chunks = M * N / 8;
+  int64_t grid = (chunks + 2 * 256 - 1) / (2 * 256);
+  int64_t cap = (int64_t)L.info.cus * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  e = mk::launch_reduce(peer_dtype, c_dtype, r, (int)grid, s);
+  if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
+  return MK_OK;
+}
+
+mk_status_t mk_stream_status(void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws.find(std::make_pair(dev, s));
+  if (it == g_ws.end()) return MK_OK;
+  unsigned long long word = 0;
+  e = hipMemcpy(&word, it->second->slots + (size_t)mk::S_ERROR * mk::kSlotWords, sizeof word,
+                hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+  if (word == 0) return MK_OK;
+  e = mk::launch_clear_error(it->second->slots, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
+  int code = (int)(word & 0xFFFFFFFFu);
+  return fail((mk_status_t)code, "device reported error %d (%s)", code, mk_status_string(code));
+}
+
+mk_status_t mk_workspace_reset(int device) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipSetDevice(%d): %s", device, hipGetErrorString(e));
+  e = hipDeviceSynchronize();
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    if (it->first.first == device) {
+      free_ws(it->second);
+      it = g_ws.erase(it);
+    } else {
+      ++it;
+    }
+  }
+  (void)hipSetDevice(cur);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  return MK_OK;
+}
+
+int mk_num_workgroups(int device) {
+  DeviceInfo d;
+  mk_status_t st = device_info(device, d);
+  if (st != MK_OK) return -(int)st;
+  return d.cus * d.occ[mk::SHAPE_256][MK_DT_BF16][MK_DT_BF16];
+}
+
+mk_status_t mk_set_option(int option, int64_t value) {
+  std::lock_guard<std::mutex> lk(g_opt_mu);
+  switch (option) {
+    case MK_OPT_SPIN_TIMEOUT_US:
+      if (value < 1) return fail(MK_ERR_INVALID_ARG, "spin timeout must be >= 1 us");
+      g_opt.spin_timeout_us = value;
+      return MK_OK;
+    case MK_OPT_WITHHOLD_TILE:
+      g_opt.withhold_tile = value < 0 ? -1 : value;
+      return MK_OK;
+    case MK_OPT_CTRL_PERIOD:
+      if (value < 1) return fail(MK_ERR_INVALID_ARG, "controller period must be >= 1");
+      g_opt.ctrl_period = value;
+      return MK_OK;
+    case MK_OPT_TILE_SHAPE:
+      if (value < 0 || value > 2) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
+      g_opt.tile_shape = value;
+      return MK_OK;
+  }
+  return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
+}
+
+int64_t mk_get_option(int option) {
+  std::lock_guard<std::mutex> lk(g_opt_mu);
+  switch (option) {
+    case MK_OPT_SPIN_TIMEOUT_US: return g_opt.spin_timeout_us;
+    case MK_OPT_WITHHOLD_TILE: return g_opt.withhold_tile;
+    case MK_OPT_CTRL_PERIOD: return g_opt.ctrl_period;
+    case MK_OPT_TILE_SHAPE: return g_opt.tile_shape;
+  }
+  return -1;
+}
+
+int mk_controller_eval(int G, int T, int computed, int reduced, uint64_t busy_c, uint64_t busy_r,
+                       float seed_x, int current) {
+  return mk::controller_rule(G, T, computed, reduced, busy_c, busy_r, seed_x, current);
+}
+
+const char* mk_status_string(int status) {
+  switch (status) {
+    case MK_OK: return "MK_OK";
+    case MK_ERR_INVALID_ARG: return "MK_ERR_INVALID_ARG";
+    case MK_ERR_UNSUPPORTED: return "MK_ERR_UNSUPPORTED";
+    case MK_ERR_HIP: return "MK_ERR_HIP";
+    case MK_ERR_TIMEOUT: return "MK_ERR_TIMEOUT";
+    case MK_ERR_NO_DEVICE: return "MK_ERR_NO_DEVICE";
+    case MK_ERR_WORKSPACE: return "MK_ERR_WORKSPACE";
+  }
+  return "MK_ERR_UNKNOWN";
+}
+
+const char* mk_last_error(void) { return g_last_error.c_str(); }
+
+int mk_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// mk_kernels.h -- interface between the host library (mk_api.cpp) and the
+// kernels (mk_kernels.hip). Internal; the public ABI is include/mk.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk.h"
+
+namespace mk {
+
+// Workspace control words, each on its own 128-byte line (kSlotWords 64-bit words).
+enum Slot : int {
+  S_COMPUTE_NEXT = 0,  // next GEMM tile to claim
+  S_REDUCE_NEXT,       // next tile to reduce
+  S_COMPUTED,          // tiles published
+  S_REDUCED,           // tiles reduced
+  S_EXIT,              // workgroups that have left the persistent loop
+  S_ERROR,             // device error word (mk_status_t), kept across calls
+  S_ABORT,             // set on error: every workgroup leaves its loop
+  S_LOCK,              // controller try-lock
+  S_TARGET,            // (epoch << 32) | reducer target published by the controller
+  S_BUSY_C,            // summed compute-tile ticks
+  S_BUSY_R,            // summed reduce-tile ticks (flag waits excluded)
+  S_WAIT_R,            // summed flag-wait ticks
+  S_UPDATES,           // controller target changes
+  S_SWITCHES,          // workgroup role changes
+  S_RBC,               // tiles reduced by workgroups of the compute role (draining)
+  S_NTRACE,            // controller trace entries written
+  S_TSTART,            // min start tick
+  S_TEND,              // max exit tick
+  S_COUNT
+};
+constexpr int kSlotWords = 16;
+constexpr int kThreadsHost = 256;  // workgroup size of every kernel
+
+enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2 };
+
+struct FusedArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  const void* peers;
+  void* C;
+  float* P;                    // fp32 partial tiles, [M][N]
+  int* flags;                  // one per tile, holds the epoch of the call that published it
+  unsigned long long* slots;   // S_COUNT * kSlotWords words
+  mk_telemetry_t* tel;         // optional
+  int64_t M, N, K;
+  int n_peers, tiles_m, tiles_n, T;
+  int G;                       // workgroups in the grid
+  int epoch;                   // this call's flag value (never 0)
+  int init_target;             // reducer target before the controller's first update
+  int adaptive;                // controller on/off
+  float seed_x;                // controller seed share
+  int ctrl_period;
+  int withhold_tile;           // debug: -1 = off
+  int pad_;
+  unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
+};
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  float* P;
+  int64_t M, N, K;
+  int tiles_m, tiles_n;
+};
+
+struct ReduceArgs {
+  const float* P;
+  const void* peers;
+  void* C;
+  int64_t M, N;
+  int n_peers;
+  int pad_;
+};
+
+const void* fused_kernel_ptr(int shape, int pt, int ct);
+const void* gemm_kernel_ptr(int shape);
+const void* reduce_kernel_ptr(int pt, int ct);
+int shape_bm(int shape);
+int shape_bn(int shape);
+
+hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s);
+hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s);
+hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s);
+hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s);
+hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStream_t s);
+
+}  // namespace mk

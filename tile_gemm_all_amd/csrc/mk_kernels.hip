@@ -1,0 +1,323 @@
+// mk_kernels.hip -- the fused persistent GEMM+AllReduce kernel (one GPU's share)
+// and the two-kernel baseline, for gfx950.
+//
+// Fused schedule: Figure 1(c) and Figure 2 of the thelatestinai.com page of
+// "mKernel: Fast Multi-GPU, Multi-Node Fused Kernels": a persistent kernel whose
+// workgroups take compute or communication roles; compute publishes each
+// finished tile with a readiness flag, communication consumes it as soon as it
+// is ready, and a controller retunes the number of communication workgroups.
+// Baseline: Figure 1(a)/(b)'s kernel-boundary schedule reduced to one GPU: a GEMM
+// kernel writes every partial tile, then a reduce kernel runs.
+#include "mk_kernels.h"
+
+#include "mk_controller.h"
+#include "mk_device.h"
+
+namespace mk {
+
+// ------------------------------------------------------------ workspace slots
+
+__device__ __forceinline__ int* slot32(unsigned long long* s, int i) {
+  return (int*)(s + (size_t)i * kSlotWords);
+}
+__device__ __forceinline__ unsigned long long* slot64(unsigned long long* s, int i) {
+  return s + (size_t)i * kSlotWords;
+}
+
+__device__ __forceinline__ int current_target(const FusedArgs& a) {
+  unsigned long long w =
+      __hip_atomic_load(slot64(a.slots, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((int)(w >> 32) == a.epoch) return (int)(w & 0xFFFFFFFFu);
+  return a.init_target;
+}
+
+__device__ __forceinline__ void raise_error(unsigned long long* S, int code) {
+  atomicCAS(slot32(S, S_ERROR), 0, code);
+  __hip_atomic_store(slot32(S, S_ABORT), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One controller evaluation (thread 0 of the workgroup that wins the try-lock).
+__device__ void controller_step(const FusedArgs& a) {
+  unsigned long long* S = a.slots;
+  if (atomicCAS(slot32(S, S_LOCK), 0, 1) != 0) return;
+  int c = load_relaxed(slot32(S, S_COMPUTED));
+  int r = load_relaxed(slot32(S, S_REDUCED));
+  unsigned long long bc =
+      __hip_atomic_load(slot64(S, S_BUSY_C), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long br =
+      __hip_atomic_load(slot64(S, S_BUSY_R), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int cur = current_target(a);
+  int nt = controller_rule(a.G, a.T, c, r, bc, br, a.seed_x, cur);
+  if (nt != cur) {
+    unsigned long long w = ((unsigned long long)(unsigned)a.epoch << 32) | (unsigned)nt;
+    __hip_atomic_store(slot64(S, S_TARGET), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    atomicAdd(slot32(S, S_UPDATES), 1);
+  }
+  if (a.tel) {
+    int i = atomicAdd(slot32(S, S_NTRACE), 1);
+    if (i < MK_TRACE_CAP) {
+      mk_trace_entry_t e;
+      e.t = ticks();
+      e.computed = c;
+      e.reduced = r;
+      e.target = nt;
+      e.spare = 0;
+      a.tel->trace[i] = e;
+    }
+  }
+  __hip_atomic_store(slot32(S, S_LOCK), 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
+
+template <class Cfg, typename PT, typename CT>
+__global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
+  __shared__ __align__(16) uint16_t lds[2 * Cfg::STAGE];
+  __shared__ int s_kind, s_tile, s_ok;
+  const int tid = threadIdx.x;
+  const int wg = blockIdx.x;
+  unsigned long long* S = a.slots;
+  const PT* peers = (const PT*)a.peers;
+  CT* C = (CT*)a.C;
+  const unsigned long long t_begin = ticks();
+  int last_kind = -1;  // thread 0 only
+  GemmTile<Cfg> g;
+
+  for (;;) {
+    // ---- thread 0 picks the next task (role from the published target)
+    if (tid == 0) {
+      int kind = K_EXIT, tile = -1;
+      bool draining = false;
+      const unsigned long long w0 = ticks();
+      for (;;) {
+        if (load_relaxed(slot32(S, S_ABORT))) break;
+        const bool reducer = wg < current_target(a);
+        if (!reducer && load_relaxed(slot32(S, S_COMPUTE_NEXT)) < a.T) {
+          int t = atomicAdd(slot32(S, S_COMPUTE_NEXT), 1);
+          if (t < a.T) {
+            kind = K_COMPUTE;
+            tile = t;
+            break;
+          }
+        }
+        // Reduce: claim only tiles a compute workgroup has already claimed, so a
+        // reducer never waits on a tile nobody is producing.
+        int r = load_relaxed(slot32(S, S_REDUCE_NEXT));
+        if (r >= a.T) break;
+        int c = load_relaxed(slot32(S, S_COMPUTE_NEXT));
+        if (r < c) {
+          if (atomicCAS(slot32(S, S_REDUCE_NEXT), r, r + 1) == r) {
+            kind = K_REDUCE;
+            tile = r;
+            draining = !reducer;
+            break;
+          }
+          continue;
+        }
+        if (ticks() - w0 > a.spin_limit) {
+          raise_error(S, MK_ERR_TIMEOUT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (kind != K_EXIT && last_kind >= 0 && kind != last_kind) atomicAdd(slot32(S, S_SWITCHES), 1);
+      if (kind != K_EXIT) last_kind = kind;
+      if (draining) atomicAdd(slot32(S, S_RBC), 1);
+      s_kind = kind;
+      s_tile = tile;
+    }
+    __syncthreads();
+    const int kind = s_kind, tile = s_tile;
+    if (kind == K_EXIT) break;
+    int tm, tn;
+    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
+
+    if (kind == K_COMPUTE) {
+      const unsigned long long t0 = ticks();
+      g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+      g.store_partial(a.P, a.M, a.N, m0, n0);
+      __syncthreads();  // every wave's partial stores precede the flag
+      if (tid == 0) {
+        if (tile != a.withhold_tile) publish_flag(a.flags + tile, a.epoch);
+        int done = atomicAdd(slot32(S, S_COMPUTED), 1) + 1;
+        atomicAdd(slot64(S, S_BUSY_C), ticks() - t0);
+        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(a);
+      }
+    } else {
+      if (tid == 0) {
+        const unsigned long long w0 = ticks();
+        int ok = 1;
+        while (load_relaxed(a.flags + tile) != a.epoch) {
+          if (load_relaxed(slot32(S, S_ABORT))) {
+            ok = 0;
+            break;
+          }
+          if (ticks() - w0 > a.spin_limit) {
+            raise_error(S, MK_ERR_TIMEOUT);
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        acquire_fence();
+        atomicAdd(slot64(S, S_WAIT_R), ticks() - w0);
+        s_ok = ok;
+      }
+      __syncthreads();
+      if (!s_ok) break;
+      const unsigned long long t0 = ticks();
+      const int rows = (int)(a.M - m0 < Cfg::BM ? a.M - m0 : Cfg::BM);
+      const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
+      reduce_region<PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, m0, n0, rows, cols);
+      __syncthreads();
+      if (tid == 0) {
+        int done = atomicAdd(slot32(S, S_REDUCED), 1) + 1;
+        atomicAdd(slot64(S, S_BUSY_R), ticks() - t0);
+        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(a);
+      }
+    }
+    __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
+  }
+
+  // ---- exit: the last workgroup out resets the claim and progress counters
+  if (tid == 0) {
+    atomicMin(slot64(S, S_TSTART), t_begin);
+    atomicMax(slot64(S, S_TEND), ticks());
+    int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_ACQ_REL,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    if (out == a.G - 1) {
+      if (a.tel) {
+        mk_telemetry_t* t = a.tel;
+        t->t_start = *slot64(S, S_TSTART);
+        t->t_end = *slot64(S, S_TEND);
+        t->busy_compute = *slot64(S, S_BUSY_C);
+        t->busy_reduce = *slot64(S, S_BUSY_R);
+        t->wait_reduce = *slot64(S, S_WAIT_R);
+        t->tiles = a.T;
+        t->grid = a.G;
+        t->initial_target = a.init_target;
+        t->final_target = current_target(a);
+        t->n_updates = *slot32(S, S_UPDATES);
+        int nt = *slot32(S, S_NTRACE);
+        t->n_trace = nt < MK_TRACE_CAP ? nt : MK_TRACE_CAP;
+        t->role_switches = *slot32(S, S_SWITCHES);
+        t->reduced_by_compute = *slot32(S, S_RBC);
+      }
+      const int zero_slots[] = {S_COMPUTE_NEXT, S_REDUCE_NEXT, S_COMPUTED, S_REDUCED, S_EXIT,
+                                S_ABORT,        S_LOCK,        S_BUSY_C,   S_BUSY_R,  S_WAIT_R,
+                                S_UPDATES,      S_SWITCHES,    S_RBC,      S_NTRACE,  S_TEND};
+      for (int i : zero_slots)
+        __hip_atomic_store(slot64(S, i), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot64(S, S_TSTART), ~0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ------------------------------------------------------------ baseline kernels
+
+template <class Cfg>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint16_t lds[2 * Cfg::STAGE];
+  int tm, tn;
+  tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
+  GemmTile<Cfg> g;
+  g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+  g.store_partial(a.P, a.M, a.N, m0, n0);
+}
+
+template <typename PT, typename CT>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
+  const PT* peers = (const PT*)a.peers;
+  CT* C = (CT*)a.C;
+  const int64_t Q = a.M * a.N / 8;  // chunks of 8 elements over the dense arrays
+  const int64_t step = (int64_t)gridDim.x * kThreads;
+  const int64_t stride = a.M * a.N;
+  int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; q + step < Q; q += 2 * step) {
+    int64_t e[2] = {q * 8, (q + step) * 8};
+    reduce_chunks<2, PT, CT>(a.P, peers, a.n_peers, stride, C, e);
+  }
+  if (q < Q) {
+    int64_t e[1] = {q * 8};
+    reduce_chunks<1, PT, CT>(a.P, peers, a.n_peers, stride, C, e);
+  }
+}
+
+// Workspace initialisation: flags to 0, slots to their reset values.
+__global__ void ws_init_kernel(int* flags, int n_flags, unsigned long long* slots) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_flags; i += gridDim.x * blockDim.x)
+    flags[i] = 0;
+  if (slots && blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < S_COUNT * kSlotWords; i += blockDim.x)
+      slots[i] = (i == S_TSTART * kSlotWords) ? ~0ull : 0ull;
+  }
+}
+
+// Clears the error word only (after the host has read it).
+__global__ void clear_error_kernel(unsigned long long* slots) {
+  if (threadIdx.x == 0) slots[(size_t)S_ERROR * kSlotWords] = 0ull;
+}
+
+// ------------------------------------------------------------ host-side launchers
+
+using T256 = TileCfg<256, 256>;
+using T128 = TileCfg<128, 128>;
+
+template <class Cfg>
+static const void* fused_ptr(int pt, int ct) {
+  if (pt == MK_DT_BF16 && ct == MK_DT_BF16)
+    return (const void*)fused_kernel<Cfg, uint16_t, uint16_t>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)fused_kernel<Cfg, uint16_t, float>;
+  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)fused_kernel<Cfg, float, uint16_t>;
+  return (const void*)fused_kernel<Cfg, float, float>;
+}
+
+const void* fused_kernel_ptr(int shape, int pt, int ct) {
+  return shape == SHAPE_256 ? fused_ptr<T256>(pt, ct) : fused_ptr<T128>(pt, ct);
+}
+
+const void* gemm_kernel_ptr(int shape) {
+  return shape == SHAPE_256 ? (const void*)gemm_kernel<T256> : (const void*)gemm_kernel<T128>;
+}
+
+const void* reduce_kernel_ptr(int pt, int ct) {
+  if (pt == MK_DT_BF16 && ct == MK_DT_BF16) return (const void*)reduce_kernel<uint16_t, uint16_t>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)reduce_kernel<uint16_t, float>;
+  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)reduce_kernel<float, uint16_t>;
+  return (const void*)reduce_kernel<float, float>;
+}
+
+int shape_bm(int shape) { return shape == SHAPE_256 ? 256 : 128; }
+int shape_bn(int shape) { return shape == SHAPE_256 ? 256 : 128; }
+
+hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s) {
+  hipLaunchKernelGGL(ws_init_kernel, dim3(64), dim3(256), 0, s, flags, n_flags, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s) {
+  hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(64), 0, s, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s) {
+  const void* f = fused_kernel_ptr(shape, pt, ct);
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel(f, dim3(a.G), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s) {
+  const void* f = gemm_kernel_ptr(shape);
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel(f, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStream_t s) {
+  const void* f = reduce_kernel_ptr(pt, ct);
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+}  // namespace mk
