@@ -66,7 +66,8 @@ typedef enum {
   MK_ERR_HIP = 3,         /* a HIP runtime call failed; see mk_last_error() */
   MK_ERR_TIMEOUT = 4,     /* a reducer waited on a tile flag past its time limit */
   MK_ERR_NO_DEVICE = 5,   /* no usable gfx950 device */
-  MK_ERR_WORKSPACE = 6    /* workspace allocation failed */
+  MK_ERR_WORKSPACE = 6,   /* workspace allocation failed */
+  MK_ERR_INTERNAL = 7     /* the fused kernel ended with tiles left unreduced */
 } mk_status_t;
 
 typedef enum { MK_DT_BF16 = 0, MK_DT_F32 = 1 } mk_dtype_t;
@@ -101,7 +102,9 @@ typedef struct {
   int32_t n_updates;         /* controller updates that changed the target */
   int32_t n_trace;           /* valid entries in trace[] (<= MK_TRACE_CAP) */
   int32_t role_switches;     /* workgroup role changes, summed */
-  int32_t reduced_by_compute;/* tiles reduced by workgroups draining the queue */
+  int32_t reduced_by_compute;/* tiles reduced by compute-role workgroups (draining) */
+  int32_t computed_by_reducers; /* tiles computed by reducer-role workgroups with nothing to reduce */
+  int32_t n_xcd;             /* XCDs; each XCD computes and reduces its own share of tiles */
   mk_trace_entry_t trace[MK_TRACE_CAP];
 } mk_telemetry_t;
 
@@ -143,16 +146,24 @@ mk_status_t mk_stream_status(void* stream);
  * recreates them zeroed. Use after an error. */
 mk_status_t mk_workspace_reset(int device);
 
-/* G: workgroups of the fused kernel's persistent grid on `device` (one per
- * compute unit). Returns a negative mk_status_t on failure. */
+/* G: workgroups of the fused kernel's persistent grid on `device` with its
+ * large (256x256) tiles: one per compute unit. Returns a negative mk_status_t on
+ * failure. */
 int mk_num_workgroups(int device);
+
+/* G for a call with these arguments on the current device (the tile shape, and
+ * with it the number of workgroups per compute unit, depends on the shape).
+ * n_reduce_wg of that call must lie in [0, G-1] or be MK_ADAPTIVE. Returns a
+ * negative mk_status_t on failure. */
+int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype);
 
 /* Tunables and debug switches (process-wide; read at each call). */
 typedef enum {
   MK_OPT_SPIN_TIMEOUT_US = 0,   /* reducer flag-wait limit, microseconds (default 2000000) */
   MK_OPT_WITHHOLD_TILE = 1,     /* debug: compute skips publishing this tile (-1 = off) */
   MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
-  MK_OPT_TILE_SHAPE = 3         /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
+  MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
+  MK_OPT_FLAG_SCOPE = 4         /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

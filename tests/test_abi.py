@@ -101,5 +101,5 @@ def test_options_roundtrip():
 
 
 def test_telemetry_struct_size():
-    # 5 u64 + 8 i32 + MK_TRACE_CAP entries of 24 bytes
-    assert mk.TELEMETRY_BYTES == 5 * 8 + 8 * 4 + mk.MK_TRACE_CAP * 24
+    # 5 u64 + 10 i32 + MK_TRACE_CAP entries of 24 bytes
+    assert mk.TELEMETRY_BYTES == 5 * 8 + 10 * 4 + mk.MK_TRACE_CAP * 24

@@ -162,7 +162,7 @@ def test_bitwise_invariance_across_reducer_counts():
     announce("invariance across reducer counts")
     M, N, K, npeer = 1024, 2048, 576, 7
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "gaussian", 21, device=DEV)
-    G = mk.num_workgroups()
+    G = mk.fused_grid(A, B, peers, new_c(M, N, "bf16"))
     ref = c_bits(run(A, B, peers, "bf16", "baseline"))
     for mode in ["adaptive", "0", "1", "4", "16", "64", str(G - 1)]:
         check_exact(c_bits(run(A, B, peers, "bf16", mode)), ref, f"mode {mode}")
@@ -178,8 +178,8 @@ def test_back_to_back_alternating_inputs():
         A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", s, device="cpu")
         _, want = oracle_rows(A, B, peers, "bf16")
         sets.append((A.to(DEV), B.to(DEV), peers.to(DEV), want))
-    G = mk.num_workgroups()
     C = new_c(M, N, "bf16")
+    G = mk.fused_grid(sets[0][0], sets[0][1], sets[0][2], C)
     for i in range(60):
         A, B, peers, want = sets[i % 2]
         nr = [None, 0, G - 1, 8, 200][i % 5]
@@ -230,9 +230,10 @@ def test_telemetry_and_controller_trace():
     mk.gemm_ar_local(A, B, peers, C, telemetry=tel)
     mk.stream_status()
     t = mk.read_telemetry(tel)
-    G = mk.num_workgroups()
-    assert t.tiles == (w.M // 256) * (w.N // 256)
+    G = mk.fused_grid(A, B, peers, C)
+    assert t.tiles in ((w.M // 256) * (w.N // 256), (w.M // 128) * (w.N // 128))
     assert t.grid == G
+    assert t.n_xcd == 8
     assert 1 <= t.initial_target <= G - 1
     assert 1 <= t.final_target <= G
     assert 0 < t.n_trace <= mk.MK_TRACE_CAP

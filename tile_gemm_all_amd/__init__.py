@@ -30,9 +30,11 @@ MK_ADAPTIVE = -1
 MK_MAX_PEERS = 64
 MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
+OPT_FLAG_SCOPE = 4
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_stream_status",
-           "mk_workspace_reset", "mk_num_workgroups", "mk_set_option", "mk_get_option",
+           "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
+           "mk_get_option",
            "mk_controller_eval", "mk_status_string", "mk_last_error", "mk_version"]
 
 
@@ -60,6 +62,8 @@ _lib.mk_workspace_reset.argtypes = [_int]
 _lib.mk_workspace_reset.restype = _int
 _lib.mk_num_workgroups.argtypes = [_int]
 _lib.mk_num_workgroups.restype = _int
+_lib.mk_fused_grid.argtypes = [_i64, _i64, _i64, _int, _int, _int]
+_lib.mk_fused_grid.restype = _int
 _lib.mk_set_option.argtypes = [_int, _i64]
 _lib.mk_set_option.restype = _int
 _lib.mk_get_option.argtypes = [_int]
@@ -87,7 +91,8 @@ class Telemetry(ctypes.Structure):
                 ("grid", ctypes.c_int32), ("initial_target", ctypes.c_int32),
                 ("final_target", ctypes.c_int32), ("n_updates", ctypes.c_int32),
                 ("n_trace", ctypes.c_int32), ("role_switches", ctypes.c_int32),
-                ("reduced_by_compute", ctypes.c_int32), ("trace", TraceEntry * MK_TRACE_CAP)]
+                ("reduced_by_compute", ctypes.c_int32), ("computed_by_reducers", ctypes.c_int32),
+                ("n_xcd", ctypes.c_int32), ("trace", TraceEntry * MK_TRACE_CAP)]
 
 
 TELEMETRY_BYTES = ctypes.sizeof(Telemetry)
@@ -178,6 +183,15 @@ def workspace_reset(device=None):
 def num_workgroups(device=None):
     dev = torch.cuda.current_device() if device is None else int(device)
     g = _lib.mk_num_workgroups(dev)
+    if g < 0:
+        _check(-g)
+    return g
+
+
+def fused_grid(A, B, peers, C):
+    """G of the fused kernel for these tensors (n_reduce_wg must be < G)."""
+    a = _args(A, B, peers, C)
+    g = _lib.mk_fused_grid(a[5], a[6], a[7], a[3], a[8], a[9])
     if g < 0:
         _check(-g)
     return g

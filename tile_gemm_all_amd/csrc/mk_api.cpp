@@ -41,6 +41,7 @@ struct Options {
   int64_t withhold_tile = -1;
   int64_t ctrl_period = 8;
   int64_t tile_shape = mk::SHAPE_AUTO;
+  int64_t flag_scope = 0;
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -209,11 +210,18 @@ mk_status_t validate(const void* A, const void* B, const void* peers, int n_peer
   return MK_OK;
 }
 
-int pick_shape(int64_t M, int64_t N, int cus) {
+// 256x256 tiles (one workgroup per CU) for shapes whose arithmetic intensity is
+// near or above the matrix-core/HBM ridge and that still give every CU a tile;
+// otherwise 128x128 tiles, which let two workgroups share a CU.
+int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
   int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
+  double flops = 2.0 * (double)M * (double)N * (double)K;
+  double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
+                 (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
+  double ai = bytes > 0 ? flops / bytes : 0.0;
+  return (t256 >= cus && ai >= 150.0) ? mk::SHAPE_256 : mk::SHAPE_128;
 }
 
 // Host roofline seed for the controller: the reducers' share of the work when
@@ -233,14 +241,15 @@ struct Launch {
   int64_t tiles_m, tiles_n;
 };
 
-mk_status_t prepare(int64_t M, int64_t N, Launch& L) {
+mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype,
+                    Launch& L) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
   mk_status_t st = device_info(dev, L.info);
   if (st != MK_OK) return st;
   L.dev = dev;
-  L.shape = pick_shape(M, N, L.info.cus);
+  L.shape = pick_shape(M, N, K, n_peers, peer_dtype, c_dtype, L.info.cus);
   L.tiles_m = (M + mk::shape_bm(L.shape) - 1) / mk::shape_bm(L.shape);
   L.tiles_n = (N + mk::shape_bn(L.shape) - 1) / mk::shape_bn(L.shape);
   if (L.tiles_m * L.tiles_n > (1 << 30)) return fail(MK_ERR_UNSUPPORTED, "too many tiles");
@@ -259,7 +268,7 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   if (n_reduce_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d", n_reduce_wg);
   if (((uintptr_t)telemetry) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "telemetry not 16-byte aligned");
   Launch L;
-  st = prepare(M, N, L);
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
   if (st != MK_OK) return st;
   const int G = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
   if (n_reduce_wg > G - 1)
@@ -308,6 +317,11 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   a.ctrl_period = opt.ctrl_period < 1 ? 1 : (int)opt.ctrl_period;
   a.withhold_tile = (int)opt.withhold_tile;
   a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
+  // one XCD per 32 compute units on gfx950; tiles are queued per XCD
+  int n_xcd = L.info.cus / 32;
+  a.n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
+  if (G % a.n_xcd != 0) a.n_xcd = 1;
+  a.flag_scope = (int)opt.flag_scope;
   hipError_t e = mk::launch_fused(L.shape, peer_dtype, c_dtype, a, s);
   if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   return MK_OK;
@@ -319,7 +333,7 @@ mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const voi
   mk_status_t st = validate(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype);
   if (st != MK_OK) return st;
   Launch L;
-  st = prepare(M, N, L);
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
   if (st != MK_OK) return st;
   if (M == 0 || N == 0) return MK_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -407,6 +421,16 @@ int mk_num_workgroups(int device) {
   return d.cus * d.occ[mk::SHAPE_256][MK_DT_BF16][MK_DT_BF16];
 }
 
+int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype) {
+  if (peer_dtype != MK_DT_BF16 && peer_dtype != MK_DT_F32) return -(int)MK_ERR_INVALID_ARG;
+  if (c_dtype != MK_DT_BF16 && c_dtype != MK_DT_F32) return -(int)MK_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0 || n_peers < 0) return -(int)MK_ERR_INVALID_ARG;
+  Launch L;
+  mk_status_t st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  if (st != MK_OK) return -(int)st;
+  return L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+}
+
 mk_status_t mk_set_option(int option, int64_t value) {
   std::lock_guard<std::mutex> lk(g_opt_mu);
   switch (option) {
@@ -425,6 +449,10 @@ mk_status_t mk_set_option(int option, int64_t value) {
       if (value < 0 || value > 2) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
       g_opt.tile_shape = value;
       return MK_OK;
+    case MK_OPT_FLAG_SCOPE:
+      if (value < 0 || value > 1) return fail(MK_ERR_INVALID_ARG, "flag scope %lld", (long long)value);
+      g_opt.flag_scope = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -436,6 +464,7 @@ int64_t mk_get_option(int option) {
     case MK_OPT_WITHHOLD_TILE: return g_opt.withhold_tile;
     case MK_OPT_CTRL_PERIOD: return g_opt.ctrl_period;
     case MK_OPT_TILE_SHAPE: return g_opt.tile_shape;
+    case MK_OPT_FLAG_SCOPE: return g_opt.flag_scope;
   }
   return -1;
 }
@@ -454,6 +483,7 @@ const char* mk_status_string(int status) {
     case MK_ERR_TIMEOUT: return "MK_ERR_TIMEOUT";
     case MK_ERR_NO_DEVICE: return "MK_ERR_NO_DEVICE";
     case MK_ERR_WORKSPACE: return "MK_ERR_WORKSPACE";
+    case MK_ERR_INTERNAL: return "MK_ERR_INTERNAL";
   }
   return "MK_ERR_UNKNOWN";
 }

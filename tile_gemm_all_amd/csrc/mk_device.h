@@ -41,13 +41,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // Constant 100 MHz clock shared by all compute units.
 __device__ __forceinline__ uint64_t ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
-// Readiness flag protocol (Figure 2, item 1: "write completed tiles to GPU
-// memory and set readiness flags"; Table 2's caption: completion of a transfer
-// and visibility in GPU memory are separate requirements). Every thread of the
-// producing workgroup has stored its part of the tile; the barrier orders those
-// stores before thread 0's agent-scope release store of the flag, so a consumer
-// on any XCD that acquires the flag sees the whole tile.
-__device__ __forceinline__ void publish_flag(int* flag, int epoch) {
+// Readiness flags (Figure 2, item 1: compute blocks write completed tiles to GPU
+// memory and set readiness flags; Table 2's caption: completion of a transfer and
+// its visibility in GPU memory are separate requirements).
+//
+// Every tile is produced and consumed by workgroups of the same XCD (tiles are
+// queued per XCD), and the XCD's L2 is the point where all of its compute units
+// see the same data (the per-CU vector L1 is write-through). So:
+//   producer: each wave waits until its partial-tile stores are acknowledged by
+//             the L2 (vmcnt = 0), the workgroup meets at a barrier, then one lane
+//             stores the flag with an agent-scope atomic;
+//   consumer: one lane polls the flag with agent-scope atomic loads, then
+//             invalidates its compute unit's L1 so that the partial is read from
+//             the L2, and the workgroup meets at a barrier.
+// Neither side writes back or invalidates an L2, so other tiles stay cached.
+// The agent-scope variant (L2 writeback on release, L2 invalidate on acquire)
+// is kept for flags produced on another XCD.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void invalidate_l1() {
+  asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ void store_flag(int* flag, int v) {
+  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void publish_flag_agent(int* flag, int epoch) {
   __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -55,33 +75,75 @@ __device__ __forceinline__ int load_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void acquire_fence() {
+__device__ __forceinline__ void acquire_fence_agent() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Hardware id of the XCD this wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return (int)(x & 0xF);
+}
+
+// Sleep for about n * 512 cycles (s_sleep takes an immediate).
+__device__ __forceinline__ void backoff_sleep(int n) {
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
 }
 
 // ----------------------------------------------------------------- tile GEMM
 
-// Tile shape: BM x BN outputs per workgroup, BK = 64 k-values per stage.
-// Four waves in a 2 x 2 arrangement; each wave owns a (BM/2) x (BN/2) block made
-// of 32 x 32 matrix-core blocks (v_mfma_f32_32x32x16_bf16).
-// LDS layout, double-buffered:
-//   As[BM][BK+8]   A tile, k contiguous (row pitch 144 B spreads 16 rows over all banks)
-//   Bs[BK][BN+32]  B tile, n contiguous, read with the gfx950 transposing LDS load
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One 16-byte-per-lane direct load into LDS: lane i's 16 bytes from g land at
+// LDS byte address lds + 16*i (global_load_lds_dwordx4, LDS base in M0).
+// Issued through inline asm so that the compiler does not treat the pending LDS
+// write as aliasing every later LDS read (it would then wait for all
+// outstanding loads before each stage and undo the prefetch). The caller orders
+// the writes with explicit vmcnt waits and barriers; loads complete in issue
+// order, so the compiler's own vmcnt waits stay correct.
+__device__ __forceinline__ void dma16(const void* g, const char* lds) {
+  unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(const lds_char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
+}
+
+// Tile shape: BM x BN outputs per workgroup, BK = 32 k-values per stage, NS = 4
+// stages in LDS (three stages of loads in flight while one is computed: one
+// stage per CU was latency-bound). Four waves in a 2 x 2 arrangement; each wave
+// owns a (BM/2) x (BN/2) block made of 32 x 32 matrix-core blocks
+// (v_mfma_f32_32x32x16_bf16, 32 cycles each).
+//
+// LDS holds the tiles unpadded and XOR-swizzled in 16-byte chunks so that
+// (a) global_load_lds_dwordx4 can fill them (it writes a wave's 64 x 16 bytes to
+//     consecutive LDS addresses; the swizzle is applied on the global side), and
+// (b) the fragment reads hit distinct banks (64 banks of 4 bytes):
+//   A tile [BM][32]: 64-byte rows, chunk c of row r stored at c ^ ((r >> 2) & 3);
+//     a 16-lane phase of ds_read_b128 covers rows r..r+15 of one chunk column.
+//   B tile [32][BN]: chunk c of row k stored at c ^ (4 * (k & 3)); the gfx950
+//     transposing read (ds_read_b64_tr_b16) has 16 lanes read a 4(k) x 16(n) block,
+//     so 32 lanes touch 4 rows x 4 chunks = all 64 banks once.
 template <int BM_, int BN_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = 32, NS = 4;
+  // fused kernel: workgroups per CU, and chunks in flight per reducer lane
+  static constexpr int OCC = BM * BN >= 256 * 256 ? 1 : 2;
+  static constexpr int RDEPTH = OCC == 1 ? 3 : 2;
+  static constexpr int KSTEPS = BK / 16;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int AP = BK + 8;
-  static constexpr int BP = BN + 32;
-  static constexpr int A_ELEMS = BM * AP;
-  static constexpr int B_ELEMS = BK * BP;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;  // bf16 elements per stage
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int A_LD = BM * BK / 8 / kThreads;  // 16-byte chunks per thread
-  static constexpr int B_LD = BK * BN / 8 / kThreads;
-  static_assert(FM >= 1 && FN >= 1, "tile too small");
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
+  static constexpr int A_ROW = BK * 2;              // bytes per A row
+  static constexpr int A_BYTES = BM * A_ROW;
+  static constexpr int B_ROW = BN * 2;              // bytes per B row
+  static constexpr int B_BYTES = BK * B_ROW;
+  static constexpr int STAGE = A_BYTES + B_BYTES;   // bytes per stage
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static constexpr int A_LD = A_BYTES / 1024 / 4;   // 1 KiB direct loads per wave
+  static constexpr int B_LD = B_BYTES / 1024 / 4;
+  static constexpr int LD = A_LD + B_LD;            // direct loads per wave per stage
+  static constexpr int A_ROWS_PER_LD = 1024 / A_ROW;
+  static constexpr int B_ROWS_PER_LD = 1024 / B_ROW;
+  static_assert(FM >= 1 && FN >= 1 && FN <= 4, "tile shape");
+  static_assert(A_LD >= 1 && B_LD >= 1 && B_ROW <= 1024, "tile too small for 4 waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -101,90 +163,172 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 template <class Cfg>
 struct GemmTile {
   f32x16 acc[Cfg::FM][Cfg::FN];
-  u32x4 ra[Cfg::A_LD];
-  u32x4 rb[Cfg::B_LD];
 
-  __device__ __forceinline__ void load_global(const uint16_t* __restrict__ A,
-                                              const uint16_t* __restrict__ B, int64_t M, int64_t N,
-                                              int64_t K, int64_t m0, int64_t n0, int64_t k0,
-                                              int tid) {
+  // Per-lane global element offsets of this wave's 16-byte chunks of a stage,
+  // before the k offset. Rows beyond M and columns beyond N are clamped to the
+  // last valid one: they only feed outputs that are never stored.
+  struct Src {
+    int64_t a[Cfg::A_LD];
+    int64_t b[Cfg::B_LD];
+  };
+
+  __device__ __forceinline__ static void sources(Src& s, int64_t M, int64_t N, int64_t K,
+                                                 int64_t m0, int64_t n0, int wave, int lane) {
 #pragma unroll
-    for (int c = 0; c < Cfg::A_LD; ++c) {
-      int idx = c * kThreads + tid;
-      int row = idx >> 3;  // BK/8 = 8 chunks per row
-      int kc = idx & 7;
-      int64_t gm = m0 + row, gk = k0 + kc * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gm < M && gk < K) v = *(const u32x4*)(A + gm * K + gk);
-      ra[c] = v;
+    for (int i = 0; i < Cfg::A_LD; ++i) {
+      int blk = wave * Cfg::A_LD + i;
+      int byte = lane * 16;
+      int row = blk * Cfg::A_ROWS_PER_LD + byte / Cfg::A_ROW;
+      int p = (byte % Cfg::A_ROW) / 16;
+      int c = p ^ ((row >> 2) & 3);
+      int64_t gm = m0 + row < M ? m0 + row : M - 1;
+      s.a[i] = gm * K + c * 8;
     }
-    constexpr int CPR = Cfg::BN / 8;  // chunks per B row
 #pragma unroll
-    for (int c = 0; c < Cfg::B_LD; ++c) {
-      int idx = c * kThreads + tid;
-      int row = idx / CPR;
-      int nc = idx % CPR;
-      int64_t gk = k0 + row, gn = n0 + nc * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gk < K && gn < N) v = *(const u32x4*)(B + gk * N + gn);
-      rb[c] = v;
+    for (int i = 0; i < Cfg::B_LD; ++i) {
+      int blk = wave * Cfg::B_LD + i;
+      int byte = lane * 16;
+      int row = blk * Cfg::B_ROWS_PER_LD + byte / Cfg::B_ROW;
+      int p = (byte % Cfg::B_ROW) / 16;
+      int c = p ^ (4 * (row & 3));
+      int64_t gn = n0 + c * 8 < N ? n0 + c * 8 : N - 8;
+      s.b[i] = (int64_t)row * N + gn;
     }
   }
 
-  __device__ __forceinline__ void store_lds(uint16_t* stage, int tid) {
-    uint16_t* As = stage;
-    uint16_t* Bs = stage + Cfg::A_ELEMS;
+  // Full k-tile [k0, k0+BK) straight into LDS (no register staging).
+  __device__ __forceinline__ static void load_direct(const Src& s, const uint16_t* __restrict__ A,
+                                                     const uint16_t* __restrict__ B, int64_t N,
+                                                     int64_t k0, char* stage, int wave) {
 #pragma unroll
-    for (int c = 0; c < Cfg::A_LD; ++c) {
-      int idx = c * kThreads + tid;
-      *(u32x4*)(As + (idx >> 3) * Cfg::AP + (idx & 7) * 8) = ra[c];
-    }
-    constexpr int CPR = Cfg::BN / 8;
+    for (int i = 0; i < Cfg::A_LD; ++i)
+      dma16(A + s.a[i] + k0, stage + (wave * Cfg::A_LD + i) * 1024);
 #pragma unroll
-    for (int c = 0; c < Cfg::B_LD; ++c) {
-      int idx = c * kThreads + tid;
-      *(u32x4*)(Bs + (idx / CPR) * Cfg::BP + (idx % CPR) * 8) = rb[c];
-    }
+    for (int i = 0; i < Cfg::B_LD; ++i)
+      dma16(B + s.b[i] + k0 * N, stage + Cfg::A_BYTES + (wave * Cfg::B_LD + i) * 1024);
   }
 
-  // 4 steps of k=16 on one LDS stage.
-  __device__ __forceinline__ void mma_stage(const uint16_t* stage, int wave, int lane) {
-    const uint16_t* As = stage;
-    const uint16_t* Bs = stage + Cfg::A_ELEMS;
+  // Last, partial k-tile: same LDS image, but k >= K reads as zero. Goes through
+  // registers; used at most once per tile, when K is not a multiple of BK.
+  __device__ __forceinline__ static void load_guarded(const Src& s, const uint16_t* __restrict__ A,
+                                                      const uint16_t* __restrict__ B, int64_t N,
+                                                      int64_t K, int64_t k0, char* stage, int wave,
+                                                      int lane) {
+    u32x4 va[Cfg::A_LD], vb[Cfg::B_LD];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LD; ++i) {
+      int byte = lane * 16;
+      int row = (wave * Cfg::A_LD + i) * Cfg::A_ROWS_PER_LD + byte / Cfg::A_ROW;
+      int c = ((byte % Cfg::A_ROW) / 16) ^ ((row >> 2) & 3);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (k0 + c * 8 < K) v = *(const u32x4*)(A + s.a[i] + k0);
+      va[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LD; ++i) {
+      int row = (wave * Cfg::B_LD + i) * Cfg::B_ROWS_PER_LD + (lane * 16) / Cfg::B_ROW;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (k0 + row < K) v = *(const u32x4*)(B + s.b[i] + k0 * N);
+      vb[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LD; ++i)
+      *(u32x4*)(stage + (wave * Cfg::A_LD + i) * 1024 + lane * 16) = va[i];
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LD; ++i)
+      *(u32x4*)(stage + Cfg::A_BYTES + (wave * Cfg::B_LD + i) * 1024 + lane * 16) = vb[i];
+  }
+
+  // Fragment addresses within a stage (bytes), per lane.
+  struct Frag {
+    int a[Cfg::KSTEPS];    // A offset for step kk (row and swizzled chunk)
+    int b[Cfg::FN];        // B offset for step 0, low half (step kk adds 16 rows)
+  };
+
+  __device__ __forceinline__ static void frag_offsets(Frag& f, int wave, int lane) {
     const int wm = wave >> 1, wn = wave & 1;
-    const int arow = wm * Cfg::WM + (lane & 31);
-    const int akof = (lane >> 5) * 8;
-    // transposing read: 16-lane group g reads a 4(k) x 16(n) block per instruction;
-    // lane r of the group supplies row r/4, columns 4*(r%4) .. +3.
+    const int arow = wm * Cfg::WM + (lane & 31);  // + 32*fm keeps (row >> 2) & 3
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+      int c = 2 * kk + (lane >> 5);
+      f.a[kk] = arow * Cfg::A_ROW + ((c ^ ((arow >> 2) & 3)) * 16);
+    }
     const int g = lane >> 4, r = lane & 15;
-    const int bk = (g >> 1) * 8 + (r >> 2);
-    const int bn = wn * Cfg::WN + (g & 1) * 16 + 4 * (r & 3);
+    const int brow = (g >> 1) * 8 + (r >> 2);  // + 16*kk (+4 for the high half)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[Cfg::FM], b[Cfg::FN];
-#pragma unroll
-      for (int fm = 0; fm < Cfg::FM; ++fm)
-        a[fm] = *(const bf16x8*)(As + (arow + fm * 32) * Cfg::AP + kk * 16 + akof);
-#pragma unroll
-      for (int fn = 0; fn < Cfg::FN; ++fn) {
-        const uint16_t* p = Bs + (kk * 16 + bk) * Cfg::BP + bn + fn * 32;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * Cfg::BP));
-        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        b[fn] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int fm = 0; fm < Cfg::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < Cfg::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    for (int fn = 0; fn < Cfg::FN; ++fn) {
+      int c = (wn * Cfg::WN + fn * 32) / 8 + (g & 1) * 2 + ((r & 3) >> 1);
+      int p = c ^ (4 * (brow & 3));
+      f.b[fn] = Cfg::A_BYTES + brow * Cfg::B_ROW + p * 16 + (r & 1) * 8;
     }
   }
 
-  // Full K loop of one tile; lds holds two stages of Cfg::STAGE elements.
+  __device__ __forceinline__ static void read_frags(const char* stage, const Frag& f, int kk,
+                                                    bf16x8 (&a)[Cfg::FM], bf16x8 (&b)[Cfg::FN]) {
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+      a[fm] = *(const bf16x8*)(stage + f.a[kk] + fm * 32 * Cfg::A_ROW);
+#pragma unroll
+    for (int fn = 0; fn < Cfg::FN; ++fn) {
+      const char* p = stage + f.b[fn] + kk * 16 * Cfg::B_ROW;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * Cfg::B_ROW));
+      b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+
+  __device__ __forceinline__ void mma(const bf16x8 (&a)[Cfg::FM], const bf16x8 (&b)[Cfg::FN]) {
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < Cfg::FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+  }
+
+  // NM MFMAs, each followed by up to RPM of the LEFT remaining LDS reads.
+  template <int NM, int RPM, int LEFT>
+  __device__ __forceinline__ static void interleave() {
+    if constexpr (NM > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int n = LEFT < RPM ? LEFT : RPM;
+      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+      interleave<NM - 1, RPM, LEFT - n>();
+    }
+  }
+
+  // One stage: KSTEPS steps of k = 16. The fragments of step kk+1 are read from
+  // LDS while the matrix cores work on step kk; each step is its own scheduling
+  // region (its MFMAs are independent of each other) and the group barriers pin
+  // one LDS read between consecutive MFMAs, so LDS latency hides behind MFMAs.
+  __device__ __forceinline__ void compute_stage(const char* stage, const Frag& f) {
+    constexpr int NR = Cfg::FM + 2 * Cfg::FN;  // LDS reads per step
+    constexpr int NM = Cfg::FM * Cfg::FN;      // MFMAs per step
+    constexpr int RPM = (NR + NM - 1) / NM;
+    bf16x8 a[2][Cfg::FM], b[2][Cfg::FN];
+    read_frags(stage, f, 0, a[0], b[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+      if (kk + 1 < Cfg::KSTEPS) read_frags(stage, f, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+      mma(a[kk & 1], b[kk & 1]);
+      if (kk + 1 < Cfg::KSTEPS) interleave<NM, RPM, NR>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Wait until at most n of this wave's loads are outstanding (n is 0 .. 2*LD).
+  __device__ __forceinline__ static void wait_loads(int n) {
+    if (n >= 2 * Cfg::LD) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * Cfg::LD) : "memory");
+    else if (n >= Cfg::LD) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(Cfg::LD) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // Full K loop of one tile. Stage kt lives in LDS slot kt % NS; loads for
+  // stages kt+1 .. kt+NS-1 are in flight while stage kt is computed.
   __device__ __forceinline__ void run(const uint16_t* __restrict__ A,
                                       const uint16_t* __restrict__ B, int64_t M, int64_t N,
-                                      int64_t K, int64_t m0, int64_t n0, uint16_t* lds) {
+                                      int64_t K, int64_t m0, int64_t n0, char* lds) {
+    static_assert(Cfg::NS == 4, "wait_loads assumes up to two later stages in flight");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int fm = 0; fm < Cfg::FM; ++fm)
@@ -194,18 +338,33 @@ struct GemmTile {
         for (int i = 0; i < 16; ++i) acc[fm][fn][i] = 0.0f;
     const int KT = (int)((K + Cfg::BK - 1) / Cfg::BK);
     if (KT == 0) return;
-    load_global(A, B, M, N, K, m0, n0, 0, tid);
-    store_lds(lds, tid);
-    __syncthreads();
+    const int KF = (int)(K / Cfg::BK);  // full k-tiles; tile KF (if < KT) is partial
+    Src s;
+    sources(s, M, N, K, m0, n0, wave, lane);
+    Frag f;
+    frag_offsets(f, wave, lane);
+    // Prologue: stages 0 .. NS-2. The partial tile, if any, is the last stage
+    // and is loaded through registers when its turn comes.
+#pragma unroll
+    for (int j = 0; j < Cfg::NS - 1; ++j)
+      if (j < KF) load_direct(s, A, B, N, (int64_t)j * Cfg::BK, lds + j * Cfg::STAGE, wave);
     for (int kt = 0; kt < KT; ++kt) {
-      uint16_t* cur = lds + (kt & 1) * Cfg::STAGE;
-      uint16_t* nxt = lds + ((kt + 1) & 1) * Cfg::STAGE;
-      const bool more = kt + 1 < KT;
-      if (more) load_global(A, B, M, N, K, m0, n0, (int64_t)(kt + 1) * Cfg::BK, tid);
-      mma_stage(cur, wave, lane);
-      if (more) store_lds(nxt, tid);
-      __syncthreads();
+      char* cur = lds + (kt % Cfg::NS) * Cfg::STAGE;
+      if (kt == KF) {
+        // partial tile: loaded now (the slot was freed by the previous barrier)
+        load_guarded(s, A, B, N, K, (int64_t)kt * Cfg::BK, cur, wave, lane);
+      } else {
+        // direct loads of the full stages after kt that are already issued
+        int later = KF - 1 - kt;
+        later = later < Cfg::NS - 2 ? later : Cfg::NS - 2;
+        wait_loads(later * Cfg::LD);
+      }
+      __syncthreads();  // stage kt complete in LDS; slot (kt-1) % NS is free
+      const int kn = kt + Cfg::NS - 1;
+      if (kn < KF) load_direct(s, A, B, N, (int64_t)kn * Cfg::BK, lds + (kn % Cfg::NS) * Cfg::STAGE, wave);
+      compute_stage(cur, f);
     }
+    __syncthreads();  // every wave is done with LDS before it is reused
   }
 
   // Store the fp32 tile into P[M][N] (row-major). Accumulator layout of the
@@ -322,9 +481,98 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
   for (int c = 0; c < CH; ++c) store_c<CT>(C, e[c], acc[c]);
 }
 
+// One chunk of 8 elements in flight: up to SLOTS peer loads. The fp32 partial
+// is read when the chunk is summed (it was just written by a compute unit of
+// the same XCD, so it comes from the L2), which keeps registers for peers.
+template <typename PT>
+struct ChunkLoads {
+  static constexpr int SLOTS = sizeof(PT) == 2 ? 16 : 8;  // 16-byte loads per peer slot: 1 (bf16) or 2 (fp32)
+  PeerLoad<PT> v[SLOTS];
+  __device__ __forceinline__ void load(const PT* __restrict__ peers, int n_peers, int64_t peer_stride,
+                                       int64_t e) {
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      int p = s < n_peers ? s : n_peers - 1;  // past the last peer: re-read it, never added
+      if (n_peers > 0) v[s].load(peers + (int64_t)p * peer_stride, e);
+    }
+  }
+  template <typename CT>
+  __device__ __forceinline__ void finish(const float* __restrict__ P, int n_peers,
+                                         CT* __restrict__ C, int64_t e) const {
+    f32x4 pa = *(const f32x4*)(P + e);
+    f32x4 pb = *(const f32x4*)(P + e + 4);
+    float acc[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+      if (s < n_peers) v[s].add_to(acc);
+    store_c<CT>(C, e, acc);
+  }
+};
+
 // Reduce the region rows [m0, m0+rows) x cols [n0, n0+cols) of an M x N output;
-// cols is a multiple of 8. All 256 threads of the workgroup take part.
-template <typename PT, typename CT>
+// cols is a multiple of 8. All 256 threads of the workgroup take part; thread t
+// handles chunks t, t+256, ... For up to SLOTS peers the loads of the next
+// DEPTH-1 chunks are in flight while the current chunk is summed, which keeps a
+// single workgroup's share of HBM bandwidth high (it is the only reducer on its
+// compute unit, so latency has to be covered by loads in flight, not by waves).
+template <int DEPTH, typename PT>
+struct ReduceRing;
+
+template <typename PT>
+struct ReduceRing<2, PT> {
+  template <typename CT, typename Off>
+  __device__ __forceinline__ static void run(const float* __restrict__ P,
+                                             const PT* __restrict__ peers, int n_peers,
+                                             int64_t stride, CT* __restrict__ C, int total, Off off) {
+    int q = threadIdx.x;
+    if (q >= total) return;
+    ChunkLoads<PT> x, y;
+    x.load(peers, n_peers, stride, off(q));
+    for (;;) {
+      const int q1 = q + kThreads;
+      if (q1 < total) y.load(peers, n_peers, stride, off(q1));
+      x.finish(P, n_peers, C, off(q));
+      if (q1 >= total) break;
+      const int q2 = q1 + kThreads;
+      if (q2 < total) x.load(peers, n_peers, stride, off(q2));
+      y.finish(P, n_peers, C, off(q1));
+      if (q2 >= total) break;
+      q = q2;
+    }
+  }
+};
+
+template <typename PT>
+struct ReduceRing<3, PT> {
+  template <typename CT, typename Off>
+  __device__ __forceinline__ static void run(const float* __restrict__ P,
+                                             const PT* __restrict__ peers, int n_peers,
+                                             int64_t stride, CT* __restrict__ C, int total, Off off) {
+    int q = threadIdx.x;
+    if (q >= total) return;
+    ChunkLoads<PT> x, y, z;
+    x.load(peers, n_peers, stride, off(q));
+    if (q + kThreads < total) y.load(peers, n_peers, stride, off(q + kThreads));
+    for (;;) {
+      // invariant: chunks q (in x) and q+256 (in y, if it exists) are loading
+      const int q1 = q + kThreads, q2 = q + 2 * kThreads;
+      if (q2 < total) z.load(peers, n_peers, stride, off(q2));
+      x.finish(P, n_peers, C, off(q));
+      if (q1 >= total) break;
+      const int q3 = q + 3 * kThreads;
+      if (q3 < total) x.load(peers, n_peers, stride, off(q3));
+      y.finish(P, n_peers, C, off(q1));
+      if (q2 >= total) break;
+      const int q4 = q + 4 * kThreads;
+      if (q4 < total) y.load(peers, n_peers, stride, off(q4));
+      z.finish(P, n_peers, C, off(q2));
+      if (q3 >= total) break;
+      q = q3;
+    }
+  }
+};
+
+template <int DEPTH, typename PT, typename CT>
 __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
                                               const PT* __restrict__ peers, int n_peers,
                                               CT* __restrict__ C, int64_t M, int64_t N, int64_t m0,
@@ -332,19 +580,21 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
   const int cpr = cols >> 3;
   const int total = rows * cpr;
   const int64_t stride = M * N;
+  auto off = [&](int q) { return (m0 + q / cpr) * N + n0 + (q % cpr) * 8; };
+  if (n_peers <= ChunkLoads<PT>::SLOTS) {
+    ReduceRing<DEPTH, PT>::template run<CT>(P, peers, n_peers, stride, C, total, off);
+    return;
+  }
   constexpr int CH = 2;
   int q = threadIdx.x;
   for (; q + (CH - 1) * kThreads < total; q += CH * kThreads) {
     int64_t e[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      int qq = q + c * kThreads;
-      e[c] = (m0 + qq / cpr) * N + n0 + (qq % cpr) * 8;
-    }
+    for (int c = 0; c < CH; ++c) e[c] = off(q + c * kThreads);
     reduce_chunks<CH, PT, CT>(P, peers, n_peers, stride, C, e);
   }
   for (; q < total; q += kThreads) {
-    int64_t e[1] = {(m0 + q / cpr) * N + n0 + (q % cpr) * 8};
+    int64_t e[1] = {off(q)};
     reduce_chunks<1, PT, CT>(P, peers, n_peers, stride, C, e);
   }
 }

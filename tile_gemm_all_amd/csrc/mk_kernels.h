@@ -10,10 +10,8 @@ namespace mk {
 
 // Workspace control words, each on its own 128-byte line (kSlotWords 64-bit words).
 enum Slot : int {
-  S_COMPUTE_NEXT = 0,  // next GEMM tile to claim
-  S_REDUCE_NEXT,       // next tile to reduce
-  S_COMPUTED,          // tiles published
-  S_REDUCED,           // tiles reduced
+  S_COMPUTED = 0,      // tiles published (all XCDs)
+  S_REDUCED,           // tiles reduced (all XCDs)
   S_EXIT,              // workgroups that have left the persistent loop
   S_ERROR,             // device error word (mk_status_t), kept across calls
   S_ABORT,             // set on error: every workgroup leaves its loop
@@ -24,12 +22,17 @@ enum Slot : int {
   S_WAIT_R,            // summed flag-wait ticks
   S_UPDATES,           // controller target changes
   S_SWITCHES,          // workgroup role changes
-  S_RBC,               // tiles reduced by workgroups of the compute role (draining)
+  S_RBC,               // tiles reduced by workgroups that prefer compute (draining)
+  S_CBR,               // tiles computed by workgroups that prefer reducing (helping)
   S_NTRACE,            // controller trace entries written
   S_TSTART,            // min start tick
   S_TEND,              // max exit tick
-  S_COUNT
+  S_XCD_BASE,          // per-XCD words follow: kXcdWords per XCD
+  S_COUNT = S_XCD_BASE + 3 * 16
 };
+// Per-XCD words, at S_XCD_BASE + 3 * xcd + {0, 1, 2}.
+enum XcdSlot : int { X_COMPUTE_NEXT = 0, X_REDUCE_NEXT = 1, X_ARRIVE = 2, kXcdWords = 3 };
+constexpr int kMaxXcd = 16;
 constexpr int kSlotWords = 16;
 constexpr int kThreadsHost = 256;  // workgroup size of every kernel
 
@@ -53,6 +56,8 @@ struct FusedArgs {
   float seed_x;                // controller seed share
   int ctrl_period;
   int withhold_tile;           // debug: -1 = off
+  int n_xcd;                   // XCDs of the device; tiles are queued per XCD
+  int flag_scope;              // 0: producer and consumer share an XCD's L2; 1: agent scope
   int pad_;
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
 };

@@ -70,59 +70,97 @@ __device__ void controller_step(const FusedArgs& a) {
 
 enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
 
+__device__ __forceinline__ int* xslot(unsigned long long* s, int x, int w) {
+  return slot32(s, S_XCD_BASE + x * kXcdWords + w);
+}
+
+// Claims the next GEMM tile of this XCD's queue; returns its local index or -1.
+__device__ __forceinline__ int claim_compute(unsigned long long* S, int x, int cnt) {
+  int* next = xslot(S, x, X_COMPUTE_NEXT);
+  if (load_relaxed(next) >= cnt) return -1;
+  int i = atomicAdd(next, 1);
+  return i < cnt ? i : -1;
+}
+
+// Persistent fused kernel. Tiles [start_x, start_x + cnt_x) belong to XCD x: only
+// workgroups running on XCD x compute or reduce them, so a tile's partial is
+// produced and consumed behind the same L2. In each XCD, workgroups whose
+// arrival rank is below that XCD's share of the reducer target prefer reducing;
+// the others prefer computing. A workgroup with nothing to do in its preferred
+// role takes work of the other role (reducers help compute while no tile is
+// ready; compute workgroups drain the reduce queue when no GEMM tile is left).
 template <class Cfg, typename PT, typename CT>
-__global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
-  __shared__ __align__(16) uint16_t lds[2 * Cfg::STAGE];
+__global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) {
+  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
   __shared__ int s_kind, s_tile, s_ok;
   const int tid = threadIdx.x;
-  const int wg = blockIdx.x;
   unsigned long long* S = a.slots;
   const PT* peers = (const PT*)a.peers;
   CT* C = (CT*)a.C;
   const unsigned long long t_begin = ticks();
-  int last_kind = -1;  // thread 0 only
-  GemmTile<Cfg> g;
+
+  // thread 0 state
+  const int x = xcc_id() % a.n_xcd;
+  const int q0 = (int)(((int64_t)x * a.T) / a.n_xcd);
+  const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
+  int rank = 0, last_kind = -1;
+  if (tid == 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
 
   for (;;) {
-    // ---- thread 0 picks the next task (role from the published target)
     if (tid == 0) {
       int kind = K_EXIT, tile = -1;
-      bool draining = false;
+      bool off_role = false;
       const unsigned long long w0 = ticks();
+      int backoff = 1;
       for (;;) {
         if (load_relaxed(slot32(S, S_ABORT))) break;
-        const bool reducer = wg < current_target(a);
-        if (!reducer && load_relaxed(slot32(S, S_COMPUTE_NEXT)) < a.T) {
-          int t = atomicAdd(slot32(S, S_COMPUTE_NEXT), 1);
-          if (t < a.T) {
+        const int target = current_target(a);
+        const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
+        const bool pref_reduce = rank < tx;
+        if (!pref_reduce) {
+          int i = claim_compute(S, x, cnt);
+          if (i >= 0) {
             kind = K_COMPUTE;
-            tile = t;
+            tile = q0 + i;
             break;
           }
         }
-        // Reduce: claim only tiles a compute workgroup has already claimed, so a
-        // reducer never waits on a tile nobody is producing.
-        int r = load_relaxed(slot32(S, S_REDUCE_NEXT));
-        if (r >= a.T) break;
-        int c = load_relaxed(slot32(S, S_COMPUTE_NEXT));
+        // Reduce: only tiles that a compute workgroup has claimed (it is running,
+        // so its flag will be set).
+        int* rnext = xslot(S, x, X_REDUCE_NEXT);
+        int r = load_relaxed(rnext);
+        if (r >= cnt) break;  // this XCD's work is all claimed: leave
+        int c = load_relaxed(xslot(S, x, X_COMPUTE_NEXT));
         if (r < c) {
-          if (atomicCAS(slot32(S, S_REDUCE_NEXT), r, r + 1) == r) {
+          if (atomicCAS(rnext, r, r + 1) == r) {
             kind = K_REDUCE;
-            tile = r;
-            draining = !reducer;
+            tile = q0 + r;
+            off_role = !pref_reduce;
             break;
           }
           continue;
+        }
+        if (pref_reduce) {
+          int i = claim_compute(S, x, cnt);
+          if (i >= 0) {
+            kind = K_COMPUTE;
+            tile = q0 + i;
+            off_role = true;
+            break;
+          }
         }
         if (ticks() - w0 > a.spin_limit) {
           raise_error(S, MK_ERR_TIMEOUT);
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        backoff_sleep(backoff);
+        backoff = backoff < 8 ? backoff * 2 : 8;
       }
-      if (kind != K_EXIT && last_kind >= 0 && kind != last_kind) atomicAdd(slot32(S, S_SWITCHES), 1);
-      if (kind != K_EXIT) last_kind = kind;
-      if (draining) atomicAdd(slot32(S, S_RBC), 1);
+      if (kind != K_EXIT) {
+        if (last_kind >= 0 && kind != last_kind) atomicAdd(slot32(S, S_SWITCHES), 1);
+        last_kind = kind;
+        if (off_role) atomicAdd(slot32(S, kind == K_REDUCE ? S_RBC : S_CBR), 1);
+      }
       s_kind = kind;
       s_tile = tile;
     }
@@ -135,11 +173,16 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
 
     if (kind == K_COMPUTE) {
       const unsigned long long t0 = ticks();
+      GemmTile<Cfg> g;
       g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
       g.store_partial(a.P, a.M, a.N, m0, n0);
-      __syncthreads();  // every wave's partial stores precede the flag
+      wait_stores();    // this wave's partial stores have reached the L2
+      __syncthreads();  // ... and so have every other wave's
       if (tid == 0) {
-        if (tile != a.withhold_tile) publish_flag(a.flags + tile, a.epoch);
+        if (tile != a.withhold_tile) {
+          if (a.flag_scope == 0) store_flag(a.flags + tile, a.epoch);
+          else publish_flag_agent(a.flags + tile, a.epoch);
+        }
         int done = atomicAdd(slot32(S, S_COMPUTED), 1) + 1;
         atomicAdd(slot64(S, S_BUSY_C), ticks() - t0);
         if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(a);
@@ -147,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
     } else {
       if (tid == 0) {
         const unsigned long long w0 = ticks();
-        int ok = 1;
+        int ok = 1, backoff = 1;
         while (load_relaxed(a.flags + tile) != a.epoch) {
           if (load_relaxed(slot32(S, S_ABORT))) {
             ok = 0;
@@ -158,9 +201,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
             ok = 0;
             break;
           }
-          __builtin_amdgcn_s_sleep(1);
+          backoff_sleep(backoff);
+          backoff = backoff < 4 ? backoff * 2 : 4;
         }
-        acquire_fence();
+        if (a.flag_scope == 0) invalidate_l1();
+        else acquire_fence_agent();
         atomicAdd(slot64(S, S_WAIT_R), ticks() - w0);
         s_ok = ok;
       }
@@ -169,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
       const unsigned long long t0 = ticks();
       const int rows = (int)(a.M - m0 < Cfg::BM ? a.M - m0 : Cfg::BM);
       const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
-      reduce_region<PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, m0, n0, rows, cols);
+      reduce_region<Cfg::RDEPTH, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, m0, n0, rows, cols);
       __syncthreads();
       if (tid == 0) {
         int done = atomicAdd(slot32(S, S_REDUCED), 1) + 1;
@@ -187,6 +232,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
     int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_ACQ_REL,
                                      __HIP_MEMORY_SCOPE_AGENT);
     if (out == a.G - 1) {
+      // Every tile must have been reduced unless an error stopped the kernel
+      // (e.g. an XCD on which no workgroup ran would leave its queue behind).
+      if (!*slot32(S, S_ABORT) && *slot32(S, S_REDUCED) != a.T) atomicCAS(slot32(S, S_ERROR), 0, MK_ERR_INTERNAL);
       if (a.tel) {
         mk_telemetry_t* t = a.tel;
         t->t_start = *slot64(S, S_TSTART);
@@ -203,13 +251,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
         t->n_trace = nt < MK_TRACE_CAP ? nt : MK_TRACE_CAP;
         t->role_switches = *slot32(S, S_SWITCHES);
         t->reduced_by_compute = *slot32(S, S_RBC);
+        t->computed_by_reducers = *slot32(S, S_CBR);
+        t->n_xcd = a.n_xcd;
       }
-      const int zero_slots[] = {S_COMPUTE_NEXT, S_REDUCE_NEXT, S_COMPUTED, S_REDUCED, S_EXIT,
-                                S_ABORT,        S_LOCK,        S_BUSY_C,   S_BUSY_R,  S_WAIT_R,
-                                S_UPDATES,      S_SWITCHES,    S_RBC,      S_NTRACE,  S_TEND};
-      for (int i : zero_slots)
-        __hip_atomic_store(slot64(S, i), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(slot64(S, S_TSTART), ~0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < S_COUNT; ++i) {
+        if (i == S_ERROR || i == S_TARGET) continue;
+        __hip_atomic_store(slot64(S, i), i == S_TSTART ? ~0ull : 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -218,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
 
 template <class Cfg>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t lds[2 * Cfg::STAGE];
+  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
   int tm, tn;
   tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
