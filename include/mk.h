@@ -163,7 +163,8 @@ typedef enum {
   MK_OPT_WITHHOLD_TILE = 1,     /* debug: compute skips publishing this tile (-1 = off) */
   MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
   MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
-  MK_OPT_FLAG_SCOPE = 4         /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
+  MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
+  MK_OPT_REDUCER_CAP = 5        /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);
@@ -175,9 +176,10 @@ int64_t mk_get_option(int option);
  *   busy_c   summed compute-tile time; busy_r summed reduce time without waits
  *   seed_x   the host's initial reducer fraction in [0,1]
  *   current  the target now in force
+ *   cap      most reducers while GEMM tiles remain (<= 0: G-1)
  * Returns the new target. */
 int mk_controller_eval(int G, int T, int computed, int reduced, uint64_t busy_c,
-                       uint64_t busy_r, float seed_x, int current);
+                       uint64_t busy_r, float seed_x, int current, int cap);
 
 const char* mk_status_string(int status);
 const char* mk_last_error(void);

@@ -124,3 +124,13 @@ def test_waiting_does_not_count_as_reduce_time():
     a = ev(1000, 200, 100, 200 * 100, 100 * 20, 0.5, 64)
     b = ev(1000, 200, 100, 200 * 100, 100 * 200, 0.5, 64)
     assert a < b
+
+
+def test_cap_limits_reducers_while_compute_remains():
+    # HBM-bound: the rate rule alone would hand almost everything to reducers
+    free = ev(2048, 500, 400, 500 * 30, 400 * 90, 0.9, 128)
+    capped = mk.controller_eval(G, 2048, 500, 400, 500 * 30, 400 * 90, 0.9, 128, 64)
+    assert free > 64
+    assert capped == 64
+    # once every tile is computed, the cap no longer applies
+    assert mk.controller_eval(G, 2048, 2048, 1900, 1, 1, 0.9, 64, 64) == G

@@ -30,7 +30,7 @@ MK_ADAPTIVE = -1
 MK_MAX_PEERS = 64
 MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
-OPT_FLAG_SCOPE = 4
+OPT_FLAG_SCOPE, OPT_REDUCER_CAP = 4, 5
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
@@ -69,7 +69,7 @@ _lib.mk_set_option.restype = _int
 _lib.mk_get_option.argtypes = [_int]
 _lib.mk_get_option.restype = _i64
 _lib.mk_controller_eval.argtypes = [_int, _int, _int, _int, ctypes.c_uint64, ctypes.c_uint64,
-                                    ctypes.c_float, _int]
+                                    ctypes.c_float, _int, _int]
 _lib.mk_controller_eval.restype = _int
 _lib.mk_status_string.argtypes = [_int]
 _lib.mk_status_string.restype = ctypes.c_char_p
@@ -205,8 +205,9 @@ def get_option(option):
     return int(_lib.mk_get_option(int(option)))
 
 
-def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current):
-    return int(_lib.mk_controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current))
+def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap=0):
+    return int(_lib.mk_controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current,
+                                       cap))
 
 
 def read_telemetry(buf):

@@ -42,6 +42,7 @@ struct Options {
   int64_t ctrl_period = 8;
   int64_t tile_shape = mk::SHAPE_AUTO;
   int64_t flag_scope = 0;
+  int64_t reducer_cap = 0;  // 0: derived from HBM bandwidth and a reducer's streaming rate
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -210,9 +211,9 @@ mk_status_t validate(const void* A, const void* B, const void* peers, int n_peer
   return MK_OK;
 }
 
-// 256x256 tiles (one workgroup per CU) for shapes whose arithmetic intensity is
-// near or above the matrix-core/HBM ridge and that still give every CU a tile;
-// otherwise 128x128 tiles, which let two workgroups share a CU.
+// 256x256 tiles (one workgroup per CU) whenever they still give every CU a
+// tile: they need less L2 traffic per flop and their reducers keep three chunks
+// in flight. Otherwise 128x128 tiles (two workgroups per CU).
 int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
@@ -221,7 +222,8 @@ int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int
   double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
                  (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
   double ai = bytes > 0 ? flops / bytes : 0.0;
-  return (t256 >= cus && ai >= 150.0) ? mk::SHAPE_256 : mk::SHAPE_128;
+  (void)ai;
+  return t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
 }
 
 // Host roofline seed for the controller: the reducers' share of the work when
@@ -322,6 +324,15 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   a.n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
   if (G % a.n_xcd != 0) a.n_xcd = 1;
   a.flag_scope = (int)opt.flag_scope;
+  a.reducer_cap = (int)opt.reducer_cap;
+  if (a.reducer_cap <= 0) {
+    // reducers that saturate HBM: about 5.5 TB/s sustained over about 85 GB/s
+    // streamed by one reducer workgroup; a multiple of the XCD count
+    int cap = (int)ceil(5.5e12 / 85e9);
+    cap = (cap + a.n_xcd - 1) / a.n_xcd * a.n_xcd;
+    a.reducer_cap = cap < G - 1 ? cap : G - 1;
+  }
+  if (a.adaptive && a.init_target > a.reducer_cap) a.init_target = a.reducer_cap < 1 ? 1 : a.reducer_cap;
   hipError_t e = mk::launch_fused(L.shape, peer_dtype, c_dtype, a, s);
   if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   return MK_OK;
@@ -453,6 +464,10 @@ mk_status_t mk_set_option(int option, int64_t value) {
       if (value < 0 || value > 1) return fail(MK_ERR_INVALID_ARG, "flag scope %lld", (long long)value);
       g_opt.flag_scope = value;
       return MK_OK;
+    case MK_OPT_REDUCER_CAP:
+      if (value < 0) return fail(MK_ERR_INVALID_ARG, "reducer cap %lld", (long long)value);
+      g_opt.reducer_cap = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -465,13 +480,14 @@ int64_t mk_get_option(int option) {
     case MK_OPT_CTRL_PERIOD: return g_opt.ctrl_period;
     case MK_OPT_TILE_SHAPE: return g_opt.tile_shape;
     case MK_OPT_FLAG_SCOPE: return g_opt.flag_scope;
+    case MK_OPT_REDUCER_CAP: return g_opt.reducer_cap;
   }
   return -1;
 }
 
 int mk_controller_eval(int G, int T, int computed, int reduced, uint64_t busy_c, uint64_t busy_r,
-                       float seed_x, int current) {
-  return mk::controller_rule(G, T, computed, reduced, busy_c, busy_r, seed_x, current);
+                       float seed_x, int current, int cap) {
+  return mk::controller_rule(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap);
 }
 
 const char* mk_status_string(int status) {

@@ -19,6 +19,13 @@
 // the reducers hold the share x of the workgroups. Until both rates have been
 // measured, x is the host's seed (roofline estimate). A change smaller than
 // max(1, G/64) is ignored (hysteresis).
+//
+// The reduce is a stream from HBM: past the number of reducers that saturates
+// HBM bandwidth (`cap`), more reducers do not reduce faster, they only take
+// compute units away from the GEMM, and the per-workgroup rate rho_r that the
+// rule sees drops because the stream is shared. While compute remains the
+// target is therefore limited to `cap` (the host derives it from HBM bandwidth
+// over one reducer workgroup's streaming rate).
 #pragma once
 #include <stdint.h>
 
@@ -31,7 +38,7 @@
 namespace mk {
 
 MK_HD inline int controller_rule(int G, int T, int computed, int reduced, uint64_t busy_c,
-                                 uint64_t busy_r, float seed_x, int current) {
+                                 uint64_t busy_r, float seed_x, int current, int cap) {
   if (G <= 1) return G <= 0 ? 0 : current;
   if (computed >= T) return G;
   float x = seed_x;
@@ -44,12 +51,13 @@ MK_HD inline int controller_rule(int G, int T, int computed, int reduced, uint64
   if (!(x >= 0.0f)) x = 0.0f;  // also catches NaN
   if (x > 1.0f) x = 1.0f;
   int target = (int)(x * (float)G + 0.5f);
+  int hi = cap >= 1 && cap < G - 1 ? cap : G - 1;
+  if (target > hi) target = hi;
   if (target < 1) target = 1;
-  if (target > G - 1) target = G - 1;
   int band = G / 64 > 1 ? G / 64 : 1;
   int d = target - current;
   if (d < 0) d = -d;
-  if (current >= 1 && current <= G - 1 && d < band) return current;
+  if (current >= 1 && current <= hi && d < band) return current;
   return target;
 }
 

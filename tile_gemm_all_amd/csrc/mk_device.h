@@ -29,11 +29,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // float -> bfloat16 bits, round to nearest even; NaN stays a (quiet) NaN.
+// Branch-free (a select), so it never splits the surrounding code into blocks.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? quiet : rounded;
 }
 
 // ----------------------------------------------------------------- timers, flags
@@ -396,9 +397,11 @@ struct PeerLoad;
 template <>
 struct PeerLoad<uint16_t> {  // bfloat16 peers: one 16-byte load
   u32x4 v;
-  __device__ __forceinline__ void load(const uint16_t* p, int64_t e) {
-    v = __builtin_nontemporal_load((const u32x4*)(p + e));
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v = __builtin_nontemporal_load((const u32x4*)p);
   }
+  // acc[j] += peer[j], j = 0..7: widen each bfloat16 half exactly, then one
+  // correctly rounded fp32 add (the sum order every path shares).
   __device__ __forceinline__ void add_to(float* acc) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -410,9 +413,9 @@ struct PeerLoad<uint16_t> {  // bfloat16 peers: one 16-byte load
 template <>
 struct PeerLoad<float> {  // float32 peers: two 16-byte loads
   f32x4 a, b;
-  __device__ __forceinline__ void load(const float* p, int64_t e) {
-    a = __builtin_nontemporal_load((const f32x4*)(p + e));
-    b = __builtin_nontemporal_load((const f32x4*)(p + e + 4));
+  __device__ __forceinline__ void load(const float* p) {
+    a = __builtin_nontemporal_load((const f32x4*)p);
+    b = __builtin_nontemporal_load((const f32x4*)(p + 4));
   }
   __device__ __forceinline__ void add_to(float* acc) const {
 #pragma unroll
@@ -440,10 +443,13 @@ __device__ __forceinline__ void store_c<float>(float* C, int64_t e, const float*
   __builtin_nontemporal_store(b, (f32x4*)(C + e + 4));
 }
 
-// Sum for CH chunks of 8 elements at element offsets e[0..CH-1]:
-//   C = (((P + peer_0) + peer_1) + ... + peer_{n-1}), float32, then rounded once.
-// Peers are fetched in batches of 8 (indices past the last peer re-read the last
-// peer and are not added), so that many loads are in flight before the adds.
+// Every path sums the same way, element by element:
+//   C = round(((P + peer_0) + peer_1) + ... + peer_{n-1}) in float32,
+// so all reducer counts, the controller and the two-kernel baseline give the
+// same bits.
+
+// Generic path (any peer count): CH chunks of 8 elements at offsets e[], peers
+// fetched in batches of 8 so that many loads are in flight before the adds.
 template <int CH, typename PT, typename CT>
 __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
                                               const PT* __restrict__ peers, int n_peers,
@@ -465,9 +471,10 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
     PeerLoad<PT> v[CH][PB];
 #pragma unroll
     for (int s = 0; s < PB; ++s) {
-      int p = p0 + s < n_peers ? p0 + s : n_peers - 1;
+      if (p0 + s < n_peers) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) v[c][s].load(peers + (int64_t)p * peer_stride, e[c]);
+        for (int c = 0; c < CH; ++c) v[c][s].load(peers + (int64_t)(p0 + s) * peer_stride + e[c]);
+      }
     }
 #pragma unroll
     for (int s = 0; s < PB; ++s) {
@@ -481,97 +488,101 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
   for (int c = 0; c < CH; ++c) store_c<CT>(C, e[c], acc[c]);
 }
 
-// One chunk of 8 elements in flight: up to SLOTS peer loads. The fp32 partial
-// is read when the chunk is summed (it was just written by a compute unit of
-// the same XCD, so it comes from the L2), which keeps registers for peers.
-template <typename PT>
+// Ring path (NP peers known at compile time): one chunk of 8 elements in flight
+// = NP peer loads, plus the fp32 partial, which is fetched later (it was just
+// written by a compute unit of the same XCD, so it comes from the L2) to keep
+// registers for peers. Loads complete in issue order, so the partial of a chunk
+// is issued before the peer loads of the chunks that follow it; waiting for it
+// then leaves those in flight. No branch separates loads from their uses, so
+// the compiler's wait counts stay exact.
+template <typename PT, int NP>
 struct ChunkLoads {
-  static constexpr int SLOTS = sizeof(PT) == 2 ? 16 : 8;  // 16-byte loads per peer slot: 1 (bf16) or 2 (fp32)
-  PeerLoad<PT> v[SLOTS];
-  __device__ __forceinline__ void load(const PT* __restrict__ peers, int n_peers, int64_t peer_stride,
-                                       int64_t e) {
+  PeerLoad<PT> v[NP];
+  f32x4 pa, pb;
+  __device__ __forceinline__ void load(const PT* __restrict__ peers, int64_t peer_stride, int64_t e) {
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      int p = s < n_peers ? s : n_peers - 1;  // past the last peer: re-read it, never added
-      if (n_peers > 0) v[s].load(peers + (int64_t)p * peer_stride, e);
-    }
+    for (int s = 0; s < NP; ++s) v[s].load(peers + (int64_t)s * peer_stride + e);
+    __builtin_amdgcn_sched_barrier(0);  // keep the group where the ring puts it
+  }
+  // Issued before the next chunk's peer loads; the scheduling barrier keeps the
+  // compiler from hoisting those above it.
+  __device__ __forceinline__ void load_partial(const float* __restrict__ P, int64_t e) {
+    pa = *(const f32x4*)(P + e);
+    pb = *(const f32x4*)(P + e + 4);
+    __builtin_amdgcn_sched_barrier(0);
   }
   template <typename CT>
-  __device__ __forceinline__ void finish(const float* __restrict__ P, int n_peers,
-                                         CT* __restrict__ C, int64_t e) const {
-    f32x4 pa = *(const f32x4*)(P + e);
-    f32x4 pb = *(const f32x4*)(P + e + 4);
+  __device__ __forceinline__ void finish(CT* __restrict__ C, int64_t e) const {
     float acc[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
-      if (s < n_peers) v[s].add_to(acc);
+    for (int s = 0; s < NP; ++s) v[s].add_to(acc);
     store_c<CT>(C, e, acc);
   }
 };
 
-// Reduce the region rows [m0, m0+rows) x cols [n0, n0+cols) of an M x N output;
-// cols is a multiple of 8. All 256 threads of the workgroup take part; thread t
-// handles chunks t, t+256, ... For up to SLOTS peers the loads of the next
-// DEPTH-1 chunks are in flight while the current chunk is summed, which keeps a
-// single workgroup's share of HBM bandwidth high (it is the only reducer on its
-// compute unit, so latency has to be covered by loads in flight, not by waves).
-template <int DEPTH, typename PT>
+// Thread t handles chunks t, t+256, ... of the region; while chunk q is summed
+// the peer loads of the next DEPTH-1 chunks are in flight. A chunk index past
+// the end is clamped to the last chunk: the lane reads the same inputs as the
+// lane that owns that chunk and stores the same bits to the same place, so no
+// lane needs a branch and the loads and waits are identical on every path. A reducer workgroup is the only one on its compute unit, so
+// latency has to be covered by loads in flight rather than by more waves.
+template <int DEPTH, typename PT, int NP>
 struct ReduceRing;
 
-template <typename PT>
-struct ReduceRing<2, PT> {
+template <typename PT, int NP>
+struct ReduceRing<2, PT, NP> {
   template <typename CT, typename Off>
   __device__ __forceinline__ static void run(const float* __restrict__ P,
-                                             const PT* __restrict__ peers, int n_peers,
-                                             int64_t stride, CT* __restrict__ C, int total, Off off) {
-    int q = threadIdx.x;
-    if (q >= total) return;
-    ChunkLoads<PT> x, y;
-    x.load(peers, n_peers, stride, off(q));
-    for (;;) {
-      const int q1 = q + kThreads;
-      if (q1 < total) y.load(peers, n_peers, stride, off(q1));
-      x.finish(P, n_peers, C, off(q));
-      if (q1 >= total) break;
-      const int q2 = q1 + kThreads;
-      if (q2 < total) x.load(peers, n_peers, stride, off(q2));
-      y.finish(P, n_peers, C, off(q1));
-      if (q2 >= total) break;
-      q = q2;
+                                             const PT* __restrict__ peers, int64_t stride,
+                                             CT* __restrict__ C, int total, Off off) {
+    auto e = [&](int q) { return off(q < total ? q : total - 1); };
+    // loop bound on the wave's first chunk: a uniform (scalar) loop
+    const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
+    const int t = threadIdx.x;
+    ChunkLoads<PT, NP> x, y;
+    x.load(peers, stride, e(t));
+    for (int k = 0; w0 + k < total; k += 2 * kThreads) {
+      const int q = t + k, q1 = q + kThreads, q2 = q + 2 * kThreads;
+      x.load_partial(P, e(q));
+      y.load(peers, stride, e(q1));
+      x.template finish<CT>(C, e(q));
+      y.load_partial(P, e(q1));
+      x.load(peers, stride, e(q2));
+      y.template finish<CT>(C, e(q1));
     }
   }
 };
 
-template <typename PT>
-struct ReduceRing<3, PT> {
+template <typename PT, int NP>
+struct ReduceRing<3, PT, NP> {
   template <typename CT, typename Off>
   __device__ __forceinline__ static void run(const float* __restrict__ P,
-                                             const PT* __restrict__ peers, int n_peers,
-                                             int64_t stride, CT* __restrict__ C, int total, Off off) {
-    int q = threadIdx.x;
-    if (q >= total) return;
-    ChunkLoads<PT> x, y, z;
-    x.load(peers, n_peers, stride, off(q));
-    if (q + kThreads < total) y.load(peers, n_peers, stride, off(q + kThreads));
-    for (;;) {
-      // invariant: chunks q (in x) and q+256 (in y, if it exists) are loading
-      const int q1 = q + kThreads, q2 = q + 2 * kThreads;
-      if (q2 < total) z.load(peers, n_peers, stride, off(q2));
-      x.finish(P, n_peers, C, off(q));
-      if (q1 >= total) break;
-      const int q3 = q + 3 * kThreads;
-      if (q3 < total) x.load(peers, n_peers, stride, off(q3));
-      y.finish(P, n_peers, C, off(q1));
-      if (q2 >= total) break;
-      const int q4 = q + 4 * kThreads;
-      if (q4 < total) y.load(peers, n_peers, stride, off(q4));
-      z.finish(P, n_peers, C, off(q2));
-      if (q3 >= total) break;
-      q = q3;
+                                             const PT* __restrict__ peers, int64_t stride,
+                                             CT* __restrict__ C, int total, Off off) {
+    auto e = [&](int q) { return off(q < total ? q : total - 1); };
+    const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
+    const int t = threadIdx.x;
+    ChunkLoads<PT, NP> x, y, z;
+    x.load(peers, stride, e(t));
+    y.load(peers, stride, e(t + kThreads));
+    for (int k = 0; w0 + k < total; k += 3 * kThreads) {
+      // the peers of chunks q (in x) and q+256 (in y) are loading
+      const int q = t + k, q1 = q + kThreads, q2 = q + 2 * kThreads;
+      x.load_partial(P, e(q));
+      z.load(peers, stride, e(q2));
+      x.template finish<CT>(C, e(q));
+      y.load_partial(P, e(q1));
+      x.load(peers, stride, e(q + 3 * kThreads));
+      y.template finish<CT>(C, e(q1));
+      z.load_partial(P, e(q2));
+      y.load(peers, stride, e(q + 4 * kThreads));
+      z.template finish<CT>(C, e(q2));
     }
   }
 };
 
+// Reduce the region rows [m0, m0+rows) x cols [n0, n0+cols) of an M x N output;
+// cols is a multiple of 8. All 256 threads of the workgroup take part.
 template <int DEPTH, typename PT, typename CT>
 __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
                                               const PT* __restrict__ peers, int n_peers,
@@ -579,12 +590,18 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
                                               int64_t n0, int rows, int cols) {
   const int cpr = cols >> 3;
   const int total = rows * cpr;
+  if (total <= 0) return;
   const int64_t stride = M * N;
   auto off = [&](int q) { return (m0 + q / cpr) * N + n0 + (q % cpr) * 8; };
-  if (n_peers <= ChunkLoads<PT>::SLOTS) {
-    ReduceRing<DEPTH, PT>::template run<CT>(P, peers, n_peers, stride, C, total, off);
+#define MK_RING(NPV)                                                            \
+  case NPV:                                                                     \
+    ReduceRing<DEPTH, PT, NPV>::template run<CT>(P, peers, stride, C, total, off); \
     return;
+  switch (n_peers) {
+    MK_RING(1) MK_RING(2) MK_RING(3) MK_RING(4) MK_RING(7) MK_RING(8) MK_RING(15)
+    default: break;
   }
+#undef MK_RING
   constexpr int CH = 2;
   int q = threadIdx.x;
   for (; q + (CH - 1) * kThreads < total; q += CH * kThreads) {

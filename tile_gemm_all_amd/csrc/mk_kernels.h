@@ -58,7 +58,7 @@ struct FusedArgs {
   int withhold_tile;           // debug: -1 = off
   int n_xcd;                   // XCDs of the device; tiles are queued per XCD
   int flag_scope;              // 0: producer and consumer share an XCD's L2; 1: agent scope
-  int pad_;
+  int reducer_cap;             // controller's upper bound on reducers while compute remains
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
 };
 

@@ -24,11 +24,11 @@ __device__ __forceinline__ unsigned long long* slot64(unsigned long long* s, int
   return s + (size_t)i * kSlotWords;
 }
 
-__device__ __forceinline__ int current_target(const FusedArgs& a) {
+__device__ __forceinline__ int current_target(unsigned long long* S, int epoch, int init_target) {
   unsigned long long w =
-      __hip_atomic_load(slot64(a.slots, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((int)(w >> 32) == a.epoch) return (int)(w & 0xFFFFFFFFu);
-  return a.init_target;
+      __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((int)(w >> 32) == epoch) return (int)(w & 0xFFFFFFFFu);
+  return init_target;
 }
 
 __device__ __forceinline__ void raise_error(unsigned long long* S, int code) {
@@ -37,8 +37,11 @@ __device__ __forceinline__ void raise_error(unsigned long long* S, int code) {
 }
 
 // One controller evaluation (thread 0 of the workgroup that wins the try-lock).
-__device__ void controller_step(const FusedArgs& a) {
-  unsigned long long* S = a.slots;
+// Takes its inputs by value: the kernel's argument block must not escape to
+// memory, or every pointer read from it loses its global address space.
+__device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry_t* tel, int G,
+                                             int T, int epoch, int init_target, float seed_x,
+                                             int cap) {
   if (atomicCAS(slot32(S, S_LOCK), 0, 1) != 0) return;
   int c = load_relaxed(slot32(S, S_COMPUTED));
   int r = load_relaxed(slot32(S, S_REDUCED));
@@ -46,14 +49,14 @@ __device__ void controller_step(const FusedArgs& a) {
       __hip_atomic_load(slot64(S, S_BUSY_C), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   unsigned long long br =
       __hip_atomic_load(slot64(S, S_BUSY_R), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  int cur = current_target(a);
-  int nt = controller_rule(a.G, a.T, c, r, bc, br, a.seed_x, cur);
+  int cur = current_target(S, epoch, init_target);
+  int nt = controller_rule(G, T, c, r, bc, br, seed_x, cur, cap);
   if (nt != cur) {
-    unsigned long long w = ((unsigned long long)(unsigned)a.epoch << 32) | (unsigned)nt;
+    unsigned long long w = ((unsigned long long)(unsigned)epoch << 32) | (unsigned)nt;
     __hip_atomic_store(slot64(S, S_TARGET), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     atomicAdd(slot32(S, S_UPDATES), 1);
   }
-  if (a.tel) {
+  if (tel) {
     int i = atomicAdd(slot32(S, S_NTRACE), 1);
     if (i < MK_TRACE_CAP) {
       mk_trace_entry_t e;
@@ -62,7 +65,7 @@ __device__ void controller_step(const FusedArgs& a) {
       e.reduced = r;
       e.target = nt;
       e.spare = 0;
-      a.tel->trace[i] = e;
+      tel->trace[i] = e;
     }
   }
   __hip_atomic_store(slot32(S, S_LOCK), 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       int backoff = 1;
       for (;;) {
         if (load_relaxed(slot32(S, S_ABORT))) break;
-        const int target = current_target(a);
+        const int target = current_target(S, a.epoch, a.init_target);
         const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
         const bool pref_reduce = rank < tx;
         if (!pref_reduce) {
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         }
         int done = atomicAdd(slot32(S, S_COMPUTED), 1) + 1;
         atomicAdd(slot64(S, S_BUSY_C), ticks() - t0);
-        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(a);
+        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap);
       }
     } else {
       if (tid == 0) {
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       if (tid == 0) {
         int done = atomicAdd(slot32(S, S_REDUCED), 1) + 1;
         atomicAdd(slot64(S, S_BUSY_R), ticks() - t0);
-        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(a);
+        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap);
       }
     }
     __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         t->tiles = a.T;
         t->grid = a.G;
         t->initial_target = a.init_target;
-        t->final_target = current_target(a);
+        t->final_target = current_target(S, a.epoch, a.init_target);
         t->n_updates = *slot32(S, S_UPDATES);
         int nt = *slot32(S, S_NTRACE);
         t->n_trace = nt < MK_TRACE_CAP ? nt : MK_TRACE_CAP;
