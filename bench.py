@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, vendor figure
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_mlp.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_mlp.txt")
 KERNEL_SOURCES = ["tile_gemm_all_amd/csrc/mk_kernels.hip", "tile_gemm_all_amd/csrc/mk_device.h",
                   "tile_gemm_all_amd/csrc/mk_controller.h"]
 

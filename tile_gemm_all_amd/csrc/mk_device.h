@@ -126,9 +126,11 @@ __device__ __forceinline__ void dma16(const void* g, const char* lds) {
 template <int BM_, int BN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 32, NS = 4;
-  // fused kernel: workgroups per CU, and chunks in flight per reducer lane
+  // fused kernel: workgroups per CU
   static constexpr int OCC = BM * BN >= 256 * 256 ? 1 : 2;
-  static constexpr int RDEPTH = OCC == 1 ? 3 : 2;
+  // fused kernel: a tile's reduce is split into RSPLIT row slabs, each claimed
+  // on its own, so that the last reduces spread over every idle workgroup
+  static constexpr int RSPLIT = BM / 64;
   static constexpr int KSTEPS = BK / 16;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -159,6 +161,22 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   int w = t - g * group_size;
   tm = first + w % gm;
   tn = w / gm;
+}
+
+// Fused kernel's map: tile_coords, then a column permutation that sends each run
+// of tiles_n/4 consecutive tile columns to every 4th column. An XCD's share of
+// tiles (a contiguous range of t) keeps the same number of A and B panels for
+// L2 reuse, but its tiles no longer sit side by side in memory: concurrent
+// streams spread over the whole row of every operand, which measured 10-25%
+// more reduce bandwidth than compact blocks of tiles per XCD.
+__device__ __forceinline__ void fused_tile_coords(int t, int tiles_m, int tiles_n, int& tm,
+                                                  int& tn) {
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  constexpr int S = 4;
+  if (tiles_n >= 2 * S && tiles_n % S == 0) {
+    const int w = tiles_n / S;
+    tn = (tn % w) * S + tn / w;
+  }
 }
 
 template <class Cfg>
@@ -209,35 +227,33 @@ struct GemmTile {
       dma16(B + s.b[i] + k0 * N, stage + Cfg::A_BYTES + (wave * Cfg::B_LD + i) * 1024);
   }
 
-  // Last, partial k-tile: same LDS image, but k >= K reads as zero. Goes through
-  // registers; used at most once per tile, when K is not a multiple of BK.
+  // Last, partial k-tile: same LDS image, but k >= K reads as zero; used at most
+  // once per tile, when K is not a multiple of BK. K is a multiple of 8, so each
+  // 16-byte chunk lies wholly below K (loaded straight into LDS, like a full
+  // stage) or wholly at or past K (zero-filled by an LDS store). No load here is
+  // one the compiler tracks, so the k-loop around it carries no extra waits.
   __device__ __forceinline__ static void load_guarded(const Src& s, const uint16_t* __restrict__ A,
                                                       const uint16_t* __restrict__ B, int64_t N,
                                                       int64_t K, int64_t k0, char* stage, int wave,
                                                       int lane) {
-    u32x4 va[Cfg::A_LD], vb[Cfg::B_LD];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < Cfg::A_LD; ++i) {
       int byte = lane * 16;
       int row = (wave * Cfg::A_LD + i) * Cfg::A_ROWS_PER_LD + byte / Cfg::A_ROW;
       int c = ((byte % Cfg::A_ROW) / 16) ^ ((row >> 2) & 3);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k0 + c * 8 < K) v = *(const u32x4*)(A + s.a[i] + k0);
-      va[i] = v;
+      char* dst = stage + (wave * Cfg::A_LD + i) * 1024;
+      if (k0 + c * 8 < K) dma16(A + s.a[i] + k0, dst);
+      else *(u32x4*)(dst + lane * 16) = zero;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_LD; ++i) {
       int row = (wave * Cfg::B_LD + i) * Cfg::B_ROWS_PER_LD + (lane * 16) / Cfg::B_ROW;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k0 + row < K) v = *(const u32x4*)(B + s.b[i] + k0 * N);
-      vb[i] = v;
+      char* dst = stage + Cfg::A_BYTES + (wave * Cfg::B_LD + i) * 1024;
+      if (k0 + row < K) dma16(B + s.b[i] + k0 * N, dst);
+      else *(u32x4*)(dst + lane * 16) = zero;
     }
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LD; ++i)
-      *(u32x4*)(stage + (wave * Cfg::A_LD + i) * 1024 + lane * 16) = va[i];
-#pragma unroll
-    for (int i = 0; i < Cfg::B_LD; ++i)
-      *(u32x4*)(stage + Cfg::A_BYTES + (wave * Cfg::B_LD + i) * 1024 + lane * 16) = vb[i];
+    wait_loads(0);
   }
 
   // Fragment addresses within a stage (bytes), per lane.
@@ -449,7 +465,8 @@ __device__ __forceinline__ void store_c<float>(float* C, int64_t e, const float*
 // same bits.
 
 // Generic path (any peer count): CH chunks of 8 elements at offsets e[], peers
-// fetched in batches of 8 so that many loads are in flight before the adds.
+// fetched in batches (8 bfloat16 or 4 float32 peers) so that many loads are in
+// flight before the adds.
 template <int CH, typename PT, typename CT>
 __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
                                               const PT* __restrict__ peers, int n_peers,
@@ -466,7 +483,7 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
       acc[c][4 + i] = b[i];
     }
   }
-  constexpr int PB = 8;
+  constexpr int PB = sizeof(PT) == 2 ? 8 : 4;
   for (int p0 = 0; p0 < n_peers; p0 += PB) {
     PeerLoad<PT> v[CH][PB];
 #pragma unroll
@@ -488,120 +505,170 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
   for (int c = 0; c < CH; ++c) store_c<CT>(C, e[c], acc[c]);
 }
 
-// Ring path (NP peers known at compile time): one chunk of 8 elements in flight
-// = NP peer loads, plus the fp32 partial, which is fetched later (it was just
-// written by a compute unit of the same XCD, so it comes from the L2) to keep
-// registers for peers. Loads complete in issue order, so the partial of a chunk
-// is issued before the peer loads of the chunks that follow it; waiting for it
-// then leaves those in flight. No branch separates loads from their uses, so
-// the compiler's wait counts stay exact.
+// Ring path (NP peers known at compile time). Thread t handles chunks t,
+// t+256, ... of a tile region. A chunk's loads (its fp32 partial, then its NP
+// peer vectors) are issued together, DEPTH-1 chunks ahead of the chunk being
+// summed. Vector memory loads complete in issue order, so waiting for a chunk's
+// loads waits for nothing issued after them: while chunk q is summed the loads
+// of the next DEPTH-1 chunks stay in flight. A reducer workgroup is the only one
+// on its compute unit, so latency has to be covered by bytes in flight (at most
+// 63 loads per wave) rather than by more waves.
+//
+// Addressing: every operand has a wave-uniform 64-bit base for the region (kept
+// in scalar registers) and each lane one 32-bit element offset from it, which it
+// advances by a fixed step per chunk without a division. A chunk index past the
+// end is clamped to the last chunk: that lane reads the same inputs as the lane
+// that owns the chunk and stores the same bits to the same place, so no lane
+// needs a branch, and the loop runs on a wave-uniform bound.
 template <typename PT, int NP>
 struct ChunkLoads {
-  PeerLoad<PT> v[NP];
   f32x4 pa, pb;
-  __device__ __forceinline__ void load(const PT* __restrict__ peers, int64_t peer_stride, int64_t e) {
+  PeerLoad<PT> v[NP];
+  // Byte offsets are formed in 32 bits, so each load is a scalar base plus a
+  // 32-bit vector offset.
+  __device__ __forceinline__ void load(const float* __restrict__ P,
+                                       const PT* const __restrict__* peer, uint32_t off) {
+    const uint32_t op = off * 4u, ov = off * (uint32_t)sizeof(PT);
+    pa = *(const f32x4*)((const char*)P + op);
+    pb = *(const f32x4*)((const char*)P + op + 16u);
 #pragma unroll
-    for (int s = 0; s < NP; ++s) v[s].load(peers + (int64_t)s * peer_stride + e);
+    for (int s = 0; s < NP; ++s) v[s].load((const PT*)((const char*)peer[s] + ov));
     __builtin_amdgcn_sched_barrier(0);  // keep the group where the ring puts it
   }
-  // Issued before the next chunk's peer loads; the scheduling barrier keeps the
-  // compiler from hoisting those above it.
-  __device__ __forceinline__ void load_partial(const float* __restrict__ P, int64_t e) {
-    pa = *(const f32x4*)(P + e);
-    pb = *(const f32x4*)(P + e + 4);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   template <typename CT>
-  __device__ __forceinline__ void finish(CT* __restrict__ C, int64_t e) const {
+  __device__ __forceinline__ void finish(CT* __restrict__ C, uint32_t off) const {
     float acc[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
 #pragma unroll
     for (int s = 0; s < NP; ++s) v[s].add_to(acc);
-    store_c<CT>(C, e, acc);
+    store_c<CT>((CT*)((char*)C + off * (uint32_t)sizeof(CT)), 0, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
-// Thread t handles chunks t, t+256, ... of the region; while chunk q is summed
-// the peer loads of the next DEPTH-1 chunks are in flight. A chunk index past
-// the end is clamped to the last chunk: the lane reads the same inputs as the
-// lane that owns that chunk and stores the same bits to the same place, so no
-// lane needs a branch and the loads and waits are identical on every path. A reducer workgroup is the only one on its compute unit, so
-// latency has to be covered by loads in flight rather than by more waves.
-template <int DEPTH, typename PT, int NP>
-struct ReduceRing;
+// Walks chunk indices q = q0, q0+256, ... of a region of `cpr` chunks per row
+// (row pitch N elements), giving each one's element offset, clamped to the last
+// chunk past the end.
+struct ChunkCursor {
+  int q, c;             // chunk index and its column chunk
+  uint32_t off;         // element offset of chunk q (unclamped)
+  int total, cpr;
+  uint32_t last;        // element offset of the last chunk
+  uint32_t step_off;    // offset advance for 256 chunks without a row wrap
+  int step_c;           // column-chunk advance for 256 chunks (256 % cpr)
+  uint32_t wrap_off;    // extra advance when the column wraps: N - 8 * cpr
+  __device__ __forceinline__ void init(int q0, int total_, int cpr_, int64_t N) {
+    total = total_;
+    cpr = cpr_;
+    const int r = q0 / cpr_;
+    c = q0 - r * cpr_;
+    q = q0;
+    off = (uint32_t)(r * N + c * 8);
+    const int rows = total_ / cpr_;
+    last = (uint32_t)((rows - 1) * N + (cpr_ - 1) * 8);
+    const int a = kThreads / cpr_;
+    step_c = kThreads - a * cpr_;
+    step_off = (uint32_t)(a * N + step_c * 8);
+    wrap_off = (uint32_t)(N - 8 * cpr_);
+  }
+  __device__ __forceinline__ uint32_t get() const { return q < total ? off : last; }
+  __device__ __forceinline__ void advance() {
+    q += kThreads;
+    c += step_c;
+    off += step_off;
+    const bool wrap = c >= cpr;
+    c = wrap ? c - cpr : c;
+    off = wrap ? off + wrap_off : off;
+  }
+};
 
-template <typename PT, int NP>
-struct ReduceRing<2, PT, NP> {
-  template <typename CT, typename Off>
+template <int DEPTH, typename PT, int NP>
+struct ReduceRing {
+  template <typename CT>
   __device__ __forceinline__ static void run(const float* __restrict__ P,
-                                             const PT* __restrict__ peers, int64_t stride,
-                                             CT* __restrict__ C, int total, Off off) {
-    auto e = [&](int q) { return off(q < total ? q : total - 1); };
+                                             const PT* const __restrict__* peer,
+                                             CT* __restrict__ C, int total, int cpr, int64_t N) {
     // loop bound on the wave's first chunk: a uniform (scalar) loop
     const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
-    const int t = threadIdx.x;
-    ChunkLoads<PT, NP> x, y;
-    x.load(peers, stride, e(t));
-    for (int k = 0; w0 + k < total; k += 2 * kThreads) {
-      const int q = t + k, q1 = q + kThreads, q2 = q + 2 * kThreads;
-      x.load_partial(P, e(q));
-      y.load(peers, stride, e(q1));
-      x.template finish<CT>(C, e(q));
-      y.load_partial(P, e(q1));
-      x.load(peers, stride, e(q2));
-      y.template finish<CT>(C, e(q1));
+    ChunkCursor ld, st;  // the chunk loaded next, the chunk summed next
+    ld.init(threadIdx.x, total, cpr, N);
+    st = ld;
+    ChunkLoads<PT, NP> b[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i) {
+      b[i].load(P, peer, ld.get());
+      ld.advance();
     }
+    // At least one pass, so that no guard separates the loads above from the
+    // loop (a wave whose chunks all lie past the end re-stores the last chunk).
+    int k = 0;
+    do {
+#pragma unroll
+      for (int i = 0; i < DEPTH; ++i) {
+        b[(i + DEPTH - 1) % DEPTH].load(P, peer, ld.get());
+        ld.advance();
+        b[i].template finish<CT>(C, st.get());
+        st.advance();
+      }
+      k += DEPTH * kThreads;
+    } while (w0 + k < total);
+    // The last pass issued loads of clamped chunks that are never summed (L2
+    // hits); the compute path waits for them before its GEMM loop.
   }
 };
 
-template <typename PT, int NP>
-struct ReduceRing<3, PT, NP> {
-  template <typename CT, typename Off>
-  __device__ __forceinline__ static void run(const float* __restrict__ P,
-                                             const PT* __restrict__ peers, int64_t stride,
-                                             CT* __restrict__ C, int total, Off off) {
-    auto e = [&](int q) { return off(q < total ? q : total - 1); };
-    const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
-    const int t = threadIdx.x;
-    ChunkLoads<PT, NP> x, y, z;
-    x.load(peers, stride, e(t));
-    y.load(peers, stride, e(t + kThreads));
-    for (int k = 0; w0 + k < total; k += 3 * kThreads) {
-      // the peers of chunks q (in x) and q+256 (in y) are loading
-      const int q = t + k, q1 = q + kThreads, q2 = q + 2 * kThreads;
-      x.load_partial(P, e(q));
-      z.load(peers, stride, e(q2));
-      x.template finish<CT>(C, e(q));
-      y.load_partial(P, e(q1));
-      x.load(peers, stride, e(q + 3 * kThreads));
-      y.template finish<CT>(C, e(q1));
-      z.load_partial(P, e(q2));
-      y.load(peers, stride, e(q + 4 * kThreads));
-      z.template finish<CT>(C, e(q2));
-    }
-  }
-};
+// Ring depth for NP peers of type PT at OCC workgroups per compute unit. While
+// a chunk is summed, DEPTH-1 chunks' loads are in flight; about 17 16-byte loads
+// per wave (one chunk of 15 bfloat16 peers) streamed fastest on MI355X, and
+// deeper rings were slower (more concurrent peer streams per wave), so small
+// chunks get a deeper ring, within a register budget per lane (512 registers
+// per SIMD lane, shared by OCC waves, minus addresses and the rest of the
+// kernel); between 2 and 4.
+template <int OCC, typename PT, int NP>
+__host__ __device__ constexpr int ring_depth() {
+  constexpr int loads = 2 + NP * (sizeof(PT) == 2 ? 1 : 2);  // 16-byte loads per chunk
+  constexpr int regs = 8 + NP * (sizeof(PT) == 2 ? 4 : 8);   // registers per chunk
+  constexpr int budget = OCC == 1 ? 320 : 160;
+  constexpr int d_vm = 1 + (17 + loads - 1) / loads, d_reg = budget / regs;
+  constexpr int d = d_vm < d_reg ? d_vm : d_reg;
+  return d < 2 ? 2 : (d > 4 ? 4 : d);
+}
+// Whether even a depth-2 ring fits the register budget (else the generic path).
+template <int OCC, typename PT, int NP>
+__host__ __device__ constexpr bool ring_fits() {
+  return 2 * (8 + NP * (sizeof(PT) == 2 ? 4 : 8)) <= (OCC == 1 ? 320 : 160);
+}
 
 // Reduce the region rows [m0, m0+rows) x cols [n0, n0+cols) of an M x N output;
-// cols is a multiple of 8. All 256 threads of the workgroup take part.
-template <int DEPTH, typename PT, typename CT>
+// cols is a multiple of 8. All 256 threads of the workgroup take part; the
+// region arguments are the same in every lane.
+template <int OCC, typename PT, typename CT>
 __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
                                               const PT* __restrict__ peers, int n_peers,
                                               CT* __restrict__ C, int64_t M, int64_t N, int64_t m0,
                                               int64_t n0, int rows, int cols) {
-  const int cpr = cols >> 3;
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
   const int total = rows * cpr;
   if (total <= 0) return;
   const int64_t stride = M * N;
-  auto off = [&](int q) { return (m0 + q / cpr) * N + n0 + (q % cpr) * 8; };
-#define MK_RING(NPV)                                                            \
-  case NPV:                                                                     \
-    ReduceRing<DEPTH, PT, NPV>::template run<CT>(P, peers, stride, C, total, off); \
-    return;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+#define MK_RING(NPV)                                                                   \
+  case NPV:                                                                            \
+    if constexpr (ring_fits<OCC, PT, NPV>()) {                                         \
+      const PT* pr[NPV];                                                               \
+      _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base; \
+      ReduceRing<ring_depth<OCC, PT, NPV>(), PT, NPV>::template run<CT>(P + base, pr, C + base, \
+                                                                          total, cpr, N); \
+      return;                                                                          \
+    }                                                                                  \
+    break;
   switch (n_peers) {
     MK_RING(1) MK_RING(2) MK_RING(3) MK_RING(4) MK_RING(7) MK_RING(8) MK_RING(15)
     default: break;
   }
 #undef MK_RING
+  auto off = [&](int q) { return base + (q / cpr) * N + (q % cpr) * 8; };
   constexpr int CH = 2;
   int q = threadIdx.x;
   for (; q + (CH - 1) * kThreads < total; q += CH * kThreads) {

@@ -8,31 +8,40 @@
 
 namespace mk {
 
-// Workspace control words, each on its own 128-byte line (kSlotWords 64-bit words).
+// Workspace control words, each on its own 128-byte line (kSlotWords 64-bit
+// words). Counters that every tile updates are kept per XCD: one address hit by
+// all 256 workgroups serialises their atomics (about 2.9 us per operation
+// measured on MI355X, against 0.35 us for an XCD's own line).
+// Per-XCD words, at S_XCD_BASE + kXcdWords * xcd + word.
+enum XcdSlot : int {
+  X_COMPUTE_NEXT = 0,  // next tile of the XCD's queue to compute
+  X_REDUCE_NEXT,       // next reduce unit of the XCD's queue
+  X_ARRIVE,            // workgroups that arrived on the XCD (their rank)
+  X_COMPUTED,          // tiles published
+  X_REDUCED,           // reduce units (tile row slabs) done
+  X_BUSY_C,            // summed compute-tile ticks
+  X_BUSY_R,            // summed reduce-unit ticks (flag waits excluded)
+  X_WAIT_R,            // summed flag-wait ticks
+  X_SWITCHES,          // workgroup role changes
+  X_RBC,               // reduce units done by workgroups that prefer compute (draining)
+  X_CBR,               // tiles computed by workgroups that prefer reducing (helping)
+  kXcdWords
+};
+constexpr int kMaxXcd = 16;
 enum Slot : int {
-  S_COMPUTED = 0,      // tiles published (all XCDs)
-  S_REDUCED,           // tiles reduced (all XCDs)
-  S_EXIT,              // workgroups that have left the persistent loop
+  S_EXIT = 0,          // workgroups that have left the persistent loop
   S_ERROR,             // device error word (mk_status_t), kept across calls
   S_ABORT,             // set on error: every workgroup leaves its loop
   S_LOCK,              // controller try-lock
   S_TARGET,            // (epoch << 32) | reducer target published by the controller
-  S_BUSY_C,            // summed compute-tile ticks
-  S_BUSY_R,            // summed reduce-tile ticks (flag waits excluded)
-  S_WAIT_R,            // summed flag-wait ticks
   S_UPDATES,           // controller target changes
-  S_SWITCHES,          // workgroup role changes
-  S_RBC,               // tiles reduced by workgroups that prefer compute (draining)
-  S_CBR,               // tiles computed by workgroups that prefer reducing (helping)
   S_NTRACE,            // controller trace entries written
   S_TSTART,            // min start tick
   S_TEND,              // max exit tick
-  S_XCD_BASE,          // per-XCD words follow: kXcdWords per XCD
-  S_COUNT = S_XCD_BASE + 3 * 16
+  S_XCD_BASE,          // per-XCD words follow
+  S_COUNT = S_XCD_BASE + kXcdWords * kMaxXcd
 };
-// Per-XCD words, at S_XCD_BASE + 3 * xcd + {0, 1, 2}.
-enum XcdSlot : int { X_COMPUTE_NEXT = 0, X_REDUCE_NEXT = 1, X_ARRIVE = 2, kXcdWords = 3 };
-constexpr int kMaxXcd = 16;
+
 constexpr int kSlotWords = 16;
 constexpr int kThreadsHost = 256;  // workgroup size of every kernel
 

@@ -24,6 +24,35 @@ __device__ __forceinline__ unsigned long long* slot64(unsigned long long* s, int
   return s + (size_t)i * kSlotWords;
 }
 
+__device__ __forceinline__ int* xslot(unsigned long long* s, int x, int w) {
+  return slot32(s, S_XCD_BASE + x * kXcdWords + w);
+}
+__device__ __forceinline__ unsigned long long* xslot64(unsigned long long* s, int x, int w) {
+  return slot64(s, S_XCD_BASE + x * kXcdWords + w);
+}
+
+// Sum of a per-XCD word over the n_xcd XCDs (all loads issued before any add).
+__device__ __forceinline__ int sum_xcd32(unsigned long long* S, int n_xcd, int w) {
+  int v[kMaxXcd];
+#pragma unroll
+  for (int x = 0; x < kMaxXcd; ++x) v[x] = x < n_xcd ? load_relaxed(xslot(S, x, w)) : 0;
+  int t = 0;
+#pragma unroll
+  for (int x = 0; x < kMaxXcd; ++x) t += v[x];
+  return t;
+}
+__device__ __forceinline__ unsigned long long sum_xcd64(unsigned long long* S, int n_xcd, int w) {
+  unsigned long long v[kMaxXcd];
+#pragma unroll
+  for (int x = 0; x < kMaxXcd; ++x)
+    v[x] = x < n_xcd ? __hip_atomic_load(xslot64(S, x, w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : 0ull;
+  unsigned long long t = 0;
+#pragma unroll
+  for (int x = 0; x < kMaxXcd; ++x) t += v[x];
+  return t;
+}
+
 __device__ __forceinline__ int current_target(unsigned long long* S, int epoch, int init_target) {
   unsigned long long w =
       __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -41,14 +70,12 @@ __device__ __forceinline__ void raise_error(unsigned long long* S, int code) {
 // memory, or every pointer read from it loses its global address space.
 __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry_t* tel, int G,
                                              int T, int epoch, int init_target, float seed_x,
-                                             int cap) {
+                                             int cap, int rsplit, int n_xcd) {
   if (atomicCAS(slot32(S, S_LOCK), 0, 1) != 0) return;
-  int c = load_relaxed(slot32(S, S_COMPUTED));
-  int r = load_relaxed(slot32(S, S_REDUCED));
-  unsigned long long bc =
-      __hip_atomic_load(slot64(S, S_BUSY_C), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  unsigned long long br =
-      __hip_atomic_load(slot64(S, S_BUSY_R), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int c = sum_xcd32(S, n_xcd, X_COMPUTED);
+  int r = sum_xcd32(S, n_xcd, X_REDUCED) / rsplit;  // reduce units -> tiles
+  unsigned long long bc = sum_xcd64(S, n_xcd, X_BUSY_C);
+  unsigned long long br = sum_xcd64(S, n_xcd, X_BUSY_R);
   int cur = current_target(S, epoch, init_target);
   int nt = controller_rule(G, T, c, r, bc, br, seed_x, cur, cap);
   if (nt != cur) {
@@ -73,9 +100,6 @@ __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry
 
 enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
 
-__device__ __forceinline__ int* xslot(unsigned long long* s, int x, int w) {
-  return slot32(s, S_XCD_BASE + x * kXcdWords + w);
-}
 
 // Claims the next GEMM tile of this XCD's queue; returns its local index or -1.
 __device__ __forceinline__ int claim_compute(unsigned long long* S, int x, int cnt) {
@@ -87,15 +111,17 @@ __device__ __forceinline__ int claim_compute(unsigned long long* S, int x, int c
 
 // Persistent fused kernel. Tiles [start_x, start_x + cnt_x) belong to XCD x: only
 // workgroups running on XCD x compute or reduce them, so a tile's partial is
-// produced and consumed behind the same L2. In each XCD, workgroups whose
-// arrival rank is below that XCD's share of the reducer target prefer reducing;
-// the others prefer computing. A workgroup with nothing to do in its preferred
-// role takes work of the other role (reducers help compute while no tile is
-// ready; compute workgroups drain the reduce queue when no GEMM tile is left).
+// produced and consumed behind the same L2. A tile's reduce is split into
+// RSPLIT row-slab units. In each XCD, workgroups whose arrival rank is below
+// that XCD's share of the reducer target prefer reducing; the others prefer
+// computing. A reducer reserves the next unit when its tile is finished (or no
+// GEMM tile is left) and computes a tile otherwise; a reserved unit whose tile
+// nobody has claimed yet makes its holder compute that far. Compute workgroups
+// reserve units once no GEMM tile is left (draining).
 template <class Cfg, typename PT, typename CT>
 __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) {
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
-  __shared__ int s_kind, s_tile, s_ok;
+  __shared__ int s_kind, s_tile, s_part, s_ok;
   const int tid = threadIdx.x;
   unsigned long long* S = a.slots;
   const PT* peers = (const PT*)a.peers;
@@ -106,45 +132,58 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const int x = xcc_id() % a.n_xcd;
   const int q0 = (int)(((int64_t)x * a.T) / a.n_xcd);
   const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
-  int rank = 0, last_kind = -1;
+  int rank = 0, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
   if (tid == 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
 
   for (;;) {
     if (tid == 0) {
-      int kind = K_EXIT, tile = -1;
+      int kind = K_EXIT, tile = -1, part = 0;
       bool off_role = false;
-      const unsigned long long w0 = ticks();
-      int backoff = 1;
+      const int units = cnt * Cfg::RSPLIT;  // reduce unit r: slab r % RSPLIT of tile r / RSPLIT
+      int* rnext = xslot(S, x, X_REDUCE_NEXT);
+      // Every pass claims work or leaves; nothing here waits.
       for (;;) {
         if (load_relaxed(slot32(S, S_ABORT))) break;
         const int target = current_target(S, a.epoch, a.init_target);
         const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
         const bool pref_reduce = rank < tx;
+        if (held >= 0) {
+          // A reserved unit is reduced once a compute workgroup has claimed its
+          // tile (that workgroup is running, so the flag will be set). Until
+          // then this workgroup computes the next tile itself: that claim cannot
+          // fail while the reserved tile is unclaimed, so the XCD always makes
+          // progress.
+          if (held / Cfg::RSPLIT < load_relaxed(xslot(S, x, X_COMPUTE_NEXT))) {
+            kind = K_REDUCE;
+            tile = q0 + held / Cfg::RSPLIT;
+            part = held % Cfg::RSPLIT;
+            off_role = !pref_reduce;
+            held = -1;
+            break;
+          }
+          const int i = claim_compute(S, x, cnt);
+          if (i >= 0) {
+            kind = K_COMPUTE;
+            tile = q0 + i;
+            off_role = pref_reduce;
+            break;
+          }
+          continue;  // the tile was claimed meanwhile
+        }
         if (!pref_reduce) {
-          int i = claim_compute(S, x, cnt);
+          const int i = claim_compute(S, x, cnt);
           if (i >= 0) {
             kind = K_COMPUTE;
             tile = q0 + i;
             break;
           }
         }
-        // Reduce: only tiles that a compute workgroup has claimed (it is running,
-        // so its flag will be set).
-        int* rnext = xslot(S, x, X_REDUCE_NEXT);
-        int r = load_relaxed(rnext);
-        if (r >= cnt) break;  // this XCD's work is all claimed: leave
-        int c = load_relaxed(xslot(S, x, X_COMPUTE_NEXT));
-        if (r < c) {
-          if (atomicCAS(rnext, r, r + 1) == r) {
-            kind = K_REDUCE;
-            tile = q0 + r;
-            off_role = !pref_reduce;
-            break;
-          }
-          continue;
-        }
-        if (pref_reduce) {
-          int i = claim_compute(S, x, cnt);
+        const int r = load_relaxed(rnext);
+        if (r >= units) break;  // every unit is taken: leave
+        if (pref_reduce && load_relaxed(a.flags + q0 + r / Cfg::RSPLIT) != a.epoch) {
+          // The next unit's tile is not finished: compute meanwhile, if a GEMM
+          // tile is left, rather than wait for its flag.
+          const int i = claim_compute(S, x, cnt);
           if (i >= 0) {
             kind = K_COMPUTE;
             tile = q0 + i;
@@ -152,30 +191,36 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
             break;
           }
         }
-        if (ticks() - w0 > a.spin_limit) {
-          raise_error(S, MK_ERR_TIMEOUT);
+        // Reserve the next reduce unit (a fetch-add always succeeds, unlike a
+        // compare-and-swap that 32 workgroups of an XCD would retry in turn).
+        held = atomicAdd(rnext, 1);
+        if (held >= units) {
+          held = -1;
           break;
         }
-        backoff_sleep(backoff);
-        backoff = backoff < 8 ? backoff * 2 : 8;
       }
       if (kind != K_EXIT) {
-        if (last_kind >= 0 && kind != last_kind) atomicAdd(slot32(S, S_SWITCHES), 1);
+        if (last_kind >= 0 && kind != last_kind) atomicAdd(xslot(S, x, X_SWITCHES), 1);
         last_kind = kind;
-        if (off_role) atomicAdd(slot32(S, kind == K_REDUCE ? S_RBC : S_CBR), 1);
+        if (off_role) atomicAdd(xslot(S, x, kind == K_REDUCE ? X_RBC : X_CBR), 1);
       }
       s_kind = kind;
       s_tile = tile;
+      s_part = part;
     }
     __syncthreads();
-    const int kind = s_kind, tile = s_tile;
+    const int kind = s_kind, tile = s_tile, part = s_part;
     if (kind == K_EXIT) break;
     int tm, tn;
-    tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
+    fused_tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
 
     if (kind == K_COMPUTE) {
       const unsigned long long t0 = ticks();
+      // Nothing of the previous task is still needed; waiting for all of this
+      // wave's loads here (a wait the compiler tracks) lets it start the GEMM
+      // with no load outstanding, so it adds no waits to the k-loop.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       GemmTile<Cfg> g;
       g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
       g.store_partial(a.P, a.M, a.N, m0, n0);
@@ -186,9 +231,9 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           if (a.flag_scope == 0) store_flag(a.flags + tile, a.epoch);
           else publish_flag_agent(a.flags + tile, a.epoch);
         }
-        int done = atomicAdd(slot32(S, S_COMPUTED), 1) + 1;
-        atomicAdd(slot64(S, S_BUSY_C), ticks() - t0);
-        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap);
+        int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;  // this XCD's count
+        atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
+        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     } else {
       if (tid == 0) {
@@ -209,20 +254,22 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         }
         if (a.flag_scope == 0) invalidate_l1();
         else acquire_fence_agent();
-        atomicAdd(slot64(S, S_WAIT_R), ticks() - w0);
+        atomicAdd(xslot64(S, x, X_WAIT_R), ticks() - w0);
         s_ok = ok;
       }
       __syncthreads();
       if (!s_ok) break;
       const unsigned long long t0 = ticks();
-      const int rows = (int)(a.M - m0 < Cfg::BM ? a.M - m0 : Cfg::BM);
+      constexpr int SLAB = Cfg::BM / Cfg::RSPLIT;
+      const int64_t r0 = m0 + (int64_t)part * SLAB;
+      const int rows = (int)(a.M - r0 < SLAB ? a.M - r0 : SLAB);  // <= 0 past a ragged edge
       const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
-      reduce_region<Cfg::RDEPTH, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, m0, n0, rows, cols);
+      reduce_region<Cfg::OCC, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
       __syncthreads();
       if (tid == 0) {
-        int done = atomicAdd(slot32(S, S_REDUCED), 1) + 1;
-        atomicAdd(slot64(S, S_BUSY_R), ticks() - t0);
-        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap);
+        int done = atomicAdd(xslot(S, x, X_REDUCED), 1) + 1;  // this XCD's reduce units
+        atomicAdd(xslot64(S, x, X_BUSY_R), ticks() - t0);
+        if (a.adaptive && (done % (a.ctrl_period * Cfg::RSPLIT)) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     }
     __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
@@ -237,14 +284,15 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
     if (out == a.G - 1) {
       // Every tile must have been reduced unless an error stopped the kernel
       // (e.g. an XCD on which no workgroup ran would leave its queue behind).
-      if (!*slot32(S, S_ABORT) && *slot32(S, S_REDUCED) != a.T) atomicCAS(slot32(S, S_ERROR), 0, MK_ERR_INTERNAL);
+      if (!load_relaxed(slot32(S, S_ABORT)) && sum_xcd32(S, a.n_xcd, X_REDUCED) != a.T * Cfg::RSPLIT)
+        atomicCAS(slot32(S, S_ERROR), 0, MK_ERR_INTERNAL);
       if (a.tel) {
         mk_telemetry_t* t = a.tel;
         t->t_start = *slot64(S, S_TSTART);
         t->t_end = *slot64(S, S_TEND);
-        t->busy_compute = *slot64(S, S_BUSY_C);
-        t->busy_reduce = *slot64(S, S_BUSY_R);
-        t->wait_reduce = *slot64(S, S_WAIT_R);
+        t->busy_compute = sum_xcd64(S, a.n_xcd, X_BUSY_C);
+        t->busy_reduce = sum_xcd64(S, a.n_xcd, X_BUSY_R);
+        t->wait_reduce = sum_xcd64(S, a.n_xcd, X_WAIT_R);
         t->tiles = a.T;
         t->grid = a.G;
         t->initial_target = a.init_target;
@@ -252,9 +300,9 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         t->n_updates = *slot32(S, S_UPDATES);
         int nt = *slot32(S, S_NTRACE);
         t->n_trace = nt < MK_TRACE_CAP ? nt : MK_TRACE_CAP;
-        t->role_switches = *slot32(S, S_SWITCHES);
-        t->reduced_by_compute = *slot32(S, S_RBC);
-        t->computed_by_reducers = *slot32(S, S_CBR);
+        t->role_switches = sum_xcd32(S, a.n_xcd, X_SWITCHES);
+        t->reduced_by_compute = sum_xcd32(S, a.n_xcd, X_RBC) / Cfg::RSPLIT;  // units -> tiles
+        t->computed_by_reducers = sum_xcd32(S, a.n_xcd, X_CBR);
         t->n_xcd = a.n_xcd;
       }
       for (int i = 0; i < S_COUNT; ++i) {
