@@ -211,9 +211,11 @@ mk_status_t validate(const void* A, const void* B, const void* peers, int n_peer
   return MK_OK;
 }
 
-// 256x256 tiles (one workgroup per CU) whenever they still give every CU a
-// tile: they need less L2 traffic per flop and their reducers keep three chunks
-// in flight. Otherwise 128x128 tiles (two workgroups per CU).
+// 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile
+// and the shape has some arithmetic to hide the reduce behind: they need less L2
+// traffic per flop. Otherwise 128x128 tiles (two workgroups per CU): more tiles,
+// finished sooner, for shapes with fewer 256-tiles than CUs or whose work is
+// almost all reduce (below 48 flops per compulsory byte, e.g. K = 512).
 int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
@@ -222,8 +224,7 @@ int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int
   double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
                  (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
   double ai = bytes > 0 ? flops / bytes : 0.0;
-  (void)ai;
-  return t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
+  return t256 >= cus && ai >= 48.0 ? mk::SHAPE_256 : mk::SHAPE_128;
 }
 
 // Host roofline seed for the controller: the reducers' share of the work when
@@ -326,9 +327,11 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   a.flag_scope = (int)opt.flag_scope;
   a.reducer_cap = (int)opt.reducer_cap;
   if (a.reducer_cap <= 0) {
-    // reducers that saturate HBM: about 5.5 TB/s sustained over about 85 GB/s
-    // streamed by one reducer workgroup; a multiple of the XCD count
-    int cap = (int)ceil(5.5e12 / 85e9);
+    // Compute units that saturate HBM with the reduce stream: about 5.5 TB/s
+    // sustained over about 40 GB/s, the most one compute unit streams (measured
+    // on MI355X whatever the loads in flight), times the workgroups per compute
+    // unit; a multiple of the XCD count.
+    int cap = (int)ceil(5.5e12 / 40e9) * (G / L.info.cus > 0 ? G / L.info.cus : 1);
     cap = (cap + a.n_xcd - 1) / a.n_xcd * a.n_xcd;
     a.reducer_cap = cap < G - 1 ? cap : G - 1;
   }
@@ -362,6 +365,9 @@ mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const voi
   g.K = K;
   g.tiles_m = (int)L.tiles_m;
   g.tiles_n = (int)L.tiles_n;
+  const int n_xcd = L.info.cus / 32;  // 32 compute units per XCD on gfx950
+  g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
+  g.pad_ = 0;
   hipError_t e = mk::launch_gemm(L.shape, g, s);
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
   mk::ReduceArgs r;

@@ -77,6 +77,8 @@ struct GemmArgs {
   float* P;
   int64_t M, N, K;
   int tiles_m, tiles_n;
+  int n_xcd;  // workgroup b runs on XCD b % n_xcd; 1 = no XCD-aware mapping
+  int pad_;
 };
 
 struct ReduceArgs {

@@ -319,8 +319,16 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
 template <class Cfg>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
+  // The dispatcher deals workgroups to XCDs in turn (workgroup b on XCD
+  // b % n_xcd). Giving each XCD a contiguous range of the tile order, mapped as
+  // in the fused kernel, lets the tiles that run together on an XCD share A and B
+  // panels in its L2 (dealt in turn, each XCD would read every B panel).
+  const int T = a.tiles_m * a.tiles_n;
+  const int b = blockIdx.x;
+  int t = b;
+  if (a.n_xcd > 1 && T % a.n_xcd == 0) t = (b % a.n_xcd) * (T / a.n_xcd) + b / a.n_xcd;
   int tm, tn;
-  tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  fused_tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
   GemmTile<Cfg> g;
   g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
