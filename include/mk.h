@@ -20,7 +20,9 @@
  *   - reducer workgroups wait for a tile's flag, then add the peer partials and
  *     write C.
  * An on-GPU controller (Figure 2 caption, Figure 7) reads progress counters and
- * publishes how many workgroups should be reducers.
+ * publishes how many workgroups should be reducers. The last tiles of each
+ * XCD's queue, which have no GEMM work left to overlap with, are reduced in
+ * place by the workgroup that computed them (MK_OPT_INPLACE).
  *
  * Layout of every tensor argument: dense, row-major, 16-byte aligned device
  * memory owned by the caller:
@@ -164,7 +166,10 @@ typedef enum {
   MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
   MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
-  MK_OPT_REDUCER_CAP = 5        /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
+  MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
+  MK_OPT_INPLACE = 6            /* tiles per XCD reduced in place by the workgroup that computed them,
+                                   taken from the end of the XCD's queue and capped at half of it:
+                                   -1 = one per workgroup of the XCD (default), 0 = none */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);
@@ -172,13 +177,15 @@ int64_t mk_get_option(int option);
 /* Host copy of the controller rule that the fused kernel runs on the device;
  * exported so that its behaviour can be simulated on the CPU.
  *   G        workgroups, T tiles
- *   computed/reduced   progress counters
- *   busy_c   summed compute-tile time; busy_r summed reduce time without waits
+ *   T_r      tiles handed to reducers (T minus those reduced in place)
+ *   computed tiles computed; reduced: handed-over tiles reduced
+ *   busy_c   summed compute time (in-place tiles whole); busy_r summed reduce
+ *            time of handed-over tiles, without flag waits
  *   seed_x   the host's initial reducer fraction in [0,1]
  *   current  the target now in force
  *   cap      most reducers while GEMM tiles remain (<= 0: G-1)
  * Returns the new target. */
-int mk_controller_eval(int G, int T, int computed, int reduced, uint64_t busy_c,
+int mk_controller_eval(int G, int T, int T_r, int computed, int reduced, uint64_t busy_c,
                        uint64_t busy_r, float seed_x, int current, int cap);
 
 const char* mk_status_string(int status);

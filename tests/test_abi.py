@@ -98,6 +98,13 @@ def test_options_roundtrip():
         mk.set_option(mk.OPT_TILE_SHAPE, 7)
     with pytest.raises(mk.MkError):
         mk.set_option(99, 1)
+    old = mk.get_option(mk.OPT_INPLACE)
+    assert old == -1
+    mk.set_option(mk.OPT_INPLACE, 0)
+    assert mk.get_option(mk.OPT_INPLACE) == 0
+    mk.set_option(mk.OPT_INPLACE, old)
+    with pytest.raises(mk.MkError):
+        mk.set_option(mk.OPT_INPLACE, -2)
 
 
 def test_telemetry_struct_size():

@@ -134,3 +134,16 @@ def test_cap_limits_reducers_while_compute_remains():
     assert capped == 64
     # once every tile is computed, the cap no longer applies
     assert mk.controller_eval(G, 2048, 2048, 1900, 1, 1, 0.9, 64, 64) == G
+
+
+def test_tiles_reduced_in_place_are_compute_work():
+    # Half the tiles reduced in place by their compute workgroup: less work is left
+    # for reducers, so the target drops; once every handed-over tile is reduced the
+    # reducers are told to compute.
+    all_handed = mk.controller_eval(G, 1024, 300, 200, 300 * 50, 200 * 60, 0.5, 128)
+    half_handed = mk.controller_eval(G, 1024, 300, 200, 300 * 50, 200 * 60, 0.5, 128, T_r=512)
+    assert half_handed < all_handed
+    assert mk.controller_eval(G, 1024, 700, 512, 700 * 50, 512 * 60, 0.5, 128, T_r=512) == 1
+    # T_r = T is the rule without in-place tiles
+    assert (mk.controller_eval(G, 1024, 300, 200, 300 * 50, 200 * 60, 0.5, 128, T_r=1024)
+            == all_handed)

@@ -168,6 +168,45 @@ def test_bitwise_invariance_across_reducer_counts():
         check_exact(c_bits(run(A, B, peers, "bf16", mode)), ref, f"mode {mode}")
 
 
+INPLACE_SHAPES = [
+    # M, N, K, n_peers, peer dtype, C dtype: 128x128 tiles with a ragged edge, 256x256
+    # tiles (>= 256 of them), fp32 peers and C
+    (300, 264, 200, 3, "bf16", "bf16"),
+    (1024, 2048, 576, 7, "bf16", "bf16"),
+    (4096, 4096, 256, 1, "bf16", "bf16"),
+    (4096, 4096, 256, 3, "f32", "bf16"),
+    (1024, 1024, 320, 4, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", INPLACE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_inplace_reduce_matches_published(shape):
+    """Tiles reduced in place (partial staged through LDS) give the same bits as tiles
+    handed to reducers, and integer inputs stay exact against the oracle."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"in-place reduce {shape}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 61, device="cpu")
+    rows = sample_rows(M)
+    _, want = oracle_rows(A, B, peers, cdt, rows)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    old = mk.get_option(mk.OPT_INPLACE)
+    try:
+        outs = {}
+        for inplace in (-1, 0, 1 << 20):
+            mk.set_option(mk.OPT_INPLACE, inplace)
+            for nr in (None, 0, 8):
+                C = new_c(M, N, cdt)
+                mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr)
+                mk.stream_status()
+                outs[(inplace, nr)] = (c_bits(C), c_bits(C, rows))
+    finally:
+        mk.set_option(mk.OPT_INPLACE, old)
+    ref = outs[(0, None)][0]
+    for key, (got, got_rows) in outs.items():
+        check_exact(got, ref, f"in-place {key}")
+        check_exact(got_rows, want, f"in-place {key} against the oracle")
+
+
 def test_back_to_back_alternating_inputs():
     """Reducers must never read a partial before its flag: alternate two input sets so
     that any early read would pick up the other set's partial."""
@@ -202,7 +241,7 @@ def test_withheld_flag_times_out_and_recovers():
     old = mk.get_option(mk.OPT_SPIN_TIMEOUT_US)
     try:
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 20000)
-        mk.set_option(mk.OPT_WITHHOLD_TILE, 1)
+        mk.set_option(mk.OPT_WITHHOLD_TILE, 0)  # the first tile of a queue is always published
         mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=4)
         with pytest.raises(mk.MkError) as ei:
             mk.stream_status()

@@ -30,7 +30,7 @@ MK_ADAPTIVE = -1
 MK_MAX_PEERS = 64
 MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
-OPT_FLAG_SCOPE, OPT_REDUCER_CAP = 4, 5
+OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE = 4, 5, 6
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
@@ -68,8 +68,8 @@ _lib.mk_set_option.argtypes = [_int, _i64]
 _lib.mk_set_option.restype = _int
 _lib.mk_get_option.argtypes = [_int]
 _lib.mk_get_option.restype = _i64
-_lib.mk_controller_eval.argtypes = [_int, _int, _int, _int, ctypes.c_uint64, ctypes.c_uint64,
-                                    ctypes.c_float, _int, _int]
+_lib.mk_controller_eval.argtypes = [_int, _int, _int, _int, _int, ctypes.c_uint64,
+                                    ctypes.c_uint64, ctypes.c_float, _int, _int]
 _lib.mk_controller_eval.restype = _int
 _lib.mk_status_string.argtypes = [_int]
 _lib.mk_status_string.restype = ctypes.c_char_p
@@ -205,9 +205,10 @@ def get_option(option):
     return int(_lib.mk_get_option(int(option)))
 
 
-def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap=0):
-    return int(_lib.mk_controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current,
-                                       cap))
+def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap=0, T_r=None):
+    """The controller rule; T_r (tiles handed to reducers) defaults to T."""
+    return int(_lib.mk_controller_eval(G, T, T if T_r is None else T_r, computed, reduced, busy_c,
+                                       busy_r, seed_x, current, cap))
 
 
 def read_telemetry(buf):

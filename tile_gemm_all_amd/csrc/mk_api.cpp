@@ -43,6 +43,7 @@ struct Options {
   int64_t tile_shape = mk::SHAPE_AUTO;
   int64_t flag_scope = 0;
   int64_t reducer_cap = 0;  // 0: derived from HBM bandwidth and a reducer's streaming rate
+  int64_t inplace = -1;     // -1: one round of tiles per XCD reduced in place; 0: none; n: at most n
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -336,6 +337,28 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
     a.reducer_cap = cap < G - 1 ? cap : G - 1;
   }
   if (a.adaptive && a.init_target > a.reducer_cap) a.init_target = a.reducer_cap < 1 ? 1 : a.reducer_cap;
+  // In-place tiles per XCD (the kernel caps them at half of the XCD's queue):
+  // by default one round, i.e. one tile per workgroup of the XCD.
+  a.n_inplace = opt.inplace < 0 ? G / a.n_xcd : (int)opt.inplace;
+  const bool inpl_ok = mk::inplace_supported(G / L.info.cus > 1 ? 2 : 1, dt_size(peer_dtype), n_peers);
+  a.T_r = 0;
+  for (int xi = 0; xi < a.n_xcd; ++xi) {
+    const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
+    a.T_r += cnt - mk::xcd_inplace(cnt, a.n_inplace, inpl_ok);
+  }
+  // The seed share counts the in-place tiles' reduce as compute-side work.
+  if (a.T > 0 && a.T_r < a.T) {
+    double flops = 2.0 * (double)M * (double)N * (double)K;
+    double red_bytes = (double)M * (double)N * (4.0 + n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
+    double t_r = red_bytes * ((double)a.T_r / a.T) / 8.0e12;
+    double t_c = flops / 2.5e15 + red_bytes * ((double)(a.T - a.T_r) / a.T) / 8.0e12;
+    a.seed_x = (float)(t_r / (t_r + t_c));
+    if (a.adaptive) {
+      int it = (int)(a.seed_x * G + 0.5f);
+      it = it < 1 ? 1 : (it > a.reducer_cap ? a.reducer_cap : it);
+      a.init_target = it;
+    }
+  }
   hipError_t e = mk::launch_fused(L.shape, peer_dtype, c_dtype, a, s);
   if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   return MK_OK;
@@ -474,6 +497,10 @@ mk_status_t mk_set_option(int option, int64_t value) {
       if (value < 0) return fail(MK_ERR_INVALID_ARG, "reducer cap %lld", (long long)value);
       g_opt.reducer_cap = value;
       return MK_OK;
+    case MK_OPT_INPLACE:
+      if (value < -1 || value > (1 << 30)) return fail(MK_ERR_INVALID_ARG, "in-place tiles %lld", (long long)value);
+      g_opt.inplace = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -487,13 +514,14 @@ int64_t mk_get_option(int option) {
     case MK_OPT_TILE_SHAPE: return g_opt.tile_shape;
     case MK_OPT_FLAG_SCOPE: return g_opt.flag_scope;
     case MK_OPT_REDUCER_CAP: return g_opt.reducer_cap;
+    case MK_OPT_INPLACE: return g_opt.inplace;
   }
   return -1;
 }
 
-int mk_controller_eval(int G, int T, int computed, int reduced, uint64_t busy_c, uint64_t busy_r,
-                       float seed_x, int current, int cap) {
-  return mk::controller_rule(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap);
+int mk_controller_eval(int G, int T, int T_r, int computed, int reduced, uint64_t busy_c,
+                       uint64_t busy_r, float seed_x, int current, int cap) {
+  return mk::controller_rule(G, T, T_r, computed, reduced, busy_c, busy_r, seed_x, current, cap);
 }
 
 const char* mk_status_string(int status) {

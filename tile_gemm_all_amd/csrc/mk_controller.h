@@ -8,14 +8,16 @@
 // the pages, so this file states the rule adopted here:
 //
 //   remaining compute work   W_c = (T - c) / rho_c   (workgroup-time)
-//   remaining reduce work    W_r = (T - r) / rho_r
+//   remaining reduce work    W_r = (T_r - r) / rho_r
 //   reducer share            x   = W_r / (W_c + W_r)
 //   target                   clamp(round(G * x), 1, G - 1) while compute remains,
 //                            G once every tile is computed.
 //
-// rho_c = tiles computed per unit of compute-role busy time; rho_r = tiles
-// reduced per unit of reducer busy time *excluding* time spent waiting for
-// flags, so idle reducers do not look slow. Both finish at the same time when
+// T_r <= T is the number of tiles handed to reducers (the others are reduced in
+// place by the workgroup that computed them, and their whole time counts as
+// compute). rho_c = tiles computed per unit of compute-role busy time; rho_r =
+// handed-over tiles reduced per unit of reducer busy time *excluding* time
+// spent waiting for flags, so idle reducers do not look slow. Both finish at the same time when
 // the reducers hold the share x of the workgroups. Until both rates have been
 // measured, x is the host's seed (roofline estimate). A change smaller than
 // max(1, G/64) is ignored (hysteresis).
@@ -37,15 +39,18 @@
 
 namespace mk {
 
-MK_HD inline int controller_rule(int G, int T, int computed, int reduced, uint64_t busy_c,
-                                 uint64_t busy_r, float seed_x, int current, int cap) {
+MK_HD inline int controller_rule(int G, int T, int T_r, int computed, int reduced,
+                                 uint64_t busy_c, uint64_t busy_r, float seed_x, int current,
+                                 int cap) {
   if (G <= 1) return G <= 0 ? 0 : current;
   if (computed >= T) return G;
   float x = seed_x;
-  if (computed > 0 && reduced > 0 && busy_c > 0 && busy_r > 0) {
+  if (reduced >= T_r) {
+    x = 0.0f;  // nothing left for reducers while compute remains
+  } else if (computed > 0 && reduced > 0 && busy_c > 0 && busy_r > 0) {
     // W = remaining / rate = remaining * busy / done
     float wc = (float)(T - computed) * ((float)busy_c / (float)computed);
-    float wr = (float)(T - reduced) * ((float)busy_r / (float)reduced);
+    float wr = (float)(T_r - reduced) * ((float)busy_r / (float)reduced);
     x = (wc + wr) > 0.0f ? wr / (wc + wr) : seed_x;
   }
   if (!(x >= 0.0f)) x = 0.0f;  // also catches NaN

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mk_kernels.h"
+
 namespace mk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -403,6 +405,39 @@ struct GemmTile {
         }
       }
   }
+
+  // In-place reduce of a tile: the fp32 accumulators go through LDS (BN floats
+  // per row) in NPASS passes. Pass p takes accumulator blocks fm in
+  // [p*FM/NPASS, (p+1)*FM/NPASS) of every wave, i.e. for each wave row wm the
+  // band of BAND tile rows starting at wm*WM + p*BAND; the two bands sit one
+  // after the other in LDS. Blocks of later passes stay in registers meanwhile
+  // (at most half of them), so the reduce that follows has room.
+  static constexpr int LDS_ROWS = Cfg::LDS_BYTES / (Cfg::BN * 4);
+  static constexpr int NPASS = Cfg::BM / LDS_ROWS;
+  static constexpr int BAND = Cfg::WM / NPASS;
+  static_assert(NPASS >= 1 && Cfg::BM % LDS_ROWS == 0 && Cfg::FM % NPASS == 0, "LDS passes");
+  static_assert(2 * BAND == LDS_ROWS, "two bands of wave rows per pass");
+
+  // Lanes 0-31 and 32-63 each write 128 contiguous bytes per store, which
+  // touches every bank once.
+  template <int PASS>
+  __device__ __forceinline__ void stage_pass_lds(char* lds) const {
+    typedef __attribute__((address_space(3))) float lds_float;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    lds_float* f = (lds_float*)(lds_char*)lds;
+    constexpr int F0 = PASS * Cfg::FM / NPASS, F1 = (PASS + 1) * Cfg::FM / NPASS;
+#pragma unroll
+    for (int fm = F0; fm < F1; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < Cfg::FN; ++fn) {
+        const int col = wn * Cfg::WN + fn * 32 + (lane & 31);
+        const int rbase = wm * BAND + (fm - F0) * 32 + (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          f[(rbase + (i >> 2) * 8 + (i & 3)) * Cfg::BN + col] = acc[fm][fn][i];
+      }
+  }
 };
 
 // ----------------------------------------------------------------- reduce
@@ -520,17 +555,37 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
 // end is clamped to the last chunk: that lane reads the same inputs as the lane
 // that owns the chunk and stores the same bits to the same place, so no lane
 // needs a branch, and the loop runs on a wave-uniform bound.
+// Where a chunk's fp32 partial comes from: the workspace in device memory, or
+// LDS (a tile reduced in place by the workgroup that computed it). Both give
+// the same bits.
+struct PartialGlobal {
+  const float* __restrict__ P;  // region base
+  __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t off, uint32_t) const {
+    const uint32_t op = off * 4u;
+    a = *(const f32x4*)((const char*)P + op);
+    b = *(const f32x4*)((const char*)P + op + 16u);
+  }
+};
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+struct PartialLds {
+  const lds_char* base;  // region base in LDS, rows of the LDS pitch
+  __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t, uint32_t loff) const {
+    a = *(const lds_f32x4*)(base + loff * 4u);
+    b = *(const lds_f32x4*)(base + loff * 4u + 16u);
+  }
+};
+
 template <typename PT, int NP>
 struct ChunkLoads {
   f32x4 pa, pb;
   PeerLoad<PT> v[NP];
   // Byte offsets are formed in 32 bits, so each load is a scalar base plus a
   // 32-bit vector offset.
-  __device__ __forceinline__ void load(const float* __restrict__ P,
-                                       const PT* const __restrict__* peer, uint32_t off) {
-    const uint32_t op = off * 4u, ov = off * (uint32_t)sizeof(PT);
-    pa = *(const f32x4*)((const char*)P + op);
-    pb = *(const f32x4*)((const char*)P + op + 16u);
+  template <typename PS>
+  __device__ __forceinline__ void load(const PS& ps, const PT* const __restrict__* peer,
+                                       uint32_t off, uint32_t loff) {
+    ps.load(pa, pb, off, loff);
+    const uint32_t ov = off * (uint32_t)sizeof(PT);
 #pragma unroll
     for (int s = 0; s < NP; ++s) v[s].load((const PT*)((const char*)peer[s] + ov));
     __builtin_amdgcn_sched_barrier(0);  // keep the group where the ring puts it
@@ -545,57 +600,64 @@ struct ChunkLoads {
   }
 };
 
-// Walks chunk indices q = q0, q0+256, ... of a region of `cpr` chunks per row
-// (row pitch N elements), giving each one's element offset, clamped to the last
-// chunk past the end.
+// Walks chunk indices q = q0, q0+256, ... of a region of `cpr` chunks per row,
+// giving each one's element offset for two row pitches (N for device memory, LP
+// for a copy of the partial in LDS), clamped to the last chunk past the end.
 struct ChunkCursor {
-  int q, c;             // chunk index and its column chunk
-  uint32_t off;         // element offset of chunk q (unclamped)
+  int q, c;                 // chunk index and its column chunk
+  uint32_t off, loff;       // element offsets of chunk q (unclamped)
   int total, cpr;
-  uint32_t last;        // element offset of the last chunk
-  uint32_t step_off;    // offset advance for 256 chunks without a row wrap
-  int step_c;           // column-chunk advance for 256 chunks (256 % cpr)
-  uint32_t wrap_off;    // extra advance when the column wraps: N - 8 * cpr
-  __device__ __forceinline__ void init(int q0, int total_, int cpr_, int64_t N) {
+  uint32_t last, llast;     // element offsets of the last chunk
+  uint32_t step_off, step_loff;  // advance for 256 chunks without a row wrap
+  int step_c;               // column-chunk advance for 256 chunks (256 % cpr)
+  uint32_t wrap_off, wrap_loff;  // extra advance when the column wraps: pitch - 8 * cpr
+  __device__ __forceinline__ void init(int q0, int total_, int cpr_, int64_t N, int64_t LP) {
     total = total_;
     cpr = cpr_;
     const int r = q0 / cpr_;
     c = q0 - r * cpr_;
     q = q0;
     off = (uint32_t)(r * N + c * 8);
+    loff = (uint32_t)(r * LP + c * 8);
     const int rows = total_ / cpr_;
     last = (uint32_t)((rows - 1) * N + (cpr_ - 1) * 8);
+    llast = (uint32_t)((rows - 1) * LP + (cpr_ - 1) * 8);
     const int a = kThreads / cpr_;
     step_c = kThreads - a * cpr_;
     step_off = (uint32_t)(a * N + step_c * 8);
+    step_loff = (uint32_t)(a * LP + step_c * 8);
     wrap_off = (uint32_t)(N - 8 * cpr_);
+    wrap_loff = (uint32_t)(LP - 8 * cpr_);
   }
   __device__ __forceinline__ uint32_t get() const { return q < total ? off : last; }
+  __device__ __forceinline__ uint32_t lget() const { return q < total ? loff : llast; }
   __device__ __forceinline__ void advance() {
     q += kThreads;
     c += step_c;
     off += step_off;
+    loff += step_loff;
     const bool wrap = c >= cpr;
     c = wrap ? c - cpr : c;
     off = wrap ? off + wrap_off : off;
+    loff = wrap ? loff + wrap_loff : loff;
   }
 };
 
 template <int DEPTH, typename PT, int NP>
 struct ReduceRing {
-  template <typename CT>
-  __device__ __forceinline__ static void run(const float* __restrict__ P,
-                                             const PT* const __restrict__* peer,
-                                             CT* __restrict__ C, int total, int cpr, int64_t N) {
+  template <typename CT, typename PS>
+  __device__ __forceinline__ static void run(const PS& ps, const PT* const __restrict__* peer,
+                                             CT* __restrict__ C, int total, int cpr, int64_t N,
+                                             int64_t LP) {
     // loop bound on the wave's first chunk: a uniform (scalar) loop
     const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
     ChunkCursor ld, st;  // the chunk loaded next, the chunk summed next
-    ld.init(threadIdx.x, total, cpr, N);
+    ld.init(threadIdx.x, total, cpr, N, LP);
     st = ld;
     ChunkLoads<PT, NP> b[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH - 1; ++i) {
-      b[i].load(P, peer, ld.get());
+      b[i].load(ps, peer, ld.get(), ld.lget());
       ld.advance();
     }
     // At least one pass, so that no guard separates the loads above from the
@@ -604,7 +666,7 @@ struct ReduceRing {
     do {
 #pragma unroll
       for (int i = 0; i < DEPTH; ++i) {
-        b[(i + DEPTH - 1) % DEPTH].load(P, peer, ld.get());
+        b[(i + DEPTH - 1) % DEPTH].load(ps, peer, ld.get(), ld.lget());
         ld.advance();
         b[i].template finish<CT>(C, st.get());
         st.advance();
@@ -635,8 +697,11 @@ __host__ __device__ constexpr int ring_depth() {
 // Whether even a depth-2 ring fits the register budget (else the generic path).
 template <int OCC, typename PT, int NP>
 __host__ __device__ constexpr bool ring_fits() {
-  return 2 * (8 + NP * (sizeof(PT) == 2 ? 4 : 8)) <= (OCC == 1 ? 320 : 160);
+  return ring_fits_regs(OCC, (int)sizeof(PT), NP);
 }
+
+// Peer counts with a compile-time ring (others take the generic path).
+#define MK_RING_PEER_COUNTS(X) X(1) X(2) X(3) X(4) X(7) X(8) X(15)
 
 // Reduce the region rows [m0, m0+rows) x cols [n0, n0+cols) of an M x N output;
 // cols is a multiple of 8. All 256 threads of the workgroup take part; the
@@ -658,13 +723,13 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
     if constexpr (ring_fits<OCC, PT, NPV>()) {                                         \
       const PT* pr[NPV];                                                               \
       _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base; \
-      ReduceRing<ring_depth<OCC, PT, NPV>(), PT, NPV>::template run<CT>(P + base, pr, C + base, \
-                                                                          total, cpr, N); \
+      ReduceRing<ring_depth<OCC, PT, NPV>(), PT, NPV>::template run<CT>(                \
+          PartialGlobal{P + base}, pr, C + base, total, cpr, N, N);                    \
       return;                                                                          \
     }                                                                                  \
     break;
   switch (n_peers) {
-    MK_RING(1) MK_RING(2) MK_RING(3) MK_RING(4) MK_RING(7) MK_RING(8) MK_RING(15)
+    MK_RING_PEER_COUNTS(MK_RING)
     default: break;
   }
 #undef MK_RING
@@ -681,6 +746,38 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
     int64_t e[1] = {off(q)};
     reduce_chunks<1, PT, CT>(P, peers, n_peers, stride, C, e);
   }
+}
+
+// The same for a region whose fp32 partial sits in LDS (row pitch LP elements,
+// first row and column of the region at lds). Only peer counts for which
+// lds_reduce_supported() holds.
+template <int OCC, typename PT, typename CT>
+__device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
+                                                  const PT* __restrict__ peers, int n_peers,
+                                                  CT* __restrict__ C, int64_t M, int64_t N,
+                                                  int64_t m0, int64_t n0, int rows, int cols) {
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  const int total = rows * cpr;
+  if (total <= 0) return;
+  const int64_t stride = M * N;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+  const PartialLds ps{(const lds_char*)lds};
+#define MK_RING(NPV)                                                                   \
+  case NPV:                                                                            \
+    if constexpr (ring_fits<OCC, PT, NPV>()) {                                         \
+      const PT* pr[NPV];                                                               \
+      _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base; \
+      ReduceRing<ring_depth<OCC, PT, NPV>(), PT, NPV>::template run<CT>(ps, pr, C + base, \
+                                                                          total, cpr, N, LP); \
+    }                                                                                  \
+    return;
+  switch (n_peers) {
+    MK_RING_PEER_COUNTS(MK_RING)
+    default: return;
+  }
+#undef MK_RING
 }
 
 }  // namespace mk

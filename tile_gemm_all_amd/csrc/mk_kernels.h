@@ -25,6 +25,7 @@ enum XcdSlot : int {
   X_SWITCHES,          // workgroup role changes
   X_RBC,               // reduce units done by workgroups that prefer compute (draining)
   X_CBR,               // tiles computed by workgroups that prefer reducing (helping)
+  X_INPLACE,           // tiles reduced in place by the workgroup that computed them
   kXcdWords
 };
 constexpr int kMaxXcd = 16;
@@ -47,6 +48,30 @@ constexpr int kThreadsHost = 256;  // workgroup size of every kernel
 
 enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2 };
 
+// Peer counts that have a compile-time reduce ring, and whether that ring fits
+// the register budget of a lane at `occ` workgroups per compute unit (peers of
+// peer_bytes bytes: 8 registers of partial plus 4 or 8 per peer per chunk, two
+// chunks at least). A tile can be reduced in place (partial in LDS) only then.
+// Shared by the host (which counts the tiles handed to reducers) and the kernels.
+constexpr bool ring_peer_count(int np) {
+  return np == 1 || np == 2 || np == 3 || np == 4 || np == 7 || np == 8 || np == 15;
+}
+constexpr bool ring_fits_regs(int occ, int peer_bytes, int np) {
+  return 2 * (8 + np * (peer_bytes == 2 ? 4 : 8)) <= (occ == 1 ? 320 : 160);
+}
+constexpr bool inplace_supported(int occ, int peer_bytes, int np) {
+  return ring_peer_count(np) && ring_fits_regs(occ, peer_bytes, np);
+}
+// Tiles of XCD x's queue (T tiles over n_xcd XCDs) and how many of them are
+// reduced in place (the last ones, at most half).
+constexpr int xcd_tiles(int T, int n_xcd, int x) {
+  return (int)(((int64_t)(x + 1) * T) / n_xcd - ((int64_t)x * T) / n_xcd);
+}
+constexpr int xcd_inplace(int cnt, int n_inplace, bool supported) {
+  if (!supported) return 0;
+  return n_inplace < cnt / 2 ? n_inplace : cnt / 2;
+}
+
 struct FusedArgs {
   const uint16_t* A;
   const uint16_t* B;
@@ -68,6 +93,8 @@ struct FusedArgs {
   int n_xcd;                   // XCDs of the device; tiles are queued per XCD
   int flag_scope;              // 0: producer and consumer share an XCD's L2; 1: agent scope
   int reducer_cap;             // controller's upper bound on reducers while compute remains
+  int n_inplace;               // per XCD: last tiles of the queue reduced in place (capped at half)
+  int T_r;                     // tiles handed to reducers (T minus the in-place ones)
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
 };
 

@@ -69,15 +69,16 @@ __device__ __forceinline__ void raise_error(unsigned long long* S, int code) {
 // Takes its inputs by value: the kernel's argument block must not escape to
 // memory, or every pointer read from it loses its global address space.
 __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry_t* tel, int G,
-                                             int T, int epoch, int init_target, float seed_x,
-                                             int cap, int rsplit, int n_xcd) {
+                                             int T, int T_r, int epoch, int init_target,
+                                             float seed_x, int cap, int rsplit, int n_xcd) {
   if (atomicCAS(slot32(S, S_LOCK), 0, 1) != 0) return;
   int c = sum_xcd32(S, n_xcd, X_COMPUTED);
-  int r = sum_xcd32(S, n_xcd, X_REDUCED) / rsplit;  // reduce units -> tiles
+  // handed-over tiles reduced: reduce units -> tiles, minus those done in place
+  int r = sum_xcd32(S, n_xcd, X_REDUCED) / rsplit - sum_xcd32(S, n_xcd, X_INPLACE);
   unsigned long long bc = sum_xcd64(S, n_xcd, X_BUSY_C);
   unsigned long long br = sum_xcd64(S, n_xcd, X_BUSY_R);
   int cur = current_target(S, epoch, init_target);
-  int nt = controller_rule(G, T, c, r, bc, br, seed_x, cur, cap);
+  int nt = controller_rule(G, T, T_r, c, r, bc, br, seed_x, cur, cap);
   if (nt != cur) {
     unsigned long long w = ((unsigned long long)(unsigned)epoch << 32) | (unsigned)nt;
     __hip_atomic_store(slot64(S, S_TARGET), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -134,12 +135,19 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
   int rank = 0, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
   if (tid == 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+  // The last n_in tiles of the XCD's queue are reduced in place by the workgroup
+  // that computes them: no compute is left to overlap with, so handing them to
+  // reducers would only add the partial's round trip through memory. At most
+  // half of the queue, so that flags and reducers carry the rest.
+  const int n_in = xcd_inplace(cnt, a.n_inplace,
+                               inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers));
+  const int published = cnt - n_in;
 
   for (;;) {
     if (tid == 0) {
       int kind = K_EXIT, tile = -1, part = 0;
       bool off_role = false;
-      const int units = cnt * Cfg::RSPLIT;  // reduce unit r: slab r % RSPLIT of tile r / RSPLIT
+      const int units = published * Cfg::RSPLIT;  // unit r: slab r % RSPLIT of tile r / RSPLIT
       int* rnext = xslot(S, x, X_REDUCE_NEXT);
       // Every pass claims work or leaves; nothing here waits.
       for (;;) {
@@ -179,7 +187,19 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           }
         }
         const int r = load_relaxed(rnext);
-        if (r >= units) break;  // every unit is taken: leave
+        if (r >= units) {
+          // Every reduce unit is taken. Tiles reduced in place have no units, so
+          // GEMM tiles may remain: take one before leaving.
+          if (pref_reduce) {
+            const int i = claim_compute(S, x, cnt);
+            if (i >= 0) {
+              kind = K_COMPUTE;
+              tile = q0 + i;
+              off_role = true;
+            }
+          }
+          break;
+        }
         if (pref_reduce && load_relaxed(a.flags + q0 + r / Cfg::RSPLIT) != a.epoch) {
           // The next unit's tile is not finished: compute meanwhile, if a GEMM
           // tile is left, rather than wait for its flag.
@@ -223,6 +243,36 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       GemmTile<Cfg> g;
       g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+      if (tile - q0 >= published) {
+        // In place: the partial goes through LDS (freed by the GEMM's last
+        // barrier) in passes, each summed in the same order as a reducer would.
+        const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
+        auto pass = [&](auto pass_c) {
+          constexpr int PASS = decltype(pass_c)::value;
+          constexpr int BAND = GemmTile<Cfg>::BAND;
+          g.template stage_pass_lds<PASS>(lds);
+          __syncthreads();
+#pragma unroll
+          for (int wm = 0; wm < 2; ++wm) {
+            const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
+            const int rows = (int)(a.M - r0 < BAND ? a.M - r0 : BAND);  // <= 0 past the edge
+            reduce_region_lds<Cfg::OCC, PT, CT>(lds + wm * BAND * Cfg::BN * 4, Cfg::BN, peers,
+                                                a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
+          }
+          __syncthreads();
+        };
+        pass(std::integral_constant<int, 0>{});
+        if constexpr (GemmTile<Cfg>::NPASS > 1) pass(std::integral_constant<int, 1>{});
+        if (tid == 0) {
+          // the whole tile counts as compute work for the controller
+          atomicAdd(xslot(S, x, X_COMPUTED), 1);
+          atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
+          atomicAdd(xslot(S, x, X_REDUCED), Cfg::RSPLIT);
+          atomicAdd(xslot(S, x, X_INPLACE), 1);
+        }
+        __syncthreads();
+        continue;
+      }
       g.store_partial(a.P, a.M, a.N, m0, n0);
       wait_stores();    // this wave's partial stores have reached the L2
       __syncthreads();  // ... and so have every other wave's
@@ -233,7 +283,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         }
         int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;  // this XCD's count
         atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
-        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
+        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     } else {
       if (tid == 0) {
@@ -269,7 +319,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       if (tid == 0) {
         int done = atomicAdd(xslot(S, x, X_REDUCED), 1) + 1;  // this XCD's reduce units
         atomicAdd(xslot64(S, x, X_BUSY_R), ticks() - t0);
-        if (a.adaptive && (done % (a.ctrl_period * Cfg::RSPLIT)) == 0) controller_step(S, a.tel, a.G, a.T, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
+        if (a.adaptive && (done % (a.ctrl_period * Cfg::RSPLIT)) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     }
     __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
@@ -277,8 +327,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
 
   // ---- exit: the last workgroup out resets the claim and progress counters
   if (tid == 0) {
-    atomicMin(slot64(S, S_TSTART), t_begin);
-    atomicMax(slot64(S, S_TEND), ticks());
+    if (a.tel) {  // kernel span, for telemetry only (chip-wide atomics serialise)
+      atomicMin(slot64(S, S_TSTART), t_begin);
+      atomicMax(slot64(S, S_TEND), ticks());
+    }
     int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_ACQ_REL,
                                      __HIP_MEMORY_SCOPE_AGENT);
     if (out == a.G - 1) {
