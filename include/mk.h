@@ -120,7 +120,7 @@ typedef struct {
  *   c_dtype        : MK_DT_BF16 or MK_DT_F32.
  *   stream         : hipStream_t (NULL = default stream).
  *   n_reduce_wg    : 0 .. G-1 dedicated reducer workgroups (G =
- *                    mk_num_workgroups()), or MK_ADAPTIVE. With 0, compute
+ *                    mk_fused_grid() of these arguments), or MK_ADAPTIVE. With 0, compute
  *                    workgroups reduce the tiles once no GEMM tile is left;
  *                    the same draining applies in every mode.
  *   telemetry      : NULL or a device buffer of sizeof(mk_telemetry_t).
@@ -153,10 +153,12 @@ mk_status_t mk_workspace_reset(int device);
  * failure. */
 int mk_num_workgroups(int device);
 
-/* G for a call with these arguments on the current device (the tile shape, and
- * with it the number of workgroups per compute unit, depends on the shape).
- * n_reduce_wg of that call must lie in [0, G-1] or be MK_ADAPTIVE. Returns a
- * negative mk_status_t on failure. */
+/* G for a call with these arguments on the current device: the resident
+ * workgroup slots of the chosen tile shape (compute units times 1 for 256x256
+ * tiles, times 2 for 128x128), but at most two per tile (rounded up to a
+ * multiple of the XCD count) for calls with few tiles. n_reduce_wg of that call
+ * must lie in [0, G-1] or be MK_ADAPTIVE. Returns a negative mk_status_t on
+ * failure. */
 int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype);
 
 /* Tunables and debug switches (process-wide; read at each call). */

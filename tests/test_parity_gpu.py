@@ -221,7 +221,7 @@ def test_back_to_back_alternating_inputs():
     G = mk.fused_grid(sets[0][0], sets[0][1], sets[0][2], C)
     for i in range(60):
         A, B, peers, want = sets[i % 2]
-        nr = [None, 0, G - 1, 8, 200][i % 5]
+        nr = [None, 0, G - 1, 8, min(200, G - 2)][i % 5]
         mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr)
         if i % 2 == 1 or i > 50:
             mk.stream_status()

@@ -245,6 +245,21 @@ struct Launch {
   int64_t tiles_m, tiles_n;
 };
 
+// Persistent grid of the fused kernel: every resident workgroup slot (compute
+// units times workgroups per unit), but no more than two workgroups per tile,
+// rounded up to a multiple of the XCD count, so that a call with few tiles does
+// not start hundreds of workgroups that only find no work and leave.
+int fused_grid_size(const Launch& L, int peer_dtype, int c_dtype) {
+  const int full = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  int n_xcd = L.info.cus / 32;
+  if (n_xcd < 1) n_xcd = 1;
+  const int64_t T = L.tiles_m * L.tiles_n;
+  int64_t want = 2 * T;
+  want = (want + n_xcd - 1) / n_xcd * n_xcd;
+  if (want < n_xcd) want = n_xcd;
+  return want < full ? (int)want : full;
+}
+
 mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype,
                     Launch& L) {
   int dev = 0;
@@ -274,7 +289,7 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   Launch L;
   st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
   if (st != MK_OK) return st;
-  const int G = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  const int G = fused_grid_size(L, peer_dtype, c_dtype);
   if (n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
   if (M == 0 || N == 0) return MK_OK;
@@ -332,7 +347,8 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
     // sustained over about 40 GB/s, the most one compute unit streams (measured
     // on MI355X whatever the loads in flight), times the workgroups per compute
     // unit; a multiple of the XCD count.
-    int cap = (int)ceil(5.5e12 / 40e9) * (G / L.info.cus > 0 ? G / L.info.cus : 1);
+    const int occ = L.shape == mk::SHAPE_256 ? 1 : 2;  // workgroups per compute unit
+    int cap = (int)ceil(5.5e12 / 40e9) * occ;
     cap = (cap + a.n_xcd - 1) / a.n_xcd * a.n_xcd;
     a.reducer_cap = cap < G - 1 ? cap : G - 1;
   }
@@ -340,7 +356,8 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   // In-place tiles per XCD (the kernel caps them at half of the XCD's queue):
   // by default one round, i.e. one tile per workgroup of the XCD.
   a.n_inplace = opt.inplace < 0 ? G / a.n_xcd : (int)opt.inplace;
-  const bool inpl_ok = mk::inplace_supported(G / L.info.cus > 1 ? 2 : 1, dt_size(peer_dtype), n_peers);
+  const bool inpl_ok =
+      mk::inplace_supported(L.shape == mk::SHAPE_256 ? 1 : 2, dt_size(peer_dtype), n_peers);
   a.T_r = 0;
   for (int xi = 0; xi < a.n_xcd; ++xi) {
     const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
@@ -468,7 +485,7 @@ int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, 
   Launch L;
   mk_status_t st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
   if (st != MK_OK) return -(int)st;
-  return L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  return fused_grid_size(L, peer_dtype, c_dtype);
 }
 
 mk_status_t mk_set_option(int option, int64_t value) {
