@@ -127,7 +127,8 @@ uint16_t mko_f64_to_bf16_rne(double x) {
  * addition is split into its rounded sum and the exact rounding error by the
  * two-sum transformation), then adds the partials from the largest down and
  * corrects the single case where that last rounding lands on a tie. */
-#define MKO_MAX_PARTIALS 64
+#define MKO_MAX_PARTIALS 64 /* non-overlapping partials of doubles: about 40 at most */
+#define MKO_MAX_PEERS 64    /* peer values held per output element */
 static double exact_sum(const double* x, int n) {
   double p[MKO_MAX_PARTIALS];
   int np = 0;
@@ -189,7 +190,7 @@ static double peer_value(const void* peers, int dtype, int64_t idx) {
 int mko_gemm_ar(const uint16_t* A, const uint16_t* B, const void* peers, int n_peers,
                 int peer_dtype, int64_t M, int64_t N, int64_t K, const int64_t* rows,
                 int64_t n_rows, double* C64, void* C_out, int c_dtype, int n_threads) {
-  if (M < 0 || N < 0 || K < 0 || n_peers < 0 || n_peers > MKO_MAX_PARTIALS - 8) return -1;
+  if (M < 0 || N < 0 || K < 0 || n_peers < 0 || n_peers > MKO_MAX_PEERS) return -1;
   if ((K > 0 && (!A || !B)) || (n_peers > 0 && !peers)) return -1;
   if (peer_dtype != MKO_BF16 && peer_dtype != MKO_F32) return -1;
   if (c_dtype != MKO_BF16 && c_dtype != MKO_F32) return -1;
@@ -205,7 +206,7 @@ int mko_gemm_ar(const uint16_t* A, const uint16_t* B, const void* peers, int n_p
 #pragma omp parallel
   {
     double* G = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
-    double pv[MKO_MAX_PARTIALS];
+    double pv[MKO_MAX_PEERS];
     if (!G) {
 #pragma omp atomic write
       status = -1;

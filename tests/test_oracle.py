@@ -357,6 +357,24 @@ def test_oracle_rejects_bad_arguments():
         oracle.gemm_ar(A, np.zeros((7, 8), np.uint16), None)
     with pytest.raises(ValueError):
         oracle.gemm_ar(A, np.zeros((8, 8), np.uint16), None, rows=[4])
+    with pytest.raises(ValueError):  # more peers than the library accepts (64)
+        oracle.gemm_ar(A, np.zeros((8, 8), np.uint16), np.zeros((65, 4, 8), np.uint16))
+
+
+def test_oracle_sums_the_most_peers_exactly():
+    """64 peers spanning many binades: the peer sum equals math.fsum of them, and the
+    result with A = 0 is its correct rounding."""
+    rng = np.random.default_rng(9)
+    vals = (rng.standard_normal((64, 2, 8)) * np.exp2(rng.integers(-60, 60, (64, 2, 8))))
+    peers = vals.astype(np.float32)
+    A = np.zeros((2, 8), np.uint16)
+    B = np.zeros((8, 8), np.uint16)
+    C64, C32 = oracle.gemm_ar(A, B, peers, "f32")
+    for i in range(2):
+        for j in range(8):
+            want = math.fsum(float(v) for v in peers[:, i, j])
+            assert C64[i, j] == want
+            assert C32[i, j] == np.float32(want)
 
 
 MUTANTS = {1: "drops the last peer", 2: "reads a mirrored column of B", 3: "subtracts the peers",
