@@ -36,7 +36,8 @@
  * identical for every reducer count, for the adaptive controller and for the
  * two-kernel baseline.
  *
- * Supported shapes: M >= 0 (any), N and K multiples of 8 (16-byte rows).
+ * Supported shapes: M >= 0 (any), N and K multiples of 8 (16-byte rows),
+ * N <= 4194304 (2^22).
  * M == 0 or N == 0 is a no-op. K == 0 gives C = sum of peers. n_peers == 0
  * gives C = A*B. 0 <= n_peers <= MK_MAX_PEERS.
  *

@@ -68,6 +68,7 @@ def base(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt
     (dict(C=A16), mk.MK_ERR_INVALID_ARG),               # C aliases A
     (dict(C=P16 + 64 * 64 * 2), mk.MK_ERR_INVALID_ARG),  # C inside peer 1
     (dict(M=1 << 41), mk.MK_ERR_UNSUPPORTED),
+    (dict(M=1, N=(1 << 22) + 8, C=C16 + (1 << 30)), mk.MK_ERR_UNSUPPORTED),  # N beyond 2^22
 ])
 def test_validation_rejects(kw, status):
     assert call(**kw) == status, mk.last_error()

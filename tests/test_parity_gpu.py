@@ -93,6 +93,9 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
     (64, 64, 0, 2, "bf16", "f32"),           # K == 0: C is the peer sum
     (257, 520, 264, 7, "f32", "bf16"),
     (520, 776, 1032, 1, "bf16", "f32"),
+    (200, 136, 96, 5, "bf16", "bf16"),       # peer counts without a compile-time ring
+    (130, 264, 104, 9, "f32", "f32"),
+    (72, 64, 48, 64, "bf16", "bf16"),        # most peers
 ]
 
 

@@ -191,6 +191,10 @@ mk_status_t validate(const void* A, const void* B, const void* peers, int n_peer
   if (N % 8 != 0 || K % 8 != 0)
     return fail(MK_ERR_UNSUPPORTED, "N=%lld and K=%lld must be multiples of 8", (long long)N,
                 (long long)K);
+  // The reducers address a tile's rows (at most 256) with 32-bit byte offsets
+  // from the tile's first element: 256 rows of N fp32 values must stay below 4 GiB.
+  if (N > ((int64_t)1 << 22))
+    return fail(MK_ERR_UNSUPPORTED, "N=%lld exceeds 4194304", (long long)N);
   const int64_t lim = (int64_t)1 << 40;
   if (M > lim || N > lim || K > lim || (M > 0 && N > lim / M) || (M > 0 && K > lim / M) ||
       (N > 0 && K > lim / N) || (n_peers > 0 && M * N > lim / n_peers))
