@@ -172,7 +172,8 @@ typedef enum {
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
   MK_OPT_INPLACE = 6            /* tiles per XCD reduced in place by the workgroup that computed them,
                                    taken from the end of the XCD's queue and capped at half of it:
-                                   -1 = one per workgroup of the XCD (default), 0 = none */
+                                   -1 = automatic (default: one per workgroup of the XCD for shapes
+                                   below 315 flops per compulsory byte, else none), 0 = none */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

@@ -357,9 +357,19 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
     a.reducer_cap = cap < G - 1 ? cap : G - 1;
   }
   if (a.adaptive && a.init_target > a.reducer_cap) a.init_target = a.reducer_cap < 1 ? 1 : a.reducer_cap;
-  // In-place tiles per XCD (the kernel caps them at half of the XCD's queue):
-  // by default one round, i.e. one tile per workgroup of the XCD.
-  a.n_inplace = opt.inplace < 0 ? G / a.n_xcd : (int)opt.inplace;
+  // In-place tiles per XCD (the kernel caps them at half of the XCD's queue).
+  // Automatic: one round, i.e. one tile per workgroup of the XCD, for shapes
+  // bound by memory traffic (below the ridge of about 315 flops per byte), where
+  // skipping the partial's round trip pays; none for compute-bound shapes, whose
+  // last round would then run GEMM and reduce back to back on the same units.
+  if (opt.inplace < 0) {
+    const double flops = 2.0 * (double)M * (double)N * (double)K;
+    const double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
+                         (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
+    a.n_inplace = bytes > 0 && flops / bytes < 315.0 ? G / a.n_xcd : 0;
+  } else {
+    a.n_inplace = (int)opt.inplace;
+  }
   const bool inpl_ok =
       mk::inplace_supported(L.shape == mk::SHAPE_256 ? 1 : 2, dt_size(peer_dtype), n_peers);
   a.T_r = 0;
