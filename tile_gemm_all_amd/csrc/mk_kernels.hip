@@ -331,9 +331,16 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       atomicMin(slot64(S, S_TSTART), t_begin);
       atomicMax(slot64(S, S_TEND), ticks());
     }
-    int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_ACQ_REL,
+    // Every counter this workgroup updated is an atomic, performed where all
+    // XCDs see it; waiting for them to complete (vmcnt = 0) before counting out
+    // orders them before the exit count without the agent-scope release, which
+    // would write back the whole XCD L2 for every workgroup. The last workgroup
+    // out acquires before it reads the counters.
+    wait_stores();
+    int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     if (out == a.G - 1) {
+      acquire_fence_agent();
       // Every tile must have been reduced unless an error stopped the kernel
       // (e.g. an XCD on which no workgroup ran would leave its queue behind).
       if (!load_relaxed(slot32(S, S_ABORT)) && sum_xcd32(S, a.n_xcd, X_REDUCED) != a.T * Cfg::RSPLIT)
