@@ -96,7 +96,10 @@ __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry
       tel->trace[i] = e;
     }
   }
-  __hip_atomic_store(slot32(S, S_LOCK), 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  // Unlock once this thread's stores (target, trace) have completed; an
+  // agent-scope release would write back the whole XCD L2 at every update.
+  wait_stores();
+  __hip_atomic_store(slot32(S, S_LOCK), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
