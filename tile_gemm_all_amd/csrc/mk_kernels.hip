@@ -105,13 +105,6 @@ __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry
 enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
 
 
-// Claims the next GEMM tile of this XCD's queue; returns its local index or -1.
-__device__ __forceinline__ int claim_compute(unsigned long long* S, int x, int cnt) {
-  int* next = xslot(S, x, X_COMPUTE_NEXT);
-  if (load_relaxed(next) >= cnt) return -1;
-  int i = atomicAdd(next, 1);
-  return i < cnt ? i : -1;
-}
 
 // Persistent fused kernel. Tiles [start_x, start_x + cnt_x) belong to XCD x: only
 // workgroups running on XCD x compute or reduce them, so a tile's partial is
@@ -137,6 +130,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const int q0 = (int)(((int64_t)x * a.T) / a.n_xcd);
   const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
   int rank = 0, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
+  bool flag_seen = false;  // thread 0: the claimed unit's flag was already read as set
   if (tid == 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
   // The last n_in tiles of the XCD's queue are reduced in place by the workgroup
   // that computes them: no compute is left to overlap with, so handing them to
@@ -152,10 +146,19 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       bool off_role = false;
       const int units = published * Cfg::RSPLIT;  // unit r: slab r % RSPLIT of tile r / RSPLIT
       int* rnext = xslot(S, x, X_REDUCE_NEXT);
-      // Every pass claims work or leaves; nothing here waits.
+      int* cnext = xslot(S, x, X_COMPUTE_NEXT);
+      flag_seen = false;
+      // Every pass claims work or leaves; nothing here waits for other
+      // workgroups. The state every decision reads is loaded in one round trip
+      // (independent loads), and a pass ends with at most two atomics.
       for (;;) {
-        if (load_relaxed(slot32(S, S_ABORT))) break;
-        const int target = current_target(S, a.epoch, a.init_target);
+        const int abort = load_relaxed(slot32(S, S_ABORT));
+        const unsigned long long tw =
+            __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int cn = load_relaxed(cnext);  // tiles claimed for compute (a lower bound)
+        const int rn = load_relaxed(rnext);  // next reduce unit
+        if (abort) break;
+        const int target = (int)(tw >> 32) == a.epoch ? (int)(tw & 0xFFFFFFFFu) : a.init_target;
         const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
         const bool pref_reduce = rank < tx;
         if (held >= 0) {
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           // then this workgroup computes the next tile itself: that claim cannot
           // fail while the reserved tile is unclaimed, so the XCD always makes
           // progress.
-          if (held / Cfg::RSPLIT < load_relaxed(xslot(S, x, X_COMPUTE_NEXT))) {
+          if (held / Cfg::RSPLIT < cn) {
             kind = K_REDUCE;
             tile = q0 + held / Cfg::RSPLIT;
             part = held % Cfg::RSPLIT;
@@ -172,8 +175,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
             held = -1;
             break;
           }
-          const int i = claim_compute(S, x, cnt);
-          if (i >= 0) {
+          const int i = atomicAdd(cnext, 1);
+          if (i < cnt) {
             kind = K_COMPUTE;
             tile = q0 + i;
             off_role = pref_reduce;
@@ -181,21 +184,20 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           }
           continue;  // the tile was claimed meanwhile
         }
-        if (!pref_reduce) {
-          const int i = claim_compute(S, x, cnt);
-          if (i >= 0) {
+        if (!pref_reduce && cn < cnt) {
+          const int i = atomicAdd(cnext, 1);
+          if (i < cnt) {
             kind = K_COMPUTE;
             tile = q0 + i;
             break;
           }
         }
-        const int r = load_relaxed(rnext);
-        if (r >= units) {
+        if (rn >= units) {
           // Every reduce unit is taken. Tiles reduced in place have no units, so
           // GEMM tiles may remain: take one before leaving.
-          if (pref_reduce) {
-            const int i = claim_compute(S, x, cnt);
-            if (i >= 0) {
+          if (pref_reduce && cn < cnt) {
+            const int i = atomicAdd(cnext, 1);
+            if (i < cnt) {
               kind = K_COMPUTE;
               tile = q0 + i;
               off_role = true;
@@ -203,21 +205,35 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           }
           break;
         }
-        if (pref_reduce && load_relaxed(a.flags + q0 + r / Cfg::RSPLIT) != a.epoch) {
-          // The next unit's tile is not finished: compute meanwhile, if a GEMM
-          // tile is left, rather than wait for its flag.
-          const int i = claim_compute(S, x, cnt);
-          if (i >= 0) {
-            kind = K_COMPUTE;
-            tile = q0 + i;
-            off_role = true;
-            break;
+        int fl = 0;
+        if (pref_reduce && cn < cnt) {
+          // GEMM tiles are left: reserve the next unit only if its tile is
+          // finished, else compute meanwhile rather than wait for its flag.
+          fl = load_relaxed(a.flags + q0 + rn / Cfg::RSPLIT);
+          if (fl != a.epoch) {
+            const int i = atomicAdd(cnext, 1);
+            if (i < cnt) {
+              kind = K_COMPUTE;
+              tile = q0 + i;
+              off_role = true;
+              break;
+            }
           }
         }
         // Reserve the next reduce unit (a fetch-add always succeeds, unlike a
         // compare-and-swap that 32 workgroups of an XCD would retry in turn).
         held = atomicAdd(rnext, 1);
         if (held >= units) {
+          held = -1;
+          break;
+        }
+        if (held / Cfg::RSPLIT < cn) {
+          kind = K_REDUCE;
+          tile = q0 + held / Cfg::RSPLIT;
+          part = held % Cfg::RSPLIT;
+          off_role = !pref_reduce;
+          // the flag read above covers this unit when it is the same tile
+          flag_seen = fl == a.epoch && held / Cfg::RSPLIT == rn / Cfg::RSPLIT;
           held = -1;
           break;
         }
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       if (tid == 0) {
         const unsigned long long w0 = ticks();
         int ok = 1, backoff = 1;
-        while (load_relaxed(a.flags + tile) != a.epoch) {
+        while (!flag_seen && load_relaxed(a.flags + tile) != a.epoch) {
           if (load_relaxed(slot32(S, S_ABORT))) {
             ok = 0;
             break;
@@ -320,9 +336,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       reduce_region<Cfg::OCC, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
       __syncthreads();
       if (tid == 0) {
-        int done = atomicAdd(xslot(S, x, X_REDUCED), 1) + 1;  // this XCD's reduce units
+        // No returned value is needed: the controller runs on compute
+        // completions, the only phase in which its target matters.
+        atomicAdd(xslot(S, x, X_REDUCED), 1);
         atomicAdd(xslot64(S, x, X_BUSY_R), ticks() - t0);
-        if (a.adaptive && (done % (a.ctrl_period * Cfg::RSPLIT)) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     }
     __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
