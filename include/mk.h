@@ -20,9 +20,11 @@
  *   - reducer workgroups wait for a tile's flag, then add the peer partials and
  *     write C.
  * An on-GPU controller (Figure 2 caption, Figure 7) reads progress counters and
- * publishes how many workgroups should be reducers. The last tiles of each
- * XCD's queue, which have no GEMM work left to overlap with, are reduced in
- * place by the workgroup that computed them (MK_OPT_INPLACE).
+ * publishes how many workgroups should be reducers. Tiles can instead be
+ * reduced in place by the workgroup that computed them, through its LDS, with
+ * no partial in memory and no flag (MK_OPT_INPLACE): on MI355X that is the
+ * faster path for most tiles, and by default only the first tiles of each
+ * XCD's queue of a memory-bound shape are handed to reducers.
  *
  * Layout of every tensor argument: dense, row-major, 16-byte aligned device
  * memory owned by the caller:
@@ -170,10 +172,11 @@ typedef enum {
   MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
-  MK_OPT_INPLACE = 6            /* tiles per XCD reduced in place by the workgroup that computed them,
-                                   taken from the end of the XCD's queue and capped at half of it:
-                                   -1 = automatic (default: one per workgroup of the XCD for shapes
-                                   below 315 flops per compulsory byte, else none), 0 = none */
+  MK_OPT_INPLACE = 6            /* tiles per XCD reduced in place by the workgroup that computed them
+                                   (the last ones of the XCD's queue; the others are handed to
+                                   reducers through flags): -1 = automatic (default: all of them for
+                                   shapes at or above 315 flops per compulsory byte; otherwise all
+                                   but the first min(queue/4, workgroups per XCD/2)), 0 = none */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);
@@ -187,7 +190,7 @@ int64_t mk_get_option(int option);
  *            time of handed-over tiles, without flag waits
  *   seed_x   the host's initial reducer fraction in [0,1]
  *   current  the target now in force
- *   cap      most reducers while GEMM tiles remain (<= 0: G-1)
+ *   cap      most reducers while GEMM tiles remain (< 0: G-1; 0: none)
  * Returns the new target. */
 int mk_controller_eval(int G, int T, int T_r, int computed, int reduced, uint64_t busy_c,
                        uint64_t busy_r, float seed_x, int current, int cap);

@@ -147,3 +147,10 @@ def test_tiles_reduced_in_place_are_compute_work():
     # T_r = T is the rule without in-place tiles
     assert (mk.controller_eval(G, 1024, 300, 200, 300 * 50, 200 * 60, 0.5, 128, T_r=1024)
             == all_handed)
+
+
+def test_zero_cap_keeps_every_workgroup_computing():
+    # cap 0: no dedicated reducers while GEMM tiles remain, everyone at the end
+    assert mk.controller_eval(G, 1024, 300, 0, 0, 0, 0.4, 0, cap=0) == 0
+    assert mk.controller_eval(G, 1024, 300, 200, 300 * 50, 200 * 60, 0.9, 5, cap=0) == 0
+    assert mk.controller_eval(G, 1024, 1024, 200, 1, 1, 0.9, 0, cap=0) == G

@@ -99,9 +99,19 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 ]
 
 
+@pytest.fixture(params=[-1, 0], ids=["inplace-auto", "handover-all"])
+def inplace_policy(request):
+    """Runs a test under the default in-place policy and with every tile handed to
+    reducers through its flag (the role-split path)."""
+    old = mk.get_option(mk.OPT_INPLACE)
+    mk.set_option(mk.OPT_INPLACE, request.param)
+    yield request.param
+    mk.set_option(mk.OPT_INPLACE, old)
+
+
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}-{s[5]}")
 @pytest.mark.parametrize("mode", MODES)
-def test_small_integer_bit_exact(shape, mode):
+def test_small_integer_bit_exact(shape, mode, inplace_policy):
     M, N, K, npeer, pdt, cdt = shape
     announce(f"integer {shape} {mode}")
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 7, device="cpu")
@@ -161,7 +171,7 @@ def test_workload_parity(w, variant):
     torch.cuda.empty_cache()
 
 
-def test_bitwise_invariance_across_reducer_counts():
+def test_bitwise_invariance_across_reducer_counts(inplace_policy):
     announce("invariance across reducer counts")
     M, N, K, npeer = 1024, 2048, 576, 7
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "gaussian", 21, device=DEV)
@@ -210,7 +220,7 @@ def test_inplace_reduce_matches_published(shape):
         check_exact(got_rows, want, f"in-place {key} against the oracle")
 
 
-def test_back_to_back_alternating_inputs():
+def test_back_to_back_alternating_inputs(inplace_policy):
     """Reducers must never read a partial before its flag: alternate two input sets so
     that any early read would pick up the other set's partial."""
     announce("alternating inputs")
@@ -242,9 +252,11 @@ def test_withheld_flag_times_out_and_recovers():
     A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
     C = new_c(M, N, "bf16")
     old = mk.get_option(mk.OPT_SPIN_TIMEOUT_US)
+    old_inplace = mk.get_option(mk.OPT_INPLACE)
     try:
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 20000)
-        mk.set_option(mk.OPT_WITHHOLD_TILE, 0)  # the first tile of a queue is always published
+        mk.set_option(mk.OPT_INPLACE, 0)  # every tile handed over through its flag
+        mk.set_option(mk.OPT_WITHHOLD_TILE, 0)
         mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=4)
         with pytest.raises(mk.MkError) as ei:
             mk.stream_status()
@@ -252,6 +264,7 @@ def test_withheld_flag_times_out_and_recovers():
     finally:
         mk.set_option(mk.OPT_WITHHOLD_TILE, -1)
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, old)
+        mk.set_option(mk.OPT_INPLACE, old_inplace)
     mk.stream_status()  # error word was cleared
     mk.gemm_ar_local(A, B, peers, C)
     mk.stream_status()
@@ -263,8 +276,8 @@ def test_withheld_flag_times_out_and_recovers():
     check_exact(c_bits(C2), want, "after workspace reset")
 
 
-def test_telemetry_and_controller_trace():
-    announce("telemetry")
+def test_telemetry_and_controller_trace(inplace_policy):
+    announce(f"telemetry, in-place policy {inplace_policy}")
     w = mk_inputs.BY_NAME["mlp"]
     A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device=DEV)
     C = new_c(w.M, w.N, "bf16")
@@ -276,14 +289,18 @@ def test_telemetry_and_controller_trace():
     assert t.tiles in ((w.M // 256) * (w.N // 256), (w.M // 128) * (w.N // 128))
     assert t.grid == G
     assert t.n_xcd == 8
-    assert 1 <= t.initial_target <= G - 1
-    assert 1 <= t.final_target <= G
+    # with tiles reduced in place the derived cap keeps every workgroup computing
+    # (target 0) while GEMM tiles remain; with every tile handed over, at least one
+    # workgroup reduces
+    lo = 0 if inplace_policy != 0 else 1
+    assert lo <= t.initial_target <= G - 1
+    assert lo <= t.final_target <= G
     assert 0 < t.n_trace <= mk.MK_TRACE_CAP
     assert t.t_end > t.t_start
     assert t.busy_compute > 0 and t.busy_reduce > 0
     targets = [t.trace[i].target for i in range(t.n_trace)]
     computed = [t.trace[i].computed for i in range(t.n_trace)]
     assert all(a <= b for a, b in zip(computed, computed[1:]))
-    assert all(1 <= x <= G for x in targets)
+    assert all(lo <= x <= G for x in targets)
     # once every tile is computed the controller hands all workgroups to the reduce
     assert all(t.trace[i].target == G for i in range(t.n_trace) if computed[i] == t.tiles)

@@ -205,8 +205,9 @@ def get_option(option):
     return int(_lib.mk_get_option(int(option)))
 
 
-def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap=0, T_r=None):
-    """The controller rule; T_r (tiles handed to reducers) defaults to T."""
+def controller_eval(G, T, computed, reduced, busy_c, busy_r, seed_x, current, cap=-1, T_r=None):
+    """The controller rule; T_r (tiles handed to reducers) defaults to T; cap < 0 means
+    up to G-1 reducers while compute remains, 0 none."""
     return int(_lib.mk_controller_eval(G, T, T if T_r is None else T_r, computed, reduced, busy_c,
                                        busy_r, seed_x, current, cap))
 

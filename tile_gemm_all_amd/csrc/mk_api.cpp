@@ -357,16 +357,26 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
     a.reducer_cap = cap < G - 1 ? cap : G - 1;
   }
   if (a.adaptive && a.init_target > a.reducer_cap) a.init_target = a.reducer_cap < 1 ? 1 : a.reducer_cap;
-  // In-place tiles per XCD (the kernel caps them at half of the XCD's queue).
-  // Automatic: one round, i.e. one tile per workgroup of the XCD, for shapes
-  // bound by memory traffic (below the ridge of about 315 flops per byte), where
-  // skipping the partial's round trip pays; none for compute-bound shapes, whose
-  // last round would then run GEMM and reduce back to back on the same units.
+  // In-place tiles per XCD, counted from the end of the XCD's queue. Automatic:
+  //  - compute-bound shapes (at or above the ridge of about 315 flops per
+  //    compulsory byte): every tile. Workgroups drift apart over the rounds, so
+  //    one's reduce overlaps another's GEMM, and no partial makes the round trip
+  //    through memory.
+  //  - memory-bound shapes: all but the first min(cnt/4, W/2) tiles of each
+  //    queue (W = workgroups per XCD). Those are handed to reducers, so that
+  //    after the first round half of the workgroups start their next GEMM while
+  //    the other half reduce, instead of every workgroup alternating in step.
   if (opt.inplace < 0) {
     const double flops = 2.0 * (double)M * (double)N * (double)K;
     const double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
                          (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
-    a.n_inplace = bytes > 0 && flops / bytes < 315.0 ? G / a.n_xcd : 0;
+    const int cnt0 = a.T / a.n_xcd;  // shortest queue
+    int hand = 0;
+    if (bytes > 0 && flops / bytes < 315.0) {
+      const int w = G / a.n_xcd;
+      hand = cnt0 / 4 < w / 2 ? cnt0 / 4 : w / 2;
+    }
+    a.n_inplace = cnt0 - hand;
   } else {
     a.n_inplace = (int)opt.inplace;
   }
@@ -377,6 +387,13 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
     const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
     a.T_r += cnt - mk::xcd_inplace(cnt, a.n_inplace, inpl_ok);
   }
+  // With tiles reduced in place, compute workgroups do most of the reduce
+  // themselves; a dedicated reducer takes a compute unit away from the GEMM and
+  // competes with them for memory bandwidth (measured on the 4096x8192x1792
+  // shape: 0 reducers 324 us, one per XCD 351 us, 64 348 us). The derived cap
+  // is then zero: the adaptive controller keeps every workgroup computing while
+  // GEMM tiles remain, and all of them drain the handed-over tiles.
+  if (opt.reducer_cap <= 0 && a.T_r < a.T) a.reducer_cap = 0;
   // The seed share counts the in-place tiles' reduce as compute-side work.
   if (a.T > 0 && a.T_r < a.T) {
     double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -386,7 +403,8 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
     a.seed_x = (float)(t_r / (t_r + t_c));
     if (a.adaptive) {
       int it = (int)(a.seed_x * G + 0.5f);
-      it = it < 1 ? 1 : (it > a.reducer_cap ? a.reducer_cap : it);
+      const int lo = a.reducer_cap < 1 ? a.reducer_cap : 1;
+      it = it < lo ? lo : (it > a.reducer_cap ? a.reducer_cap : it);
       a.init_target = it;
     }
   }

@@ -56,13 +56,15 @@ MK_HD inline int controller_rule(int G, int T, int T_r, int computed, int reduce
   if (!(x >= 0.0f)) x = 0.0f;  // also catches NaN
   if (x > 1.0f) x = 1.0f;
   int target = (int)(x * (float)G + 0.5f);
-  int hi = cap >= 1 && cap < G - 1 ? cap : G - 1;
+  // cap < 0: up to G-1 reducers; cap == 0: none while compute remains
+  const int hi = cap >= 0 && cap < G - 1 ? cap : G - 1;
+  const int lo = hi < 1 ? hi : 1;
   if (target > hi) target = hi;
-  if (target < 1) target = 1;
+  if (target < lo) target = lo;
   int band = G / 64 > 1 ? G / 64 : 1;
   int d = target - current;
   if (d < 0) d = -d;
-  if (current >= 1 && current <= hi && d < band) return current;
+  if (current >= lo && current <= hi && d < band) return current;
   return target;
 }
 

@@ -63,13 +63,13 @@ constexpr bool inplace_supported(int occ, int peer_bytes, int np) {
   return ring_peer_count(np) && ring_fits_regs(occ, peer_bytes, np);
 }
 // Tiles of XCD x's queue (T tiles over n_xcd XCDs) and how many of them are
-// reduced in place (the last ones, at most half).
+// reduced in place (the last ones).
 constexpr int xcd_tiles(int T, int n_xcd, int x) {
   return (int)(((int64_t)(x + 1) * T) / n_xcd - ((int64_t)x * T) / n_xcd);
 }
 constexpr int xcd_inplace(int cnt, int n_inplace, bool supported) {
   if (!supported) return 0;
-  return n_inplace < cnt / 2 ? n_inplace : cnt / 2;
+  return n_inplace < cnt ? (n_inplace > 0 ? n_inplace : 0) : cnt;
 }
 
 struct FusedArgs {
@@ -93,7 +93,7 @@ struct FusedArgs {
   int n_xcd;                   // XCDs of the device; tiles are queued per XCD
   int flag_scope;              // 0: producer and consumer share an XCD's L2; 1: agent scope
   int reducer_cap;             // controller's upper bound on reducers while compute remains
-  int n_inplace;               // per XCD: last tiles of the queue reduced in place (capped at half)
+  int n_inplace;               // per XCD: last tiles of the queue reduced in place
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
 };
