@@ -1,7 +1,8 @@
 """Benchmark: fused GEMM+AllReduce (one GPU's share) on MI355X.
 
 A step is one call of the fused persistent kernel (mk_gemm_ar_local, adaptive
-reducer count) over one batch of synthetic inputs already resident in HBM:
+reducer count, default in-place policy) over one batch of synthetic inputs
+already resident in HBM:
 C = A*B + sum of 15 peer partials for the Llama-70B-like MLP down-projection
 shard (M=4096 tokens, N=8192, K=1792 = 28672/16, P=16; bf16 A/B/peers/C, fp32
 accumulation). The two-kernel baseline (GEMM kernel, then reduce kernel) is timed
@@ -134,6 +135,11 @@ def main():
         return start.elapsed_time(stop) / steps  # ms per launch
 
     base_ms = timed(two_kernel, args.steps, args.warmup)
+    # the role-split path alone: every tile handed to reducers through its flag
+    old_inplace = mk.get_option(mk.OPT_INPLACE)
+    mk.set_option(mk.OPT_INPLACE, 0)
+    handover_ms = timed(fused, args.steps, args.warmup)
+    mk.set_option(mk.OPT_INPLACE, old_inplace)
     t0 = time.perf_counter()
     fused_ms = timed(fused, args.steps, args.warmup)
     wall = time.perf_counter() - t0
@@ -165,6 +171,7 @@ def main():
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "two_kernel_ms": round(base_ms, 5),
         "speedup_vs_two_kernel": round(base_ms / fused_ms, 4),
+        "handover_all_ms": round(handover_ms, 5),
         "timed_wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -12,7 +12,7 @@ kept under profiles/.
       --kernel-trace run.
 
   python bench_rocprof.py traffic --fetch DIR --write DIR --copy-fetch DIR
-      --copy-write DIR --kernel NAME --workload NAME --cmd "<cmds>" [--out FILE]
+      --copy-write DIR --kernel NAME --workload NAME --cmd "<cmds>" [--last N] [--out FILE]
       HBM bytes per launch of kernel NAME from two --pmc runs (FETCH_SIZE, then
       WRITE_SIZE), each scaled by the factor that the same counter shows for the
       copy workload (bytes moved / counter bytes). Writes JSON with the kernel
@@ -50,12 +50,13 @@ def kernel_rows(d):
 
 
 def counter_rows(d, counter):
-    """{kernel name: [value per dispatch]} for one counter of a --pmc run."""
+    """{kernel name: [value per dispatch, in dispatch order]} for one counter of a
+    --pmc run."""
     rows = {}
     for db in _dbs(d):
         con = sqlite3.connect(db)
         q = ("select dispatch_id, kernel_name, sum(value) from counters_collection "
-             "where counter_name = ? group by dispatch_id, kernel_name")
+             "where counter_name = ? group by dispatch_id, kernel_name order by dispatch_id")
         for _, name, val in con.execute(q, (counter,)):
             rows.setdefault(name, []).append(float(val))
         con.close()
@@ -114,6 +115,8 @@ def cmd_traffic(args):
     w_factor = copy_bytes / (sum(cw) / len(cw) * kib)
     name, kf = _pick(counter_rows(args.fetch, "FETCH_SIZE"), args.kernel)
     _, kw = _pick(counter_rows(args.write, "WRITE_SIZE"), args.kernel)
+    if args.last:  # only the last dispatches (e.g. the calls bench.py times last)
+        kf, kw = kf[-args.last:], kw[-args.last:]
     fetch = sum(kf) / len(kf) * kib * f_factor
     write = sum(kw) / len(kw) * kib * w_factor
     per_kernel = {}
@@ -156,6 +159,8 @@ def main():
         t.add_argument(a, required=True)
     t.add_argument("--copy-kernel", default="neg")
     t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--last", type=int, default=0,
+                   help="use only the last N dispatches of the kernel")
     t.add_argument("--out")
     args = ap.parse_args()
     {"copy": cmd_copy, "kernels": cmd_kernels, "traffic": cmd_traffic}[args.what](args)
