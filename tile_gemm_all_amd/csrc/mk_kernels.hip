@@ -118,7 +118,7 @@ enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
 template <class Cfg, typename PT, typename CT>
 __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) {
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
-  __shared__ int s_kind, s_tile, s_part, s_ok;
+  __shared__ int s_kind, s_tile, s_part, s_ok, s_last;
   const int tid = threadIdx.x;
   unsigned long long* S = a.slots;
   const PT* peers = (const PT*)a.peers;
@@ -129,9 +129,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const int x = xcc_id() % a.n_xcd;
   const int q0 = (int)(((int64_t)x * a.T) / a.n_xcd);
   const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
-  int rank = 0, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
+  int rank = -1, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
   bool flag_seen = false;  // thread 0: the claimed unit's flag was already read as set
-  if (tid == 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
   // The last n_in tiles of the XCD's queue are reduced in place by the workgroup
   // that computes them: no compute is left to overlap with, so handing them to
   // reducers would only add the partial's round trip through memory. At most
@@ -157,6 +156,9 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
             __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int cn = load_relaxed(cnext);  // tiles claimed for compute (a lower bound)
         const int rn = load_relaxed(rnext);  // next reduce unit
+        // The arrival rank is taken in the first pass, in the same round trip
+        // as the loads above.
+        if (rank < 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
         if (abort) break;
         const int target = (int)(tw >> 32) == a.epoch ? (int)(tw & 0xFFFFFFFFu) : a.init_target;
         const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
@@ -359,7 +361,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
     wait_stores();
     int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-    if (out == a.G - 1) {
+    s_last = out == a.G - 1;
+    if (s_last) {
       acquire_fence_agent();
       // Every tile must have been reduced unless an error stopped the kernel
       // (e.g. an XCD on which no workgroup ran would leave its queue behind).
@@ -384,11 +387,17 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         t->computed_by_reducers = sum_xcd32(S, a.n_xcd, X_CBR);
         t->n_xcd = a.n_xcd;
       }
-      for (int i = 0; i < S_COUNT; ++i) {
-        if (i == S_ERROR || i == S_TARGET) continue;
-        __hip_atomic_store(slot64(S, i), i == S_TSTART ? ~0ull : 0ull, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
+    }
+  }
+  // The barrier also waits for thread 0's reads above, so the reset below
+  // cannot overtake them.
+  __syncthreads();
+  if (s_last) {
+    // One word per thread: a serial loop on one thread costs over 10 us.
+    for (int i = tid; i < S_COUNT; i += kThreads) {
+      if (i == S_ERROR || i == S_TARGET) continue;
+      __hip_atomic_store(slot64(S, i), i == S_TSTART ? ~0ull : 0ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
