@@ -32,11 +32,11 @@
  *   B      [K, N]            bfloat16
  *   peers  [n_peers, M, N]   peer_dtype (bfloat16 or float32), one contiguous block
  *   C      [M, N]            c_dtype    (bfloat16 or float32)
- * Accumulation is float32. Peer partials are added to the local fp32 partial in
- * index order (local partial first, then peers[0], peers[1], ...); the sum is
- * rounded once to c_dtype, round to nearest even. The result is bitwise
- * identical for every reducer count, for the adaptive controller and for the
- * two-kernel baseline.
+ * Accumulation is float32. The peer partials are summed in index order
+ * (peers[0] + peers[1] + ...), then the local fp32 partial is added; the sum is
+ * rounded once to c_dtype, round to nearest even (with no peers, C is the
+ * rounded partial). The result is bitwise identical for every reducer count,
+ * every option below, the adaptive controller and the two-kernel baseline.
  *
  * Supported shapes: M >= 0 (any), N and K multiples of 8 (16-byte rows),
  * N <= 4194304 (2^22).
@@ -158,8 +158,10 @@ int mk_num_workgroups(int device);
 
 /* G for a call with these arguments on the current device: the resident
  * workgroup slots of the chosen tile shape (compute units times 1 for 256x256
- * tiles, times 2 for 128x128), but at most two per tile (rounded up to a
- * multiple of the XCD count) for calls with few tiles. n_reduce_wg of that call
+ * tiles, times 2 for 128x128), but at most two per tile (with early reduce, see
+ * MK_OPT_EARLY: one per tile plus one per reduce unit of BM/64 rows), rounded
+ * up to a multiple of the XCD count, for calls with few tiles. It depends on the
+ * options in force at the time of the call. n_reduce_wg of that call
  * must lie in [0, G-1] or be MK_ADAPTIVE. Returns a negative mk_status_t on
  * failure. */
 int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype);
@@ -172,11 +174,19 @@ typedef enum {
   MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
-  MK_OPT_INPLACE = 6            /* tiles per XCD reduced in place by the workgroup that computed them
+  MK_OPT_INPLACE = 6,           /* tiles per XCD reduced in place by the workgroup that computed them
                                    (the last ones of the XCD's queue; the others are handed to
-                                   reducers through flags): -1 = automatic (default: all of them for
-                                   shapes at or above 315 flops per compulsory byte; otherwise all
-                                   but the first min(queue/4, workgroups per XCD/2)), 0 = none */
+                                   reducers through flags): -1 = automatic (default: none with early
+                                   reduce; all of them for shapes at or above 315 flops per
+                                   compulsory byte; otherwise all but the first min(queue/4,
+                                   workgroups per XCD/2)), 0 = none */
+  MK_OPT_EARLY = 7              /* early reduce: a reducer may take a unit whose tile is still being
+                                   computed and sums that unit's peers (into LDS) while it waits for
+                                   the tile's flag. -1 = automatic (default: on when every tile and
+                                   every reduce unit gets a workgroup of its own in one round, e.g.
+                                   few-tile decode shapes; the grid then holds one workgroup per
+                                   tile plus one per unit, and tiles are handed over rather than
+                                   reduced in place), 0 = off, 1 = on. Peer counts 1-4, 7, 8, 15. */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

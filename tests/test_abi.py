@@ -106,6 +106,13 @@ def test_options_roundtrip():
     mk.set_option(mk.OPT_INPLACE, old)
     with pytest.raises(mk.MkError):
         mk.set_option(mk.OPT_INPLACE, -2)
+    assert mk.get_option(mk.OPT_EARLY) == -1
+    mk.set_option(mk.OPT_EARLY, 1)
+    assert mk.get_option(mk.OPT_EARLY) == 1
+    mk.set_option(mk.OPT_EARLY, -1)
+    for bad in (-2, 2):
+        with pytest.raises(mk.MkError):
+            mk.set_option(mk.OPT_EARLY, bad)
 
 
 def test_telemetry_struct_size():

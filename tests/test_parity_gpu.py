@@ -6,7 +6,8 @@ thelatestinai.com page). Bars:
   - Gaussian inputs: tests/compare.py's rule (literal 2e-3*rms(C) bound for fp32 C;
     that bound plus half a bfloat16 ulp for bf16 C);
   - the output is bitwise identical for every reducer count, for the adaptive
-    controller and for the baseline (all reduce in the same order).
+    controller, for every reduce schedule (tiles reduced in place, handed over,
+    peers summed early) and for the baseline (all reduce in the same order).
 Full-size workloads are checked on sampled rows (first, last and one random row of
 every 256-row band), with the oracle evaluating those rows only.
 """
@@ -99,14 +100,20 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 ]
 
 
-@pytest.fixture(params=[-1, 0], ids=["inplace-auto", "handover-all"])
+@pytest.fixture(params=[(-1, -1), (0, 0), (0, 1)],
+                ids=["auto", "handover-all", "handover-all-early"])
 def inplace_policy(request):
-    """Runs a test under the default in-place policy and with every tile handed to
-    reducers through its flag (the role-split path)."""
-    old = mk.get_option(mk.OPT_INPLACE)
-    mk.set_option(mk.OPT_INPLACE, request.param)
-    yield request.param
-    mk.set_option(mk.OPT_INPLACE, old)
+    """Runs a test under the default policies (in place and early reduce automatic),
+    with every tile handed to reducers through its flag (the role-split path), and
+    the same with reducers that sum a unit's peers before its tile is finished (early
+    reduce). Yields the in-place option."""
+    inplace, early = request.param
+    old = mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY)
+    mk.set_option(mk.OPT_INPLACE, inplace)
+    mk.set_option(mk.OPT_EARLY, early)
+    yield inplace
+    mk.set_option(mk.OPT_INPLACE, old[0])
+    mk.set_option(mk.OPT_EARLY, old[1])
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}-{s[5]}")
@@ -202,19 +209,22 @@ def test_inplace_reduce_matches_published(shape):
     rows = sample_rows(M)
     _, want = oracle_rows(A, B, peers, cdt, rows)
     A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
-    old = mk.get_option(mk.OPT_INPLACE)
+    old = mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY)
     try:
         outs = {}
         for inplace in (-1, 0, 1 << 20):
             mk.set_option(mk.OPT_INPLACE, inplace)
-            for nr in (None, 0, 8):
-                C = new_c(M, N, cdt)
-                mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr)
-                mk.stream_status()
-                outs[(inplace, nr)] = (c_bits(C), c_bits(C, rows))
+            for early in (0, 1):
+                mk.set_option(mk.OPT_EARLY, early)
+                for nr in (None, 0, 8):
+                    C = new_c(M, N, cdt)
+                    mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr)
+                    mk.stream_status()
+                    outs[(inplace, early, nr)] = (c_bits(C), c_bits(C, rows))
     finally:
-        mk.set_option(mk.OPT_INPLACE, old)
-    ref = outs[(0, None)][0]
+        mk.set_option(mk.OPT_INPLACE, old[0])
+        mk.set_option(mk.OPT_EARLY, old[1])
+    ref = outs[(0, 0, None)][0]
     for key, (got, got_rows) in outs.items():
         check_exact(got, ref, f"in-place {key}")
         check_exact(got_rows, want, f"in-place {key} against the oracle")
@@ -242,10 +252,11 @@ def test_back_to_back_alternating_inputs(inplace_policy):
     mk.stream_status()
 
 
-def test_withheld_flag_times_out_and_recovers():
+@pytest.mark.parametrize("early", [0, 1])
+def test_withheld_flag_times_out_and_recovers(early):
     """Failure injection from the host: one tile's flag is never published; reducers
     give up after a short wait, the kernel exits normally, and the error is reported."""
-    announce("withheld flag")
+    announce(f"withheld flag, early reduce {early}")
     M, N, K, npeer = 512, 512, 128, 2
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", 41, device="cpu")
     _, want = oracle_rows(A, B, peers, "bf16")
@@ -253,9 +264,11 @@ def test_withheld_flag_times_out_and_recovers():
     C = new_c(M, N, "bf16")
     old = mk.get_option(mk.OPT_SPIN_TIMEOUT_US)
     old_inplace = mk.get_option(mk.OPT_INPLACE)
+    old_early = mk.get_option(mk.OPT_EARLY)
     try:
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 20000)
         mk.set_option(mk.OPT_INPLACE, 0)  # every tile handed over through its flag
+        mk.set_option(mk.OPT_EARLY, early)
         mk.set_option(mk.OPT_WITHHOLD_TILE, 0)
         mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=4)
         with pytest.raises(mk.MkError) as ei:
@@ -265,6 +278,7 @@ def test_withheld_flag_times_out_and_recovers():
         mk.set_option(mk.OPT_WITHHOLD_TILE, -1)
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, old)
         mk.set_option(mk.OPT_INPLACE, old_inplace)
+        mk.set_option(mk.OPT_EARLY, old_early)
     mk.stream_status()  # error word was cleared
     mk.gemm_ar_local(A, B, peers, C)
     mk.stream_status()
@@ -304,3 +318,28 @@ def test_telemetry_and_controller_trace(inplace_policy):
     assert all(lo <= x <= G for x in targets)
     # once every tile is computed the controller hands all workgroups to the reduce
     assert all(t.trace[i].target == G for i in range(t.n_trace) if computed[i] == t.tiles)
+
+
+def test_early_reduce_grid_and_parity_on_a_decode_shard():
+    """A shard whose tiles and reduce units fit one round of workgroups gets early
+    reduce automatically: one workgroup per tile plus one per 64-row reduce unit. The
+    result is the same bits as with early reduce off and as the baseline."""
+    announce("early reduce on a decode-sized shard")
+    M, N, K, npeer = 128, 2048, 448, 15
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", 71, device="cpu")
+    _, want = oracle_rows(A, B, peers, "bf16")
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    C = new_c(M, N, "bf16")
+    tiles = (M // 128) * (N // 128)
+    assert mk.fused_grid(A, B, peers, C) == tiles * 3  # 128x128 tiles, 2 units each
+    old = mk.get_option(mk.OPT_EARLY)
+    try:
+        mk.set_option(mk.OPT_EARLY, 0)
+        assert mk.fused_grid(A, B, peers, C) == tiles * 2
+        off = c_bits(run(A, B, peers, "bf16", "adaptive"))
+    finally:
+        mk.set_option(mk.OPT_EARLY, old)
+    for mode in ["adaptive", "0", str(tiles * 2), "baseline"]:
+        got = c_bits(run(A, B, peers, "bf16", mode))
+        check_exact(got, want, f"early reduce {mode}")
+        check_exact(got, off, f"early reduce {mode} against early off")

@@ -30,7 +30,7 @@ MK_ADAPTIVE = -1
 MK_MAX_PEERS = 64
 MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
-OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE = 4, 5, 6
+OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY = 4, 5, 6, 7
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",

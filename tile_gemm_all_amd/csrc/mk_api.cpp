@@ -43,7 +43,8 @@ struct Options {
   int64_t tile_shape = mk::SHAPE_AUTO;
   int64_t flag_scope = 0;
   int64_t reducer_cap = 0;  // 0: derived from HBM bandwidth and a reducer's streaming rate
-  int64_t inplace = -1;     // -1: one round of tiles per XCD reduced in place; 0: none; n: at most n
+  int64_t inplace = -1;     // -1: automatic; 0: none; n: the last n tiles of each XCD's queue
+  int64_t early = -1;       // reducers sum a unit's peers before its tile is finished: -1 auto
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -249,16 +250,35 @@ struct Launch {
   int64_t tiles_m, tiles_n;
 };
 
+// Whether reducers sum a unit's peers before its tile is finished (early
+// reduce), from MK_OPT_EARLY: automatic (-1) turns it on for shapes whose tiles
+// and reduce units all fit in one round of resident workgroups (one per tile
+// and one per unit), e.g. a decode-sized shard; with more tiles than that,
+// reducers would sum one unit's peers and then wait for a tile that is still
+// far from done. Only peer counts with a compile-time ring.
+bool early_reduce(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
+  const int64_t opt = options().early;
+  const int occ = L.shape == mk::SHAPE_256 ? 1 : 2;
+  if (opt == 0 || n_peers < 1 || !mk::inplace_supported(occ, (int)dt_size(peer_dtype), n_peers))
+    return false;
+  if (opt > 0) return true;
+  const int64_t T = L.tiles_m * L.tiles_n;
+  const int64_t full = (int64_t)L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  return T * (1 + mk::shape_bm(L.shape) / 64) <= full;
+}
+
 // Persistent grid of the fused kernel: every resident workgroup slot (compute
-// units times workgroups per unit), but no more than two workgroups per tile,
-// rounded up to a multiple of the XCD count, so that a call with few tiles does
-// not start hundreds of workgroups that only find no work and leave.
-int fused_grid_size(const Launch& L, int peer_dtype, int c_dtype) {
+// units times workgroups per unit), but no more than two workgroups per tile
+// (with early reduce: one per tile plus one per reduce unit), rounded up to a
+// multiple of the XCD count, so that a call with few tiles does not start
+// hundreds of workgroups that only find no work and leave.
+int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   const int full = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
   int n_xcd = L.info.cus / 32;
   if (n_xcd < 1) n_xcd = 1;
   const int64_t T = L.tiles_m * L.tiles_n;
-  int64_t want = 2 * T;
+  int64_t want = early_reduce(L, n_peers, peer_dtype, c_dtype)
+                     ? T * (1 + mk::shape_bm(L.shape) / 64) : 2 * T;
   want = (want + n_xcd - 1) / n_xcd * n_xcd;
   if (want < n_xcd) want = n_xcd;
   return want < full ? (int)want : full;
@@ -293,7 +313,7 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   Launch L;
   st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
   if (st != MK_OK) return st;
-  const int G = fused_grid_size(L, peer_dtype, c_dtype);
+  const int G = fused_grid_size(L, n_peers, peer_dtype, c_dtype);
   if (n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
   if (M == 0 || N == 0) return MK_OK;
@@ -366,7 +386,10 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   //    queue (W = workgroups per XCD). Those are handed to reducers, so that
   //    after the first round half of the workgroups start their next GEMM while
   //    the other half reduce, instead of every workgroup alternating in step.
-  if (opt.inplace < 0) {
+  a.early = early_reduce(L, n_peers, peer_dtype, c_dtype) ? 1 : 0;
+  if (opt.inplace < 0 && a.early) {
+    a.n_inplace = 0;  // early reduce applies to tiles handed to reducers
+  } else if (opt.inplace < 0) {
     const double flops = 2.0 * (double)M * (double)N * (double)K;
     const double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
                          (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
@@ -517,7 +540,7 @@ int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, 
   Launch L;
   mk_status_t st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
   if (st != MK_OK) return -(int)st;
-  return fused_grid_size(L, peer_dtype, c_dtype);
+  return fused_grid_size(L, n_peers, peer_dtype, c_dtype);
 }
 
 mk_status_t mk_set_option(int option, int64_t value) {
@@ -550,6 +573,10 @@ mk_status_t mk_set_option(int option, int64_t value) {
       if (value < -1 || value > (1 << 30)) return fail(MK_ERR_INVALID_ARG, "in-place tiles %lld", (long long)value);
       g_opt.inplace = value;
       return MK_OK;
+    case MK_OPT_EARLY:
+      if (value < -1 || value > 1) return fail(MK_ERR_INVALID_ARG, "early reduce %lld", (long long)value);
+      g_opt.early = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -564,6 +591,7 @@ int64_t mk_get_option(int option) {
     case MK_OPT_FLAG_SCOPE: return g_opt.flag_scope;
     case MK_OPT_REDUCER_CAP: return g_opt.reducer_cap;
     case MK_OPT_INPLACE: return g_opt.inplace;
+    case MK_OPT_EARLY: return g_opt.early;
   }
   return -1;
 }

@@ -451,8 +451,15 @@ struct PeerLoad<uint16_t> {  // bfloat16 peers: one 16-byte load
   __device__ __forceinline__ void load(const uint16_t* p) {
     v = __builtin_nontemporal_load((const u32x4*)p);
   }
-  // acc[j] += peer[j], j = 0..7: widen each bfloat16 half exactly, then one
-  // correctly rounded fp32 add (the sum order every path shares).
+  // acc[j] = peer[j], j = 0..7: each bfloat16 half widened exactly
+  __device__ __forceinline__ void set(float* acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = bf16_lo(v[i]);
+      acc[2 * i + 1] = bf16_hi(v[i]);
+    }
+  }
+  // acc[j] += peer[j]: widen exactly, then one correctly rounded fp32 add
   __device__ __forceinline__ void add_to(float* acc) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -467,6 +474,13 @@ struct PeerLoad<float> {  // float32 peers: two 16-byte loads
   __device__ __forceinline__ void load(const float* p) {
     a = __builtin_nontemporal_load((const f32x4*)p);
     b = __builtin_nontemporal_load((const f32x4*)(p + 4));
+  }
+  __device__ __forceinline__ void set(float* acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = a[i];
+      acc[4 + i] = b[i];
+    }
   }
   __device__ __forceinline__ void add_to(float* acc) const {
 #pragma unroll
@@ -494,10 +508,13 @@ __device__ __forceinline__ void store_c<float>(float* C, int64_t e, const float*
   __builtin_nontemporal_store(b, (f32x4*)(C + e + 4));
 }
 
-// Every path sums the same way, element by element:
-//   C = round(((P + peer_0) + peer_1) + ... + peer_{n-1}) in float32,
-// so all reducer counts, the controller and the two-kernel baseline give the
-// same bits.
+// Every path sums the same way, element by element, in float32:
+//   C = round((((peer_0 + peer_1) + ...) + peer_{n-1}) + P)
+// (C = round(P) without peers): the peers in index order, then the local
+// partial P. Reducer counts, the controller, tiles reduced in place or handed
+// over, peers summed ahead of the partial, and the two-kernel baseline all give
+// the same bits. Since the partial comes last, a reducer can sum a tile's peers
+// before the tile's GEMM has finished.
 
 // Generic path (any peer count): CH chunks of 8 elements at offsets e[], peers
 // fetched in batches (8 bfloat16 or 4 float32 peers) so that many loads are in
@@ -508,15 +525,11 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
                                               int64_t peer_stride, CT* __restrict__ C,
                                               const int64_t* e) {
   float acc[CH][8];
+  f32x4 pa[CH], pb[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    f32x4 a = *(const f32x4*)(P + e[c]);
-    f32x4 b = *(const f32x4*)(P + e[c] + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[c][i] = a[i];
-      acc[c][4 + i] = b[i];
-    }
+    pa[c] = *(const f32x4*)(P + e[c]);
+    pb[c] = *(const f32x4*)(P + e[c] + 4);
   }
   constexpr int PB = sizeof(PT) == 2 ? 8 : 4;
   for (int p0 = 0; p0 < n_peers; p0 += PB) {
@@ -532,22 +545,33 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
     for (int s = 0; s < PB; ++s) {
       if (p0 + s < n_peers) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) v[c][s].add_to(acc[c]);
+        for (int c = 0; c < CH; ++c) {
+          if (s == 0 && p0 == 0) v[c][s].set(acc[c]);
+          else v[c][s].add_to(acc[c]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int c = 0; c < CH; ++c) store_c<CT>(C, e[c], acc[c]);
+  for (int c = 0; c < CH; ++c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[c][i] = n_peers > 0 ? acc[c][i] + pa[c][i] : pa[c][i];
+      acc[c][4 + i] = n_peers > 0 ? acc[c][4 + i] + pb[c][i] : pb[c][i];
+    }
+    store_c<CT>(C, e[c], acc[c]);
+  }
 }
 
-// Ring path (NP peers known at compile time). Thread t handles chunks t,
-// t+256, ... of a tile region. A chunk's loads (its fp32 partial, then its NP
-// peer vectors) are issued together, DEPTH-1 chunks ahead of the chunk being
-// summed. Vector memory loads complete in issue order, so waiting for a chunk's
-// loads waits for nothing issued after them: while chunk q is summed the loads
-// of the next DEPTH-1 chunks stay in flight. A reducer workgroup is the only one
-// on its compute unit, so latency has to be covered by bytes in flight (at most
-// 63 loads per wave) rather than by more waves.
+// Ring path (NP >= 1 peers known at compile time). Thread t handles chunks t,
+// t+256, ... of a tile region. A chunk's loads (its NP peer vectors, and its
+// fp32 partial when the sum ends with one) are issued together, DEPTH-1 chunks
+// ahead of the chunk being summed. Vector memory loads complete in issue order,
+// so waiting for a chunk's loads waits for nothing issued after them: while
+// chunk q is summed the loads of the next DEPTH-1 chunks stay in flight. A
+// reducer workgroup is the only one on its compute unit, so latency has to be
+// covered by bytes in flight (at most 63 loads per wave) rather than by more
+// waves.
 //
 // Addressing: every operand has a wave-uniform 64-bit base for the region (kept
 // in scalar registers) and each lane one 32-bit element offset from it, which it
@@ -555,10 +579,12 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
 // end is clamped to the last chunk: that lane reads the same inputs as the lane
 // that owns the chunk and stores the same bits to the same place, so no lane
 // needs a branch, and the loop runs on a wave-uniform bound.
-// Where a chunk's fp32 partial comes from: the workspace in device memory, or
-// LDS (a tile reduced in place by the workgroup that computed it). Both give
-// the same bits.
+//
+// Where a chunk's fp32 partial comes from: the workspace in device memory, LDS
+// (a tile reduced in place by the workgroup that computed it), or nowhere (peers
+// summed ahead of their tile's partial). The first two give the same bits.
 struct PartialGlobal {
+  static constexpr bool kHas = true;
   const float* __restrict__ P;  // region base
   __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t off, uint32_t) const {
     const uint32_t op = off * 4u;
@@ -568,41 +594,104 @@ struct PartialGlobal {
 };
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 struct PartialLds {
+  static constexpr bool kHas = true;
   const lds_char* base;  // region base in LDS, rows of the LDS pitch
   __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t, uint32_t loff) const {
     a = *(const lds_f32x4*)(base + loff * 4u);
     b = *(const lds_f32x4*)(base + loff * 4u + 16u);
   }
 };
+struct NoPartial {
+  static constexpr bool kHas = false;
+  __device__ __forceinline__ void load(f32x4&, f32x4&, uint32_t, uint32_t) const {}
+};
 
-template <typename PT, int NP>
-struct ChunkLoads {
-  f32x4 pa, pb;
-  PeerLoad<PT> v[NP];
+// Where a chunk's sum goes: the output in device memory (rounded to CT), or the
+// float32 peer sum into LDS (row pitch of the LDS region).
+template <typename CT>
+struct OutC {
+  CT* __restrict__ C;  // region base
+  __device__ __forceinline__ void store(uint32_t off, uint32_t, const float* acc) const {
+    store_c<CT>((CT*)((char*)C + off * (uint32_t)sizeof(CT)), 0, acc);
+  }
+};
+struct OutLds {
+  lds_char* base;
+  __device__ __forceinline__ void store(uint32_t, uint32_t loff, const float* acc) const {
+    const f32x4 a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
+    *(lds_f32x4*)(base + loff * 4u) = a;
+    *(lds_f32x4*)(base + loff * 4u + 16u) = b;
+  }
+};
+
+// sum = peer_0 + ... + peer_{NP-1} (+ partial), to OUT.
+template <typename PT, int NP, typename PS, typename OUT>
+struct SumOp {
+  static_assert(NP >= 1, "ring sums have peers");
+  PS ps;
+  const PT* const __restrict__* peer;  // NP region bases
+  OUT out;
+  struct Chunk {
+    f32x4 pa, pb;
+    PeerLoad<PT> v[NP];
+  };
   // Byte offsets are formed in 32 bits, so each load is a scalar base plus a
   // 32-bit vector offset.
-  template <typename PS>
-  __device__ __forceinline__ void load(const PS& ps, const PT* const __restrict__* peer,
-                                       uint32_t off, uint32_t loff) {
-    ps.load(pa, pb, off, loff);
+  __device__ __forceinline__ void load(Chunk& k, uint32_t off, uint32_t loff) const {
+    ps.load(k.pa, k.pb, off, loff);
     const uint32_t ov = off * (uint32_t)sizeof(PT);
 #pragma unroll
-    for (int s = 0; s < NP; ++s) v[s].load((const PT*)((const char*)peer[s] + ov));
+    for (int s = 0; s < NP; ++s) k.v[s].load((const PT*)((const char*)peer[s] + ov));
     __builtin_amdgcn_sched_barrier(0);  // keep the group where the ring puts it
   }
-  template <typename CT>
-  __device__ __forceinline__ void finish(CT* __restrict__ C, uint32_t off) const {
-    float acc[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+  __device__ __forceinline__ void finish(const Chunk& k, uint32_t off, uint32_t loff) const {
+    float acc[8];
+    k.v[0].set(acc);
 #pragma unroll
-    for (int s = 0; s < NP; ++s) v[s].add_to(acc);
-    store_c<CT>((CT*)((char*)C + off * (uint32_t)sizeof(CT)), 0, acc);
+    for (int s = 1; s < NP; ++s) k.v[s].add_to(acc);
+    if constexpr (PS::kHas) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += k.pa[i];
+        acc[4 + i] += k.pb[i];
+      }
+    }
+    out.store(off, loff, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
+// sum = (peer sum left in LDS by a SumOp with NoPartial/OutLds) + partial, to
+// C: the same float32 additions as one SumOp with the partial.
+template <typename CT>
+struct PresumOp {
+  PartialGlobal ps;
+  const lds_char* pre;  // region base in LDS
+  OutC<CT> out;
+  struct Chunk {
+    f32x4 pa, pb;
+  };
+  __device__ __forceinline__ void load(Chunk& k, uint32_t off, uint32_t loff) const {
+    ps.load(k.pa, k.pb, off, loff);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void finish(const Chunk& k, uint32_t off, uint32_t loff) const {
+    const f32x4 x = *(const lds_f32x4*)(pre + loff * 4u);
+    const f32x4 y = *(const lds_f32x4*)(pre + loff * 4u + 16u);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = x[i] + k.pa[i];
+      acc[4 + i] = y[i] + k.pb[i];
+    }
+    out.store(off, loff, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
 };
 
 // Walks chunk indices q = q0, q0+256, ... of a region of `cpr` chunks per row,
 // giving each one's element offset for two row pitches (N for device memory, LP
-// for a copy of the partial in LDS), clamped to the last chunk past the end.
+// for a region in LDS), clamped to the last chunk past the end.
 struct ChunkCursor {
   int q, c;                 // chunk index and its column chunk
   uint32_t off, loff;       // element offsets of chunk q (unclamped)
@@ -643,21 +732,19 @@ struct ChunkCursor {
   }
 };
 
-template <int DEPTH, typename PT, int NP>
+template <int DEPTH, typename OP>
 struct ReduceRing {
-  template <typename CT, typename PS>
-  __device__ __forceinline__ static void run(const PS& ps, const PT* const __restrict__* peer,
-                                             CT* __restrict__ C, int total, int cpr, int64_t N,
+  __device__ __forceinline__ static void run(const OP& op, int total, int cpr, int64_t N,
                                              int64_t LP) {
     // loop bound on the wave's first chunk: a uniform (scalar) loop
     const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
     ChunkCursor ld, st;  // the chunk loaded next, the chunk summed next
     ld.init(threadIdx.x, total, cpr, N, LP);
     st = ld;
-    ChunkLoads<PT, NP> b[DEPTH];
+    typename OP::Chunk b[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH - 1; ++i) {
-      b[i].load(ps, peer, ld.get(), ld.lget());
+      op.load(b[i], ld.get(), ld.lget());
       ld.advance();
     }
     // At least one pass, so that no guard separates the loads above from the
@@ -666,9 +753,9 @@ struct ReduceRing {
     do {
 #pragma unroll
       for (int i = 0; i < DEPTH; ++i) {
-        b[(i + DEPTH - 1) % DEPTH].load(ps, peer, ld.get(), ld.lget());
+        op.load(b[(i + DEPTH - 1) % DEPTH], ld.get(), ld.lget());
         ld.advance();
-        b[i].template finish<CT>(C, st.get());
+        op.finish(b[i], st.get(), st.lget());
         st.advance();
       }
       k += DEPTH * kThreads;
@@ -678,17 +765,17 @@ struct ReduceRing {
   }
 };
 
-// Ring depth for NP peers of type PT at OCC workgroups per compute unit. While
-// a chunk is summed, DEPTH-1 chunks' loads are in flight; about 17 16-byte loads
-// per wave (one chunk of 15 bfloat16 peers) streamed fastest on MI355X, and
-// deeper rings were slower (more concurrent peer streams per wave), so small
-// chunks get a deeper ring, within a register budget per lane (512 registers
-// per SIMD lane, shared by OCC waves, minus addresses and the rest of the
-// kernel); between 2 and 4.
-template <int OCC, typename PT, int NP>
+// Ring depth for NP peers of type PT (plus a partial if HAS_P) at OCC workgroups
+// per compute unit. While a chunk is summed, DEPTH-1 chunks' loads are in
+// flight; about 17 16-byte loads per wave (one chunk of 15 bfloat16 peers)
+// streamed fastest on MI355X, and deeper rings were slower (more concurrent
+// peer streams per wave), so small chunks get a deeper ring, within a register
+// budget per lane (512 registers per SIMD lane, shared by OCC waves, minus
+// addresses and the rest of the kernel); between 2 and 4.
+template <int OCC, typename PT, int NP, bool HAS_P = true>
 __host__ __device__ constexpr int ring_depth() {
-  constexpr int loads = 2 + NP * (sizeof(PT) == 2 ? 1 : 2);  // 16-byte loads per chunk
-  constexpr int regs = 8 + NP * (sizeof(PT) == 2 ? 4 : 8);   // registers per chunk
+  constexpr int loads = (HAS_P ? 2 : 0) + NP * (sizeof(PT) == 2 ? 1 : 2);  // 16-byte loads
+  constexpr int regs = (HAS_P ? 8 : 0) + NP * (sizeof(PT) == 2 ? 4 : 8);   // per chunk
   constexpr int budget = OCC == 1 ? 320 : 160;
   constexpr int d_vm = 1 + (17 + loads - 1) / loads, d_reg = budget / regs;
   constexpr int d = d_vm < d_reg ? d_vm : d_reg;
@@ -723,8 +810,9 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
     if constexpr (ring_fits<OCC, PT, NPV>()) {                                         \
       const PT* pr[NPV];                                                               \
       _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base; \
-      ReduceRing<ring_depth<OCC, PT, NPV>(), PT, NPV>::template run<CT>(                \
-          PartialGlobal{P + base}, pr, C + base, total, cpr, N, N);                    \
+      typedef SumOp<PT, NPV, PartialGlobal, OutC<CT>> Op;                              \
+      ReduceRing<ring_depth<OCC, PT, NPV>(), Op>::run(                                 \
+          Op{PartialGlobal{P + base}, pr, OutC<CT>{C + base}}, total, cpr, N, N);      \
       return;                                                                          \
     }                                                                                  \
     break;
@@ -750,7 +838,7 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
 
 // The same for a region whose fp32 partial sits in LDS (row pitch LP elements,
 // first row and column of the region at lds). Only peer counts for which
-// lds_reduce_supported() holds.
+// inplace_supported() holds.
 template <int OCC, typename PT, typename CT>
 __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
                                                   const PT* __restrict__ peers, int n_peers,
@@ -769,8 +857,9 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
     if constexpr (ring_fits<OCC, PT, NPV>()) {                                         \
       const PT* pr[NPV];                                                               \
       _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base; \
-      ReduceRing<ring_depth<OCC, PT, NPV>(), PT, NPV>::template run<CT>(ps, pr, C + base, \
-                                                                          total, cpr, N, LP); \
+      typedef SumOp<PT, NPV, PartialLds, OutC<CT>> Op;                                 \
+      ReduceRing<ring_depth<OCC, PT, NPV>(), Op>::run(Op{ps, pr, OutC<CT>{C + base}},  \
+                                                      total, cpr, N, LP);              \
     }                                                                                  \
     return;
   switch (n_peers) {
@@ -778,6 +867,57 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
     default: return;
   }
 #undef MK_RING
+}
+
+// A reduce unit in two phases, for a reducer that takes the unit before its
+// tile's partial is published. Phase 1 sums the region's peers into LDS (row
+// pitch LP); it reads nothing the GEMM produces. Phase 2, once the partial is
+// published, adds it and writes C. Together they make the same float32
+// additions as reduce_region. Only peer counts for which inplace_supported()
+// holds.
+template <int OCC, typename PT>
+__device__ __forceinline__ void reduce_region_peers_lds(char* lds, int64_t LP,
+                                                        const PT* __restrict__ peers, int n_peers,
+                                                        int64_t M, int64_t N, int64_t m0,
+                                                        int64_t n0, int rows, int cols) {
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  const int total = rows * cpr;
+  if (total <= 0) return;
+  const int64_t stride = M * N;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+  const OutLds out{(lds_char*)lds};
+#define MK_RING(NPV)                                                                    \
+  case NPV:                                                                             \
+    if constexpr (ring_fits<OCC, PT, NPV>()) {                                          \
+      const PT* pr[NPV];                                                                \
+      _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base;  \
+      typedef SumOp<PT, NPV, NoPartial, OutLds> Op;                                     \
+      ReduceRing<ring_depth<OCC, PT, NPV, false>(), Op>::run(Op{NoPartial{}, pr, out},   \
+                                                             total, cpr, N, LP);        \
+    }                                                                                   \
+    return;
+  switch (n_peers) {
+    MK_RING_PEER_COUNTS(MK_RING)
+    default: return;
+  }
+#undef MK_RING
+}
+template <typename CT>
+__device__ __forceinline__ void reduce_region_finish(const float* __restrict__ P,
+                                                     const char* lds, int64_t LP,
+                                                     CT* __restrict__ C, int64_t N, int64_t m0,
+                                                     int64_t n0, int rows, int cols) {
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  const int total = rows * cpr;
+  if (total <= 0) return;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+  typedef PresumOp<CT> Op;
+  ReduceRing<4, Op>::run(Op{PartialGlobal{P + base}, (const lds_char*)lds, OutC<CT>{C + base}},
+                         total, cpr, N, LP);
 }
 
 }  // namespace mk

@@ -95,6 +95,8 @@ struct FusedArgs {
   int reducer_cap;             // controller's upper bound on reducers while compute remains
   int n_inplace;               // per XCD: last tiles of the queue reduced in place
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
+  int early;                   // 1: a reducer may take a unit whose tile is still being
+                               // computed, and sums its peers while it waits
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
 };
 

@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
   int rank = -1, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
   bool flag_seen = false;  // thread 0: the claimed unit's flag was already read as set
+  unsigned long long t_busy = 0;  // thread 0: a reduce unit's busy ticks, less its end tick
   // The last n_in tiles of the XCD's queue are reduced in place by the workgroup
   // that computes them: no compute is left to overlap with, so handing them to
   // reducers would only add the partial's round trip through memory. At most
@@ -138,6 +139,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const int n_in = xcd_inplace(cnt, a.n_inplace,
                                inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers));
   const int published = cnt - n_in;
+  // Early reduce: a unit's peers are summed into LDS before its flag is read.
+  static_assert(Cfg::BM / Cfg::RSPLIT * Cfg::BN * 4 <= Cfg::LDS_BYTES, "peer sum of a unit in LDS");
+  const bool early = a.early && a.n_peers > 0 &&
+                     inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers);
 
   for (;;) {
     if (tid == 0) {
@@ -210,9 +215,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         int fl = 0;
         if (pref_reduce && cn < cnt) {
           // GEMM tiles are left: reserve the next unit only if its tile is
-          // finished, else compute meanwhile rather than wait for its flag.
+          // finished (or, with early reduce, being computed: its peers are
+          // summed meanwhile), else compute rather than wait for its flag.
           fl = load_relaxed(a.flags + q0 + rn / Cfg::RSPLIT);
-          if (fl != a.epoch) {
+          if (fl != a.epoch && !(early && rn / Cfg::RSPLIT < cn)) {
             const int i = atomicAdd(cnext, 1);
             if (i < cnt) {
               kind = K_COMPUTE;
@@ -307,6 +313,17 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     } else {
+      constexpr int SLAB = Cfg::BM / Cfg::RSPLIT;
+      const int64_t r0 = m0 + (int64_t)part * SLAB;
+      const int rows = (int)(a.M - r0 < SLAB ? a.M - r0 : SLAB);  // <= 0 past a ragged edge
+      const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
+      const unsigned long long t0 = ticks();
+      if (early) {
+        // phase 1: the peers need no flag
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load of the last task in flight
+        reduce_region_peers_lds<Cfg::OCC, PT>(lds, Cfg::BN, peers, a.n_peers, a.M, a.N, r0, n0,
+                                              rows, cols);
+      }
       if (tid == 0) {
         const unsigned long long w0 = ticks();
         int ok = 1, backoff = 1;
@@ -325,23 +342,24 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         }
         if (a.flag_scope == 0) invalidate_l1();
         else acquire_fence_agent();
-        atomicAdd(xslot64(S, x, X_WAIT_R), ticks() - w0);
+        const unsigned long long w1 = ticks();
+        atomicAdd(xslot64(S, x, X_WAIT_R), w1 - w0);
         s_ok = ok;
+        // busy time: phase 1 plus what follows the wait
+        t_busy = (w0 - t0) - w1;
       }
-      __syncthreads();
+      __syncthreads();  // also: phase 1's LDS writes are done
       if (!s_ok) break;
-      const unsigned long long t0 = ticks();
-      constexpr int SLAB = Cfg::BM / Cfg::RSPLIT;
-      const int64_t r0 = m0 + (int64_t)part * SLAB;
-      const int rows = (int)(a.M - r0 < SLAB ? a.M - r0 : SLAB);  // <= 0 past a ragged edge
-      const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
-      reduce_region<Cfg::OCC, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
+      if (early)
+        reduce_region_finish<CT>(a.P, lds, Cfg::BN, C, a.N, r0, n0, rows, cols);
+      else
+        reduce_region<Cfg::OCC, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
       __syncthreads();
       if (tid == 0) {
         // No returned value is needed: the controller runs on compute
         // completions, the only phase in which its target matters.
         atomicAdd(xslot(S, x, X_REDUCED), 1);
-        atomicAdd(xslot64(S, x, X_BUSY_R), ticks() - t0);
+        atomicAdd(xslot64(S, x, X_BUSY_R), t_busy + ticks());
       }
     }
     __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
