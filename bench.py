@@ -120,6 +120,9 @@ def main():
     def two_kernel():
         mk.gemm_then_reduce_baseline(A, B, peers, C)
 
+    def two_stream():
+        mk.gemm_ar_two_stream(A, B, peers, C)
+
     def timed(fn, steps, warmup):
         for _ in range(warmup):
             fn()
@@ -135,6 +138,8 @@ def main():
         return start.elapsed_time(stop) / steps  # ms per launch
 
     base_ms = timed(two_kernel, args.steps, args.warmup)
+    # stream overlap: per-chunk GEMM kernels, per-chunk reduces on a second stream
+    two_stream_ms = timed(two_stream, args.steps, args.warmup)
     # the role-split path alone: every tile handed to reducers through its flag
     old_inplace = mk.get_option(mk.OPT_INPLACE)
     mk.set_option(mk.OPT_INPLACE, 0)
@@ -171,6 +176,8 @@ def main():
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "two_kernel_ms": round(base_ms, 5),
         "speedup_vs_two_kernel": round(base_ms / fused_ms, 4),
+        "two_stream_ms": round(two_stream_ms, 5),
+        "speedup_vs_two_stream": round(two_stream_ms / fused_ms, 4),
         "handover_all_ms": round(handover_ms, 5),
         "timed_wall_s": round(wall, 3),
     }

@@ -80,6 +80,8 @@ typedef enum { MK_DT_BF16 = 0, MK_DT_F32 = 1 } mk_dtype_t;
 /* n_reduce_wg value that hands the reducer count to the on-GPU controller. */
 #define MK_ADAPTIVE (-1)
 #define MK_MAX_PEERS 64
+/* Most chunks of mk_gemm_ar_two_stream. */
+#define MK_MAX_CHUNKS 64
 
 /* Telemetry written by the fused kernel when the caller passes a device buffer
  * of sizeof(mk_telemetry_t) bytes (else NULL). Times are in ticks of the GPU's
@@ -142,6 +144,26 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
 mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const void* peers,
                                          int n_peers, void* C, int64_t M, int64_t N, int64_t K,
                                          int peer_dtype, int c_dtype, void* stream);
+
+/*
+ * mk_gemm_ar_two_stream -- the stream-overlap schedule of Figure 1(b) on the
+ * thelatestinai.com page: the output rows are cut into n_chunks chunks of
+ * whole tile rows; the GEMM kernel of each chunk runs on `stream`, and the
+ * reduce kernel of a chunk runs on a second stream of the library as soon as
+ * that chunk's GEMM kernel has ended (an event), overlapping the GEMM of the
+ * following chunks. Kernel boundaries are the only readiness signal; no flag
+ * is involved. The second stream (default priority) and its events belong to
+ * the (device, stream) workspace. The call is ordered on `stream` like the
+ * others: every reduce waits for an event recorded on `stream` after its
+ * chunk's GEMM, and `stream` waits for the last reduce.
+ *   n_chunks : 0 = automatic (4), else 1..MK_MAX_CHUNKS; at most the number of
+ *              tile rows (the tile shape is chosen as for the fused kernel).
+ * Other arguments and result as mk_gemm_ar_local (bitwise: the same GEMM tile
+ * and reduce code, the same sum order).
+ */
+mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peers, int n_peers,
+                                  void* C, int64_t M, int64_t N, int64_t K, int peer_dtype,
+                                  int c_dtype, void* stream, int n_chunks);
 
 /* Synchronizes `stream`, then returns and clears the device error word of that
  * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */

@@ -50,6 +50,11 @@ def base(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt
                                                      None)
 
 
+def two(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt=0, chunks=0):
+    return mk.library().mk_gemm_ar_two_stream(A, B, peers, n_peers, C, M, N, K, pdt, cdt, None,
+                                              chunks)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(A=None), mk.MK_ERR_INVALID_ARG),
     (dict(B=None), mk.MK_ERR_INVALID_ARG),
@@ -73,7 +78,13 @@ def base(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt
 def test_validation_rejects(kw, status):
     assert call(**kw) == status, mk.last_error()
     assert base(**kw) == status, mk.last_error()
+    assert two(**kw) == status, mk.last_error()
     assert mk.last_error()
+
+
+def test_chunk_count_outside_range_is_rejected():
+    assert two(chunks=-1) == mk.MK_ERR_INVALID_ARG
+    assert two(chunks=mk.MK_MAX_CHUNKS + 1) == mk.MK_ERR_INVALID_ARG
 
 
 def test_reducer_count_below_adaptive_is_rejected():

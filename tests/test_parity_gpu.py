@@ -343,3 +343,55 @@ def test_early_reduce_grid_and_parity_on_a_decode_shard():
         got = c_bits(run(A, B, peers, "bf16", mode))
         check_exact(got, want, f"early reduce {mode}")
         check_exact(got, off, f"early reduce {mode} against early off")
+
+
+TWO_STREAM_SHAPES = [
+    # M, N, K, n_peers, peer dtype, C dtype: one tile row, ragged rows, 256x256 tiles
+    (256, 512, 512, 3, "f32", "f32"),
+    (300, 264, 200, 3, "bf16", "bf16"),
+    (1000, 776, 264, 7, "bf16", "f32"),
+    (2304, 2048, 512, 15, "bf16", "bf16"),
+    (130, 136, 72, 0, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", TWO_STREAM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_two_stream_schedule_matches_baseline(shape):
+    """The stream-overlap schedule (per-chunk GEMM kernels, per-chunk reduces on a
+    second stream) gives the baseline's bits for every chunk count, and integer
+    inputs stay exact against the oracle."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"two-stream schedule {shape}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 81, device="cpu")
+    rows = sample_rows(M)
+    _, want = oracle_rows(A, B, peers, cdt, rows)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    ref = c_bits(run(A, B, peers, cdt, "baseline"))
+    for chunks in (0, 1, 2, 3, 64):
+        C = new_c(M, N, cdt)
+        mk.gemm_ar_two_stream(A, B, peers, C, n_chunks=chunks)
+        mk.stream_status()
+        check_exact(c_bits(C), ref, f"{chunks} chunks against the baseline")
+        check_exact(c_bits(C, rows), want, f"{chunks} chunks against the oracle")
+
+
+def test_two_stream_then_fused_on_one_stream():
+    """The two schedules share the stream's partial buffer: back-to-back calls with
+    alternating inputs must each see only their own partials."""
+    announce("two-stream and fused calls alternating")
+    M, N, K, npeer = 768, 1024, 320, 3
+    sets = []
+    for s in (91, 92):
+        A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", s, device="cpu")
+        _, want = oracle_rows(A, B, peers, "bf16")
+        sets.append((A.to(DEV), B.to(DEV), peers.to(DEV), want))
+    outs = [new_c(M, N, "bf16") for _ in range(4)]
+    for i in range(4):
+        A, B, peers, _ = sets[i % 2]
+        if i < 2:
+            mk.gemm_ar_two_stream(A, B, peers, outs[i], n_chunks=3)
+        else:
+            mk.gemm_ar_local(A, B, peers, outs[i])
+    mk.stream_status()
+    for i in range(4):
+        check_exact(c_bits(outs[i]), sets[i % 2][3], f"call {i}")

@@ -28,11 +28,13 @@ MK_ERR_NO_DEVICE, MK_ERR_WORKSPACE = 5, 6
 MK_DT_BF16, MK_DT_F32 = 0, 1
 MK_ADAPTIVE = -1
 MK_MAX_PEERS = 64
+MK_MAX_CHUNKS = 64
 MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
 OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY = 4, 5, 6, 7
 
-EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_stream_status",
+EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_stream",
+           "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
            "mk_get_option",
            "mk_controller_eval", "mk_status_string", "mk_last_error", "mk_version"]
@@ -56,6 +58,9 @@ _lib.mk_gemm_ar_local.restype = _int
 _lib.mk_gemm_then_reduce_baseline.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int,
                                               _int, _vp]
 _lib.mk_gemm_then_reduce_baseline.restype = _int
+_lib.mk_gemm_ar_two_stream.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _int,
+                                       _vp, _int]
+_lib.mk_gemm_ar_two_stream.restype = _int
 _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
 _lib.mk_workspace_reset.argtypes = [_int]
@@ -167,6 +172,14 @@ def gemm_then_reduce_baseline(A, B, peers, C, stream=None):
     """Same result as gemm_ar_local, by a GEMM kernel followed by a reduce kernel."""
     a = _args(A, B, peers, C)
     _check(_lib.mk_gemm_then_reduce_baseline(*a[:10], _stream_ptr(stream)))
+    return C
+
+
+def gemm_ar_two_stream(A, B, peers, C, n_chunks=0, stream=None):
+    """Same result as gemm_ar_local, by per-chunk GEMM kernels on the stream and
+    per-chunk reduce kernels on a second stream that overlap the next chunks' GEMMs."""
+    a = _args(A, B, peers, C)
+    _check(_lib.mk_gemm_ar_two_stream(*a[:10], _stream_ptr(stream), int(n_chunks)))
     return C
 
 

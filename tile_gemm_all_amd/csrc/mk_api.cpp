@@ -105,11 +105,17 @@ struct Workspace {
   int flags_cap = 0;
   unsigned long long* slots = nullptr;
   int epoch = 0;
+  // two-stream schedule: the reduce stream and its events (created on first use)
+  hipStream_t s2 = nullptr;
+  hipEvent_t ev[MK_MAX_CHUNKS + 1] = {};
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
 
 void free_ws(Workspace* w) {
+  for (hipEvent_t e : w->ev)
+    if (e) (void)hipEventDestroy(e);
+  if (w->s2) (void)hipStreamDestroy(w->s2);
   if (w->P) (void)hipFree(w->P);
   if (w->flags) (void)hipFree(w->flags);
   if (w->slots) (void)hipFree(w->slots);
@@ -282,6 +288,17 @@ int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   want = (want + n_xcd - 1) / n_xcd * n_xcd;
   if (want < n_xcd) want = n_xcd;
   return want < full ? (int)want : full;
+}
+
+// Grid of the reduce kernel for `elems` output elements: two 8-element chunks
+// per thread, at most 8 workgroups per compute unit (grid-stride beyond).
+int reduce_grid(int64_t elems, int cus) {
+  const int64_t chunks = elems / 8;
+  int64_t grid = (chunks + 2 * 256 - 1) / (2 * 256);
+  const int64_t cap = (int64_t)cus * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  return (int)grid;
 }
 
 mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype,
@@ -471,15 +488,93 @@ mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const voi
   r.C = C;
   r.M = M;
   r.N = N;
+  r.peer_stride = M * N;
   r.n_peers = n_peers;
   r.pad_ = 0;
-  int64_t chunks = M * N / 8;
-  int64_t grid = (chunks + 2 * 256 - 1) / (2 * 256);
-  int64_t cap = (int64_t)L.info.cus * 8;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  e = mk::launch_reduce(peer_dtype, c_dtype, r, (int)grid, s);
+  e = mk::launch_reduce(peer_dtype, c_dtype, r, reduce_grid(M * N, L.info.cus), s);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
+  return MK_OK;
+}
+
+mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peers, int n_peers,
+                                  void* C, int64_t M, int64_t N, int64_t K, int peer_dtype,
+                                  int c_dtype, void* stream, int n_chunks) {
+  mk_status_t st = validate(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype);
+  if (st != MK_OK) return st;
+  if (n_chunks < 0 || n_chunks > MK_MAX_CHUNKS)
+    return fail(MK_ERR_INVALID_ARG, "n_chunks=%d outside [0, %d]", n_chunks, MK_MAX_CHUNKS);
+  Launch L;
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  if (st != MK_OK) return st;
+  if (M == 0 || N == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  const int T = (int)(L.tiles_m * L.tiles_n);
+  st = get_ws(L.dev, s, (size_t)(M * N), T, &w);
+  if (st != MK_OK) return st;
+  if (!w->s2) {
+    // default priority, like every stream of the library
+    hipError_t e = hipStreamCreateWithFlags(&w->s2, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      w->s2 = nullptr;
+      return hip_fail(e, "reduce stream");
+    }
+    for (hipEvent_t& ev : w->ev) {
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        ev = nullptr;
+        return hip_fail(e, "event");
+      }
+    }
+  }
+  // Chunks of whole tile rows: chunk i is tile rows [i*tm/c, (i+1)*tm/c).
+  const int tm = (int)L.tiles_m;
+  int c = n_chunks == 0 ? 4 : n_chunks;
+  if (c > tm) c = tm;
+  const int BM = mk::shape_bm(L.shape);
+  const int n_xcd = L.info.cus / 32;
+  hipEvent_t* ev = w->ev;
+  // Every reduce waits for an event recorded on the caller's stream after its
+  // chunk's GEMM, hence after all earlier work on that stream (the previous
+  // call's reduces included, see the end): no wait is needed up front.
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < c && e == hipSuccess; ++i) {
+    const int64_t r0 = (int64_t)(i * (int64_t)tm / c) * BM;
+    int64_t r1 = (int64_t)((i + 1) * (int64_t)tm / c) * BM;
+    if (r1 > M) r1 = M;
+    mk::GemmArgs g;
+    g.A = (const uint16_t*)A + r0 * K;
+    g.B = (const uint16_t*)B;
+    g.P = w->P + r0 * N;
+    g.M = r1 - r0;
+    g.N = N;
+    g.K = K;
+    g.tiles_m = (int)((r1 - r0 + BM - 1) / BM);
+    g.tiles_n = (int)L.tiles_n;
+    g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
+    g.pad_ = 0;
+    e = mk::launch_gemm(L.shape, g, s);
+    if (e != hipSuccess) break;
+    // the chunk's partial rows are complete when the GEMM kernel ends
+    e = hipEventRecord(ev[i], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(w->s2, ev[i], 0);
+    if (e != hipSuccess) break;
+    mk::ReduceArgs r;
+    r.P = w->P + r0 * N;
+    r.peers = (const char*)peers + (size_t)(r0 * N) * dt_size(peer_dtype);
+    r.C = (char*)C + (size_t)(r0 * N) * dt_size(c_dtype);
+    r.M = r1 - r0;
+    r.N = N;
+    r.peer_stride = M * N;
+    r.n_peers = n_peers;
+    r.pad_ = 0;
+    e = mk::launch_reduce(peer_dtype, c_dtype, r, reduce_grid(r.M * N, L.info.cus), w->s2);
+  }
+  // the call ends on the caller's stream when the last reduce has finished
+  if (e == hipSuccess) e = hipEventRecord(ev[c], w->s2);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, ev[c], 0);
+  if (e != hipSuccess) return hip_fail(e, "two-stream schedule");
   return MK_OK;
 }
 

@@ -111,10 +111,11 @@ struct GemmArgs {
 };
 
 struct ReduceArgs {
-  const float* P;
-  const void* peers;
+  const float* P;      // rows [0, M) of the region
+  const void* peers;   // peer p's region at peers + p * peer_stride elements
   void* C;
-  int64_t M, N;
+  int64_t M, N;        // region rows and columns (dense, row pitch N)
+  int64_t peer_stride; // elements between two peers' arrays
   int n_peers;
   int pad_;
 };

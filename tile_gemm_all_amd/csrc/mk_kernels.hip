@@ -447,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   CT* C = (CT*)a.C;
   const int64_t Q = a.M * a.N / 8;  // chunks of 8 elements over the dense arrays
   const int64_t step = (int64_t)gridDim.x * kThreads;
-  const int64_t stride = a.M * a.N;
+  const int64_t stride = a.peer_stride;
   int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   for (; q + step < Q; q += 2 * step) {
     int64_t e[2] = {q * 8, (q + step) * 8};
