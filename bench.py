@@ -123,6 +123,19 @@ def main():
     def two_stream():
         mk.gemm_ar_two_stream(A, B, peers, C)
 
+    # GEMM+ReduceScatter share of the same GEMM: this GPU owns one P-th of the rows
+    # (slice 3), reduces them with the peers' partials of those rows, publishes the rest
+    o0, o1 = 3 * w.M // w.P, 4 * w.M // w.P
+    rs_peers = peers[:, o0:o1].contiguous()
+    rs_C = torch.empty((o1 - o0, w.N), dtype=C.dtype, device="cuda")
+    rs_send = torch.empty((w.M, w.N), dtype=peers.dtype, device="cuda")
+
+    def rs_fused():
+        mk.gemm_rs_local(A, B, rs_peers, rs_C, rs_send, o0, o1)
+
+    def rs_baseline():
+        mk.gemm_rs_baseline(A, B, rs_peers, rs_C, rs_send, o0, o1)
+
     def timed(fn, steps, warmup):
         for _ in range(warmup):
             fn()
@@ -140,6 +153,8 @@ def main():
     base_ms = timed(two_kernel, args.steps, args.warmup)
     # stream overlap: per-chunk GEMM kernels, per-chunk reduces on a second stream
     two_stream_ms = timed(two_stream, args.steps, args.warmup)
+    rs_base_ms = timed(rs_baseline, args.steps, args.warmup)
+    rs_ms = timed(rs_fused, args.steps, args.warmup)
     # the role-split path alone: every tile handed to reducers through its flag
     old_inplace = mk.get_option(mk.OPT_INPLACE)
     mk.set_option(mk.OPT_INPLACE, 0)
@@ -179,6 +194,9 @@ def main():
         "two_stream_ms": round(two_stream_ms, 5),
         "speedup_vs_two_stream": round(two_stream_ms / fused_ms, 4),
         "handover_all_ms": round(handover_ms, 5),
+        "reduce_scatter": {"owned_rows": [o0, o1], "fused_ms": round(rs_ms, 5),
+                           "baseline_ms": round(rs_base_ms, 5),
+                           "speedup": round(rs_base_ms / rs_ms, 4)},
         "timed_wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

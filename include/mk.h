@@ -165,6 +165,44 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
                                   void* C, int64_t M, int64_t N, int64_t K, int peer_dtype,
                                   int c_dtype, void* stream, int n_chunks);
 
+/*
+ * mk_gemm_rs_local -- one GPU's share of the "GEMM + ReduceScatter (TP)" kernel
+ * of Table 3 on the thelatestinai.com page (compute -> communication: each
+ * output tile is added into the buffer of the GPU that owns it). This GPU owns
+ * output rows [own_m0, own_m1) (own = own_m1 - own_m0 rows). With its local
+ * partial Pl = A*B (fp32 accumulation):
+ *   C[i - own_m0, j] = round_c((peers[0][i-own_m0][j] + ... + peers[n-1][..][j]) + Pl[i][j])
+ *                                                    for own_m0 <= i < own_m1,
+ *   send[i, j]       = round_peer(Pl[i][j])          for every other row i,
+ * i.e. the owned slice is reduced here (same sum order as mk_gemm_ar_local) and
+ * every other row is published, rounded to the peer type, for its owner (which
+ * receives it as one of its peer partials).
+ *   A [M, K] bf16; B [K, N] bf16;
+ *   peers [n_peers, own, N] peer_dtype: the other GPUs' partials of the owned rows;
+ *   C [own, N] c_dtype; send [M, N] peer_dtype, rows of [own_m0, own_m1) left
+ *   untouched (send may be NULL when every row is owned).
+ * One persistent launch of the fused kernel. The tile rows that hold owned rows
+ * lead every XCD's queue and are handed to reducers through the workspace and
+ * tile flags (64-row units: owned rows reduced, the others published); every
+ * other tile is rounded and published by the workgroup that computed it, in
+ * place. n_reduce_wg: 0 .. G-1 dedicated reducers (G as mk_fused_grid() with
+ * MK_OPT_EARLY off) or MK_ADAPTIVE. Any n_peers <= MK_MAX_PEERS. Same alignment
+ * and overlap rules as above; C and send must not overlap each other or any
+ * input.
+ */
+mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                             void* send, int64_t M, int64_t N, int64_t K, int64_t own_m0,
+                             int64_t own_m1, int peer_dtype, int c_dtype, void* stream,
+                             int n_reduce_wg);
+
+/* mk_gemm_rs_baseline -- the same result (bitwise) unfused: the GEMM kernel
+ * writes the fp32 partial of all M rows, then the reduce kernel sums the owned
+ * rows and rounds the other rows to the peer type. Any n_peers <= MK_MAX_PEERS. */
+mk_status_t mk_gemm_rs_baseline(const void* A, const void* B, const void* peers, int n_peers,
+                                void* C, void* send, int64_t M, int64_t N, int64_t K,
+                                int64_t own_m0, int64_t own_m1, int peer_dtype, int c_dtype,
+                                void* stream);
+
 /* Synchronizes `stream`, then returns and clears the device error word of that
  * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
 mk_status_t mk_stream_status(void* stream);

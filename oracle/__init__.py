@@ -1,4 +1,5 @@
-"""CPU oracle for one GPU's share of GEMM+AllReduce -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for one GPU's share of GEMM+AllReduce (and of GEMM+ReduceScatter)
+-- TEST INFRASTRUCTURE ONLY.
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package. The product path (tile_gemm_all_amd, libmk.so) never does.
@@ -87,6 +88,33 @@ class Oracle:
             raise ValueError("oracle rejected its arguments")
         return C64, Cout
 
+    def gemm_rs(self, A_bits, B_bits, peers_own, own_m0, own_m1, c_dtype="bf16",
+                peer_dtype="bf16", rows=None, threads=0):
+        """Reference for one GPU's share of GEMM+ReduceScatter ("GEMM + ReduceScatter
+        (TP)" row of Table 3, thelatestinai.com page: compute -> communication, each
+        output tile added into its owner's buffer). This GPU owns rows
+        [own_m0, own_m1). An owned row is the AllReduce share of that row with the
+        owner's peer partials (peers_own: [P-1, own, N]); every other row is this
+        GPU's partial A*B rounded to the peer type, which its owner receives as a
+        peer partial.
+
+        rows: None (all M rows) or global row indices. Returns
+        ((owned_rows, C64, C_out), (other_rows, S64, S_out)): owned_rows and
+        other_rows are the given rows split by ownership (global indices), C* the
+        reduced rows, S* the published rows (S64 = the fp64 partial).
+        """
+        A_bits = np.ascontiguousarray(A_bits, dtype=np.uint16)
+        M = A_bits.shape[0]
+        if not 0 <= own_m0 <= own_m1 <= M:
+            raise ValueError("owned rows outside [0, M]")
+        rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+        mine = (rows >= own_m0) & (rows < own_m1)
+        owned, other = rows[mine], rows[~mine]
+        C64, C_out = self.gemm_ar(A_bits[own_m0:own_m1], B_bits, peers_own, c_dtype,
+                                  rows=owned - own_m0, threads=threads)
+        S64, S_out = self.gemm_ar(A_bits, B_bits, None, peer_dtype, rows=other, threads=threads)
+        return (owned, C64, C_out), (other, S64, S_out)
+
     def bf16_to_f64(self, bits):
         b = np.ascontiguousarray(bits, dtype=np.uint16)
         out = np.empty(b.shape, dtype=np.float64)
@@ -124,6 +152,10 @@ def default():
 
 def gemm_ar(*a, **k):
     return default().gemm_ar(*a, **k)
+
+
+def gemm_rs(*a, **k):
+    return default().gemm_rs(*a, **k)
 
 
 def bf16_to_f64(bits):

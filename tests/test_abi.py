@@ -129,3 +129,42 @@ def test_options_roundtrip():
 def test_telemetry_struct_size():
     # 5 u64 + 10 i32 + MK_TRACE_CAP entries of 24 bytes
     assert mk.TELEMETRY_BYTES == 5 * 8 + 10 * 4 + mk.MK_TRACE_CAP * 24
+
+
+S16 = 0xC0000000
+
+
+def rs(A=A16, B=B16, peers=P16, n_peers=3, C=C16, send=S16, M=64, N=64, K=64, o0=0, o1=32,
+       pdt=0, cdt=0):
+    return mk.library().mk_gemm_rs_local(A, B, peers, n_peers, C, send, M, N, K, o0, o1, pdt,
+                                         cdt, None, -1)
+
+
+def rs_base(**kw):
+    a = dict(A=A16, B=B16, peers=P16, n_peers=3, C=C16, send=S16, M=64, N=64, K=64, o0=0, o1=32,
+             pdt=0, cdt=0)
+    a.update(kw)
+    return mk.library().mk_gemm_rs_baseline(a["A"], a["B"], a["peers"], a["n_peers"], a["C"],
+                                            a["send"], a["M"], a["N"], a["K"], a["o0"], a["o1"],
+                                            a["pdt"], a["cdt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o0=-1), mk.MK_ERR_INVALID_ARG),
+    (dict(o0=40, o1=32), mk.MK_ERR_INVALID_ARG),
+    (dict(o1=65), mk.MK_ERR_INVALID_ARG),
+    (dict(send=None), mk.MK_ERR_INVALID_ARG),             # rows outside [o0, o1) need send
+    (dict(send=S16 + 8), mk.MK_ERR_INVALID_ARG),
+    (dict(send=C16 + 64), mk.MK_ERR_INVALID_ARG),          # send overlaps C
+    (dict(send=P16 + 64), mk.MK_ERR_INVALID_ARG),          # send overlaps the peers
+    (dict(C=A16 + 64 * 64), mk.MK_ERR_INVALID_ARG),        # C inside A's last rows
+    (dict(N=60), mk.MK_ERR_UNSUPPORTED),
+])
+def test_reduce_scatter_validation(kw, status):
+    assert rs(**kw) == status, mk.last_error()
+    assert rs_base(**kw) == status, mk.last_error()
+
+
+def test_reduce_scatter_send_may_be_null_when_every_row_is_owned():
+    st = rs(send=None, o0=0, o1=64)
+    assert st in (mk.MK_OK, mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP), mk.last_error()

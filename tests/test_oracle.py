@@ -10,7 +10,9 @@ against something it does not share code with:
   - bfloat16 rounding: hand-derived cases in tests/golden/bf16_rne_cases.txt;
   - the exact peer summation: math.fsum (correctly rounded) on adversarial data;
   - hand-worked GEMM+AllReduce cases in tests/golden/hand_cases.json;
-  - row selection: rows computed alone equal the same rows of a full run.
+  - row selection: rows computed alone equal the same rows of a full run;
+  - the GEMM+ReduceScatter share: over a simulated K-split group, ReduceScatter
+    followed by AllGather gives numpy's exact int64 product.
 The last test builds planted-mistake variants of the oracle and checks that
 every one of them fails at least one pin.
 """
@@ -319,8 +321,48 @@ def pin_row_selection(orc, seed=5):
     check_exact(c, full[rows], "row selection")
 
 
+def pin_reduce_scatter_group(orc, seed=13):
+    """GEMM+ReduceScatter share ("GEMM + ReduceScatter (TP)" row of Table 3): over a
+    simulated group of P GPUs that split K, every GPU publishes its partial of the rows
+    it does not own, each owner reduces its rows with the others' published rows as
+    peers, and the owned slices put together are the whole product (ReduceScatter
+    followed by AllGather is an AllReduce). Integer inputs keep everything exact, so
+    the result is compared bit for bit with numpy's int64 matmul, rounded here."""
+    rng = np.random.default_rng(seed)
+    P, M, N, Kc = 4, 22, 16, 6
+    A = rng.integers(-4, 5, (M, P * Kc))
+    B = rng.integers(-4, 5, (P * Kc, N))
+    full = A @ B
+    bounds = [0, 5, 11, 11, 22]  # uneven slices, one of them empty
+    Ab = [bf16_bits_of(A[:, r * Kc:(r + 1) * Kc]) for r in range(P)]
+    Bb = [bf16_bits_of(B[r * Kc:(r + 1) * Kc]) for r in range(P)]
+    sends = []
+    for r in range(P):
+        o0, o1 = bounds[r], bounds[r + 1]
+        no_peers = np.zeros((0, o1 - o0, N), np.uint16)
+        (owned, _, _), (other, _, s_out) = orc.gemm_rs(Ab[r], Bb[r], no_peers, o0, o1, "bf16",
+                                                        "bf16")
+        assert sorted(owned) == list(range(o0, o1)) and len(other) == M - (o1 - o0)
+        send = np.zeros((M, N), np.uint16)
+        send[other] = s_out
+        # a published row is this GPU's own partial (|value| <= 96: exact in bfloat16)
+        part = A[:, r * Kc:(r + 1) * Kc] @ B[r * Kc:(r + 1) * Kc]
+        check_exact(send[other], bf16_bits_of(part[other]), f"send of GPU {r}")
+        sends.append(send)
+    C = np.zeros((M, N), np.uint16)
+    for r in range(P):
+        o0, o1 = bounds[r], bounds[r + 1]
+        peers = np.stack([sends[q][o0:o1] for q in range(P) if q != r])
+        (owned, c64, c_out), _ = orc.gemm_rs(Ab[r], Bb[r], peers, o0, o1, "bf16", "bf16")
+        assert np.array_equal(c64, full[o0:o1].astype(np.float64))
+        C[owned] = c_out
+    want = np.array([[frac_to_bf16_bits(Fraction(int(v))) for v in row] for row in full],
+                    dtype=np.uint16)
+    check_exact(C, want, "ReduceScatter then AllGather")
+
+
 PINS = [pin_integer_exact, pin_bruteforce_fraction, pin_peer_permutation, pin_bf16_rounding,
-        pin_exact_sum, pin_hand_cases, pin_row_selection]
+        pin_exact_sum, pin_hand_cases, pin_row_selection, pin_reduce_scatter_group]
 
 
 # --------------------------------------------------------------------------- tests
@@ -396,3 +438,46 @@ def test_pins_reject_planted_mistake(mutant, tmp_path):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"no pin caught the oracle that {MUTANTS[mutant]}"
+
+
+class _BrokenRS(oracle.Oracle):
+    """The ReduceScatter composition with one planted mistake."""
+
+    def __init__(self, lib, mistake):
+        super().__init__(lib)
+        self.mistake = mistake
+
+    def gemm_rs(self, A_bits, B_bits, peers_own, own_m0, own_m1, c_dtype="bf16",
+                peer_dtype="bf16", rows=None, threads=0):
+        M = A_bits.shape[0]
+        rows = np.arange(M)
+        mine = (rows >= own_m0) & (rows < own_m1)
+        owned, other = rows[mine], rows[~mine]
+        if self.mistake == "owned rows not shifted to the slice":
+            sel = np.minimum(owned, own_m1 - own_m0 - 1) if own_m1 > own_m0 else owned - own_m0
+            C64, C_out = self.gemm_ar(A_bits[own_m0:own_m1], B_bits, peers_own, c_dtype, rows=sel)
+        elif self.mistake == "local partial left out of owned rows":
+            C64, C_out = self.gemm_ar(np.zeros_like(A_bits[own_m0:own_m1]), B_bits, peers_own,
+                                      c_dtype, rows=owned - own_m0)
+        else:
+            C64, C_out = self.gemm_ar(A_bits[own_m0:own_m1], B_bits, peers_own, c_dtype,
+                                      rows=owned - own_m0)
+        if self.mistake == "published rows taken from the owned slice":
+            S64, S_out = self.gemm_ar(A_bits, B_bits, None, peer_dtype,
+                                      rows=np.where(other < own_m0, other, other - 1))
+        elif self.mistake == "publishes every row":
+            S64, S_out = self.gemm_ar(A_bits, B_bits, None, peer_dtype, rows=rows)
+            other = rows
+        else:
+            S64, S_out = self.gemm_ar(A_bits, B_bits, None, peer_dtype, rows=other)
+        return (owned, C64, C_out), (other, S64, S_out)
+
+
+@pytest.mark.parametrize("mistake", ["owned rows not shifted to the slice",
+                                     "local partial left out of owned rows",
+                                     "published rows taken from the owned slice",
+                                     "publishes every row"])
+def test_reduce_scatter_pin_rejects_planted_mistake(mistake):
+    orc = _BrokenRS(oracle.default().path, mistake)
+    with pytest.raises(AssertionError):
+        pin_reduce_scatter_group(orc)

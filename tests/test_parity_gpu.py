@@ -395,3 +395,84 @@ def test_two_stream_then_fused_on_one_stream():
     mk.stream_status()
     for i in range(4):
         check_exact(c_bits(outs[i]), sets[i % 2][3], f"call {i}")
+
+
+RS_CASES = [
+    # M, N, K, n_peers, peer dtype, C dtype, owned rows [o0, o1)
+    (520, 776, 264, 3, "bf16", "bf16", 128, 256),   # whole 128-row tiles
+    (520, 776, 264, 3, "bf16", "bf16", 100, 300),   # owned rows cut through tiles
+    (300, 264, 200, 15, "bf16", "f32", 0, 19),      # first rows, ragged everything
+    (300, 264, 200, 7, "f32", "bf16", 281, 300),    # last rows
+    (256, 512, 512, 1, "f32", "f32", 0, 256),       # every row owned: nothing published
+    (256, 512, 512, 2, "bf16", "bf16", 77, 77),     # nothing owned: everything published
+    (130, 136, 72, 0, "bf16", "bf16", 64, 130),     # no peers
+    (1024, 2048, 576, 15, "bf16", "bf16", 192, 448),  # 256x256 tiles
+    (300, 264, 200, 5, "bf16", "bf16", 10, 150),     # a peer count without a compile-time ring
+]
+
+
+def rs_poisoned(M, N, own, pdt, cdt):
+    C = new_c(own, N, cdt)
+    send = new_c(M, N, pdt)
+    return C, send
+
+
+@pytest.mark.parametrize("case", RS_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_reduce_scatter_share(case):
+    """One GPU's share of GEMM+ReduceScatter: owned rows reduced, other rows published
+    in the peer type. Integer inputs: bit-exact against the oracle, for the fused
+    kernel and the baseline; rows of send that this GPU owns are left untouched."""
+    M, N, K, npeer, pdt, cdt, o0, o1 = case
+    announce(f"reduce-scatter share {case}")
+    own = o1 - o0
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 101, device="cpu")
+    peers = peers[:, o0:o1].contiguous()
+    (owned, _, c_want), (other, _, s_want) = oracle.gemm_rs(
+        mk_inputs.bits(A), mk_inputs.bits(B), mk_inputs.bits(peers) if npeer else None, o0, o1,
+        cdt, pdt)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    outs = []
+    runs = [(f"fused, reducers {nr}", lambda C, send, nr=nr: mk.gemm_rs_local(
+        A, B, peers, C, send, o0, o1, n_reduce_wg=nr)) for nr in (None, 0, 4)]
+    runs.append(("baseline", lambda C, send: mk.gemm_rs_baseline(A, B, peers, C, send, o0, o1)))
+    for name, fn in runs:
+        C, send = rs_poisoned(M, N, own, pdt, cdt)
+        fn(C, send)
+        mk.stream_status()
+        cb, sb = c_bits(C), c_bits(send)
+        check_exact(cb, c_want, f"{name} owned rows")
+        check_exact(sb[other], s_want, f"{name} published rows")
+        poison = 0x7FC1 if pdt == "bf16" else 0x7FC00001
+        assert np.all(sb[o0:o1].view(np.uint16 if pdt == "bf16" else np.uint32) == poison)
+        outs.append((cb, sb))
+    for cb, sb in outs[:-1]:
+        check_exact(cb, outs[-1][0], "fused against baseline, owned rows")
+        check_exact(sb, outs[-1][1], "fused against baseline, send")
+
+
+def test_reduce_scatter_share_gaussian_full_size():
+    """The mlp workload's GEMM (4096x8192x1792, bf16 peers and C) as a ReduceScatter
+    share of a 16-GPU group that owns rows [768, 1024): sampled rows against the oracle
+    (tolerance rule for C, the same rule in the peer type for send), bitwise against
+    the baseline."""
+    w = mk_inputs.BY_NAME["mlp"]
+    announce("reduce-scatter share, mlp size")
+    A, B, peers_all = mk_inputs.workload_inputs(w, "gaussian", device=DEV)
+    o0, o1 = 768, 1024
+    peers = peers_all[:, o0:o1].contiguous()
+    del peers_all
+    rows = sample_rows(w.M)
+    (owned, c64, _), (other, s64, _) = oracle.gemm_rs(
+        mk_inputs.bits(A.cpu()), mk_inputs.bits(B.cpu()), mk_inputs.bits(peers.cpu()), o0, o1,
+        "bf16", "bf16", rows=rows)
+    outs = []
+    for fn in (mk.gemm_rs_local, mk.gemm_rs_baseline):
+        C, send = rs_poisoned(w.M, w.N, o1 - o0, "bf16", "bf16")
+        fn(A, B, peers, C, send, o0, o1)
+        mk.stream_status()
+        cb, sb = c_bits(C), c_bits(send)
+        check_tolerance(cb[owned - o0], c64, "bf16", f"{fn.__name__} owned rows")
+        check_tolerance(sb[other], s64, "bf16", f"{fn.__name__} published rows")
+        outs.append((cb, sb))
+    check_exact(outs[0][0], outs[1][0], "fused against baseline, owned rows")
+    check_exact(outs[0][1], outs[1][1], "fused against baseline, send")

@@ -34,6 +34,7 @@ OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 
 OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY = 4, 5, 6, 7
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_stream",
+           "mk_gemm_rs_local", "mk_gemm_rs_baseline",
            "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
            "mk_get_option",
@@ -61,6 +62,12 @@ _lib.mk_gemm_then_reduce_baseline.restype = _int
 _lib.mk_gemm_ar_two_stream.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _int,
                                        _vp, _int]
 _lib.mk_gemm_ar_two_stream.restype = _int
+_lib.mk_gemm_rs_local.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                  _int, _int, _vp, _int]
+_lib.mk_gemm_rs_baseline.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64,
+                                     _i64, _int, _int, _vp]
+_lib.mk_gemm_rs_local.restype = _int
+_lib.mk_gemm_rs_baseline.restype = _int
 _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
 _lib.mk_workspace_reset.argtypes = [_int]
@@ -181,6 +188,48 @@ def gemm_ar_two_stream(A, B, peers, C, n_chunks=0, stream=None):
     a = _args(A, B, peers, C)
     _check(_lib.mk_gemm_ar_two_stream(*a[:10], _stream_ptr(stream), int(n_chunks)))
     return C
+
+
+def _rs_args(A, B, peers, C, send, own_m0, own_m1):
+    M, K = A.shape
+    N = B.shape[1]
+    own0, own1 = int(own_m0), int(own_m1)
+    if not 0 <= own0 <= own1 <= M:
+        raise ValueError(f"owned rows [{own0}, {own1}) outside [0, {M}]")
+    own = own1 - own0
+    # A, B, peers and C as for an AllReduce share of the owned rows
+    a = _args(A[own0:own1] if own > 0 else A[:0], B, peers, C)
+    if not A.is_contiguous():
+        raise ValueError("A must be contiguous")
+    sptr = None
+    if own < M:
+        if send is None or not send.is_cuda or not send.is_contiguous():
+            raise ValueError("send must be a contiguous GPU tensor")
+        if tuple(send.shape) != (M, N) or _DT.get(send.dtype) != a[8] and a[3] > 0:
+            raise ValueError(f"send must be [{M}, {N}] of the peer type")
+        if a[3] == 0 and send.dtype not in _DT:
+            raise ValueError("send must be bfloat16 or float32")
+        sptr = send.data_ptr()
+    pdt = a[8] if a[3] > 0 else (_DT[send.dtype] if sptr is not None else MK_DT_BF16)
+    return (A.data_ptr(), B.data_ptr(), a[2], a[3], a[4], sptr, M, N, K, own0, own1, pdt, a[9])
+
+
+def gemm_rs_local(A, B, peers, C, send, own_m0, own_m1, n_reduce_wg=None, stream=None):
+    """One GPU's share of GEMM+ReduceScatter: C = peers.sum(0) + (A @ B)[own_m0:own_m1]
+    for the owned rows; send[i] = (A @ B)[i] in the peer type for every other row
+    (with no peers, send's dtype is the peer type). Fused persistent kernel;
+    n_reduce_wg: None (adaptive) or a static reducer count."""
+    nr = MK_ADAPTIVE if n_reduce_wg is None else int(n_reduce_wg)
+    _check(_lib.mk_gemm_rs_local(*_rs_args(A, B, peers, C, send, own_m0, own_m1),
+                                 _stream_ptr(stream), nr))
+    return C, send
+
+
+def gemm_rs_baseline(A, B, peers, C, send, own_m0, own_m1, stream=None):
+    """Same result as gemm_rs_local, by a GEMM kernel followed by reduce kernels."""
+    _check(_lib.mk_gemm_rs_baseline(*_rs_args(A, B, peers, C, send, own_m0, own_m1),
+                                    _stream_ptr(stream)))
+    return C, send
 
 
 def stream_status(stream=None):

@@ -223,6 +223,34 @@ mk_status_t validate(const void* A, const void* B, const void* peers, int n_peer
   return MK_OK;
 }
 
+// The same checks for a GEMM+ReduceScatter share: A [M,K], B [K,N], peers
+// [n_peers, own, N], C [own, N] (own = own_m1 - own_m0 rows), send [M, N] of the
+// peer type (not read or written when every row is owned).
+mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                        void* send, int64_t M, int64_t N, int64_t K, int64_t own_m0,
+                        int64_t own_m1, int peer_dtype, int c_dtype) {
+  if (own_m0 < 0 || own_m1 < own_m0 || own_m1 > M)
+    return fail(MK_ERR_INVALID_ARG, "owned rows [%lld, %lld) outside [0, %lld]", (long long)own_m0,
+                (long long)own_m1, (long long)M);
+  const int64_t own = own_m1 - own_m0;
+  // A, B, peers and C as for an AllReduce share of `own` rows; then A's other rows
+  mk_status_t st = validate(A, B, peers, n_peers, C, own, N, K, peer_dtype, c_dtype);
+  if (st != MK_OK) return st;
+  if (own < M) {  // send [M, N] in the peer type, like a C of all M rows
+    st = validate(A, B, nullptr, 0, send, M, N, K, peer_dtype, peer_dtype);
+    if (st != MK_OK) return st;
+  }
+  const size_t a_bytes = (size_t)(M * K) * 2;
+  const size_t p_bytes = (size_t)n_peers * (size_t)(own * N) * dt_size(peer_dtype);
+  const size_t c_bytes = (size_t)(own * N) * dt_size(c_dtype);
+  const size_t s_bytes = own < M ? (size_t)(M * N) * dt_size(peer_dtype) : 0;
+  if (s_bytes && !send) return fail(MK_ERR_INVALID_ARG, "send is NULL");
+  if (overlaps(C, c_bytes, A, a_bytes) || overlaps(send, s_bytes, peers, p_bytes) ||
+      overlaps(send, s_bytes, C, c_bytes))
+    return fail(MK_ERR_INVALID_ARG, "C or send overlaps another argument");
+  return MK_OK;
+}
+
 // 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile
 // and the shape has some arithmetic to hide the reduce behind: they need less L2
 // traffic per flop. Otherwise 128x128 tiles (two workgroups per CU): more tiles,
@@ -299,6 +327,18 @@ int reduce_grid(int64_t elems, int cus) {
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   return (int)grid;
+}
+
+// Grid of a ReduceScatter share: as for the AllReduce share without early
+// reduce (at most two workgroups per tile).
+int rs_grid_size(const Launch& L, int peer_dtype, int c_dtype) {
+  const int full = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  int n_xcd = L.info.cus / 32;
+  if (n_xcd < 1) n_xcd = 1;
+  int64_t want = 2 * L.tiles_m * L.tiles_n;
+  want = (want + n_xcd - 1) / n_xcd * n_xcd;
+  if (want < n_xcd) want = n_xcd;
+  return want < full ? (int)want : full;
 }
 
 mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype,
@@ -575,6 +615,166 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
   if (e == hipSuccess) e = hipEventRecord(ev[c], w->s2);
   if (e == hipSuccess) e = hipStreamWaitEvent(s, ev[c], 0);
   if (e != hipSuccess) return hip_fail(e, "two-stream schedule");
+  return MK_OK;
+}
+
+mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                             void* send, int64_t M, int64_t N, int64_t K, int64_t own_m0,
+                             int64_t own_m1, int peer_dtype, int c_dtype, void* stream,
+                             int n_reduce_wg) {
+  mk_status_t st = validate_rs(A, B, peers, n_peers, C, send, M, N, K, own_m0, own_m1, peer_dtype,
+                               c_dtype);
+  if (st != MK_OK) return st;
+  if (n_reduce_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d", n_reduce_wg);
+  Launch L;
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  if (st != MK_OK) return st;
+  const int G = rs_grid_size(L, peer_dtype, c_dtype);
+  if (n_reduce_wg > G - 1)
+    return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
+  if (M == 0 || N == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const Options opt = options();
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  const int T = (int)(L.tiles_m * L.tiles_n);
+  st = get_ws(L.dev, s, (size_t)(M * N), T, &w);
+  if (st != MK_OK) return st;
+  if (++w->epoch >= 0x7FFFFFFF) {
+    hipError_t e = mk::launch_ws_init(w->flags, w->flags_cap, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "flag reset");
+    w->epoch = 1;
+  }
+  int n_xcd = L.info.cus / 32;
+  n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
+  mk::FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = (const uint16_t*)A;
+  a.B = (const uint16_t*)B;
+  a.peers = peers;
+  a.C = C;
+  a.P = w->P;
+  a.flags = w->flags;
+  a.slots = w->slots;
+  a.tel = nullptr;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.n_peers = n_peers;
+  a.tiles_m = (int)L.tiles_m;
+  a.tiles_n = (int)L.tiles_n;
+  a.T = T;
+  a.G = G;
+  a.epoch = w->epoch;
+  a.ctrl_period = opt.ctrl_period < 1 ? 1 : (int)opt.ctrl_period;
+  a.withhold_tile = (int)opt.withhold_tile;
+  a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
+  a.n_xcd = G % n_xcd == 0 ? n_xcd : 1;
+  a.flag_scope = (int)opt.flag_scope;
+  a.early = 0;
+  a.rs = 1;
+  // Tile rows that hold owned rows are handed to reducers (their reduce is the
+  // heavy part and spreads over 64-row units); every other tile is computed and
+  // published in place. They lead each XCD's queue.
+  const int BM = mk::shape_bm(L.shape);
+  a.tmo0 = (int)(own_m0 / BM);
+  a.tmo1 = own_m1 > own_m0 ? (int)((own_m1 + BM - 1) / BM) : a.tmo0;
+  a.own0 = own_m0;
+  a.own1 = own_m1;
+  a.send = send;
+  a.n_inplace = 0;  // not used by a ReduceScatter share
+  a.T_r = (a.tmo1 - a.tmo0) * a.tiles_n;
+  // Controller: the handed-over tiles' reduce against the GEMM and the publish
+  // stores, both at roofline speed; at most the reducers that saturate HBM.
+  {
+    const int occ = L.shape == mk::SHAPE_256 ? 1 : 2;
+    int cap = (int)ceil(5.5e12 / 40e9) * occ;
+    cap = (cap + a.n_xcd - 1) / a.n_xcd * a.n_xcd;
+    a.reducer_cap = opt.reducer_cap > 0 ? (int)opt.reducer_cap : (cap < G - 1 ? cap : G - 1);
+    // As for the AllReduce share: with tiles handled in place, a dedicated
+    // reducer takes a compute unit from the GEMM (on the 4096x8192x1792 shape one
+    // reducer per XCD leaves a third round of tiles: 175 -> 211 us); the derived
+    // cap is then zero and every workgroup drains the handed-over units.
+    if (opt.reducer_cap <= 0 && a.T_r < a.T) a.reducer_cap = 0;
+    const double rows_h = (double)(a.tmo1 - a.tmo0) * BM;
+    const double own = (double)(own_m1 - own_m0);
+    const double t_r = (rows_h * N * 4.0 + own * N * (n_peers * (double)dt_size(peer_dtype) +
+                        dt_size(c_dtype)) + (rows_h - own) * N * dt_size(peer_dtype)) / 8.0e12;
+    const double t_c = 2.0 * M * N * K / 2.5e15 + ((double)M - rows_h) * N * dt_size(peer_dtype) / 8.0e12;
+    a.seed_x = t_r + t_c > 0 ? (float)(t_r / (t_r + t_c)) : 0.0f;
+  }
+  if (n_reduce_wg == MK_ADAPTIVE) {
+    a.adaptive = 1;
+    int it = (int)(a.seed_x * G + 0.5f);
+    it = it < 0 ? 0 : (it > a.reducer_cap ? a.reducer_cap : it);
+    a.init_target = it;
+  } else {
+    a.adaptive = 0;
+    a.init_target = n_reduce_wg;
+  }
+  hipError_t e = mk::launch_fused(L.shape, peer_dtype, c_dtype, a, s);
+  if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}
+
+mk_status_t mk_gemm_rs_baseline(const void* A, const void* B, const void* peers, int n_peers,
+                                void* C, void* send, int64_t M, int64_t N, int64_t K,
+                                int64_t own_m0, int64_t own_m1, int peer_dtype, int c_dtype,
+                                void* stream) {
+  mk_status_t st = validate_rs(A, B, peers, n_peers, C, send, M, N, K, own_m0, own_m1, peer_dtype,
+                               c_dtype);
+  if (st != MK_OK) return st;
+  Launch L;
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  if (st != MK_OK) return st;
+  if (M == 0 || N == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  const int T = (int)(L.tiles_m * L.tiles_n);
+  st = get_ws(L.dev, s, (size_t)(M * N), T, &w);
+  if (st != MK_OK) return st;
+  mk::GemmArgs g;
+  g.A = (const uint16_t*)A;
+  g.B = (const uint16_t*)B;
+  g.P = w->P;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tiles_m = (int)L.tiles_m;
+  g.tiles_n = (int)L.tiles_n;
+  const int n_xcd = L.info.cus / 32;
+  g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
+  g.pad_ = 0;
+  hipError_t e = mk::launch_gemm(L.shape, g, s);
+  if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
+  const int64_t own = own_m1 - own_m0;
+  // owned rows: the reduce kernel; the other rows: the same kernel without
+  // peers, which rounds the partial to the peer type
+  const int64_t r0[3] = {own_m0, 0, own_m1}, r1[3] = {own_m1, own_m0, M};
+  for (int part = 0; part < 3; ++part) {
+    const int64_t rows = r1[part] - r0[part];
+    if (rows <= 0) continue;
+    mk::ReduceArgs r;
+    r.P = w->P + r0[part] * N;
+    r.M = rows;
+    r.N = N;
+    r.pad_ = 0;
+    if (part == 0) {
+      r.peers = peers;
+      r.C = C;
+      r.peer_stride = own * N;
+      r.n_peers = n_peers;
+      e = mk::launch_reduce(peer_dtype, c_dtype, r, reduce_grid(rows * N, L.info.cus), s);
+    } else {
+      r.peers = nullptr;
+      r.C = (char*)send + (size_t)(r0[part] * N) * dt_size(peer_dtype);
+      r.peer_stride = 0;
+      r.n_peers = 0;
+      e = mk::launch_reduce(peer_dtype, peer_dtype, r, reduce_grid(rows * N, L.info.cus), s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
+  }
   return MK_OK;
 }
 

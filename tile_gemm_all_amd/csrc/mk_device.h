@@ -181,6 +181,40 @@ __device__ __forceinline__ void fused_tile_coords(int t, int tiles_m, int tiles_
   }
 }
 
+// GEMM+ReduceScatter order: each XCD's queue (local index i of cnt, first
+// global index q0) starts with its share [ox0, ox0 + ox) of the tiles in the
+// tile rows that hold owned rows, [tmo0, tmo1), so that their reduce overlaps
+// the other tiles' GEMMs rather than ending the kernel; the other tiles follow.
+// Both groups keep the grouped order of tile_coords.
+__device__ __forceinline__ void rs_tile_coords(int i, int q0, int ox0, int ox, int tiles_m,
+                                               int tiles_n, int tmo0, int tmo1, int& tm,
+                                               int& tn) {
+  const int h = tmo1 - tmo0;
+  if (i < ox) {
+    tile_coords(ox0 + i, h, tiles_n, tm, tn);
+    tm += tmo0;
+  } else {
+    tile_coords(q0 - ox0 + (i - ox), tiles_m - h, tiles_n, tm, tn);
+    if (tm >= tmo0) tm += h;
+  }
+}
+// XCD x's share of the n_ot tiles with owned rows: at most ceil(n_ot / n_xcd)
+// and at most its queue, in XCD order, so that every one of them is placed.
+__device__ __forceinline__ void rs_share(int x, int n_xcd, int T, int n_ot, int& ox0, int& ox) {
+  const int q = (n_ot + n_xcd - 1) / n_xcd;
+  int acc = 0, o = 0;
+  for (int y = 0; y <= x; ++y) {
+    const int cnt = (int)(((int64_t)(y + 1) * T) / n_xcd - ((int64_t)y * T) / n_xcd);
+    int v = cnt < q ? cnt : q;
+    v = v < n_ot - acc ? v : n_ot - acc;
+    v = v > 0 ? v : 0;
+    if (y == x) o = v;
+    else acc += v;
+  }
+  ox0 = acc;
+  ox = o;
+}
+
 template <class Cfg>
 struct GemmTile {
   f32x16 acc[Cfg::FM][Cfg::FN];
@@ -689,6 +723,27 @@ struct PresumOp {
   }
 };
 
+// out = round(partial in LDS): a tile's rows published as they are (no peers).
+template <typename OT>
+struct CopyLdsOp {
+  const lds_char* src;  // region base in LDS
+  OutC<OT> out;
+  struct Chunk {
+    f32x4 a, b;
+  };
+  // the LDS reads run ahead of the stores, like a ring's loads
+  __device__ __forceinline__ void load(Chunk& k, uint32_t, uint32_t loff) const {
+    k.a = *(const lds_f32x4*)(src + loff * 4u);
+    k.b = *(const lds_f32x4*)(src + loff * 4u + 16u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void finish(const Chunk& k, uint32_t off, uint32_t loff) const {
+    const float acc[8] = {k.a[0], k.a[1], k.a[2], k.a[3], k.b[0], k.b[1], k.b[2], k.b[3]};
+    out.store(off, loff, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
 // Walks chunk indices q = q0, q0+256, ... of a region of `cpr` chunks per row,
 // giving each one's element offset for two row pitches (N for device memory, LP
 // for a region in LDS), clamped to the last chunk past the end.
@@ -867,6 +922,22 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
     default: return;
   }
 #undef MK_RING
+}
+
+// Rounds the fp32 partial of a region in LDS (row pitch LP) to OT and stores it
+// to rows [m0, m0+rows) x cols [n0, n0+cols) of an N-column output.
+template <typename OT>
+__device__ __forceinline__ void copy_region_lds(const char* lds, int64_t LP, OT* __restrict__ out,
+                                                int64_t N, int64_t m0, int64_t n0, int rows,
+                                                int cols) {
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  const int total = rows * cpr;
+  if (total <= 0) return;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+  typedef CopyLdsOp<OT> Op;
+  ReduceRing<4, Op>::run(Op{(const lds_char*)lds, OutC<OT>{out + base}}, total, cpr, N, LP);
 }
 
 // A reduce unit in two phases, for a reducer that takes the unit before its

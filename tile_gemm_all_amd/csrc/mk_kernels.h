@@ -97,6 +97,14 @@ struct FusedArgs {
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
   int early;                   // 1: a reducer may take a unit whose tile is still being
                                // computed, and sums its peers while it waits
+  // GEMM+ReduceScatter share (rs = 1): rows [own0, own1) are reduced into C
+  // ([own1-own0, N]) with peers [n_peers, own1-own0, N]; the partial of every
+  // other row is rounded to the peer type and stored to send ([M, N]). Tiles
+  // in tile rows [tmo0, tmo1) are handed over, the others published in place.
+  int rs;
+  int tmo0, tmo1;              // tile rows that hold owned rows: [tmo0, tmo1)
+  int64_t own0, own1;
+  void* send;
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
 };
 

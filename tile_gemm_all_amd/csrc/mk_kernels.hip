@@ -104,6 +104,36 @@ __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry
 
 enum { K_EXIT = 0, K_COMPUTE = 1, K_REDUCE = 2 };
 
+// GEMM+ReduceScatter share, a reduce unit of a handed-over tile: rows
+// [r0, r0+rows) whose fp32 partial is in the workspace (all M rows). Owned rows
+// are reduced into C, the others rounded to the peer type into send.
+template <int OCC, typename PT, typename CT>
+__device__ __forceinline__ void rs_unit(const FusedArgs& a, int64_t r0, int64_t n0, int rows,
+                                        int cols) {
+  const int64_t r1 = r0 + rows;  // rows <= 0: nothing
+  const int64_t lo = r1 < a.own0 ? r1 : a.own0, hi = r1 < a.own1 ? r1 : a.own1;
+  const int64_t o0 = r0 > lo ? r0 : lo;  // owned rows [o0, o1)
+  const int64_t o1 = o0 > hi ? o0 : hi;
+  const int64_t own_rows = a.own1 - a.own0;
+  reduce_region<OCC, PT, PT>(a.P, (const PT*)nullptr, 0, (PT*)a.send, a.M, a.N, r0, n0,
+                             (int)(o0 - r0), cols);
+  if (o1 > o0)  // the workspace shifted so that its row o0 is row o0 - own0 of C
+    reduce_region<OCC, PT, CT>(a.P + a.own0 * a.N, (const PT*)a.peers, a.n_peers, (CT*)a.C,
+                               own_rows, a.N, o0 - a.own0, n0, (int)(o1 - o0), cols);
+  reduce_region<OCC, PT, PT>(a.P, (const PT*)nullptr, 0, (PT*)a.send, a.M, a.N, o1, n0,
+                             (int)(r1 - o1), cols);
+}
+
+// GEMM+ReduceScatter share, one band of a tile's rows [r0, r0+rows) whose fp32
+// partial sits in LDS (pitch LP). Tiles handled in place hold no owned row (the
+// tile rows with owned rows are handed over), so the band is published: rounded
+// to the peer type into send, which the rows' owners receive as a peer partial.
+template <typename PT>
+__device__ __forceinline__ void rs_band(const FusedArgs& a, const char* band, int64_t LP,
+                                        int64_t r0, int64_t n0, int rows, int cols) {
+  copy_region_lds<PT>(band, LP, (PT*)a.send, a.N, r0, n0, rows, cols);
+}
+
 
 
 // Persistent fused kernel. Tiles [start_x, start_x + cnt_x) belong to XCD x: only
@@ -132,12 +162,16 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   int rank = -1, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
   bool flag_seen = false;  // thread 0: the claimed unit's flag was already read as set
   unsigned long long t_busy = 0;  // thread 0: a reduce unit's busy ticks, less its end tick
+  // ReduceScatter share: the XCD's queue starts with its share of the tiles in
+  // the tile rows that hold owned rows; those are handed to reducers, the rest
+  // (published rows only) are handled in place.
+  int rs_ox0 = 0, rs_ox = 0;
+  if (a.rs) rs_share(x, a.n_xcd, a.T, (a.tmo1 - a.tmo0) * a.tiles_n, rs_ox0, rs_ox);
   // The last n_in tiles of the XCD's queue are reduced in place by the workgroup
-  // that computes them: no compute is left to overlap with, so handing them to
-  // reducers would only add the partial's round trip through memory. At most
-  // half of the queue, so that flags and reducers carry the rest.
-  const int n_in = xcd_inplace(cnt, a.n_inplace,
-                               inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers));
+  // that computes them: no partial goes through memory, no flag is involved.
+  const int n_in = a.rs ? cnt - rs_ox
+                        : xcd_inplace(cnt, a.n_inplace,
+                                      inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers));
   const int published = cnt - n_in;
   // Early reduce: a unit's peers are summed into LDS before its flag is read.
   static_assert(Cfg::BM / Cfg::RSPLIT * Cfg::BN * 4 <= Cfg::LDS_BYTES, "peer sum of a unit in LDS");
@@ -259,7 +293,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
     const int kind = s_kind, tile = s_tile, part = s_part;
     if (kind == K_EXIT) break;
     int tm, tn;
-    fused_tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
+    if (a.rs)
+      rs_tile_coords(tile - q0, q0, rs_ox0, rs_ox, a.tiles_m, a.tiles_n, a.tmo0, a.tmo1, tm, tn);
+    else
+      fused_tile_coords(tile, a.tiles_m, a.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
 
     if (kind == K_COMPUTE) {
@@ -283,8 +320,12 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           for (int wm = 0; wm < 2; ++wm) {
             const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
             const int rows = (int)(a.M - r0 < BAND ? a.M - r0 : BAND);  // <= 0 past the edge
-            reduce_region_lds<Cfg::OCC, PT, CT>(lds + wm * BAND * Cfg::BN * 4, Cfg::BN, peers,
-                                                a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
+            const char* band = lds + wm * BAND * Cfg::BN * 4;
+            if (a.rs)
+              rs_band<PT>(a, band, Cfg::BN, r0, n0, rows, cols);
+            else
+              reduce_region_lds<Cfg::OCC, PT, CT>(band, Cfg::BN, peers, a.n_peers, C, a.M, a.N,
+                                                  r0, n0, rows, cols);
           }
           __syncthreads();
         };
@@ -352,6 +393,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       if (!s_ok) break;
       if (early)
         reduce_region_finish<CT>(a.P, lds, Cfg::BN, C, a.N, r0, n0, rows, cols);
+      else if (a.rs)
+        rs_unit<Cfg::OCC, PT, CT>(a, r0, n0, rows, cols);
       else
         reduce_region<Cfg::OCC, PT, CT>(a.P, peers, a.n_peers, C, a.M, a.N, r0, n0, rows, cols);
       __syncthreads();
