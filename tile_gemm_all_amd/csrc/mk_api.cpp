@@ -251,20 +251,17 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
   return MK_OK;
 }
 
-// 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile
-// and the shape has some arithmetic to hide the reduce behind: they need less L2
-// traffic per flop. Otherwise 128x128 tiles (two workgroups per CU): more tiles,
-// finished sooner, for shapes with fewer 256-tiles than CUs or whose work is
-// almost all reduce (below 48 flops per compulsory byte, e.g. K = 512).
+// 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile:
+// they need half the L2 traffic per flop of 128x128 tiles. Otherwise 128x128
+// tiles (two workgroups per CU), so that shapes with fewer 256-tiles than CUs
+// still occupy the chip. Measured on the 16384x8192x512 shape with 15 peers
+// (interleaved runs on one box): 256-tiles 969-979 us, 128-tiles 1073-1081 us.
 int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
+  (void)K; (void)n_peers; (void)peer_dtype; (void)c_dtype;
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
   int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  double flops = 2.0 * (double)M * (double)N * (double)K;
-  double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
-                 (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
-  double ai = bytes > 0 ? flops / bytes : 0.0;
-  return t256 >= cus && ai >= 48.0 ? mk::SHAPE_256 : mk::SHAPE_128;
+  return t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
 }
 
 // Host roofline seed for the controller: the reducers' share of the work when
