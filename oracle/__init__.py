@@ -1,5 +1,5 @@
-"""CPU oracle for one GPU's share of GEMM+AllReduce (and of GEMM+ReduceScatter)
--- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for one GPU's share of GEMM+AllReduce (and of GEMM+ReduceScatter and
+AllGather+GEMM) -- TEST INFRASTRUCTURE ONLY.
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package. The product path (tile_gemm_all_amd, libmk.so) never does.
@@ -115,6 +115,30 @@ class Oracle:
         S64, S_out = self.gemm_ar(A_bits, B_bits, None, peer_dtype, rows=other, threads=threads)
         return (owned, C64, C_out), (other, S64, S_out)
 
+    def gemm_ag(self, A_local, peers_A, rank, B_bits, c_dtype="bf16", rows=None, threads=0):
+        """Reference for one GPU's share of AllGather+GEMM ("AllGather + GEMM (TP)" row
+        of Table 3, thelatestinai.com page: communication -> compute, each GPU's row
+        shard of the activations broadcast to every GPU, which multiplies the
+        gathered matrix by its own weight shard).
+
+        A_local: uint16 [Ms, K], this GPU's shard (rank `rank` of P); peers_A: uint16
+        [P-1, Ms, K], the other GPUs' shards in rank order with `rank` left out;
+        B_bits: uint16 [K, N]. The gathered matrix holds shard q at rows
+        [q*Ms, (q+1)*Ms). Returns (A_full uint16 [P*Ms, K], C64, C_out) with C the
+        product of the gathered matrix and B (rows: None for all, else indices).
+        """
+        A_local = np.ascontiguousarray(A_local, dtype=np.uint16)
+        peers_A = np.ascontiguousarray(peers_A, dtype=np.uint16)
+        if peers_A.ndim != 3 or peers_A.shape[1:] != A_local.shape:
+            raise ValueError("peers_A must be [P-1, Ms, K] like A_local")
+        if not 0 <= rank <= peers_A.shape[0]:
+            raise ValueError("rank outside [0, P)")
+        shards = [peers_A[q] for q in range(peers_A.shape[0])]
+        shards.insert(rank, A_local)
+        A_full = np.concatenate(shards, axis=0)
+        C64, C_out = self.gemm_ar(A_full, B_bits, None, c_dtype, rows=rows, threads=threads)
+        return A_full, C64, C_out
+
     def bf16_to_f64(self, bits):
         b = np.ascontiguousarray(bits, dtype=np.uint16)
         out = np.empty(b.shape, dtype=np.float64)
@@ -156,6 +180,10 @@ def gemm_ar(*a, **k):
 
 def gemm_rs(*a, **k):
     return default().gemm_rs(*a, **k)
+
+
+def gemm_ag(*a, **k):
+    return default().gemm_ag(*a, **k)
 
 
 def bf16_to_f64(bits):

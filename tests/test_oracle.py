@@ -361,8 +361,41 @@ def pin_reduce_scatter_group(orc, seed=13):
     check_exact(C, want, "ReduceScatter then AllGather")
 
 
+def pin_allgather_group(orc, seed=17):
+    """AllGather+GEMM share ("AllGather + GEMM (TP)" row of Table 3): over a simulated
+    group of P GPUs, GPU r holds row shard r of the activation matrix X and column
+    shard r of the weight W. After the gather every GPU holds all of X in rank order,
+    and the GPUs' outputs side by side are X times W. The test builds X and W whole
+    and slices them, so the shard order is fixed by the slicing, not by the oracle.
+    Integer inputs keep the products exact: compared bit for bit with numpy's int64
+    matmul, rounded here."""
+    rng = np.random.default_rng(seed)
+    P, Ms, K, Nc = 4, 3, 10, 5
+    X = rng.integers(-4, 5, (P * Ms, K))
+    W = rng.integers(-4, 5, (K, P * Nc))
+    Xb = bf16_bits_of(X)
+    outs = []
+    for r in range(P):
+        peers_A = np.stack([Xb[q * Ms:(q + 1) * Ms] for q in range(P) if q != r])
+        A_full, c64, c_out = orc.gemm_ag(Xb[r * Ms:(r + 1) * Ms], peers_A, r,
+                                         bf16_bits_of(W[:, r * Nc:(r + 1) * Nc]), "bf16")
+        check_exact(A_full, Xb, f"gathered activations of GPU {r}")
+        assert np.array_equal(c64, (X @ W[:, r * Nc:(r + 1) * Nc]).astype(np.float64))
+        outs.append(c_out)
+        # a row selection returns those rows of the whole result
+        _, c64s, c_outs = orc.gemm_ag(Xb[r * Ms:(r + 1) * Ms], peers_A, r,
+                                      bf16_bits_of(W[:, r * Nc:(r + 1) * Nc]), "bf16",
+                                      rows=[P * Ms - 1, r * Ms, 0])
+        check_exact(c_outs, c_out[[P * Ms - 1, r * Ms, 0]], f"selected rows of GPU {r}")
+    full = X @ W
+    want = np.array([[frac_to_bf16_bits(Fraction(int(v))) for v in row] for row in full],
+                    dtype=np.uint16)
+    check_exact(np.concatenate(outs, axis=1), want, "AllGather then column-parallel GEMM")
+
+
 PINS = [pin_integer_exact, pin_bruteforce_fraction, pin_peer_permutation, pin_bf16_rounding,
-        pin_exact_sum, pin_hand_cases, pin_row_selection, pin_reduce_scatter_group]
+        pin_exact_sum, pin_hand_cases, pin_row_selection, pin_reduce_scatter_group,
+        pin_allgather_group]
 
 
 # --------------------------------------------------------------------------- tests
@@ -481,3 +514,34 @@ def test_reduce_scatter_pin_rejects_planted_mistake(mistake):
     orc = _BrokenRS(oracle.default().path, mistake)
     with pytest.raises(AssertionError):
         pin_reduce_scatter_group(orc)
+
+
+class _BrokenAG(oracle.Oracle):
+    """The AllGather composition with one planted mistake."""
+
+    def __init__(self, lib, mistake):
+        super().__init__(lib)
+        self.mistake = mistake
+
+    def gemm_ag(self, A_local, peers_A, rank, B_bits, c_dtype="bf16", rows=None, threads=0):
+        shards = [peers_A[q] for q in range(peers_A.shape[0])]
+        if self.mistake == "local shard first":
+            shards.insert(0, A_local)
+        elif self.mistake == "local shard last":
+            shards.append(A_local)
+        elif self.mistake == "peers in reverse order":
+            shards = shards[::-1]
+            shards.insert(rank, A_local)
+        else:  # "rank off by one"
+            shards.insert(min(rank + 1, len(shards)), A_local)
+        A_full = np.concatenate(shards, axis=0)
+        C64, C_out = self.gemm_ar(A_full, B_bits, None, c_dtype, rows=rows, threads=threads)
+        return A_full, C64, C_out
+
+
+@pytest.mark.parametrize("mistake", ["local shard first", "local shard last",
+                                     "peers in reverse order", "rank off by one"])
+def test_allgather_pin_rejects_planted_mistake(mistake):
+    orc = _BrokenAG(oracle.default().path, mistake)
+    with pytest.raises(AssertionError):
+        pin_allgather_group(orc)
