@@ -203,6 +203,46 @@ mk_status_t mk_gemm_rs_baseline(const void* A, const void* B, const void* peers,
                                 int64_t own_m0, int64_t own_m1, int peer_dtype, int c_dtype,
                                 void* stream);
 
+/*
+ * mk_gemm_ag_local -- one GPU's share of the "AllGather + GEMM (TP)" kernel of
+ * Table 3 on the thelatestinai.com page (communication -> compute: each GPU's
+ * row shard of the activations is broadcast to every GPU, and the GEMM consumes
+ * gathered rows in row chunks as they arrive). With P = n_peers + 1 GPUs, this
+ * one of rank `rank`:
+ *   A_full[q*Ms + i, k] = (q == rank ? A_local : peers_A[q < rank ? q : q-1])[i, k]
+ *   C[i, j]             = round_c( sum_k A_full[i, k] * B[k, j] )   (fp32 accumulation)
+ *   A_local [Ms, K] bf16: this GPU's shard;
+ *   peers_A [n_peers, Ms, K] bf16: the other GPUs' shards in rank order, `rank`
+ *           left out (inputs standing in for the broadcast data);
+ *   A_full  [P*Ms, K] bf16: the gathered matrix (written);
+ *   B [K, N] bf16; C [P*Ms, N] c_dtype (written).
+ * One persistent launch. The other GPUs' shards are landed in A_full in bands of
+ * tile rows (128 or 256), each in pieces with a counter per band; a tile is
+ * computed once its band has landed, this GPU's own bands at once (read from
+ * A_local). A workgroup whose band is missing lands pieces itself, so any
+ * n_comm_wg is deadlock-free. n_comm_wg: workgroups that prefer landing,
+ * 0 .. mk_ag_grid()-1, or MK_ADAPTIVE for the library's default. Requires Ms a
+ * multiple of 128, N and K multiples of 8, 16-byte aligned pointers, rank in
+ * [0, n_peers], n_peers <= MK_MAX_PEERS; else MK_ERR_INVALID_ARG or
+ * MK_ERR_UNSUPPORTED. A_full and C must not overlap each other or any input.
+ * Asynchronous on `stream`; a band wait past MK_OPT_SPIN_TIMEOUT_US stops the
+ * kernel and sets the error word that mk_stream_status returns.
+ */
+mk_status_t mk_gemm_ag_local(const void* A_local, const void* peers_A, int n_peers, void* A_full,
+                             const void* B, void* C, int64_t Ms, int64_t N, int64_t K, int rank,
+                             int c_dtype, void* stream, int n_comm_wg);
+
+/* mk_gemm_ag_baseline -- the same result (bitwise) unfused: a copy kernel
+ * gathers every shard into A_full, then a GEMM kernel (one workgroup per tile)
+ * writes C, in order on `stream`. Same arguments as mk_gemm_ag_local. */
+mk_status_t mk_gemm_ag_baseline(const void* A_local, const void* peers_A, int n_peers,
+                                void* A_full, const void* B, void* C, int64_t Ms, int64_t N,
+                                int64_t K, int rank, int c_dtype, void* stream);
+
+/* G of mk_gemm_ag_local for these sizes on the current device (negative
+ * mk_status_t on failure). */
+int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype);
+
 /* Synchronizes `stream`, then returns and clears the device error word of that
  * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
 mk_status_t mk_stream_status(void* stream);

@@ -13,6 +13,12 @@ Workloads (model-shaped, synthetic; no dataset or weights are involved):
   large    M=8192  N=8192 K=8192  P=8   compute-bound shard
   decode   M=128   N=8192 K=1792  P=16  decode-sized skinny shard
 
+AllGather+GEMM share (the "AllGather + GEMM (TP)" row of Table 3):
+
+  ag_up    Ms=256 rows per GPU, P=16 (4096 gathered rows), K=8192, N=3584:
+           Llama-70B-like MLP gate+up projection, column-parallel shard
+           (2*28672/16 columns); bf16 C
+
 Value distributions:
   gaussian  A, B ~ N(0,1)/sqrt(K) drawn in fp32 and rounded to bfloat16 by
             torch's conversion (round to nearest even); peers ~ N(0,1) in the
@@ -114,6 +120,61 @@ def make_inputs(M, N, K, n_peers, peer_dtype="bf16", variant="gaussian", seed_ba
     else:
         raise ValueError(f"unknown variant {variant}")
     return A, B, peers
+
+
+@dataclass(frozen=True)
+class AgWorkload:
+    index: int
+    name: str
+    Ms: int  # rows per GPU's shard
+    P: int
+    N: int
+    K: int
+    c_dtype: str
+    description: str
+
+    @property
+    def M(self):
+        return self.P * self.Ms
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def compulsory_bytes(self):
+        """Shards read once, gathered matrix written once, B read once, C written once."""
+        cb = 2 if self.c_dtype == "bf16" else 4
+        return 2 * self.M * self.K * 2 + 2 * self.K * self.N + cb * self.M * self.N
+
+
+AG_WORKLOADS = [
+    AgWorkload(6, "ag_up", 256, 16, 3584, 8192, "bf16",
+               "Llama-70B-like MLP gate+up column-parallel shard, activations gathered"),
+]
+AG_BY_NAME = {w.name: w for w in AG_WORKLOADS}
+
+
+def make_ag_inputs(Ms, P, N, K, variant="gaussian", seed_base=0, device="cpu"):
+    """Returns (shards [P,Ms,K] bf16: every GPU's row shard of the activations,
+    B [K,N] bf16). A GPU of rank r takes shards[r] as its own and the others as
+    its peers' (shard_split)."""
+    if variant == "integer":
+        sb = seed_base + 100
+        shards = integers((P, Ms, K), sb + 0, device=device)
+        B = integers((K, N), sb + 1, device=device)
+    elif variant == "gaussian":
+        s = 1.0 / math.sqrt(K) if K > 0 else 1.0
+        shards = gaussian((P, Ms, K), seed_base + 0, s, device=device)
+        B = gaussian((K, N), seed_base + 1, s, device=device)
+    else:
+        raise ValueError(f"unknown variant {variant}")
+    return shards, B
+
+
+def shard_split(shards, rank):
+    """(own shard [Ms,K], the others [P-1,Ms,K] in rank order with `rank` left out)."""
+    idx = [q for q in range(shards.shape[0]) if q != rank]
+    return shards[rank].contiguous(), shards[idx].contiguous()
 
 
 def workload_inputs(w: Workload, variant="gaussian", device="cpu"):

@@ -168,3 +168,47 @@ def test_reduce_scatter_validation(kw, status):
 def test_reduce_scatter_send_may_be_null_when_every_row_is_owned():
     st = rs(send=None, o0=0, o1=64)
     assert st in (mk.MK_OK, mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP), mk.last_error()
+
+
+F16 = 0xC0000000  # fake gathered-matrix address
+
+
+def ag(A_local=A16, peers_A=P16, n_peers=3, A_full=F16, B=B16, C=C16, Ms=128, N=64, K=64, rank=1,
+       cdt=0, nc=-1):
+    return mk.library().mk_gemm_ag_local(A_local, peers_A, n_peers, A_full, B, C, Ms, N, K, rank,
+                                         cdt, None, nc)
+
+
+def ag_base(A_local=A16, peers_A=P16, n_peers=3, A_full=F16, B=B16, C=C16, Ms=128, N=64, K=64,
+            rank=1, cdt=0):
+    return mk.library().mk_gemm_ag_baseline(A_local, peers_A, n_peers, A_full, B, C, Ms, N, K,
+                                            rank, cdt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A_local=None), mk.MK_ERR_INVALID_ARG),
+    (dict(peers_A=None), mk.MK_ERR_INVALID_ARG),
+    (dict(A_full=None), mk.MK_ERR_INVALID_ARG),
+    (dict(B=None), mk.MK_ERR_INVALID_ARG),
+    (dict(C=None), mk.MK_ERR_INVALID_ARG),
+    (dict(A_full=F16 + 4), mk.MK_ERR_INVALID_ARG),
+    (dict(rank=4), mk.MK_ERR_INVALID_ARG),               # rank beyond P-1
+    (dict(rank=-1), mk.MK_ERR_INVALID_ARG),
+    (dict(n_peers=65), mk.MK_ERR_INVALID_ARG),
+    (dict(Ms=-128), mk.MK_ERR_INVALID_ARG),
+    (dict(cdt=2), mk.MK_ERR_INVALID_ARG),
+    (dict(Ms=192), mk.MK_ERR_UNSUPPORTED),               # bands of 128 rows
+    (dict(N=60), mk.MK_ERR_UNSUPPORTED),
+    (dict(K=12), mk.MK_ERR_UNSUPPORTED),
+    (dict(A_full=A16), mk.MK_ERR_INVALID_ARG),           # gathered matrix over the local shard
+    (dict(A_full=P16 + 64), mk.MK_ERR_INVALID_ARG),      # ... over a peer shard
+    (dict(C=F16 + 64), mk.MK_ERR_INVALID_ARG),           # C over the gathered matrix
+    (dict(C=B16), mk.MK_ERR_INVALID_ARG),                # C over B
+])
+def test_allgather_validation_rejects(kw, status):
+    assert ag(**kw) == status, mk.last_error()
+    assert ag_base(**kw) == status, mk.last_error()
+
+
+def test_allgather_static_count_below_minus_one_is_rejected():
+    assert ag(nc=-2) == mk.MK_ERR_INVALID_ARG

@@ -476,3 +476,108 @@ def test_reduce_scatter_share_gaussian_full_size():
         outs.append((cb, sb))
     check_exact(outs[0][0], outs[1][0], "fused against baseline, owned rows")
     check_exact(outs[0][1], outs[1][1], "fused against baseline, send")
+
+
+AG_CASES = [
+    # Ms (rows per GPU), P, N, K, rank, C dtype
+    (128, 4, 264, 200, 1, "bf16"),     # ragged N, partial k-tile
+    (256, 3, 512, 512, 0, "f32"),
+    (128, 1, 136, 64, 0, "bf16"),      # no peers: the gather is a copy
+    (128, 16, 256, 72, 15, "bf16"),    # last rank, many bands
+    (384, 2, 136, 1040, 1, "f32"),
+    (128, 5, 8, 8, 2, "bf16"),         # the smallest N and K
+    (256, 4, 2048, 576, 3, "bf16"),
+]
+
+
+def ag_poisoned(M, N, K, cdt):
+    A_full = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    A_full.view(torch.int16).fill_(0x7FC1)
+    return A_full, new_c(M, N, cdt)
+
+
+@pytest.mark.parametrize("shape_opt", [0, 1], ids=["auto-tiles", "256-tiles"])
+@pytest.mark.parametrize("case", AG_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_allgather_share(case, shape_opt):
+    """One GPU's share of AllGather+GEMM ("AllGather + GEMM (TP)" row of Table 3).
+    Integer inputs: the gathered matrix and C bit-exact against the oracle, for the
+    fused kernel with the default, no and the most landing workgroups, and for the
+    baseline."""
+    Ms, P, N, K, rank, cdt = case
+    if shape_opt == 1 and Ms % 256 != 0:
+        pytest.skip("256-row bands need Ms a multiple of 256")
+    announce(f"allgather share {case} tile option {shape_opt}")
+    shards, B = mk_inputs.make_ag_inputs(Ms, P, N, K, "integer", 201, device="cpu")
+    A_local, peers_A = mk_inputs.shard_split(shards, rank)
+    f_want, _, c_want = oracle.gemm_ag(mk_inputs.bits(A_local), mk_inputs.bits(peers_A), rank,
+                                       mk_inputs.bits(B), cdt)
+    A_local, peers_A, B = A_local.to(DEV), peers_A.to(DEV), B.to(DEV)
+    old = mk.get_option(mk.OPT_TILE_SHAPE)
+    mk.set_option(mk.OPT_TILE_SHAPE, shape_opt)
+    try:
+        A_full, C = ag_poisoned(P * Ms, N, K, cdt)
+        G = mk.ag_grid(A_local, peers_A, A_full, B, C)
+        runs = [(f"fused, landing {nc}", lambda F, C, nc=nc: mk.gemm_ag_local(
+            A_local, peers_A, F, B, C, rank, n_comm_wg=nc)) for nc in (None, 0, G - 1)]
+        runs.append(("baseline", lambda F, C: mk.gemm_ag_baseline(A_local, peers_A, F, B, C,
+                                                                   rank)))
+        for name, fn in runs:
+            A_full, C = ag_poisoned(P * Ms, N, K, cdt)
+            fn(A_full, C)
+            mk.stream_status()
+            check_exact(mk_inputs.bits(A_full), f_want, f"{name} gathered matrix")
+            check_exact(c_bits(C), c_want, f"{name} C")
+    finally:
+        mk.set_option(mk.OPT_TILE_SHAPE, old)
+
+
+def test_allgather_share_gaussian_and_alternating_ranks():
+    """Gaussian inputs within the tolerance rule; then calls that alternate the rank
+    (and so which bands are local and which XCD lands each band) on the same
+    buffers, each checked bitwise against the baseline of the same rank."""
+    Ms, P, N, K = 256, 6, 776, 520
+    announce(f"allgather share gaussian {Ms}x{P}x{N}x{K}")
+    shards, B = mk_inputs.make_ag_inputs(Ms, P, N, K, "gaussian", 202, device="cpu")
+    Bd = B.to(DEV)
+    A_full, C = ag_poisoned(P * Ms, N, K, "bf16")
+    A_ref, C_ref = ag_poisoned(P * Ms, N, K, "bf16")
+    for i, rank in enumerate([2, 5, 0, 2, 3]):
+        A_local, peers_A = mk_inputs.shard_split(shards, rank)
+        if i == 0:
+            _, c64, _ = oracle.gemm_ag(mk_inputs.bits(A_local), mk_inputs.bits(peers_A), rank,
+                                       mk_inputs.bits(B), "bf16")
+        A_local, peers_A = A_local.to(DEV), peers_A.to(DEV)
+        mk.gemm_ag_local(A_local, peers_A, A_full, Bd, C, rank)
+        mk.gemm_ag_baseline(A_local, peers_A, A_ref, Bd, C_ref, rank)
+        mk.stream_status()
+        if i == 0:
+            check_tolerance(c_bits(C), c64, "bf16", "fused gaussian")
+        check_exact(mk_inputs.bits(A_full), mk_inputs.bits(shards.reshape(P * Ms, K)),
+                    f"gathered matrix, rank {rank}")
+        check_exact(c_bits(C), c_bits(C_ref), f"fused against baseline, rank {rank}")
+
+
+def test_allgather_share_full_size():
+    """The ag_up workload (16 GPUs x 256 rows, K=8192, N=3584, bf16): sampled rows of C
+    against the oracle (tolerance rule), the gathered matrix and C bitwise against the
+    baseline."""
+    w = mk_inputs.AG_BY_NAME["ag_up"]
+    rank = 5
+    announce(f"allgather share, {w.name} size")
+    shards, B = mk_inputs.make_ag_inputs(w.Ms, w.P, w.N, w.K, "gaussian", 1000 * w.index,
+                                         device=DEV)
+    A_local, peers_A = mk_inputs.shard_split(shards, rank)
+    rows = sample_rows(w.M)
+    _, c64, _ = oracle.gemm_ag(mk_inputs.bits(A_local), mk_inputs.bits(peers_A), rank,
+                               mk_inputs.bits(B), "bf16", rows=rows)
+    outs = []
+    for fn in (mk.gemm_ag_local, mk.gemm_ag_baseline):
+        A_full, C = ag_poisoned(w.M, w.N, w.K, "bf16")
+        fn(A_local, peers_A, A_full, B, C, rank)
+        mk.stream_status()
+        cb = c_bits(C)
+        check_tolerance(cb[rows], c64, "bf16", f"{fn.__name__} sampled rows")
+        outs.append((mk_inputs.bits(A_full), cb))
+    check_exact(outs[0][0], mk_inputs.bits(shards.reshape(w.M, w.K)), "gathered matrix")
+    check_exact(outs[0][0], outs[1][0], "fused against baseline, gathered matrix")
+    check_exact(outs[0][1], outs[1][1], "fused against baseline, C")

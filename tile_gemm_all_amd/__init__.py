@@ -34,7 +34,8 @@ OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 
 OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY = 4, 5, 6, 7
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_stream",
-           "mk_gemm_rs_local", "mk_gemm_rs_baseline",
+           "mk_gemm_rs_local", "mk_gemm_rs_baseline", "mk_gemm_ag_local", "mk_gemm_ag_baseline",
+           "mk_ag_grid",
            "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
            "mk_get_option",
@@ -68,6 +69,14 @@ _lib.mk_gemm_rs_baseline.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, 
                                      _i64, _int, _int, _vp]
 _lib.mk_gemm_rs_local.restype = _int
 _lib.mk_gemm_rs_baseline.restype = _int
+_lib.mk_gemm_ag_local.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                  _vp, _int]
+_lib.mk_gemm_ag_local.restype = _int
+_lib.mk_gemm_ag_baseline.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                     _vp]
+_lib.mk_gemm_ag_baseline.restype = _int
+_lib.mk_ag_grid.argtypes = [_i64, _int, _i64, _i64, _int]
+_lib.mk_ag_grid.restype = _int
 _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
 _lib.mk_workspace_reset.argtypes = [_int]
@@ -230,6 +239,57 @@ def gemm_rs_baseline(A, B, peers, C, send, own_m0, own_m1, stream=None):
     _check(_lib.mk_gemm_rs_baseline(*_rs_args(A, B, peers, C, send, own_m0, own_m1),
                                     _stream_ptr(stream)))
     return C, send
+
+
+def _ag_args(A_local, peers_A, A_full, B, C, rank):
+    for name, t in (("A_local", A_local), ("A_full", A_full), ("B", B)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    if C.dtype not in _DT or not C.is_cuda or not C.is_contiguous():
+        raise ValueError("C must be a contiguous bfloat16/float32 GPU tensor")
+    Ms, K = A_local.shape
+    K2, N = B.shape
+    if peers_A is None or peers_A.numel() == 0:
+        n_peers, pptr = 0, None
+    else:
+        if peers_A.dtype != torch.bfloat16 or not peers_A.is_cuda or not peers_A.is_contiguous():
+            raise ValueError("peers_A must be a contiguous bfloat16 GPU tensor")
+        if peers_A.dim() != 3 or tuple(peers_A.shape[1:]) != (Ms, K):
+            raise ValueError(f"peers_A must be [P-1, {Ms}, {K}], got {tuple(peers_A.shape)}")
+        n_peers, pptr = peers_A.shape[0], peers_A.data_ptr()
+    M = (n_peers + 1) * Ms
+    if K2 != K or tuple(A_full.shape) != (M, K) or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A_local{tuple(A_local.shape)} A_full"
+                         f"{tuple(A_full.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    return (A_local.data_ptr(), pptr, n_peers, A_full.data_ptr(), B.data_ptr(), C.data_ptr(), Ms,
+            N, K, int(rank), _DT[C.dtype])
+
+
+def gemm_ag_local(A_local, peers_A, A_full, B, C, rank, n_comm_wg=None, stream=None):
+    """One GPU's share of AllGather+GEMM: A_full = the shards in rank order (this
+    GPU's A_local at `rank`, peers_A the others), C = A_full @ B. Persistent kernel
+    whose tiles wait for their band of A_full to land; n_comm_wg: None (default)
+    or the count of workgroups that prefer landing bands."""
+    nc = MK_ADAPTIVE if n_comm_wg is None else int(n_comm_wg)
+    _check(_lib.mk_gemm_ag_local(*_ag_args(A_local, peers_A, A_full, B, C, rank),
+                                 _stream_ptr(stream), nc))
+    return A_full, C
+
+
+def gemm_ag_baseline(A_local, peers_A, A_full, B, C, rank, stream=None):
+    """Same result as gemm_ag_local, by a gather kernel followed by a GEMM kernel."""
+    _check(_lib.mk_gemm_ag_baseline(*_ag_args(A_local, peers_A, A_full, B, C, rank),
+                                    _stream_ptr(stream)))
+    return A_full, C
+
+
+def ag_grid(A_local, peers_A, A_full, B, C):
+    """G of gemm_ag_local for these tensors (n_comm_wg must be < G)."""
+    a = _ag_args(A_local, peers_A, A_full, B, C, 0)
+    g = _lib.mk_ag_grid(a[6], a[2], a[7], a[8], a[10])
+    if g < 0:
+        _check(-g)
+    return g
 
 
 def stream_status(stream=None):

@@ -60,6 +60,7 @@ struct DeviceInfo {
   bool ok = false;
   int cus = 0;
   int occ[3][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU)
+  int ag_occ[3][2] = {};  // AllGather+GEMM kernel occupancy per [shape][ct]
 };
 std::mutex g_dev_mu;
 std::map<int, DeviceInfo> g_dev;
@@ -89,6 +90,15 @@ mk_status_t device_info(int dev, DeviceInfo& out) {
           return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         d.occ[s][pt][ct] = n;
       }
+  for (int s = 1; s <= 2; ++s)
+    for (int ct = 0; ct < 2; ++ct) {
+      int n = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mk::ag_kernel_ptr(s, ct),
+                                                       mk::kThreadsHost, 0);
+      if (e != hipSuccess || n < 1)
+        return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+      d.ag_occ[s][ct] = n;
+    }
   d.ok = true;
   g_dev[dev] = d;
   out = d;
@@ -103,6 +113,8 @@ struct Workspace {
   size_t P_elems = 0;
   int* flags = nullptr;
   int flags_cap = 0;
+  int* ag_landed = nullptr;  // AllGather+GEMM piece flags (zero between calls)
+  int ag_cap = 0;
   unsigned long long* slots = nullptr;
   int epoch = 0;
   // two-stream schedule: the reduce stream and its events (created on first use)
@@ -118,6 +130,7 @@ void free_ws(Workspace* w) {
   if (w->s2) (void)hipStreamDestroy(w->s2);
   if (w->P) (void)hipFree(w->P);
   if (w->flags) (void)hipFree(w->flags);
+  if (w->ag_landed) (void)hipFree(w->ag_landed);
   if (w->slots) (void)hipFree(w->slots);
   delete w;
 }
@@ -351,6 +364,79 @@ mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype
   L.tiles_n = (N + mk::shape_bn(L.shape) - 1) / mk::shape_bn(L.shape);
   if (L.tiles_m * L.tiles_n > (1 << 30)) return fail(MK_ERR_UNSUPPORTED, "too many tiles");
   return MK_OK;
+}
+
+
+// ------------------------------------------------------------ AllGather+GEMM share
+
+// A_local [Ms,K], peers_A [n_peers,Ms,K], A_full [P*Ms,K], B [K,N], C [P*Ms,N].
+mk_status_t validate_ag(const void* A_local, const void* peers_A, int n_peers, void* A_full,
+                        const void* B, void* C, int64_t Ms, int64_t N, int64_t K, int rank,
+                        int c_dtype) {
+  if (Ms < 0 || N < 0 || K < 0)
+    return fail(MK_ERR_INVALID_ARG, "negative size Ms=%lld N=%lld K=%lld", (long long)Ms,
+                (long long)N, (long long)K);
+  if (n_peers < 0 || n_peers > MK_MAX_PEERS)
+    return fail(MK_ERR_INVALID_ARG, "n_peers=%d outside [0, %d]", n_peers, MK_MAX_PEERS);
+  if (rank < 0 || rank > n_peers)
+    return fail(MK_ERR_INVALID_ARG, "rank=%d outside [0, %d]", rank, n_peers);
+  if (c_dtype != MK_DT_BF16 && c_dtype != MK_DT_F32)
+    return fail(MK_ERR_INVALID_ARG, "c_dtype=%d", c_dtype);
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(MK_ERR_UNSUPPORTED, "N=%lld and K=%lld must be multiples of 8", (long long)N,
+                (long long)K);
+  if (Ms % 128 != 0)
+    return fail(MK_ERR_UNSUPPORTED, "Ms=%lld must be a multiple of 128", (long long)Ms);
+  if (N > ((int64_t)1 << 22))
+    return fail(MK_ERR_UNSUPPORTED, "N=%lld exceeds 4194304", (long long)N);
+  const int64_t M = (int64_t)(n_peers + 1) * Ms;
+  const int64_t lim = (int64_t)1 << 40;
+  if (M > lim || K > lim || (M > 0 && N > lim / M) || (M > 0 && K > lim / M) ||
+      (N > 0 && K > lim / N))
+    return fail(MK_ERR_UNSUPPORTED, "sizes too large");
+  const size_t l_bytes = (size_t)(Ms * K) * 2, p_bytes = (size_t)n_peers * l_bytes;
+  const size_t f_bytes = (size_t)(M * K) * 2, b_bytes = (size_t)(K * N) * 2;
+  const size_t c_bytes = (size_t)(M * N) * dt_size(c_dtype);
+  if (l_bytes && !A_local) return fail(MK_ERR_INVALID_ARG, "A_local is NULL");
+  if (p_bytes && !peers_A) return fail(MK_ERR_INVALID_ARG, "peers_A is NULL with n_peers=%d", n_peers);
+  if (f_bytes && !A_full) return fail(MK_ERR_INVALID_ARG, "A_full is NULL");
+  if (b_bytes && !B) return fail(MK_ERR_INVALID_ARG, "B is NULL");
+  if (c_bytes && !C) return fail(MK_ERR_INVALID_ARG, "C is NULL");
+  const void* ptrs[] = {A_local, peers_A, A_full, B, C};
+  const char* names[] = {"A_local", "peers_A", "A_full", "B", "C"};
+  for (int i = 0; i < 5; ++i)
+    if (((uintptr_t)ptrs[i]) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if (overlaps(A_full, f_bytes, A_local, l_bytes) || overlaps(A_full, f_bytes, peers_A, p_bytes) ||
+      overlaps(A_full, f_bytes, B, b_bytes) || overlaps(A_full, f_bytes, C, c_bytes))
+    return fail(MK_ERR_INVALID_ARG, "A_full overlaps another argument");
+  if (overlaps(C, c_bytes, A_local, l_bytes) || overlaps(C, c_bytes, peers_A, p_bytes) ||
+      overlaps(C, c_bytes, B, b_bytes))
+    return fail(MK_ERR_INVALID_ARG, "C overlaps an input");
+  return MK_OK;
+}
+
+// Tile shape of an AllGather+GEMM share: bands never straddle two shards, so
+// 256-row tiles need Ms a multiple of 256; they are taken when at least half of
+// the CUs get a tile (on the 4096x3584x8192 shape, 224 tiles of 256x256 ran in
+// 246-253 us, 896 tiles of 128x128 in 294-342 us).
+int ag_shape(int64_t Ms, int P, int64_t N, int cus) {
+  const int64_t forced = options().tile_shape;
+  const bool ok256 = Ms % 256 == 0;
+  if (forced == mk::SHAPE_128 || (forced == mk::SHAPE_256 && !ok256)) return mk::SHAPE_128;
+  if (forced == mk::SHAPE_256) return mk::SHAPE_256;
+  const int64_t t256 = (int64_t)P * (Ms / 256) * ((N + 255) / 256);
+  return ok256 && 2 * t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
+}
+
+// Persistent grid of the AllGather+GEMM kernel: one workgroup per tile plus
+// four landing workgroups per XCD, at most every resident slot, a multiple of
+// the XCD count.
+int ag_grid_size(const DeviceInfo& info, int shape, int c_dtype, int64_t T) {
+  const int full = info.cus * info.ag_occ[shape][c_dtype];
+  int n_xcd = info.cus / 32;
+  n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
+  const int64_t want = (T + 4 * n_xcd + n_xcd - 1) / n_xcd * n_xcd;
+  return want < full ? (int)want : full / n_xcd * n_xcd;
 }
 
 }  // namespace
@@ -773,6 +859,158 @@ mk_status_t mk_gemm_rs_baseline(const void* A, const void* B, const void* peers,
     if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   }
   return MK_OK;
+}
+
+mk_status_t mk_gemm_ag_local(const void* A_local, const void* peers_A, int n_peers, void* A_full,
+                             const void* B, void* C, int64_t Ms, int64_t N, int64_t K, int rank,
+                             int c_dtype, void* stream, int n_comm_wg) {
+  mk_status_t st = validate_ag(A_local, peers_A, n_peers, A_full, B, C, Ms, N, K, rank, c_dtype);
+  if (st != MK_OK) return st;
+  if (n_comm_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_comm_wg=%d", n_comm_wg);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  DeviceInfo info;
+  st = device_info(dev, info);
+  if (st != MK_OK) return st;
+  const int P = n_peers + 1;
+  const int shape = ag_shape(Ms, P, N, info.cus);
+  const int BM = mk::shape_bm(shape), BN = mk::shape_bn(shape);
+  const int64_t M = (int64_t)P * Ms;
+  const int64_t NB = M / BM, tiles_n = (N + BN - 1) / BN;
+  if (NB * tiles_n > (1 << 30) || NB * mk::kAgMaxPieces > (1 << 30))
+    return fail(MK_ERR_UNSUPPORTED, "too many tiles");
+  const int G = ag_grid_size(info, shape, c_dtype, NB * tiles_n);
+  if (n_comm_wg > G - 1)
+    return fail(MK_ERR_INVALID_ARG, "n_comm_wg=%d outside [0, %d]", n_comm_wg, G - 1);
+  if (M == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const Options opt = options();
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  st = get_ws(dev, s, 0, 0, &w);
+  if (st != MK_OK) return st;
+  const int64_t n_flags = NB * mk::kAgMaxPieces;
+  if (n_flags > w->ag_cap) {
+    e = hipStreamSynchronize(s);  // earlier calls on this stream may still use the old flags
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (w->ag_landed) (void)hipFree(w->ag_landed);
+    w->ag_landed = nullptr;
+    w->ag_cap = 0;
+    const int cap = n_flags < 4096 ? 4096 : (int)n_flags;
+    e = hipMalloc(&w->ag_landed, sizeof(int) * (size_t)cap);
+    if (e != hipSuccess) return fail(MK_ERR_WORKSPACE, "piece flags: %s", hipGetErrorString(e));
+    e = mk::launch_ws_init(w->ag_landed, cap, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "piece flag init");
+    w->ag_cap = cap;
+  }
+  int n_xcd = info.cus / 32;
+  n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
+  // Pieces: at most kAgMaxPieces per band, each a whole number of 32-column
+  // k-tiles, so that a k-tile never waits for two pieces. A tile may read a piece
+  // while the next ones are still landing only if no 128-byte line holds bytes
+  // of two pieces: A_full 128-byte aligned, rows and piece widths multiples of
+  // 64 columns. Otherwise a tile waits for every piece of its band.
+  const int64_t kt_total = (K + 31) / 32;
+  int64_t ktpp = (kt_total + 7) / 8;  // about eight pieces per band
+  const bool lines_ok = ((uintptr_t)A_full) % 128 == 0 && K % 64 == 0;
+  if (lines_ok && ktpp % 2 == 1) ktpp += 1;
+  mk::AgArgs a;
+  memset(&a, 0, sizeof a);
+  a.A_local = (const uint16_t*)A_local;
+  a.peers = (const uint16_t*)peers_A;
+  a.A_full = (uint16_t*)A_full;
+  a.B = (const uint16_t*)B;
+  a.C = C;
+  a.landed = w->ag_landed;
+  a.slots = w->slots;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.Ms = Ms;
+  a.KP = ktpp * 32;
+  a.P = P;
+  a.rank = rank;
+  a.bps = (int)(Ms / BM);
+  a.NB = (int)NB;
+  a.ktpp = ktpp > 0 ? (int)ktpp : 1;
+  a.npc = K > 0 ? (int)((K + a.KP - 1) / a.KP) : 0;
+  a.inloop = lines_ok ? 1 : 0;
+  a.tiles_n = (int)tiles_n;
+  a.T = (int)(NB * tiles_n);
+  a.G = G;
+  a.n_xcd = G % n_xcd == 0 ? n_xcd : 1;
+  // Default: four landing workgroups per XCD (the grid's workgroups beyond the
+  // tiles when it has room); the others land pieces only while the first piece
+  // of their tile's band is missing.
+  a.n_comm = n_comm_wg >= 0 ? n_comm_wg : (4 * a.n_xcd < G ? 4 * a.n_xcd : G - 1);
+  a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
+  e = mk::launch_ag(shape, c_dtype, a, s);
+  if (e != hipSuccess) return hip_fail(e, "AllGather+GEMM kernel launch");
+  return MK_OK;
+}
+
+mk_status_t mk_gemm_ag_baseline(const void* A_local, const void* peers_A, int n_peers,
+                                void* A_full, const void* B, void* C, int64_t Ms, int64_t N,
+                                int64_t K, int rank, int c_dtype, void* stream) {
+  mk_status_t st = validate_ag(A_local, peers_A, n_peers, A_full, B, C, Ms, N, K, rank, c_dtype);
+  if (st != MK_OK) return st;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  DeviceInfo info;
+  st = device_info(dev, info);
+  if (st != MK_OK) return st;
+  const int P = n_peers + 1;
+  const int64_t M = (int64_t)P * Ms;
+  if (M == 0) return MK_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (K > 0) {
+    mk::AgCopyArgs c;
+    c.A_local = (const uint16_t*)A_local;
+    c.peers = (const uint16_t*)peers_A;
+    c.A_full = (uint16_t*)A_full;
+    c.Ms = Ms;
+    c.K = K;
+    c.P = P;
+    c.rank = rank;
+    e = mk::launch_ag_copy(c, reduce_grid(M * K, info.cus), s);
+    if (e != hipSuccess) return hip_fail(e, "gather kernel launch");
+  }
+  if (N == 0) return MK_OK;
+  const int shape = ag_shape(Ms, P, N, info.cus);
+  mk::GemmArgs g;
+  g.A = (const uint16_t*)A_full;
+  g.B = (const uint16_t*)B;
+  g.P = nullptr;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tiles_m = (int)(M / mk::shape_bm(shape));
+  g.tiles_n = (int)((N + mk::shape_bn(shape) - 1) / mk::shape_bn(shape));
+  const int n_xcd = info.cus / 32;
+  g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
+  g.pad_ = 0;
+  e = mk::launch_gemm_c(shape, c_dtype, g, C, s);
+  if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
+  return MK_OK;
+}
+
+int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype) {
+  (void)K;
+  if (c_dtype != MK_DT_BF16 && c_dtype != MK_DT_F32) return -(int)MK_ERR_INVALID_ARG;
+  if (Ms < 0 || N < 0 || n_peers < 0 || n_peers > MK_MAX_PEERS || Ms % 128 != 0)
+    return -(int)MK_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -(int)MK_ERR_NO_DEVICE;
+  DeviceInfo info;
+  mk_status_t st = device_info(dev, info);
+  if (st != MK_OK) return -(int)st;
+  const int P = n_peers + 1;
+  const int shape = ag_shape(Ms, P, N, info.cus);
+  const int64_t NB = (int64_t)P * Ms / mk::shape_bm(shape);
+  const int64_t tiles_n = (N + mk::shape_bn(shape) - 1) / mk::shape_bn(shape);
+  return ag_grid_size(info, shape, c_dtype, NB * tiles_n);
 }
 
 mk_status_t mk_stream_status(void* stream) {

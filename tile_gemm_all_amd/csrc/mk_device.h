@@ -125,6 +125,11 @@ __device__ __forceinline__ void dma16(const void* g, const char* lds) {
 //   B tile [32][BN]: chunk c of row k stored at c ^ (4 * (k & 3)); the gfx950
 //     transposing read (ds_read_b64_tr_b16) has 16 lanes read a 4(k) x 16(n) block,
 //     so 32 lanes touch 4 rows x 4 chunks = all 64 banks once.
+// Default gate of GemmTile::run: every k-tile's inputs are already in memory.
+struct NoGate {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 template <int BM_, int BN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 32, NS = 4;
@@ -378,9 +383,13 @@ struct GemmTile {
 
   // Full K loop of one tile. Stage kt lives in LDS slot kt % NS; loads for
   // stages kt+1 .. kt+NS-1 are in flight while stage kt is computed.
+  // gate(kt) runs in every lane before the loads of k-tile kt are issued (a
+  // consumer that waits for its inputs to arrive); NoGate does nothing.
+  template <class Gate = NoGate>
   __device__ __forceinline__ void run(const uint16_t* __restrict__ A,
                                       const uint16_t* __restrict__ B, int64_t M, int64_t N,
-                                      int64_t K, int64_t m0, int64_t n0, char* lds) {
+                                      int64_t K, int64_t m0, int64_t n0, char* lds,
+                                      Gate gate = Gate()) {
     static_assert(Cfg::NS == 4, "wait_loads assumes up to two later stages in flight");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
@@ -400,11 +409,15 @@ struct GemmTile {
     // and is loaded through registers when its turn comes.
 #pragma unroll
     for (int j = 0; j < Cfg::NS - 1; ++j)
-      if (j < KF) load_direct(s, A, B, N, (int64_t)j * Cfg::BK, lds + j * Cfg::STAGE, wave);
+      if (j < KF) {
+        gate(j);
+        load_direct(s, A, B, N, (int64_t)j * Cfg::BK, lds + j * Cfg::STAGE, wave);
+      }
     for (int kt = 0; kt < KT; ++kt) {
       char* cur = lds + (kt % Cfg::NS) * Cfg::STAGE;
       if (kt == KF) {
         // partial tile: loaded now (the slot was freed by the previous barrier)
+        gate(kt);
         load_guarded(s, A, B, N, K, (int64_t)kt * Cfg::BK, cur, wave, lane);
       } else {
         // direct loads of the full stages after kt that are already issued
@@ -414,7 +427,10 @@ struct GemmTile {
       }
       __syncthreads();  // stage kt complete in LDS; slot (kt-1) % NS is free
       const int kn = kt + Cfg::NS - 1;
-      if (kn < KF) load_direct(s, A, B, N, (int64_t)kn * Cfg::BK, lds + (kn % Cfg::NS) * Cfg::STAGE, wave);
+      if (kn < KF) {
+        gate(kn);
+        load_direct(s, A, B, N, (int64_t)kn * Cfg::BK, lds + (kn % Cfg::NS) * Cfg::STAGE, wave);
+      }
       compute_stage(cur, f);
     }
     __syncthreads();  // every wave is done with LDS before it is reused

@@ -128,7 +128,48 @@ struct ReduceArgs {
   int pad_;
 };
 
+// AllGather+GEMM share: this GPU's row shard of the activations, the other
+// GPUs' shards (standing in for data they broadcast), the gathered matrix and
+// C = gathered x B. The gathered matrix is landed in bands of BM rows, each cut
+// into at most kAgMaxPieces column pieces of KP columns (a multiple of the GEMM's
+// k-tile); one flag per (band, piece) says the piece has landed.
+constexpr int kAgMaxPieces = 32;
+struct AgArgs {
+  const uint16_t* A_local;     // [Ms, K], rank `rank`'s shard
+  const uint16_t* peers;       // [P-1, Ms, K], the other shards in rank order (rank left out)
+  uint16_t* A_full;            // [P*Ms, K], shard q at rows [q*Ms, (q+1)*Ms)
+  const uint16_t* B;           // [K, N]
+  void* C;                     // [P*Ms, N]
+  int* landed;                 // [NB][kAgMaxPieces]: 1 once the piece has landed (zero between calls)
+  unsigned long long* slots;   // S_COUNT * kSlotWords words
+  int64_t M, N, K, Ms;         // M = P*Ms
+  int64_t KP;                  // columns per piece
+  int P, rank;
+  int bps;                     // bands per shard (Ms / BM)
+  int NB;                      // bands (M / BM)
+  int npc;                     // pieces per band (ceil(K / KP))
+  int ktpp;                    // k-tiles per piece (KP / BK)
+  int inloop;                  // 1: a tile waits for each piece in its k-loop; 0: for every
+                               // piece of its band before the GEMM (pieces share cache lines)
+  int tiles_n, T;
+  int G, n_xcd;
+  int n_comm;                  // workgroups that only land pieces while any are left
+  int pad_;
+  unsigned long long spin_limit;  // piece-wait limit in 100 MHz ticks
+};
+
+// Baseline of the AllGather+GEMM share: the gathered matrix by a copy kernel,
+// then this GEMM kernel (one workgroup per tile) writing C in its type.
+struct AgCopyArgs {
+  const uint16_t* A_local;
+  const uint16_t* peers;
+  uint16_t* A_full;
+  int64_t Ms, K;
+  int P, rank;
+};
+
 const void* fused_kernel_ptr(int shape, int pt, int ct);
+const void* ag_kernel_ptr(int shape, int ct);
 const void* gemm_kernel_ptr(int shape);
 const void* reduce_kernel_ptr(int pt, int ct);
 int shape_bm(int shape);
@@ -139,5 +180,8 @@ hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s);
 hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s);
 hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStream_t s);
+hipError_t launch_ag(int shape, int ct, const AgArgs& a, hipStream_t s);
+hipError_t launch_ag_copy(const AgCopyArgs& a, int grid, hipStream_t s);
+hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStream_t s);
 
 }  // namespace mk

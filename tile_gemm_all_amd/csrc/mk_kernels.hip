@@ -463,6 +463,330 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   }
 }
 
+// ------------------------------------------------------------ AllGather+GEMM share
+
+// "AllGather + GEMM (TP)" row of Table 3 (thelatestinai.com page): communication
+// feeds compute. Every GPU's row shard of the activations is broadcast to every
+// GPU, and the GEMM consumes gathered data in chunks as it arrives. One GPU's
+// share: the other GPUs' shards are inputs already in HBM, and landing them in
+// the gathered matrix stands in for their arrival. A band (BM rows) lands in
+// column pieces (KP columns each) with one flag per piece; a tile's k-loop waits
+// for each piece's flag just before it loads that piece's k-tiles, so a GEMM
+// starts as soon as the first piece of its band has landed. This GPU's own bands
+// are read from its shard and start at once.
+
+// Arrival position j -> band of the gathered matrix: this GPU's own bands first,
+// then the shards of ranks rank+1, rank+2, ... (mod P), each in row order.
+__device__ __forceinline__ int ag_band(int j, int bps, int P, int rank) {
+  const int s = (rank + j / bps) % P;
+  return s * bps + j % bps;
+}
+
+// Lands piece kp of band gb: BM rows by the piece's columns, 16 bytes per lane,
+// eight loads per lane in flight before their stores.
+template <int BM>
+__device__ __forceinline__ void ag_land(const AgArgs& a, int gb, int kp) {
+  const int s = gb / a.bps;
+  const int64_t r0 = (int64_t)(gb % a.bps) * BM;  // first row within the shard
+  const int64_t c0 = (int64_t)kp * a.KP;
+  const int64_t w = a.K - c0 < a.KP ? a.K - c0 : a.KP;  // columns (a multiple of 8)
+  const uint16_t* src = s == a.rank
+                            ? a.A_local + r0 * a.K + c0
+                            : a.peers + ((int64_t)(s < a.rank ? s : s - 1) * a.Ms + r0) * a.K + c0;
+  uint16_t* dst = a.A_full + ((int64_t)s * a.Ms + r0) * a.K + c0;
+  const int cpr = (int)(w / 8);  // 16-byte chunks per row
+  const int n16 = BM * cpr;
+  constexpr int U = 8;
+  int i = threadIdx.x;
+  for (; i + (U - 1) * kThreads < n16; i += U * kThreads) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = i + u * kThreads, r = q / cpr, c = q - r * cpr;
+      v[u] = *(const u32x4*)(src + (int64_t)r * a.K + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = i + u * kThreads, r = q / cpr, c = q - r * cpr;
+      *(u32x4*)(dst + (int64_t)r * a.K + c * 8) = v[u];
+    }
+  }
+  for (; i < n16; i += kThreads) {
+    const int r = i / cpr, c = i - r * cpr;
+    *(u32x4*)(dst + (int64_t)r * a.K + c * 8) = *(const u32x4*)(src + (int64_t)r * a.K + c * 8);
+  }
+}
+
+// GemmTile gate of a band that is still landing: before the loads of k-tile kt,
+// every wave waits for the flag of kt's piece (once per piece). A piece is read
+// only after its flag, so no cache holds a stale copy of it, provided that no
+// 128-byte line holds bytes of two pieces (rows and piece widths are whole
+// lines; the host checks it and otherwise sets all = 1: the first call waits
+// for every piece of the band). A wait past the spin limit raises the error
+// word; once the kernel is stopping no wait blocks (the tile is discarded).
+struct AgGate {
+  const int* flags;   // this band's piece flags
+  unsigned long long* S;
+  unsigned long long limit;
+  int ktpp;           // k-tiles per piece
+  int npc;            // pieces of the band
+  int all;            // 1: wait for every piece at the first k-tile
+  int ready;          // pieces [0, ready] have landed
+  // The flag is read by a scalar load that misses the scalar cache (its count
+  // is lgkmcnt), so the k-loop's direct loads in flight need not drain first, as
+  // they would behind a vector load of the flag.
+  __device__ __forceinline__ static int poll(const int* p) {
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+  }
+  __device__ __forceinline__ void operator()(int kt) {
+    const int kp = all ? npc - 1 : kt / ktpp;
+    for (int p = ready + 1; p <= kp; ++p) {
+      const unsigned long long w0 = ticks();
+      while (poll(flags + p) == 0) {
+        if (load_relaxed(slot32(S, S_ABORT))) break;
+        if (ticks() - w0 > limit) {
+          raise_error(S, MK_ERR_TIMEOUT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (kp > ready) ready = kp;
+  }
+};
+
+// The fp32 tile in the accumulators, rounded to CT, into C at (m0, n0): through
+// LDS (free after the GEMM's last barrier) in row-band passes, then 16-byte
+// stores of whole rows.
+template <class Cfg, typename CT>
+__device__ __forceinline__ void store_tile_c(const GemmTile<Cfg>& g, char* lds, CT* C, int64_t M,
+                                             int64_t N, int64_t m0, int64_t n0) {
+  const int cols = (int)(N - n0 < Cfg::BN ? N - n0 : Cfg::BN);
+  auto pass = [&](auto pass_c) {
+    constexpr int PASS = decltype(pass_c)::value;
+    constexpr int BAND = GemmTile<Cfg>::BAND;
+    g.template stage_pass_lds<PASS>(lds);
+    __syncthreads();
+#pragma unroll
+    for (int wm = 0; wm < 2; ++wm) {
+      const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
+      const int rows = (int)(M - r0 < BAND ? M - r0 : BAND);  // <= 0 past the edge
+      copy_region_lds<CT>(lds + wm * BAND * Cfg::BN * 4, Cfg::BN, C, N, r0, n0, rows, cols);
+    }
+    __syncthreads();
+  };
+  pass(std::integral_constant<int, 0>{});
+  if constexpr (GemmTile<Cfg>::NPASS > 1) pass(std::integral_constant<int, 1>{});
+}
+
+enum { AG_EXIT = 0, AG_COMPUTE = 1, AG_LAND = 2 };
+
+// Persistent AllGather+GEMM kernel. Band j of the arrival order belongs to XCD
+// j % n_xcd: the workgroups of that XCD land it and compute its tiles, so the
+// landed pieces are written and read behind one L2 (the flag protocol of the
+// tile flags). Each XCD has a tile queue (its bands in arrival order, every
+// tile column of a band before the next band) and a landing queue (piece 0 of
+// each of its other-GPU bands, then piece 1 of each, ..., then its own bands'
+// pieces, which the gathered matrix holds too). The first workgroups to arrive
+// on an XCD (its share of n_comm) only land pieces while any are left, and
+// never wait. A workgroup holding a tile of a landing band first lands pieces
+// while the band's first piece has not landed and pieces are unclaimed (and,
+// on an XCD without landing workgroups, until every piece of the band is
+// claimed); then it runs the GEMM, whose gate waits for each later piece. Every
+// piece it can wait for is claimed by a workgroup that lands it without
+// waiting, so no wait can stall the kernel.
+template <class Cfg, typename CT>
+__global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
+  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
+  __shared__ int s_kind, s_idx, s_last;
+  const int tid = threadIdx.x;
+  unsigned long long* S = a.slots;
+  const int x = xcc_id() % a.n_xcd;
+  // This XCD's bands: arrival positions x + i*n_xcd for i < nb; the first nl are
+  // this GPU's own, the other nbp are landing.
+  const int nb = a.NB > x ? (a.NB - x + a.n_xcd - 1) / a.n_xcd : 0;
+  const int nl = a.bps > x ? (a.bps - x + a.n_xcd - 1) / a.n_xcd : 0;
+  const int nbp = nb - nl;
+  const int cnt = nb * a.tiles_n;
+  const int units = nb * a.npc;
+  const int tx = a.n_comm / a.n_xcd + (x < a.n_comm % a.n_xcd ? 1 : 0);
+  int* cnext = xslot(S, x, X_COMPUTE_NEXT);
+  int* lnext = xslot(S, x, X_REDUCE_NEXT);
+  int rank = -1, held = -1;  // thread 0: arrival rank; a claimed tile of a landing band
+  unsigned long long w0 = 0;
+
+  for (;;) {
+    if (tid == 0) {
+      int kind = AG_EXIT, idx = -1;
+      for (;;) {
+        const int abort = load_relaxed(slot32(S, S_ABORT));
+        const int cn = load_relaxed(cnext);
+        const int ln = load_relaxed(lnext);
+        if (rank < 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+        if (abort) break;
+        if (rank < tx && ln < units) {  // a landing workgroup while pieces are left
+          const int u = atomicAdd(lnext, 1);
+          if (u < units) {
+            kind = AG_LAND;
+            idx = u;
+            break;
+          }
+          continue;
+        }
+        if (held >= 0) {
+          const int i = held / a.tiles_n - nl;  // position among the landing bands
+          const int gb = ag_band(x + (held / a.tiles_n) * a.n_xcd, a.bps, a.P, a.rank);
+          const bool first = a.npc == 0 || load_relaxed(a.landed + gb * kAgMaxPieces) != 0;
+          // unit of the band's last piece: all pieces claimed once the queue is past it
+          const bool claimed = ln > (a.npc - 1) * nbp + i;
+          if ((!first || (tx == 0 && !claimed)) && ln < units) {
+            const int u = atomicAdd(lnext, 1);  // land a piece rather than wait
+            if (u < units) {
+              kind = AG_LAND;
+              idx = u;
+              w0 = 0;
+              break;
+            }
+          }
+          if (first) {
+            kind = AG_COMPUTE;
+            idx = held;
+            held = -1;
+            break;
+          }
+          if (w0 == 0) w0 = ticks();  // the first piece is claimed: wait for it
+          if (ticks() - w0 > a.spin_limit) {
+            raise_error(S, MK_ERR_TIMEOUT);
+            break;
+          }
+          backoff_sleep(1);
+          continue;
+        }
+        if (cn < cnt) {
+          const int t = atomicAdd(cnext, 1);
+          if (t < cnt) {
+            if (t / a.tiles_n < nl) {  // a band of this GPU's own shard
+              kind = AG_COMPUTE;
+              idx = t;
+              break;
+            }
+            held = t;
+            w0 = 0;
+            continue;
+          }
+        }
+        if (ln < units) {
+          const int u = atomicAdd(lnext, 1);
+          if (u < units) {
+            kind = AG_LAND;
+            idx = u;
+          }
+        }
+        break;
+      }
+      s_kind = kind;
+      s_idx = idx;
+    }
+    __syncthreads();
+    const int kind = s_kind, idx = s_idx;
+    if (kind == AG_EXIT) break;
+    if (kind == AG_LAND) {
+      int i, kp;
+      if (idx < nbp * a.npc) {  // other GPUs' bands, piece-major
+        kp = idx / nbp;
+        i = nl + idx % nbp;
+      } else {                  // this GPU's own bands
+        const int v = idx - nbp * a.npc;
+        kp = v / nl;
+        i = v % nl;
+      }
+      const int gb = ag_band(x + i * a.n_xcd, a.bps, a.P, a.rank);
+      ag_land<Cfg::BM>(a, gb, kp);
+      wait_stores();    // this wave's stores have reached the L2
+      __syncthreads();  // ... and every other wave's
+      if (tid == 0) {
+        store_flag(a.landed + gb * kAgMaxPieces + kp, 1);
+        atomicAdd(xslot(S, x, X_REDUCED), 1);
+      }
+    } else {
+      const int pos = idx / a.tiles_n, tn = idx % a.tiles_n;
+      const int gb = ag_band(x + pos * a.n_xcd, a.bps, a.P, a.rank);
+      const int sh = gb / a.bps;
+      const int64_t rs = (int64_t)(gb % a.bps) * Cfg::BM;  // first row within the shard
+      const int64_t m0 = (int64_t)sh * a.Ms + rs, n0 = (int64_t)tn * Cfg::BN;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load of the last task in flight
+      GemmTile<Cfg> g;
+      if (sh == a.rank) {
+        g.run(a.A_local, a.B, a.Ms, a.N, a.K, rs, n0, lds);
+      } else {
+        AgGate gate{a.landed + gb * kAgMaxPieces, S, a.spin_limit, a.ktpp, a.npc, !a.inloop, -1};
+        g.run(a.A_full, a.B, a.M, a.N, a.K, m0, n0, lds, gate);
+      }
+      store_tile_c<Cfg, CT>(g, lds, (CT*)a.C, a.M, a.N, m0, n0);
+      if (tid == 0) atomicAdd(xslot(S, x, X_COMPUTED), 1);
+    }
+    __syncthreads();  // s_kind/s_idx and LDS are reused by the next task
+  }
+
+  // ---- exit: the last workgroup out checks the work and resets the counters
+  if (tid == 0) {
+    wait_stores();
+    int out = __hip_atomic_fetch_add(slot32(S, S_EXIT), 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    s_last = out == a.G - 1;
+    if (s_last) {
+      acquire_fence_agent();
+      if (!load_relaxed(slot32(S, S_ABORT)) &&
+          (sum_xcd32(S, a.n_xcd, X_COMPUTED) != a.T ||
+           sum_xcd32(S, a.n_xcd, X_REDUCED) != a.NB * a.npc))
+        atomicCAS(slot32(S, S_ERROR), 0, MK_ERR_INTERNAL);
+    }
+  }
+  __syncthreads();
+  if (s_last) {
+    for (int i = tid; i < S_COUNT; i += kThreads) {
+      if (i == S_ERROR || i == S_TARGET) continue;
+      __hip_atomic_store(slot64(S, i), i == S_TSTART ? ~0ull : 0ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int i = tid; i < a.NB * kAgMaxPieces; i += kThreads)
+      __hip_atomic_store(a.landed + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Baseline AllGather: every shard into the gathered matrix, 16 bytes per lane.
+__global__ __launch_bounds__(kThreads) void ag_copy_kernel(AgCopyArgs a) {
+  const int64_t per = a.Ms * a.K / 8;  // 16-byte chunks per shard
+  const int64_t total = per * a.P;
+  const int64_t step = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += step) {
+    const int s = (int)(i / per);
+    const int64_t o = i - (int64_t)s * per;
+    const uint16_t* src =
+        s == a.rank ? a.A_local : a.peers + (int64_t)(s < a.rank ? s : s - 1) * a.Ms * a.K;
+    ((u32x4*)a.A_full)[i] = ((const u32x4*)src)[o];
+  }
+}
+
+// Baseline GEMM writing C in its own type (one workgroup per tile, the tile map
+// of gemm_kernel).
+template <class Cfg, typename CT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_c_kernel(GemmArgs a, CT* C) {
+  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
+  const int T = a.tiles_m * a.tiles_n;
+  const int b = blockIdx.x;
+  int t = b;
+  if (a.n_xcd > 1 && T % a.n_xcd == 0) t = (b % a.n_xcd) * (T / a.n_xcd) + b / a.n_xcd;
+  int tm, tn;
+  fused_tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
+  GemmTile<Cfg> g;
+  g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+  store_tile_c<Cfg, CT>(g, lds, C, a.M, a.N, m0, n0);
+}
+
 // ------------------------------------------------------------ baseline kernels
 
 template <class Cfg>
@@ -535,6 +859,12 @@ const void* fused_kernel_ptr(int shape, int pt, int ct) {
   return shape == SHAPE_256 ? fused_ptr<T256>(pt, ct) : fused_ptr<T128>(pt, ct);
 }
 
+const void* ag_kernel_ptr(int shape, int ct) {
+  if (shape == SHAPE_256)
+    return ct == MK_DT_BF16 ? (const void*)ag_kernel<T256, uint16_t> : (const void*)ag_kernel<T256, float>;
+  return ct == MK_DT_BF16 ? (const void*)ag_kernel<T128, uint16_t> : (const void*)ag_kernel<T128, float>;
+}
+
 const void* gemm_kernel_ptr(int shape) {
   return shape == SHAPE_256 ? (const void*)gemm_kernel<T256> : (const void*)gemm_kernel<T128>;
 }
@@ -575,6 +905,33 @@ hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStrea
   const void* f = reduce_kernel_ptr(pt, ct);
   void* args[] = {(void*)&a};
   return hipLaunchKernel(f, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_ag(int shape, int ct, const AgArgs& a, hipStream_t s) {
+  const void* f = ag_kernel_ptr(shape, ct);
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel(f, dim3(a.G), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_ag_copy(const AgCopyArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(ag_copy_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStream_t s) {
+  const int T = a.tiles_m * a.tiles_n;
+  if (shape == SHAPE_256) {
+    if (ct == MK_DT_BF16)
+      hipLaunchKernelGGL((gemm_c_kernel<T256, uint16_t>), dim3(T), dim3(kThreads), 0, s, a, (uint16_t*)C);
+    else
+      hipLaunchKernelGGL((gemm_c_kernel<T256, float>), dim3(T), dim3(kThreads), 0, s, a, (float*)C);
+  } else {
+    if (ct == MK_DT_BF16)
+      hipLaunchKernelGGL((gemm_c_kernel<T128, uint16_t>), dim3(T), dim3(kThreads), 0, s, a, (uint16_t*)C);
+    else
+      hipLaunchKernelGGL((gemm_c_kernel<T128, float>), dim3(T), dim3(kThreads), 0, s, a, (float*)C);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace mk
