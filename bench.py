@@ -136,6 +136,22 @@ def main():
     def rs_baseline():
         mk.gemm_rs_baseline(A, B, rs_peers, rs_C, rs_send, o0, o1)
 
+    # AllGather+GEMM share (gate+up projection, column-parallel): this GPU (rank 5)
+    # holds 256 of the 4096 gathered rows; the other 15 shards land while the GEMM runs
+    aw = mk_inputs.AG_BY_NAME["ag_up"]
+    ag_shards, ag_B = mk_inputs.make_ag_inputs(aw.Ms, aw.P, aw.N, aw.K, "gaussian",
+                                               1000 * aw.index, device="cuda")
+    ag_local, ag_peers = mk_inputs.shard_split(ag_shards, 5)
+    del ag_shards
+    ag_full = torch.empty((aw.M, aw.K), dtype=torch.bfloat16, device="cuda")
+    ag_C = torch.empty((aw.M, aw.N), dtype=torch.bfloat16, device="cuda")
+
+    def ag_fused():
+        mk.gemm_ag_local(ag_local, ag_peers, ag_full, ag_B, ag_C, 5)
+
+    def ag_baseline():
+        mk.gemm_ag_baseline(ag_local, ag_peers, ag_full, ag_B, ag_C, 5)
+
     def timed(fn, steps, warmup):
         for _ in range(warmup):
             fn()
@@ -155,6 +171,8 @@ def main():
     two_stream_ms = timed(two_stream, args.steps, args.warmup)
     rs_base_ms = timed(rs_baseline, args.steps, args.warmup)
     rs_ms = timed(rs_fused, args.steps, args.warmup)
+    ag_base_ms = timed(ag_baseline, args.steps, args.warmup)
+    ag_ms = timed(ag_fused, args.steps, args.warmup)
     # the role-split path alone: every tile handed to reducers through its flag
     old_inplace = mk.get_option(mk.OPT_INPLACE)
     mk.set_option(mk.OPT_INPLACE, 0)
@@ -197,6 +215,11 @@ def main():
         "reduce_scatter": {"owned_rows": [o0, o1], "fused_ms": round(rs_ms, 5),
                            "baseline_ms": round(rs_base_ms, 5),
                            "speedup": round(rs_base_ms / rs_ms, 4)},
+        "allgather": {"workload": f"{aw.name}: {aw.description}", "Ms": aw.Ms, "P": aw.P,
+                      "N": aw.N, "K": aw.K, "rank": 5, "fused_ms": round(ag_ms, 5),
+                      "baseline_ms": round(ag_base_ms, 5),
+                      "speedup": round(ag_base_ms / ag_ms, 4),
+                      "fused_TFLOPs": round(aw.flops / (ag_ms * 1e-3) / 1e12, 2)},
         "timed_wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
