@@ -278,8 +278,9 @@ typedef enum {
                                    (the last ones of the XCD's queue; the others are handed to
                                    reducers through flags): -1 = automatic (default: none with early
                                    reduce; all of them for shapes at or above 315 flops per
-                                   compulsory byte; otherwise all but the first min(queue/4,
-                                   workgroups per XCD/2)), 0 = none */
+                                   compulsory byte or with queues of more than four rounds;
+                                   otherwise all but the first min(queue/4, workgroups per
+                                   XCD/2)), 0 = none */
   MK_OPT_EARLY = 7              /* early reduce: a reducer may take a unit whose tile is still being
                                    computed and sums that unit's peers (into LDS) while it waits for
                                    the tile's flag. -1 = automatic (default: on when every tile and

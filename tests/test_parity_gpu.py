@@ -487,6 +487,8 @@ AG_CASES = [
     (384, 2, 136, 1040, 1, "f32"),
     (128, 5, 8, 8, 2, "bf16"),         # the smallest N and K
     (256, 4, 2048, 576, 3, "bf16"),
+    (128, 3, 64, 0, 1, "bf16"),        # K = 0: nothing to gather, C = 0
+    (128, 2, 0, 64, 0, "f32"),         # N = 0: the gather alone
 ]
 
 

@@ -249,14 +249,16 @@ def _ag_args(A_local, peers_A, A_full, B, C, rank):
         raise ValueError("C must be a contiguous bfloat16/float32 GPU tensor")
     Ms, K = A_local.shape
     K2, N = B.shape
-    if peers_A is None or peers_A.numel() == 0:
+    if peers_A is None:
         n_peers, pptr = 0, None
     else:
         if peers_A.dtype != torch.bfloat16 or not peers_A.is_cuda or not peers_A.is_contiguous():
             raise ValueError("peers_A must be a contiguous bfloat16 GPU tensor")
         if peers_A.dim() != 3 or tuple(peers_A.shape[1:]) != (Ms, K):
             raise ValueError(f"peers_A must be [P-1, {Ms}, {K}], got {tuple(peers_A.shape)}")
-        n_peers, pptr = peers_A.shape[0], peers_A.data_ptr()
+        # the peer count comes from the shape, also when K = 0 leaves no elements
+        n_peers = peers_A.shape[0]
+        pptr = peers_A.data_ptr() if peers_A.numel() > 0 else None
     M = (n_peers + 1) * Ms
     if K2 != K or tuple(A_full.shape) != (M, K) or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch A_local{tuple(A_local.shape)} A_full"

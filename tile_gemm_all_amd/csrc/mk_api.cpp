@@ -522,10 +522,11 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   //    compulsory byte): every tile. Workgroups drift apart over the rounds, so
   //    one's reduce overlaps another's GEMM, and no partial makes the round trip
   //    through memory.
-  //  - memory-bound shapes: all but the first min(cnt/4, W/2) tiles of each
-  //    queue (W = workgroups per XCD). Those are handed to reducers, so that
-  //    after the first round half of the workgroups start their next GEMM while
-  //    the other half reduce, instead of every workgroup alternating in step.
+  //  - memory-bound shapes whose queues hold at most four rounds: all but the
+  //    first min(cnt/4, W/2) tiles of each queue (W = workgroups per XCD).
+  //    Those are handed to reducers, so that after the first round half of the
+  //    workgroups start their next GEMM while the other half reduce, instead of
+  //    every workgroup alternating in step. Longer queues: every tile.
   a.early = early_reduce(L, n_peers, peer_dtype, c_dtype) ? 1 : 0;
   if (opt.inplace < 0 && a.early) {
     a.n_inplace = 0;  // early reduce applies to tiles handed to reducers
@@ -535,10 +536,13 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
                          (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
     const int cnt0 = a.T / a.n_xcd;  // shortest queue
     int hand = 0;
-    if (bytes > 0 && flops / bytes < 315.0) {
-      const int w = G / a.n_xcd;
+    const int w = G / a.n_xcd;
+    // Only queues of at most four rounds: with more, the workgroups drift apart
+    // on their own (16384x8192x512, eight rounds: 965-973 us all in place,
+    // 982-986 us with handed-over first tiles; 4096x8192x1792, two rounds:
+    // 313-314 us against 316 us).
+    if (bytes > 0 && flops / bytes < 315.0 && cnt0 <= 4 * w)
       hand = cnt0 / 4 < w / 2 ? cnt0 / 4 : w / 2;
-    }
     a.n_inplace = cnt0 - hand;
   } else {
     a.n_inplace = (int)opt.inplace;
