@@ -18,6 +18,12 @@ kept under profiles/.
       copy workload (bytes moved / counter bytes). Writes JSON with the kernel
       source hash that bench.py checks before it reports the figure.
 
+  python bench_rocprof.py counters <rocprof_out_dir> --cmd "<command>" [--last N] [--out FILE]
+      Per-kernel averages of every counter of a --pmc run (all dispatches, and the
+      last N of each kernel), with two derived figures: MFMA busy fraction (MFMA
+      busy cycles over 1024 SIMDs x duration x the 2.4 GHz peak clock) and wait
+      fraction (SQ_WAIT_ANY over SQ_WAVE_CYCLES).
+
 The rocprofv3 output is its SQLite database (rocpd); only its `kernels` view
 and `counters_collection` table are read.
 """
@@ -143,6 +149,51 @@ def cmd_traffic(args):
     sys.stdout.write(text)
 
 
+def cmd_counters(args):
+    per = {}  # kernel -> [(dispatch, {counter: value}, duration ns)]
+    for db in _dbs(args.dir):
+        con = sqlite3.connect(db)
+        durs = dict(con.execute("select dispatch_id, duration from kernels"))
+        vals = {}
+        q = ("select dispatch_id, kernel_name, counter_name, sum(value) from counters_collection "
+             "group by dispatch_id, kernel_name, counter_name order by dispatch_id")
+        for did, name, cname, v in con.execute(q):
+            vals.setdefault((did, name), {})[cname] = float(v)
+        for (did, name), cs in sorted(vals.items()):
+            per.setdefault(name, []).append((did, cs, durs.get(did, 0)))
+        con.close()
+
+    def summary(rows):
+        n = len(rows)
+        dur = sum(r[2] for r in rows) / n
+        cs = {}
+        for _, c, _ in rows:
+            for k, v in c.items():
+                cs[k] = cs.get(k, 0.0) + v / n
+        out = {"dispatches": n, "avg_us": round(dur / 1e3, 1)}
+        out.update({k: round(v) for k, v in sorted(cs.items())})
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in cs and dur > 0:
+            out["mfma_busy_frac_at_2.4GHz"] = round(
+                cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * dur * 1e-9 * 2.4e9), 3)
+        if cs.get("SQ_WAVE_CYCLES"):
+            out["wait_frac"] = round(cs.get("SQ_WAIT_ANY", 0.0) / cs["SQ_WAVE_CYCLES"], 3)
+        return out
+
+    lines = ["# rocprofv3 counter summary", f"command: {args.cmd}", ""]
+    for name, rows in sorted(per.items(), key=lambda kv: -sum(r[2] for r in kv[1])):
+        if "mk::" not in name:
+            continue
+        lines.append(short(name, 100))
+        lines.append(f"  all dispatches: {json.dumps(summary(rows))}")
+        if args.last and len(rows) > args.last:
+            lines.append(f"  last {args.last}: {json.dumps(summary(rows[-args.last:]))}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -153,6 +204,11 @@ def main():
     k.add_argument("dir")
     k.add_argument("--cmd", required=True)
     k.add_argument("--out")
+    cn = sub.add_parser("counters")
+    cn.add_argument("dir")
+    cn.add_argument("--cmd", required=True)
+    cn.add_argument("--last", type=int, default=4)
+    cn.add_argument("--out")
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload",
               "--cmd"):
@@ -163,7 +219,8 @@ def main():
                    help="use only the last N dispatches of the kernel")
     t.add_argument("--out")
     args = ap.parse_args()
-    {"copy": cmd_copy, "kernels": cmd_kernels, "traffic": cmd_traffic}[args.what](args)
+    {"copy": cmd_copy, "kernels": cmd_kernels, "traffic": cmd_traffic,
+     "counters": cmd_counters}[args.what](args)
 
 
 if __name__ == "__main__":
