@@ -16,6 +16,15 @@ cpu_baseline times the CPU oracle on a bounded sample of rows of the same
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
+       python bench.py --all-configs     (one JSON line: every workload, fused /
+                                          baseline / two-stream, median p10 p90)
+       python bench.py --sweep large     (one JSON line: static reducer counts
+                                          0..64 against the adaptive controller)
+
+--all-configs times batches of calls between two HIP events (10 batches of 20
+calls after warmup; median, p10 and p90 of the per-call averages). Workloads
+whose inputs are under 600 MB rotate through enough input sets to exceed 600 MB,
+so that repeated calls do not find their peers in the 256 MB Infinity Cache.
 """
 import argparse
 import hashlib
@@ -87,6 +96,84 @@ def cpu_baseline(w, A, B, peers, budget_s=12.0):
                       f"K={w.K}, {w.n_peers} peers), fp64, {t:.1f} s"}
 
 
+def _batched(fn_of_set, n_sets, stream, batches=10, per_batch=20, warmup=10):
+    """Per-call averages of `batches` batches of `per_batch` calls (call i uses
+    input set i % n_sets), each batch between two events on `stream`."""
+    import torch
+
+    for i in range(warmup):
+        fn_of_set(i % n_sets)
+    torch.cuda.synchronize()
+    out, i = [], 0
+    for _ in range(batches):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(per_batch):
+            fn_of_set(i % n_sets)
+            i += 1
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / per_batch * 1e3)  # us per call
+    out.sort()
+    pick = lambda q: out[min(len(out) - 1, int(q * (len(out) - 1) + 0.5))]
+    return {"median_us": round(pick(0.5), 1), "p10_us": round(pick(0.1), 1),
+            "p90_us": round(pick(0.9), 1)}
+
+
+def all_configs():
+    import torch
+
+    import mk_inputs
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for w in mk_inputs.WORKLOADS:
+        n_sets = max(1, -(-600_000_000 // w.compulsory_bytes()))
+        base = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+        sets = [base] + [tuple(t.clone() for t in base) for _ in range(n_sets - 1)]
+        cdt = torch.bfloat16 if w.c_dtype == "bf16" else torch.float32
+        C = torch.empty((w.M, w.N), dtype=cdt, device="cuda")
+        r = {"n_input_sets": n_sets}
+        r["fused"] = _batched(lambda i: mk.gemm_ar_local(*sets[i], C), n_sets, stream)
+        r["baseline"] = _batched(lambda i: mk.gemm_then_reduce_baseline(*sets[i], C), n_sets, stream)
+        r["two_stream"] = _batched(lambda i: mk.gemm_ar_two_stream(*sets[i], C), n_sets, stream)
+        mk.stream_status()
+        r["speedup_vs_baseline"] = round(r["baseline"]["median_us"] / r["fused"]["median_us"], 3)
+        r["fused_TFLOPs"] = round(w.flops / (r["fused"]["median_us"] * 1e-6) / 1e12, 1)
+        r["fused_GBps"] = round(w.compulsory_bytes() / (r["fused"]["median_us"] * 1e-6) / 1e9, 1)
+        res[w.name] = r
+        del sets, base, C
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "all-configs", "unit": "us per call", "results": res}), flush=True)
+
+
+def sweep(name):
+    import torch
+
+    import mk_inputs
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    w = mk_inputs.BY_NAME[name]
+    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if w.c_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    G = mk.fused_grid(A, B, peers, C)
+    res = {"workload": name, "G": G}
+    for nr in [0, 4, 8, 12, 16, 24, 32, 48, 64]:
+        if nr < G:
+            res[str(nr)] = _batched(lambda i: mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr), 1,
+                                    stream, batches=5, per_batch=10, warmup=3)
+    res["adaptive"] = _batched(lambda i: mk.gemm_ar_local(A, B, peers, C), 1, stream, batches=5,
+                               per_batch=10, warmup=3)
+    mk.stream_status()
+    print(json.dumps({"mode": "sweep", "unit": "us per call", "results": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,11 +183,19 @@ def main():
     ap.add_argument("--n-reduce-wg", type=int, default=None,
                     help="static reducer count (default: adaptive controller)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--sweep", metavar="WORKLOAD")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the fused kernel; runs on more than one "
               "GPU are not part of this build (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.all_configs:
+        all_configs()
+        return
+    if args.sweep:
+        sweep(args.sweep)
+        return
 
     import torch
 
