@@ -243,6 +243,20 @@ mk_status_t mk_gemm_ag_baseline(const void* A_local, const void* peers_A, int n_
  * mk_status_t on failure). */
 int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype);
 
+/*
+ * mk_flag_handoff -- microbenchmark of the tile-flag protocol (Figure 2, item 1
+ * of the thelatestinai.com page: a tile is handed to communication by a
+ * readiness flag set once the tile is in GPU memory). Two workgroups on one XCD
+ * hand a flag back and forth `iters` times (1 .. 2^24); each hand-off is one
+ * publish and its acquire, with nothing else in flight. flag_scope 0 = the
+ * XCD-local protocol of the fused kernel, 1 = agent-scope release/acquire.
+ * out: 16-byte-aligned device buffer of 4 uint64, written asynchronously on
+ * `stream`: [0] 100 MHz ticks of all 2*iters hand-offs, [1] 1 if a wait passed
+ * MK_OPT_SPIN_TIMEOUT_US (both sides then stop), [2], [3] the XCDs of the two
+ * workgroups. Uses the (device, stream) workspace's control words.
+ */
+mk_status_t mk_flag_handoff(int iters, int flag_scope, void* stream, void* out);
+
 /* Synchronizes `stream`, then returns and clears the device error word of that
  * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
 mk_status_t mk_stream_status(void* stream);

@@ -212,3 +212,14 @@ def test_allgather_validation_rejects(kw, status):
 
 def test_allgather_static_count_below_minus_one_is_rejected():
     assert ag(nc=-2) == mk.MK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("iters,scope,out,status", [
+    (0, 0, A16, mk.MK_ERR_INVALID_ARG),
+    ((1 << 24) + 1, 0, A16, mk.MK_ERR_INVALID_ARG),
+    (10, 2, A16, mk.MK_ERR_INVALID_ARG),
+    (10, 0, None, mk.MK_ERR_INVALID_ARG),
+    (10, 0, A16 + 8, mk.MK_ERR_INVALID_ARG),
+])
+def test_flag_handoff_validation_rejects(iters, scope, out, status):
+    assert mk.library().mk_flag_handoff(iters, scope, None, out) == status, mk.last_error()

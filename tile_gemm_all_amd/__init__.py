@@ -35,7 +35,7 @@ OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY = 4, 5, 6, 7
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_stream",
            "mk_gemm_rs_local", "mk_gemm_rs_baseline", "mk_gemm_ag_local", "mk_gemm_ag_baseline",
-           "mk_ag_grid",
+           "mk_ag_grid", "mk_flag_handoff",
            "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
            "mk_get_option",
@@ -77,6 +77,8 @@ _lib.mk_gemm_ag_baseline.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, 
 _lib.mk_gemm_ag_baseline.restype = _int
 _lib.mk_ag_grid.argtypes = [_i64, _int, _i64, _i64, _int]
 _lib.mk_ag_grid.restype = _int
+_lib.mk_flag_handoff.argtypes = [_int, _int, _vp, _vp]
+_lib.mk_flag_handoff.restype = _int
 _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
 _lib.mk_workspace_reset.argtypes = [_int]
@@ -292,6 +294,17 @@ def ag_grid(A_local, peers_A, A_full, B, C):
     if g < 0:
         _check(-g)
     return g
+
+
+def flag_handoff(iters=1000, flag_scope=0, stream=None):
+    """Flag hand-off microbenchmark: returns (ns per hand-off, XCD of each side).
+    Synchronizes the stream."""
+    out = torch.zeros(4, dtype=torch.int64, device="cuda")
+    _check(_lib.mk_flag_handoff(int(iters), int(flag_scope), _stream_ptr(stream), out.data_ptr()))
+    vals = out.cpu().tolist()
+    if vals[1]:
+        raise MkError(MK_ERR_TIMEOUT, "flag hand-off timed out")
+    return vals[0] * 10.0 / (2 * iters), (vals[2], vals[3])
 
 
 def stream_status(stream=None):

@@ -117,6 +117,7 @@ struct Workspace {
   int ag_cap = 0;
   unsigned long long* slots = nullptr;
   int epoch = 0;
+  unsigned long long handoffs = 0;  // calls of the flag hand-off microbenchmark
   // two-stream schedule: the reduce stream and its events (created on first use)
   hipStream_t s2 = nullptr;
   hipEvent_t ev[MK_MAX_CHUNKS + 1] = {};
@@ -1015,6 +1016,32 @@ int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype) {
   const int64_t NB = (int64_t)P * Ms / mk::shape_bm(shape);
   const int64_t tiles_n = (N + mk::shape_bn(shape) - 1) / mk::shape_bn(shape);
   return ag_grid_size(info, shape, c_dtype, NB * tiles_n);
+}
+
+mk_status_t mk_flag_handoff(int iters, int flag_scope, void* stream, void* out) {
+  if (iters < 1 || iters > (1 << 24)) return fail(MK_ERR_INVALID_ARG, "iters=%d outside [1, 2^24]", iters);
+  if (flag_scope != 0 && flag_scope != 1) return fail(MK_ERR_INVALID_ARG, "flag_scope=%d", flag_scope);
+  if (!out || ((uintptr_t)out) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  DeviceInfo info;
+  mk_status_t st = device_info(dev, info);
+  if (st != MK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const Options opt = options();
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  st = get_ws(dev, s, 0, 0, &w);
+  if (st != MK_OK) return st;
+  const unsigned call = (unsigned)(++w->handoffs);
+  e = hipMemsetAsync(out, 0, 4 * sizeof(unsigned long long), s);
+  if (e != hipSuccess) return hip_fail(e, "clearing out");
+  const unsigned long long limit =
+      (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
+  e = mk::launch_pingpong(w->slots, call, iters, flag_scope, limit, (unsigned long long*)out, s);
+  if (e != hipSuccess) return hip_fail(e, "hand-off kernel launch");
+  return MK_OK;
 }
 
 mk_status_t mk_stream_status(void* stream) {

@@ -39,6 +39,8 @@ enum Slot : int {
   S_NTRACE,            // controller trace entries written
   S_TSTART,            // min start tick
   S_TEND,              // max exit tick
+  S_PING,              // flag hand-off microbenchmark: (call << 32) | step, one per side
+  S_PONG,
   S_XCD_BASE,          // per-XCD words follow
   S_COUNT = S_XCD_BASE + kXcdWords * kMaxXcd
 };
@@ -181,6 +183,8 @@ hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream
 hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStream_t s);
 hipError_t launch_ag(int shape, int ct, const AgArgs& a, hipStream_t s);
+hipError_t launch_pingpong(unsigned long long* slots, unsigned call, int iters, int scope,
+                           unsigned long long limit, unsigned long long* out, hipStream_t s);
 hipError_t launch_ag_copy(const AgCopyArgs& a, int grid, hipStream_t s);
 hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStream_t s);
 

@@ -756,6 +756,57 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
   }
 }
 
+// ------------------------------------------------------------ flag hand-off microbenchmark
+
+// Two workgroups hand a flag back and forth `iters` times: side 0 publishes step
+// i and waits for side 1 to publish it back. One hand-off is one publish (the
+// tile flag's: stores complete, then the flag store) followed by its acquire
+// (poll, then the consumer's cache maintenance), the path a tile takes from
+// its compute workgroup to its reducer. Workgroups 0 and n_xcd share an XCD
+// when the dispatcher deals workgroups to XCDs in turn; out[2] and out[3] hold
+// the two sides' XCDs. Every wait is bounded: a side that times out records it
+// in out[1] and leaves, and so does the other side at its own limit.
+// out: [0] ticks of the whole exchange (side 0), [1] 0 or 1 (timed out),
+// [2], [3] XCD of side 0 and side 1.
+__global__ void pingpong_kernel(unsigned long long* S, unsigned call, int iters, int scope,
+                                unsigned long long limit, unsigned long long* out, int side1) {
+  const int b = blockIdx.x;
+  if ((b != 0 && b != side1) || threadIdx.x != 0) return;
+  const int me = b == 0 ? 0 : 1;
+  unsigned long long* mine = slot64(S, me == 0 ? S_PING : S_PONG);
+  unsigned long long* theirs = slot64(S, me == 0 ? S_PONG : S_PING);
+  out[2 + me] = (unsigned long long)xcc_id();
+  const unsigned long long base = (unsigned long long)call << 32;
+  const unsigned long long t0 = ticks();
+  int timed_out = 0;
+  for (int i = 1; i <= iters && !timed_out; ++i) {
+    const unsigned long long want = base | (unsigned)i;
+    if (me == 1) {  // wait for side 0's step i
+      const unsigned long long w0 = ticks();
+      while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+        if (ticks() - w0 > limit) { timed_out = 1; break; }
+      }
+      if (scope == 0) invalidate_l1();
+      else acquire_fence_agent();
+    }
+    if (!timed_out) {  // publish step i
+      wait_stores();
+      if (scope == 0) __hip_atomic_store(mine, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else __hip_atomic_store(mine, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (me == 0 && !timed_out) {  // wait for side 1 to hand step i back
+      const unsigned long long w0 = ticks();
+      while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+        if (ticks() - w0 > limit) { timed_out = 1; break; }
+      }
+      if (scope == 0) invalidate_l1();
+      else acquire_fence_agent();
+    }
+  }
+  if (me == 0) out[0] = ticks() - t0;
+  if (timed_out) out[1] = 1;
+}
+
 // Baseline AllGather: every shard into the gathered matrix, 16 bytes per lane.
 __global__ __launch_bounds__(kThreads) void ag_copy_kernel(AgCopyArgs a) {
   const int64_t per = a.Ms * a.K / 8;  // 16-byte chunks per shard
@@ -931,6 +982,20 @@ hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStrea
     else
       hipLaunchKernelGGL((gemm_c_kernel<T128, float>), dim3(T), dim3(kThreads), 0, s, a, (float*)C);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pingpong(unsigned long long* slots, unsigned call, int iters, int scope,
+                           unsigned long long limit, unsigned long long* out, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int n_xcd = cus / 32 > 1 ? cus / 32 : 1;
+  const int side1 = n_xcd > 1 ? n_xcd : 1;  // dealt to the XCD of workgroup 0
+  hipLaunchKernelGGL(pingpong_kernel, dim3(side1 + 1), dim3(64), 0, s, slots, call, iters, scope,
+                     limit, out, side1);
   return hipGetLastError();
 }
 
