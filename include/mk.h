@@ -295,13 +295,20 @@ typedef enum {
                                    compulsory byte or with queues of more than four rounds;
                                    otherwise all but the first min(queue/4, workgroups per
                                    XCD/2)), 0 = none */
-  MK_OPT_EARLY = 7              /* early reduce: a reducer may take a unit whose tile is still being
+  MK_OPT_EARLY = 7,             /* early reduce: a reducer may take a unit whose tile is still being
                                    computed and sums that unit's peers (into LDS) while it waits for
                                    the tile's flag. -1 = automatic (default: on when every tile and
                                    every reduce unit gets a workgroup of its own in one round, e.g.
                                    few-tile decode shapes; the grid then holds one workgroup per
                                    tile plus one per unit, and tiles are handed over rather than
                                    reduced in place), 0 = off, 1 = on. Peer counts 1-4, 7, 8, 15. */
+  MK_OPT_KSPLIT = 8             /* with early reduce and every tile handed over: each tile computed
+                                   as two k-halves (two workgroups, two fp32 partials, a flag each;
+                                   the reducer adds P0 + P1 to the peer sum). -1 = automatic (on
+                                   when K is a multiple of 64, at least 1024, and two items per tile
+                                   plus the reduce units fit one round), 1 = off, 2 = on (K a
+                                   multiple of 64). The fp32 rounding of P0 + P1 differs from one
+                                   k-loop, so C can differ from the baseline in the last bit. */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

@@ -223,3 +223,16 @@ def test_allgather_static_count_below_minus_one_is_rejected():
 ])
 def test_flag_handoff_validation_rejects(iters, scope, out, status):
     assert mk.library().mk_flag_handoff(iters, scope, None, out) == status, mk.last_error()
+
+
+def test_ksplit_option_accepts_only_auto_off_and_two():
+    old = mk.get_option(mk.OPT_KSPLIT)
+    try:
+        for v in (3, 4, 0, -2):
+            with pytest.raises(mk.MkError):
+                mk.set_option(mk.OPT_KSPLIT, v)
+        for v in (-1, 1, 2):
+            mk.set_option(mk.OPT_KSPLIT, v)
+            assert mk.get_option(mk.OPT_KSPLIT) == v
+    finally:
+        mk.set_option(mk.OPT_KSPLIT, old)

@@ -583,3 +583,36 @@ def test_allgather_share_full_size():
     check_exact(outs[0][0], mk_inputs.bits(shards.reshape(w.M, w.K)), "gathered matrix")
     check_exact(outs[0][0], outs[1][0], "fused against baseline, gathered matrix")
     check_exact(outs[0][1], outs[1][1], "fused against baseline, C")
+
+
+@pytest.mark.parametrize("variant", ["integer", "gaussian"])
+def test_ksplit_on_a_decode_shard(variant):
+    """Early-reduce shards with K a multiple of 64 and at least 1024 compute each tile
+    as two k-halves (MK_OPT_KSPLIT automatic): the grid holds two workgroups per tile
+    plus one per reduce unit. Integer inputs: bit-exact against the oracle with the
+    split on and off and for the baseline. Gaussian inputs: within the tolerance rule
+    (the sum of the two halves' fp32 partials rounds differently from one k-loop)."""
+    announce(f"k-split on a decode shard, {variant}")
+    M, N, K, npeer = 128, 2048, 1792, 15
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", variant, 73, device="cpu")
+    C64, want = oracle_rows(A, B, peers, "bf16")
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    tiles = (M // 128) * (N // 128)
+    old = mk.get_option(mk.OPT_KSPLIT)
+    try:
+        outs = {}
+        for ks, grid in ((-1, tiles * 4), (2, tiles * 4), (1, tiles * 3)):
+            mk.set_option(mk.OPT_KSPLIT, ks)
+            assert mk.fused_grid(A, B, peers, new_c(M, N, "bf16")) == grid, ks
+            for mode in ("adaptive", "0"):
+                outs[(ks, mode)] = c_bits(run(A, B, peers, "bf16", mode))
+        outs["baseline"] = c_bits(run(A, B, peers, "bf16", "baseline"))
+    finally:
+        mk.set_option(mk.OPT_KSPLIT, old)
+    for key, got in outs.items():
+        if variant == "integer":
+            check_exact(got, want, f"k-split {key}")
+        else:
+            check_tolerance(got, C64, "bf16", f"k-split {key}")
+    check_exact(outs[(-1, "adaptive")], outs[(2, "0")], "split calls agree bitwise")
+    check_exact(outs[(1, "adaptive")], outs["baseline"], "unsplit call against the baseline")

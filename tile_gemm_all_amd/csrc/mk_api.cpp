@@ -45,6 +45,7 @@ struct Options {
   int64_t reducer_cap = 0;  // 0: derived from HBM bandwidth and a reducer's streaming rate
   int64_t inplace = -1;     // -1: automatic; 0: none; n: the last n tiles of each XCD's queue
   int64_t early = -1;       // reducers sum a unit's peers before its tile is finished: -1 auto
+  int64_t ksplit = -1;      // early-reduce tiles computed as two k-halves: -1 auto, 1 off, 2 on
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -293,6 +294,7 @@ struct Launch {
   DeviceInfo info;
   int shape;
   int64_t tiles_m, tiles_n;
+  int64_t K;
 };
 
 // Whether reducers sum a unit's peers before its tile is finished (early
@@ -312,6 +314,22 @@ bool early_reduce(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   return T * (1 + mk::shape_bm(L.shape) / 64) <= full;
 }
 
+// K-split of an early-reduce call (MK_OPT_KSPLIT): automatic (-1) computes each
+// tile as two k-halves when the call has early reduce, K is a multiple of 64 and
+// at least 1024, and every item (two per tile) and reduce unit still fits one
+// round of resident workgroups. A decode-sized tile is otherwise one workgroup
+// streaming the tile's whole B panel at one compute unit's rate. Measured on the
+// 128x8192x1792 shard with 15 peers: unsplit 38.0-40.4 us, two parts 32.2-33.7 us,
+// four parts 36.4 us (two-kernel baseline 34.5-34.9 us).
+int ksplit_of(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
+  const int64_t opt = options().ksplit;
+  if (opt == 1 || !early_reduce(L, n_peers, peer_dtype, c_dtype) || L.K % 64 != 0) return 1;
+  if (opt == 2) return 2;
+  const int64_t T = L.tiles_m * L.tiles_n;
+  const int64_t full = (int64_t)L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+  return L.K >= 1024 && T * (2 + mk::shape_bm(L.shape) / 64) <= full ? 2 : 1;
+}
+
 // Persistent grid of the fused kernel: every resident workgroup slot (compute
 // units times workgroups per unit), but no more than two workgroups per tile
 // (with early reduce: one per tile plus one per reduce unit), rounded up to a
@@ -323,7 +341,8 @@ int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   if (n_xcd < 1) n_xcd = 1;
   const int64_t T = L.tiles_m * L.tiles_n;
   int64_t want = early_reduce(L, n_peers, peer_dtype, c_dtype)
-                     ? T * (1 + mk::shape_bm(L.shape) / 64) : 2 * T;
+                     ? T * (ksplit_of(L, n_peers, peer_dtype, c_dtype) + mk::shape_bm(L.shape) / 64)
+                     : 2 * T;
   want = (want + n_xcd - 1) / n_xcd * n_xcd;
   if (want < n_xcd) want = n_xcd;
   return want < full ? (int)want : full;
@@ -360,6 +379,7 @@ mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype
   mk_status_t st = device_info(dev, L.info);
   if (st != MK_OK) return st;
   L.dev = dev;
+  L.K = K;
   L.shape = pick_shape(M, N, K, n_peers, peer_dtype, c_dtype, L.info.cus);
   L.tiles_m = (M + mk::shape_bm(L.shape) - 1) / mk::shape_bm(L.shape);
   L.tiles_n = (N + mk::shape_bn(L.shape) - 1) / mk::shape_bn(L.shape);
@@ -463,7 +483,8 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace* w = nullptr;
   const int T = (int)(L.tiles_m * L.tiles_n);
-  st = get_ws(L.dev, s, (size_t)(M * N), T, &w);
+  const int ks = ksplit_of(L, n_peers, peer_dtype, c_dtype);  // partial slices and flags per tile
+  st = get_ws(L.dev, s, (size_t)(M * N) * ks, T * ks, &w);
   if (st != MK_OK) return st;
   if (++w->epoch >= 0x7FFFFFFF) {  // flags hold old epochs: restart them from zero
     hipError_t e = mk::launch_ws_init(w->flags, w->flags_cap, nullptr, s);
@@ -548,6 +569,9 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   } else {
     a.n_inplace = (int)opt.inplace;
   }
+  // Two k-halves only when every tile is handed to a reducer (an in-place tile
+  // would reduce its own half-product).
+  a.ksplit = a.early && a.n_inplace == 0 ? ks : 1;
   const bool inpl_ok =
       mk::inplace_supported(L.shape == mk::SHAPE_256 ? 1 : 2, dt_size(peer_dtype), n_peers);
   a.T_r = 0;
@@ -1138,6 +1162,11 @@ mk_status_t mk_set_option(int option, int64_t value) {
       if (value < -1 || value > 1) return fail(MK_ERR_INVALID_ARG, "early reduce %lld", (long long)value);
       g_opt.early = value;
       return MK_OK;
+    case MK_OPT_KSPLIT:
+      if (value != -1 && value != 1 && value != 2)
+        return fail(MK_ERR_INVALID_ARG, "k-split %lld", (long long)value);
+      g_opt.ksplit = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -1153,6 +1182,7 @@ int64_t mk_get_option(int option) {
     case MK_OPT_REDUCER_CAP: return g_opt.reducer_cap;
     case MK_OPT_INPLACE: return g_opt.inplace;
     case MK_OPT_EARLY: return g_opt.early;
+    case MK_OPT_KSPLIT: return g_opt.ksplit;
   }
   return -1;
 }

@@ -232,7 +232,8 @@ struct GemmTile {
     int64_t b[Cfg::B_LD];
   };
 
-  __device__ __forceinline__ static void sources(Src& s, int64_t M, int64_t N, int64_t K,
+  // lda: A's row pitch in elements (K when A holds just the k-range multiplied).
+  __device__ __forceinline__ static void sources(Src& s, int64_t M, int64_t N, int64_t lda,
                                                  int64_t m0, int64_t n0, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < Cfg::A_LD; ++i) {
@@ -242,7 +243,7 @@ struct GemmTile {
       int p = (byte % Cfg::A_ROW) / 16;
       int c = p ^ ((row >> 2) & 3);
       int64_t gm = m0 + row < M ? m0 + row : M - 1;
-      s.a[i] = gm * K + c * 8;
+      s.a[i] = gm * lda + c * 8;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_LD; ++i) {
@@ -385,11 +386,13 @@ struct GemmTile {
   // stages kt+1 .. kt+NS-1 are in flight while stage kt is computed.
   // gate(kt) runs in every lane before the loads of k-tile kt are issued (a
   // consumer that waits for its inputs to arrive); NoGate does nothing.
+  // lda: A's row pitch (0 = K); a k-range [k0, k0+K) of a wider product is run
+  // with A and B advanced to k0 and lda the full width.
   template <class Gate = NoGate>
   __device__ __forceinline__ void run(const uint16_t* __restrict__ A,
                                       const uint16_t* __restrict__ B, int64_t M, int64_t N,
                                       int64_t K, int64_t m0, int64_t n0, char* lds,
-                                      Gate gate = Gate()) {
+                                      Gate gate = Gate(), int64_t lda = 0) {
     static_assert(Cfg::NS == 4, "wait_loads assumes up to two later stages in flight");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
@@ -402,7 +405,7 @@ struct GemmTile {
     if (KT == 0) return;
     const int KF = (int)(K / Cfg::BK);  // full k-tiles; tile KF (if < KT) is partial
     Src s;
-    sources(s, M, N, K, m0, n0, wave, lane);
+    sources(s, M, N, lda > 0 ? lda : K, m0, n0, wave, lane);
     Frag f;
     frag_offsets(f, wave, lane);
     // Prologue: stages 0 .. NS-2. The partial tile, if any, is the last stage
@@ -642,6 +645,34 @@ struct PartialGlobal {
     b = *(const f32x4*)((const char*)P + op + 16u);
   }
 };
+// The partial of a product computed in NP k-parts of equal length: ((P_0 + P_1)
+// + ...) + P_{NP-1} in float32, parts `stride` floats apart (the parts' sum is
+// the tile's partial; it is formed before anything is added to it).
+template <int NP>
+struct PartialGlobalN {
+  static constexpr bool kHas = true;
+  const float* __restrict__ P;  // region base of part 0
+  uint32_t stride_bytes;        // bytes between two parts' region bases
+  __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t off, uint32_t) const {
+    const uint32_t op = off * 4u;
+    f32x4 va[NP], vb[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const char* base = (const char*)P + (size_t)p * stride_bytes;
+      va[p] = *(const f32x4*)(base + op);
+      vb[p] = *(const f32x4*)(base + op + 16u);
+    }
+    a = va[0];
+    b = vb[0];
+#pragma unroll
+    for (int p = 1; p < NP; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = a[i] + va[p][i];
+        b[i] = b[i] + vb[p][i];
+      }
+  }
+};
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 struct PartialLds {
   static constexpr bool kHas = true;
@@ -713,9 +744,9 @@ struct SumOp {
 
 // sum = (peer sum left in LDS by a SumOp with NoPartial/OutLds) + partial, to
 // C: the same float32 additions as one SumOp with the partial.
-template <typename CT>
+template <typename CT, typename PS = PartialGlobal>
 struct PresumOp {
-  PartialGlobal ps;
+  PS ps;
   const lds_char* pre;  // region base in LDS
   OutC<CT> out;
   struct Chunk {
@@ -1004,6 +1035,26 @@ __device__ __forceinline__ void reduce_region_finish(const float* __restrict__ P
                        __builtin_amdgcn_readfirstlane((int)n0);
   typedef PresumOp<CT> Op;
   ReduceRing<4, Op>::run(Op{PartialGlobal{P + base}, (const lds_char*)lds, OutC<CT>{C + base}},
+                         total, cpr, N, LP);
+}
+
+// Phase 2 for a tile computed in NP k-parts (partials NP * M * N floats apart,
+// same layout): C = round(peer sum + ((P_0 + P_1) + ...)).
+template <int NP, typename CT>
+__device__ __forceinline__ void reduce_region_finish_parts(const float* __restrict__ P,
+                                                           int64_t part_stride, const char* lds,
+                                                           int64_t LP, CT* __restrict__ C,
+                                                           int64_t N, int64_t m0, int64_t n0,
+                                                           int rows, int cols) {
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  const int total = rows * cpr;
+  if (total <= 0) return;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+  typedef PresumOp<CT, PartialGlobalN<NP>> Op;
+  ReduceRing<4, Op>::run(Op{PartialGlobalN<NP>{P + base, (uint32_t)(part_stride * 4)},
+                            (const lds_char*)lds, OutC<CT>{C + base}},
                          total, cpr, N, LP);
 }
 

@@ -99,6 +99,9 @@ struct FusedArgs {
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
   int early;                   // 1: a reducer may take a unit whose tile is still being
                                // computed, and sums its peers while it waits
+  int ksplit;                  // 1, or 2 (early reduce only): a tile is computed as two
+                               // k-halves, each its own compute item, partial slice
+                               // (P + half*M*N) and flag (flags[2*tile + half])
   // GEMM+ReduceScatter share (rs = 1): rows [own0, own1) are reduced into C
   // ([own1-own0, N]) with peers [n_peers, own1-own0, N]; the partial of every
   // other row is rounded to the peer type and stored to send ([M, N]). Tiles

@@ -177,6 +177,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   static_assert(Cfg::BM / Cfg::RSPLIT * Cfg::BN * 4 <= Cfg::LDS_BYTES, "peer sum of a unit in LDS");
   const bool early = a.early && a.n_peers > 0 &&
                      inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers);
+  // K-split: compute item i of the XCD's queue is k-half i % KS of tile i / KS. A
+  // tile counts as claimed once all of its items are.
+  const int KS = a.ksplit > 1 ? a.ksplit : 1;
+  const int items = cnt * KS;
 
   for (;;) {
     if (tid == 0) {
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         const int abort = load_relaxed(slot32(S, S_ABORT));
         const unsigned long long tw =
             __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int cn = load_relaxed(cnext);  // tiles claimed for compute (a lower bound)
+        const int cn = load_relaxed(cnext);  // compute items claimed (a lower bound)
         const int rn = load_relaxed(rnext);  // next reduce unit
         // The arrival rank is taken in the first pass, in the same round trip
         // as the loads above.
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           // then this workgroup computes the next tile itself: that claim cannot
           // fail while the reserved tile is unclaimed, so the XCD always makes
           // progress.
-          if (held / Cfg::RSPLIT < cn) {
+          if ((held / Cfg::RSPLIT + 1) * KS <= cn) {
             kind = K_REDUCE;
             tile = q0 + held / Cfg::RSPLIT;
             part = held % Cfg::RSPLIT;
@@ -217,46 +221,53 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
             break;
           }
           const int i = atomicAdd(cnext, 1);
-          if (i < cnt) {
+          if (i < items) {
             kind = K_COMPUTE;
-            tile = q0 + i;
+            tile = q0 + i / KS;
+            part = i % KS;
             off_role = pref_reduce;
             break;
           }
           continue;  // the tile was claimed meanwhile
         }
-        if (!pref_reduce && cn < cnt) {
+        if (!pref_reduce && cn < items) {
           const int i = atomicAdd(cnext, 1);
-          if (i < cnt) {
+          if (i < items) {
             kind = K_COMPUTE;
-            tile = q0 + i;
+            tile = q0 + i / KS;
+            part = i % KS;
             break;
           }
         }
         if (rn >= units) {
           // Every reduce unit is taken. Tiles reduced in place have no units, so
           // GEMM tiles may remain: take one before leaving.
-          if (pref_reduce && cn < cnt) {
+          if (pref_reduce && cn < items) {
             const int i = atomicAdd(cnext, 1);
-            if (i < cnt) {
+            if (i < items) {
               kind = K_COMPUTE;
-              tile = q0 + i;
+              tile = q0 + i / KS;
+              part = i % KS;
               off_role = true;
             }
           }
           break;
         }
         int fl = 0;
-        if (pref_reduce && cn < cnt) {
+        if (pref_reduce && cn < items) {
           // GEMM tiles are left: reserve the next unit only if its tile is
           // finished (or, with early reduce, being computed: its peers are
           // summed meanwhile), else compute rather than wait for its flag.
-          fl = load_relaxed(a.flags + q0 + rn / Cfg::RSPLIT);
-          if (fl != a.epoch && !(early && rn / Cfg::RSPLIT < cn)) {
+          const int ft = (q0 + rn / Cfg::RSPLIT) * KS;
+          fl = load_relaxed(a.flags + ft);
+          for (int h = 1; h < KS; ++h)
+            if (load_relaxed(a.flags + ft + h) != a.epoch) fl = 0;
+          if (fl != a.epoch && !(early && (rn / Cfg::RSPLIT + 1) * KS <= cn)) {
             const int i = atomicAdd(cnext, 1);
-            if (i < cnt) {
+            if (i < items) {
               kind = K_COMPUTE;
-              tile = q0 + i;
+              tile = q0 + i / KS;
+              part = i % KS;
               off_role = true;
               break;
             }
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           held = -1;
           break;
         }
-        if (held / Cfg::RSPLIT < cn) {
+        if ((held / Cfg::RSPLIT + 1) * KS <= cn) {
           kind = K_REDUCE;
           tile = q0 + held / Cfg::RSPLIT;
           part = held % Cfg::RSPLIT;
@@ -306,7 +317,12 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       // with no load outstanding, so it adds no waits to the k-loop.
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       GemmTile<Cfg> g;
-      g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+      if (KS > 1) {  // k-half `part` of the tile: A and B advanced, A's pitch K
+        const int64_t kh = a.K / KS, k0 = kh * part;
+        g.run(a.A + k0, a.B + k0 * a.N, a.M, a.N, kh, m0, n0, lds, NoGate(), a.K);
+      } else {
+        g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+      }
       if (tile - q0 >= published) {
         // In place: the partial goes through LDS (freed by the GEMM's last
         // barrier) in passes, each summed in the same order as a reducer would.
@@ -341,17 +357,19 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         __syncthreads();
         continue;
       }
-      g.store_partial(a.P, a.M, a.N, m0, n0);
+      g.store_partial(a.P + (KS > 1 ? part * a.M * a.N : 0), a.M, a.N, m0, n0);
       wait_stores();    // this wave's partial stores have reached the L2
       __syncthreads();  // ... and so have every other wave's
       if (tid == 0) {
         if (tile != a.withhold_tile) {
-          if (a.flag_scope == 0) store_flag(a.flags + tile, a.epoch);
-          else publish_flag_agent(a.flags + tile, a.epoch);
+          int* fp = a.flags + tile * KS + part;
+          if (a.flag_scope == 0) store_flag(fp, a.epoch);
+          else publish_flag_agent(fp, a.epoch);
         }
         int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;  // this XCD's count
         atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
-        if (a.adaptive && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
+        // (with a k-split the call fits one round of workgroups: no controller)
+        if (a.adaptive && KS == 1 && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
       }
     } else {
       constexpr int SLAB = Cfg::BM / Cfg::RSPLIT;
@@ -368,18 +386,21 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       if (tid == 0) {
         const unsigned long long w0 = ticks();
         int ok = 1, backoff = 1;
-        while (!flag_seen && load_relaxed(a.flags + tile) != a.epoch) {
-          if (load_relaxed(slot32(S, S_ABORT))) {
-            ok = 0;
-            break;
+        // the tile's flags (one per k-part), each polled until set
+        for (int h = 0; h < KS && !flag_seen && ok; ++h) {
+          while (load_relaxed(a.flags + tile * KS + h) != a.epoch) {
+            if (load_relaxed(slot32(S, S_ABORT))) {
+              ok = 0;
+              break;
+            }
+            if (ticks() - w0 > a.spin_limit) {
+              raise_error(S, MK_ERR_TIMEOUT);
+              ok = 0;
+              break;
+            }
+            backoff_sleep(backoff);
+            backoff = backoff < 4 ? backoff * 2 : 4;
           }
-          if (ticks() - w0 > a.spin_limit) {
-            raise_error(S, MK_ERR_TIMEOUT);
-            ok = 0;
-            break;
-          }
-          backoff_sleep(backoff);
-          backoff = backoff < 4 ? backoff * 2 : 4;
         }
         if (a.flag_scope == 0) invalidate_l1();
         else acquire_fence_agent();
@@ -391,7 +412,11 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       }
       __syncthreads();  // also: phase 1's LDS writes are done
       if (!s_ok) break;
-      if (early)
+      if (early && KS == 2)
+        reduce_region_finish_parts<2, CT>(a.P, a.M * a.N, lds, Cfg::BN, C, a.N, r0, n0, rows, cols);
+      else if (KS > 1) {  // the host splits k only with early reduce
+        if (tid == 0) raise_error(S, MK_ERR_INTERNAL);
+      } else if (early)
         reduce_region_finish<CT>(a.P, lds, Cfg::BN, C, a.N, r0, n0, rows, cols);
       else if (a.rs)
         rs_unit<Cfg::OCC, PT, CT>(a, r0, n0, rows, cols);
