@@ -305,7 +305,7 @@ typedef enum {
   MK_OPT_KSPLIT = 8             /* with early reduce and every tile handed over: each tile computed
                                    as two k-halves (two workgroups, two fp32 partials, a flag each;
                                    the reducer adds P0 + P1 to the peer sum). -1 = automatic (on
-                                   when K is a multiple of 64, at least 1024, and two items per tile
+                                   when K is a multiple of 64, at least 512, and two items per tile
                                    plus the reduce units fit one round), 1 = off, 2 = on (K a
                                    multiple of 64). The fp32 rounding of P0 + P1 differs from one
                                    k-loop, so C can differ from the baseline in the last bit. */

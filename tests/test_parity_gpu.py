@@ -178,14 +178,26 @@ def test_workload_parity(w, variant):
     torch.cuda.empty_cache()
 
 
-def test_bitwise_invariance_across_reducer_counts(inplace_policy):
-    announce("invariance across reducer counts")
+@pytest.mark.parametrize("ksplit", [-1, 1], ids=["ksplit-auto", "ksplit-off"])
+def test_bitwise_invariance_across_reducer_counts(inplace_policy, ksplit):
+    """Every reducer count gives the bits of the adaptive call; with the k-split off
+    (one k-loop per tile) those are also the baseline's bits. (With early reduce this
+    shape's tiles are split in two k-halves by default, whose fp32 sum rounds
+    differently from one k-loop.)"""
+    announce(f"invariance across reducer counts, k-split {ksplit}")
     M, N, K, npeer = 1024, 2048, 576, 7
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "gaussian", 21, device=DEV)
-    G = mk.fused_grid(A, B, peers, new_c(M, N, "bf16"))
-    ref = c_bits(run(A, B, peers, "bf16", "baseline"))
-    for mode in ["adaptive", "0", "1", "4", "16", "64", str(G - 1)]:
-        check_exact(c_bits(run(A, B, peers, "bf16", mode)), ref, f"mode {mode}")
+    old = mk.get_option(mk.OPT_KSPLIT)
+    mk.set_option(mk.OPT_KSPLIT, ksplit)
+    try:
+        G = mk.fused_grid(A, B, peers, new_c(M, N, "bf16"))
+        ref = c_bits(run(A, B, peers, "bf16", "adaptive"))
+        if ksplit == 1:
+            check_exact(ref, c_bits(run(A, B, peers, "bf16", "baseline")), "adaptive vs baseline")
+        for mode in ["0", "1", "4", "16", "64", str(G - 1)]:
+            check_exact(c_bits(run(A, B, peers, "bf16", mode)), ref, f"mode {mode}")
+    finally:
+        mk.set_option(mk.OPT_KSPLIT, old)
 
 
 INPLACE_SHAPES = [
@@ -587,7 +599,7 @@ def test_allgather_share_full_size():
 
 @pytest.mark.parametrize("variant", ["integer", "gaussian"])
 def test_ksplit_on_a_decode_shard(variant):
-    """Early-reduce shards with K a multiple of 64 and at least 1024 compute each tile
+    """Early-reduce shards with K a multiple of 64 and at least 512 compute each tile
     as two k-halves (MK_OPT_KSPLIT automatic): the grid holds two workgroups per tile
     plus one per reduce unit. Integer inputs: bit-exact against the oracle with the
     split on and off and for the baseline. Gaussian inputs: within the tolerance rule

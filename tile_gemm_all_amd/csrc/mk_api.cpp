@@ -316,18 +316,19 @@ bool early_reduce(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
 
 // K-split of an early-reduce call (MK_OPT_KSPLIT): automatic (-1) computes each
 // tile as two k-halves when the call has early reduce, K is a multiple of 64 and
-// at least 1024, and every item (two per tile) and reduce unit still fits one
+// at least 512, and every item (two per tile) and reduce unit still fits one
 // round of resident workgroups. A decode-sized tile is otherwise one workgroup
 // streaming the tile's whole B panel at one compute unit's rate. Measured on the
 // 128x8192x1792 shard with 15 peers: unsplit 38.0-40.4 us, two parts 32.2-33.7 us,
-// four parts 36.4 us (two-kernel baseline 34.5-34.9 us).
+// four parts 36.4 us (two-kernel baseline 34.5-34.9 us); 256x512x512 with 3 fp32
+// peers: 19.3-19.6 -> 18.2-18.3 us.
 int ksplit_of(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   const int64_t opt = options().ksplit;
   if (opt == 1 || !early_reduce(L, n_peers, peer_dtype, c_dtype) || L.K % 64 != 0) return 1;
   if (opt == 2) return 2;
   const int64_t T = L.tiles_m * L.tiles_n;
   const int64_t full = (int64_t)L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
-  return L.K >= 1024 && T * (2 + mk::shape_bm(L.shape) / 64) <= full ? 2 : 1;
+  return L.K >= 512 && T * (2 + mk::shape_bm(L.shape) / 64) <= full ? 2 : 1;
 }
 
 // Persistent grid of the fused kernel: every resident workgroup slot (compute
