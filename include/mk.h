@@ -273,7 +273,8 @@ int mk_num_workgroups(int device);
 /* G for a call with these arguments on the current device: the resident
  * workgroup slots of the chosen tile shape (compute units times 1 for 256x256
  * tiles, times 2 for 128x128), but at most two per tile (with early reduce, see
- * MK_OPT_EARLY: one per tile plus one per reduce unit of BM/64 rows), rounded
+ * MK_OPT_EARLY: one per tile, or two with MK_OPT_KSPLIT, plus one per reduce
+ * unit of BM/64 rows), rounded
  * up to a multiple of the XCD count, for calls with few tiles. It depends on the
  * options in force at the time of the call. n_reduce_wg of that call
  * must lie in [0, G-1] or be MK_ADAPTIVE. Returns a negative mk_status_t on

@@ -333,7 +333,8 @@ int ksplit_of(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
 
 // Persistent grid of the fused kernel: every resident workgroup slot (compute
 // units times workgroups per unit), but no more than two workgroups per tile
-// (with early reduce: one per tile plus one per reduce unit), rounded up to a
+// (with early reduce: one per tile, or two with a k-split, plus one per reduce
+// unit), rounded up to a
 // multiple of the XCD count, so that a call with few tiles does not start
 // hundreds of workgroups that only find no work and leave.
 int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
