@@ -20,6 +20,9 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
                                           baseline / two-stream, median p10 p90)
        python bench.py --sweep large     (one JSON line: static reducer counts
                                           0..64 against the adaptive controller)
+       python bench.py --trace attn --trace-inplace 0
+                                         (one JSON line: the controller's trace
+                                          and the device-timer role breakdown)
 
 --all-configs times batches of calls between two HIP events (10 batches of 20
 calls after warmup; median, p10 and p90 of the per-call averages). Workloads
@@ -174,6 +177,43 @@ def sweep(name):
     print(json.dumps({"mode": "sweep", "unit": "us per call", "results": res}), flush=True)
 
 
+def trace(name, inplace):
+    """One call with telemetry: the controller's trace (Figure 7 style: reducer
+    target against compute and reduce progress) and the device-timer role
+    breakdown."""
+    import torch
+
+    import mk_inputs
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    w = mk_inputs.BY_NAME[name]
+    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if w.c_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    tel = torch.zeros(mk.TELEMETRY_BYTES, dtype=torch.uint8, device="cuda")
+    old = mk.get_option(mk.OPT_INPLACE)
+    mk.set_option(mk.OPT_INPLACE, inplace)
+    try:
+        for _ in range(3):
+            mk.gemm_ar_local(A, B, peers, C, telemetry=tel)
+        mk.stream_status()
+    finally:
+        mk.set_option(mk.OPT_INPLACE, old)
+    t = mk.Telemetry.from_buffer_copy(bytes(tel.cpu().numpy()))
+    span = (t.t_end - t.t_start) / 100.0  # us (100 MHz ticks)
+    slots = t.grid * span
+    pts = [{"t_us": round((t.trace[i].t - t.t_start) / 100.0, 1), "computed": t.trace[i].computed,
+            "reduced": t.trace[i].reduced, "target": t.trace[i].target} for i in range(t.n_trace)]
+    print(json.dumps({"mode": "trace", "workload": name, "inplace_option": inplace,
+                      "span_us": round(span, 1), "grid": t.grid, "tiles": t.tiles,
+                      "busy_compute_frac": round(t.busy_compute / 100.0 / slots, 3),
+                      "busy_reduce_frac": round(t.busy_reduce / 100.0 / slots, 3),
+                      "wait_reduce_frac": round(t.wait_reduce / 100.0 / slots, 3),
+                      "initial_target": t.initial_target, "final_target": t.final_target,
+                      "updates": t.n_updates, "trace": pts}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +225,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--sweep", metavar="WORKLOAD")
+    ap.add_argument("--trace", metavar="WORKLOAD",
+                    help="one call with telemetry; --trace-inplace 0 hands every tile over")
+    ap.add_argument("--trace-inplace", type=int, default=-1)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the fused kernel; runs on more than one "
@@ -195,6 +238,9 @@ def main():
         return
     if args.sweep:
         sweep(args.sweep)
+        return
+    if args.trace:
+        trace(args.trace, args.trace_inplace)
         return
 
     import torch
