@@ -244,18 +244,24 @@ mk_status_t mk_gemm_ag_baseline(const void* A_local, const void* peers_A, int n_
 int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype);
 
 /*
- * mk_flag_handoff -- microbenchmark of the tile-flag protocol (Figure 2, item 1
- * of the thelatestinai.com page: a tile is handed to communication by a
- * readiness flag set once the tile is in GPU memory). Two workgroups on one XCD
- * hand a flag back and forth `iters` times (1 .. 2^24); each hand-off is one
- * publish and its acquire, with nothing else in flight. flag_scope 0 = the
- * XCD-local protocol of the fused kernel, 1 = agent-scope release/acquire.
- * out: 16-byte-aligned device buffer of 4 uint64, written asynchronously on
+ * mk_flag_handoff -- microbenchmark and message-passing litmus of the tile-flag
+ * protocol (Figure 2, item 1 of the thelatestinai.com page: a tile is handed to
+ * communication by a readiness flag set once the tile is in GPU memory). Two
+ * workgroups hand a flag back and forth `iters` times (1 .. 2^24), nothing else
+ * in flight. Before each hand-off side 0 writes a data word (plain store); after
+ * it side 1 reads the word (plain load) and counts values that are not the one
+ * just published. flag_scope 0 = stores complete + relaxed flag store, consumer
+ * invalidate at workgroup scope only (measured not to carry the data); 1 =
+ * agent-scope release/acquire (MK_OPT_FLAG_SCOPE=1); 2 = the fused kernel's
+ * default: stores complete + relaxed flag store, agent-scope acquire. cross_xcd
+ * 0 = both workgroups on one XCD (the fused kernel's case), 1 = on two XCDs.
+ * out: 16-byte-aligned device buffer of 5 uint64, written asynchronously on
  * `stream`: [0] 100 MHz ticks of all 2*iters hand-offs, [1] 1 if a wait passed
  * MK_OPT_SPIN_TIMEOUT_US (both sides then stop), [2], [3] the XCDs of the two
- * workgroups. Uses the (device, stream) workspace's control words.
+ * workgroups, [4] stale data reads. Uses the (device, stream) workspace's
+ * control words.
  */
-mk_status_t mk_flag_handoff(int iters, int flag_scope, void* stream, void* out);
+mk_status_t mk_flag_handoff(int iters, int flag_scope, int cross_xcd, void* stream, void* out);
 
 /* Synchronizes `stream`, then returns and clears the device error word of that
  * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
@@ -287,7 +293,8 @@ typedef enum {
   MK_OPT_WITHHOLD_TILE = 1,     /* debug: compute skips publishing this tile (-1 = off) */
   MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
   MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
-  MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default), 1 = agent-scope release/acquire */
+  MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default: stores complete + relaxed flag store,
+                                   agent-scope acquire), 1 = agent-scope release/acquire */
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
   MK_OPT_INPLACE = 6,           /* tiles per XCD reduced in place by the workgroup that computed them
                                    (the last ones of the XCD's queue; the others are handed to

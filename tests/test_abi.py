@@ -217,12 +217,16 @@ def test_allgather_static_count_below_minus_one_is_rejected():
 @pytest.mark.parametrize("iters,scope,out,status", [
     (0, 0, A16, mk.MK_ERR_INVALID_ARG),
     ((1 << 24) + 1, 0, A16, mk.MK_ERR_INVALID_ARG),
-    (10, 2, A16, mk.MK_ERR_INVALID_ARG),
+    (10, 3, A16, mk.MK_ERR_INVALID_ARG),
     (10, 0, None, mk.MK_ERR_INVALID_ARG),
     (10, 0, A16 + 8, mk.MK_ERR_INVALID_ARG),
 ])
 def test_flag_handoff_validation_rejects(iters, scope, out, status):
-    assert mk.library().mk_flag_handoff(iters, scope, None, out) == status, mk.last_error()
+    assert mk.library().mk_flag_handoff(iters, scope, 0, None, out) == status, mk.last_error()
+
+
+def test_flag_handoff_rejects_a_bad_xcd_choice():
+    assert mk.library().mk_flag_handoff(10, 0, 2, None, A16) == mk.MK_ERR_INVALID_ARG
 
 
 def test_ksplit_option_accepts_only_auto_off_and_two():

@@ -77,7 +77,7 @@ _lib.mk_gemm_ag_baseline.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, 
 _lib.mk_gemm_ag_baseline.restype = _int
 _lib.mk_ag_grid.argtypes = [_i64, _int, _i64, _i64, _int]
 _lib.mk_ag_grid.restype = _int
-_lib.mk_flag_handoff.argtypes = [_int, _int, _vp, _vp]
+_lib.mk_flag_handoff.argtypes = [_int, _int, _int, _vp, _vp]
 _lib.mk_flag_handoff.restype = _int
 _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
@@ -296,15 +296,16 @@ def ag_grid(A_local, peers_A, A_full, B, C):
     return g
 
 
-def flag_handoff(iters=1000, flag_scope=0, stream=None):
-    """Flag hand-off microbenchmark: returns (ns per hand-off, XCD of each side).
-    Synchronizes the stream."""
-    out = torch.zeros(4, dtype=torch.int64, device="cuda")
-    _check(_lib.mk_flag_handoff(int(iters), int(flag_scope), _stream_ptr(stream), out.data_ptr()))
+def flag_handoff(iters=1000, flag_scope=0, cross_xcd=False, stream=None):
+    """Flag hand-off microbenchmark and message-passing litmus: returns (ns per
+    hand-off, stale data reads, XCD of each side). Synchronizes the stream."""
+    out = torch.zeros(6, dtype=torch.int64, device="cuda")
+    _check(_lib.mk_flag_handoff(int(iters), int(flag_scope), int(bool(cross_xcd)),
+                                _stream_ptr(stream), out.data_ptr()))
     vals = out.cpu().tolist()
     if vals[1]:
         raise MkError(MK_ERR_TIMEOUT, "flag hand-off timed out")
-    return vals[0] * 10.0 / (2 * iters), (vals[2], vals[3])
+    return vals[0] * 10.0 / (2 * iters), vals[4], (vals[2], vals[3])
 
 
 def stream_status(stream=None):

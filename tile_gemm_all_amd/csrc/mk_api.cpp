@@ -529,6 +529,7 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   a.n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
   if (G % a.n_xcd != 0) a.n_xcd = 1;
   a.flag_scope = (int)opt.flag_scope;
+  a.shared_lines = N % 32 != 0 ? 1 : 0;  // partial rows not whole 128-byte lines
   a.reducer_cap = (int)opt.reducer_cap;
   if (a.reducer_cap <= 0) {
     // Compute units that saturate HBM with the reduce stream: about 5.5 TB/s
@@ -785,6 +786,7 @@ mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, in
   a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
   a.n_xcd = G % n_xcd == 0 ? n_xcd : 1;
   a.flag_scope = (int)opt.flag_scope;
+  a.shared_lines = N % 32 != 0 ? 1 : 0;  // partial rows not whole 128-byte lines
   a.early = 0;
   a.rs = 1;
   // Tile rows that hold owned rows are handed to reducers (their reduce is the
@@ -1044,9 +1046,10 @@ int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype) {
   return ag_grid_size(info, shape, c_dtype, NB * tiles_n);
 }
 
-mk_status_t mk_flag_handoff(int iters, int flag_scope, void* stream, void* out) {
+mk_status_t mk_flag_handoff(int iters, int flag_scope, int cross_xcd, void* stream, void* out) {
   if (iters < 1 || iters > (1 << 24)) return fail(MK_ERR_INVALID_ARG, "iters=%d outside [1, 2^24]", iters);
-  if (flag_scope != 0 && flag_scope != 1) return fail(MK_ERR_INVALID_ARG, "flag_scope=%d", flag_scope);
+  if (flag_scope < 0 || flag_scope > 2) return fail(MK_ERR_INVALID_ARG, "flag_scope=%d", flag_scope);
+  if (cross_xcd != 0 && cross_xcd != 1) return fail(MK_ERR_INVALID_ARG, "cross_xcd=%d", cross_xcd);
   if (!out || ((uintptr_t)out) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1061,11 +1064,12 @@ mk_status_t mk_flag_handoff(int iters, int flag_scope, void* stream, void* out) 
   st = get_ws(dev, s, 0, 0, &w);
   if (st != MK_OK) return st;
   const unsigned call = (unsigned)(++w->handoffs);
-  e = hipMemsetAsync(out, 0, 4 * sizeof(unsigned long long), s);
+  e = hipMemsetAsync(out, 0, 5 * sizeof(unsigned long long), s);
   if (e != hipSuccess) return hip_fail(e, "clearing out");
   const unsigned long long limit =
       (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
-  e = mk::launch_pingpong(w->slots, call, iters, flag_scope, limit, (unsigned long long*)out, s);
+  e = mk::launch_pingpong(w->slots, call, iters, flag_scope, cross_xcd, limit,
+                          (unsigned long long*)out, s);
   if (e != hipSuccess) return hip_fail(e, "hand-off kernel launch");
   return MK_OK;
 }

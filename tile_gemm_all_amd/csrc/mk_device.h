@@ -53,16 +53,29 @@ __device__ __forceinline__ uint64_t ticks() { return __builtin_amdgcn_s_memrealt
 // see the same data (the per-CU vector L1 is write-through). So:
 //   producer: each wave waits until its partial-tile stores are acknowledged by
 //             the L2 (vmcnt = 0), the workgroup meets at a barrier, then one lane
-//             stores the flag with an agent-scope atomic;
-//   consumer: one lane polls the flag with agent-scope atomic loads, then
-//             invalidates its compute unit's L1 so that the partial is read from
-//             the L2, and the workgroup meets at a barrier.
-// Neither side writes back or invalidates an L2, so other tiles stay cached.
-// The agent-scope variant (L2 writeback on release, L2 invalidate on acquire)
-// is kept for flags produced on another XCD.
+//             stores the flag with an agent-scope atomic (no L2 write-back);
+//   consumer: one lane polls the flag with agent-scope atomic loads; the
+//             partial is then read from the L2 unless the compute unit's L1
+//             already holds a copy of one of its lines. With N a multiple of 32
+//             floats every 128-byte line of the partial belongs to one reduce
+//             unit, read once per call, so no copy can exist (the L1 starts
+//             each kernel empty) and nothing is invalidated. Otherwise the
+//             consumer acquires at agent scope (buffer_inv sc1), which
+//             invalidates its L1; the workgroup then meets at a barrier.
+// Measured with the hand-off litmus (mk_flag_handoff), which rereads one word:
+// producer as above with the agent-scope acquire carried the data in every one
+// of 200,000 same-XCD hand-offs; a workgroup-scope invalidate (buffer_inv sc0,
+// inv_group_scope below) in its place left the L1's copy in use (199,999 stale
+// reads). The acquire costs the 4096x8192x1792 call about 20 us when used on
+// every reduce unit, hence its restriction to shared lines. Across XCDs the
+// producer's L2 must be written back too: the agent-scope variant (release and
+// acquire) is kept for that.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void invalidate_l1() {
+// Workgroup-scope cache invalidate. Not a consumer acquire: it does not refresh
+// a line the compute unit's L1 already holds (see above); only the hand-off
+// litmus uses it, to show that.
+__device__ __forceinline__ void inv_group_scope() {
   asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
 }
 

@@ -41,6 +41,7 @@ enum Slot : int {
   S_TEND,              // max exit tick
   S_PING,              // flag hand-off microbenchmark: (call << 32) | step, one per side
   S_PONG,
+  S_PAYLOAD,           // ... and the data word each hand-off carries
   S_XCD_BASE,          // per-XCD words follow
   S_COUNT = S_XCD_BASE + kXcdWords * kMaxXcd
 };
@@ -94,6 +95,9 @@ struct FusedArgs {
   int withhold_tile;           // debug: -1 = off
   int n_xcd;                   // XCDs of the device; tiles are queued per XCD
   int flag_scope;              // 0: producer and consumer share an XCD's L2; 1: agent scope
+  int shared_lines;            // 1: a 128-byte line of the partial can hold two reduce units'
+                               // rows (N not a multiple of 32): consumers acquire at agent
+                               // scope; 0: every line belongs to one unit, no invalidate
   int reducer_cap;             // controller's upper bound on reducers while compute remains
   int n_inplace;               // per XCD: last tiles of the queue reduced in place
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
@@ -187,7 +191,8 @@ hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStream_t s);
 hipError_t launch_ag(int shape, int ct, const AgArgs& a, hipStream_t s);
 hipError_t launch_pingpong(unsigned long long* slots, unsigned call, int iters, int scope,
-                           unsigned long long limit, unsigned long long* out, hipStream_t s);
+                           int cross_xcd, unsigned long long limit, unsigned long long* out,
+                           hipStream_t s);
 hipError_t launch_ag_copy(const AgCopyArgs& a, int grid, hipStream_t s);
 hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStream_t s);
 

@@ -402,8 +402,11 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
             backoff = backoff < 4 ? backoff * 2 : 4;
           }
         }
-        if (a.flag_scope == 0) invalidate_l1();
-        else acquire_fence_agent();
+        // The partial must not come from a stale L1 copy: with lines that can
+        // hold two units' rows (or agent-scope flags) acquire at agent scope;
+        // otherwise this compute unit has never read the unit's lines in this
+        // call, so its L1 holds no copy of them (see mk_device.h).
+        if (a.flag_scope != 0 || a.shared_lines) acquire_fence_agent();
         const unsigned long long w1 = ticks();
         atomicAdd(xslot64(S, x, X_WAIT_R), w1 - w0);
         s_ok = ok;
@@ -783,16 +786,21 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
 
 // ------------------------------------------------------------ flag hand-off microbenchmark
 
-// Two workgroups hand a flag back and forth `iters` times: side 0 publishes step
-// i and waits for side 1 to publish it back. One hand-off is one publish (the
-// tile flag's: stores complete, then the flag store) followed by its acquire
-// (poll, then the consumer's cache maintenance), the path a tile takes from
-// its compute workgroup to its reducer. Workgroups 0 and n_xcd share an XCD
-// when the dispatcher deals workgroups to XCDs in turn; out[2] and out[3] hold
-// the two sides' XCDs. Every wait is bounded: a side that times out records it
-// in out[1] and leaves, and so does the other side at its own limit.
-// out: [0] ticks of the whole exchange (side 0), [1] 0 or 1 (timed out),
-// [2], [3] XCD of side 0 and side 1.
+// Scopes: 0 = stores complete + relaxed flag, workgroup-scope invalidate (shown
+// not to carry data); 1 = agent-scope release and acquire; 2 = the fused
+// kernel's protocol: stores complete + relaxed flag, agent-scope acquire.
+// Two workgroups hand a flag back and forth `iters` times: side 0 writes a data
+// word (plain store), publishes step i (the tile flag's publish: stores
+// complete, then the flag store) and waits for side 1 to publish it back; side 1
+// waits for step i (poll, then the consumer's cache maintenance), reads the data
+// word with a plain load and counts values other than step i (a message-passing
+// litmus: a stale read means the protocol does not carry data). One hand-off is
+// the path of a tile from its compute workgroup to its reducer. Side 1 is
+// workgroup n_xcd (dealt to the XCD of workgroup 0) or, with cross_xcd,
+// workgroup 1 (the next XCD). Every wait is bounded: a side that times out
+// records it and leaves, and so does the other side at its own limit.
+// out: [0] ticks of the whole exchange (side 0), [1] 1 if a wait timed out,
+// [2], [3] the XCDs of side 0 and side 1, [4] stale data reads (side 1).
 __global__ void pingpong_kernel(unsigned long long* S, unsigned call, int iters, int scope,
                                 unsigned long long limit, unsigned long long* out, int side1) {
   const int b = blockIdx.x;
@@ -800,23 +808,28 @@ __global__ void pingpong_kernel(unsigned long long* S, unsigned call, int iters,
   const int me = b == 0 ? 0 : 1;
   unsigned long long* mine = slot64(S, me == 0 ? S_PING : S_PONG);
   unsigned long long* theirs = slot64(S, me == 0 ? S_PONG : S_PING);
+  unsigned long long* payload = slot64(S, S_PAYLOAD);
   out[2 + me] = (unsigned long long)xcc_id();
   const unsigned long long base = (unsigned long long)call << 32;
   const unsigned long long t0 = ticks();
   int timed_out = 0;
+  unsigned long long stale = 0;
   for (int i = 1; i <= iters && !timed_out; ++i) {
     const unsigned long long want = base | (unsigned)i;
-    if (me == 1) {  // wait for side 0's step i
+    if (me == 1) {  // wait for side 0's step i, then read what it carries
       const unsigned long long w0 = ticks();
       while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
         if (ticks() - w0 > limit) { timed_out = 1; break; }
       }
-      if (scope == 0) invalidate_l1();
-      else acquire_fence_agent();
+      if (scope == 0) inv_group_scope();
+      else acquire_fence_agent();  // scopes 1 and 2
+      if (!timed_out && *payload != want) ++stale;
+    } else {
+      *payload = want;
     }
     if (!timed_out) {  // publish step i
       wait_stores();
-      if (scope == 0) __hip_atomic_store(mine, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (scope != 1) __hip_atomic_store(mine, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else __hip_atomic_store(mine, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (me == 0 && !timed_out) {  // wait for side 1 to hand step i back
@@ -824,11 +837,12 @@ __global__ void pingpong_kernel(unsigned long long* S, unsigned call, int iters,
       while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
         if (ticks() - w0 > limit) { timed_out = 1; break; }
       }
-      if (scope == 0) invalidate_l1();
+      if (scope == 0) inv_group_scope();
       else acquire_fence_agent();
     }
   }
   if (me == 0) out[0] = ticks() - t0;
+  else out[4] = stale;
   if (timed_out) out[1] = 1;
 }
 
@@ -1011,14 +1025,16 @@ hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStrea
 }
 
 hipError_t launch_pingpong(unsigned long long* slots, unsigned call, int iters, int scope,
-                           unsigned long long limit, unsigned long long* out, hipStream_t s) {
+                           int cross_xcd, unsigned long long limit, unsigned long long* out,
+                           hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int n_xcd = cus / 32 > 1 ? cus / 32 : 1;
-  const int side1 = n_xcd > 1 ? n_xcd : 1;  // dealt to the XCD of workgroup 0
+  // workgroup n_xcd is dealt to the XCD of workgroup 0, workgroup 1 to the next
+  const int side1 = cross_xcd || n_xcd == 1 ? 1 : n_xcd;
   hipLaunchKernelGGL(pingpong_kernel, dim3(side1 + 1), dim3(64), 0, s, slots, call, iters, scope,
                      limit, out, side1);
   return hipGetLastError();
