@@ -20,6 +20,8 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
                                           baseline / two-stream, median p10 p90)
        python bench.py --sweep large     (one JSON line: static reducer counts
                                           0..64 against the adaptive controller)
+       python bench.py --litmus 10000000 (one JSON line: flag hand-off latency and
+                                          stale reads per protocol)
        python bench.py --trace attn --trace-inplace 0
                                          (one JSON line: the controller's trace
                                           and the device-timer role breakdown)
@@ -214,6 +216,31 @@ def trace(name, inplace):
                       "updates": t.n_updates, "trace": pts}), flush=True)
 
 
+def litmus(n):
+    """The tile-flag message-passing litmus (mk_flag_handoff) n times for each
+    protocol, on one XCD and across two: ns per hand-off and stale data reads."""
+    import torch
+
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    res = []
+    for scope, name in ((2, "fused protocol (stores complete, relaxed flag, agent acquire)"),
+                        (1, "agent-scope release/acquire"),
+                        (0, "workgroup-scope invalidate only")):
+        for cross in (False, True):
+            left, ns_sum, stale, xcds = n, 0.0, 0, None
+            while left > 0:  # calls of at most 2^24 hand-offs
+                k = min(left, 1 << 24)
+                ns, st, xcds = mk.flag_handoff(k, scope, cross)
+                ns_sum += ns * k
+                stale += st
+                left -= k
+            res.append({"protocol": name, "flag_scope": scope, "xcds": list(xcds),
+                        "trials": n, "ns_per_handoff": round(ns_sum / n, 1), "stale": stale})
+    print(json.dumps({"mode": "litmus", "results": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +255,8 @@ def main():
     ap.add_argument("--trace", metavar="WORKLOAD",
                     help="one call with telemetry; --trace-inplace 0 hands every tile over")
     ap.add_argument("--trace-inplace", type=int, default=-1)
+    ap.add_argument("--litmus", type=int, metavar="N",
+                    help="flag message-passing litmus, N hand-offs per protocol and placement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the fused kernel; runs on more than one "
@@ -241,6 +270,9 @@ def main():
         return
     if args.trace:
         trace(args.trace, args.trace_inplace)
+        return
+    if args.litmus:
+        litmus(args.litmus)
         return
 
     import torch
