@@ -628,3 +628,37 @@ def test_ksplit_on_a_decode_shard(variant):
             check_tolerance(got, C64, "bf16", f"k-split {key}")
     check_exact(outs[(-1, "adaptive")], outs[(2, "0")], "split calls agree bitwise")
     check_exact(outs[(1, "adaptive")], outs["baseline"], "unsplit call against the baseline")
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two fused calls (and an AllGather share) in flight at once on two streams,
+    each with its own workspace and each sized for the whole GPU: every wait is on
+    work claimed by a running workgroup, so neither can stall the other; integer
+    inputs stay bit-exact."""
+    announce("concurrent calls on two streams")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = []
+    for seed, (M, N, K, npeer) in ((41, (1024, 2048, 576, 7)), (42, (768, 1024, 1792, 15))):
+        A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", seed, device="cpu")
+        _, want = oracle_rows(A, B, peers, "bf16")
+        cases.append((A.to(DEV), B.to(DEV), peers.to(DEV), want, new_c(M, N, "bf16")))
+    shards, Bag = mk_inputs.make_ag_inputs(256, 4, 1024, 512, "integer", 43, device="cpu")
+    A_loc, peers_A = mk_inputs.shard_split(shards, 2)
+    f_want, _, c_want = oracle.gemm_ag(mk_inputs.bits(A_loc), mk_inputs.bits(peers_A), 2,
+                                       mk_inputs.bits(Bag), "bf16")
+    A_loc, peers_A, Bag = A_loc.to(DEV), peers_A.to(DEV), Bag.to(DEV)
+    A_full, C_ag = ag_poisoned(1024, 1024, 512, "bf16")
+    torch.cuda.synchronize()
+    for rep in range(5):
+        (A1, B1, P1, _, C1), (A2, B2, P2, _, C2) = cases
+        with torch.cuda.stream(s1):
+            mk.gemm_ar_local(A1, B1, P1, C1, stream=s1)
+            mk.gemm_ag_local(A_loc, peers_A, A_full, Bag, C_ag, 2, stream=s1)
+        with torch.cuda.stream(s2):
+            mk.gemm_ar_local(A2, B2, P2, C2, stream=s2)
+        mk.stream_status(s1)
+        mk.stream_status(s2)
+        for i, (_, _, _, want, C) in enumerate(cases):
+            check_exact(c_bits(C), want, f"stream call {i}, repetition {rep}")
+        check_exact(mk_inputs.bits(A_full), f_want, f"gathered matrix, repetition {rep}")
+        check_exact(c_bits(C_ag), c_want, f"AllGather C, repetition {rep}")
