@@ -26,6 +26,11 @@
  * faster path for most tiles, and by default only the first tiles of each
  * XCD's queue of a memory-bound shape are handed to reducers.
  *
+ * The same library holds the shares of two more kernels of that Table 3
+ * (GEMM + ReduceScatter, AllGather + GEMM: mk_gemm_rs_local, mk_gemm_ag_local),
+ * the two-kernel and two-stream comparison schedules, and a flag hand-off
+ * microbenchmark.
+ *
  * Layout of every tensor argument: dense, row-major, 16-byte aligned device
  * memory owned by the caller:
  *   A      [M, K]            bfloat16
@@ -36,7 +41,10 @@
  * (peers[0] + peers[1] + ...), then the local fp32 partial is added; the sum is
  * rounded once to c_dtype, round to nearest even (with no peers, C is the
  * rounded partial). The result is bitwise identical for every reducer count,
- * every option below, the adaptive controller and the two-kernel baseline.
+ * every option below, the adaptive controller and the two-kernel baseline,
+ * except where a tile is computed as two k-halves (MK_OPT_KSPLIT, automatic for
+ * few-tile shapes): its local partial is then the float32 sum of the halves'
+ * partials, which can differ from one k-loop in the last bit.
  *
  * Supported shapes: M >= 0 (any), N and K multiples of 8 (16-byte rows),
  * N <= 4194304 (2^22).
@@ -54,6 +62,8 @@
  * dereferences device pointers, so it runs without touching the GPU. Errors
  * raised on the device (a reducer wait that exceeded its time limit) are
  * reported by mk_stream_status(). mk_last_error() gives a thread-local text.
+ * Every device-side wait is bounded (MK_OPT_SPIN_TIMEOUT_US), so a stuck
+ * hand-off ends the kernel with MK_ERR_TIMEOUT rather than hanging it.
  */
 #ifndef MK_H_
 #define MK_H_
@@ -69,10 +79,10 @@ typedef enum {
   MK_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad dtype, negative size, aliasing */
   MK_ERR_UNSUPPORTED = 2, /* valid but outside the supported envelope (N or K not %8) */
   MK_ERR_HIP = 3,         /* a HIP runtime call failed; see mk_last_error() */
-  MK_ERR_TIMEOUT = 4,     /* a reducer waited on a tile flag past its time limit */
+  MK_ERR_TIMEOUT = 4,     /* a device-side wait (tile flag, landed piece) passed its limit */
   MK_ERR_NO_DEVICE = 5,   /* no usable gfx950 device */
   MK_ERR_WORKSPACE = 6,   /* workspace allocation failed */
-  MK_ERR_INTERNAL = 7     /* the fused kernel ended with tiles left unreduced */
+  MK_ERR_INTERNAL = 7     /* a persistent kernel ended with work left undone */
 } mk_status_t;
 
 typedef enum { MK_DT_BF16 = 0, MK_DT_F32 = 1 } mk_dtype_t;
