@@ -7,7 +7,10 @@ thelatestinai.com page). Bars:
     that bound plus half a bfloat16 ulp for bf16 C);
   - the output is bitwise identical for every reducer count, for the adaptive
     controller, for every reduce schedule (tiles reduced in place, handed over,
-    peers summed early) and for the baseline (all reduce in the same order).
+    peers summed early) and for the baseline (all reduce in the same order),
+    except that a tile computed as two k-halves (MK_OPT_KSPLIT) sums the halves'
+    fp32 partials: such calls agree among themselves, and the baseline is matched
+    with the split off.
 Full-size workloads are checked on sampled rows (first, last and one random row of
 every 256-row band), with the oracle evaluating those rows only.
 """
