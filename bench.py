@@ -20,6 +20,8 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
                                           baseline / two-stream, median p10 p90)
        python bench.py --sweep large     (one JSON line: static reducer counts
                                           0..64 against the adaptive controller)
+       python bench.py --cpu-oracle      (one JSON line: the CPU oracle's GFLOP/s on
+                                          every workload and the host's threads)
        python bench.py --litmus 10000000 (one JSON line: flag hand-off latency and
                                           stale reads per protocol)
        python bench.py --trace attn --trace-inplace 0
@@ -241,6 +243,45 @@ def litmus(n):
     print(json.dumps({"mode": "litmus", "results": res}), flush=True)
 
 
+def cpu_oracle(budget_s=8.0):
+    """The CPU oracle's throughput on every workload: all host threads (rows
+    sampled evenly to about budget_s seconds where the whole shard would take
+    longer), and one thread for the tiny and decode shards (whole shard)."""
+    import numpy as np
+
+    import mk_inputs
+    import oracle
+
+    threads = oracle.max_threads()
+    res = {}
+    for w in mk_inputs.WORKLOADS:
+        A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cpu")
+        Bb = mk_inputs.bits(B)
+
+        def run_rows(rows, nthreads):
+            Ab = mk_inputs.bits(A[rows])
+            Pb = mk_inputs.bits(peers[:, rows, :])
+            t0 = time.perf_counter()
+            oracle.gemm_ar(Ab, Bb, Pb, w.c_dtype, threads=nthreads)
+            return time.perf_counter() - t0
+
+        r = {}
+        for nthreads in ([threads, 1] if w.name in ("tiny", "decode") else [threads]):
+            probe = list(range(min(w.M, max(nthreads, 8))))
+            t = run_rows(probe, nthreads)
+            n = int(min(w.M, len(probe) * budget_s / max(t, 1e-4)))
+            n = max(len(probe), n)
+            rows = sorted(set(np.linspace(0, w.M - 1, n).astype(int).tolist()))
+            t = run_rows(rows, nthreads)
+            r[f"threads_{nthreads}"] = {
+                "GFLOPs": round(2.0 * len(rows) * w.N * w.K / t / 1e9, 2),
+                "rows": len(rows), "of_rows": w.M, "seconds": round(t, 2)}
+        res[w.name] = r
+        del A, B, peers
+    print(json.dumps({"mode": "cpu-oracle", "host_threads": threads, "results": res}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +296,9 @@ def main():
     ap.add_argument("--trace", metavar="WORKLOAD",
                     help="one call with telemetry; --trace-inplace 0 hands every tile over")
     ap.add_argument("--trace-inplace", type=int, default=-1)
+    ap.add_argument("--cpu-oracle", action="store_true",
+                    help="the CPU oracle's GFLOP/s on every workload (all threads; one "
+                         "thread for tiny and decode)")
     ap.add_argument("--litmus", type=int, metavar="N",
                     help="flag message-passing litmus, N hand-offs per protocol and placement")
     args = ap.parse_args()
@@ -273,6 +317,9 @@ def main():
         return
     if args.litmus:
         litmus(args.litmus)
+        return
+    if args.cpu_oracle:
+        cpu_oracle()
         return
 
     import torch
