@@ -244,7 +244,8 @@ def litmus(n):
 
 
 def cpu_oracle(budget_s=8.0):
-    """The CPU oracle's throughput on every workload: all host threads (rows
+    """The cpu_baseline leg for every workload: the CPU oracle's throughput with
+    all host threads (rows
     sampled evenly to about budget_s seconds where the whole shard would take
     longer), and one thread for the tiny and decode shards (whole shard)."""
     import numpy as np
