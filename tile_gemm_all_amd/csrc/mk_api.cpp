@@ -939,15 +939,16 @@ mk_status_t mk_gemm_ag_local(const void* A_local, const void* peers_A, int n_pee
   }
   int n_xcd = info.cus / 32;
   n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
-  // Pieces: at most kAgMaxPieces per band, each a whole number of 32-column
-  // k-tiles, so that a k-tile never waits for two pieces. A tile may read a piece
-  // while the next ones are still landing only if no 128-byte line holds bytes
-  // of two pieces: A_full 128-byte aligned, rows and piece widths multiples of
-  // 64 columns. Otherwise a tile waits for every piece of its band.
+  // Pieces: at most kAgMaxPieces per band, each a whole number of 64-column
+  // steps (the deepest k-tile), so that a k-tile never waits for two pieces. A
+  // tile may read a piece while the next ones are still landing only if no
+  // 128-byte line holds bytes of two pieces: A_full 128-byte aligned, rows and
+  // piece widths multiples of 64 columns. Otherwise a tile waits for every piece
+  // of its band.
   const int64_t kt_total = (K + 31) / 32;
   int64_t ktpp = (kt_total + 7) / 8;  // about eight pieces per band
   const bool lines_ok = ((uintptr_t)A_full) % 128 == 0 && K % 64 == 0;
-  if (lines_ok && ktpp % 2 == 1) ktpp += 1;
+  if (ktpp % 2 == 1) ktpp += 1;
   mk::AgArgs a;
   memset(&a, 0, sizeof a);
   a.A_local = (const uint16_t*)A_local;

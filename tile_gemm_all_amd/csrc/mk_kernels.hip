@@ -556,10 +556,11 @@ struct AgGate {
   const int* flags;   // this band's piece flags
   unsigned long long* S;
   unsigned long long limit;
-  int ktpp;           // k-tiles per piece
+  int ktpp;           // 32-column k-steps per piece
   int npc;            // pieces of the band
   int all;            // 1: wait for every piece at the first k-tile
   int ready;          // pieces [0, ready] have landed
+  int kmul;           // 32-column k-steps per k-tile of the GEMM
   // The flag is read by a scalar load that misses the scalar cache (its count
   // is lgkmcnt), so the k-loop's direct loads in flight need not drain first, as
   // they would behind a vector load of the flag.
@@ -569,7 +570,10 @@ struct AgGate {
     return v;
   }
   __device__ __forceinline__ void operator()(int kt) {
-    const int kp = all ? npc - 1 : kt / ktpp;
+    // the piece that holds the k-tile's last 32 columns (a piece is a whole
+    // number of k-tiles when pieces are gated one by one)
+    int kp = all ? npc - 1 : (kt * kmul + kmul - 1) / ktpp;
+    if (kp > npc - 1) kp = npc - 1;
     for (int p = ready + 1; p <= kp; ++p) {
       const unsigned long long w0 = ticks();
       while (poll(flags + p) == 0) {
@@ -749,7 +753,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
       if (sh == a.rank) {
         g.run(a.A_local, a.B, a.Ms, a.N, a.K, rs, n0, lds);
       } else {
-        AgGate gate{a.landed + gb * kAgMaxPieces, S, a.spin_limit, a.ktpp, a.npc, !a.inloop, -1};
+        AgGate gate{a.landed + gb * kAgMaxPieces, S, a.spin_limit, a.ktpp, a.npc, !a.inloop, -1,
+                    Cfg::BK / 32};
         g.run(a.A_full, a.B, a.M, a.N, a.K, m0, n0, lds, gate);
       }
       store_tile_c<Cfg, CT>(g, lds, (CT*)a.C, a.M, a.N, m0, n0);
@@ -933,7 +938,7 @@ __global__ void clear_error_kernel(unsigned long long* slots) {
 
 // ------------------------------------------------------------ host-side launchers
 
-using T256 = TileCfg<256, 256>;
+using T256 = TileCfg<256, 256, 64, 2>;  // 64-deep k-tiles, two LDS stages
 using T128 = TileCfg<128, 128>;
 
 template <class Cfg>
