@@ -245,6 +245,43 @@ def test_inplace_reduce_matches_published(shape):
         check_exact(got_rows, want, f"in-place {key} against the oracle")
 
 
+TILE256_SHAPES = [  # M, N, K, n_peers, peer dtype, C dtype; ragged against 256 x 256 x 64
+    (300, 264, 200, 3, "bf16", "bf16"),      # ragged M, N and K (K: three k-tiles and a tail)
+    (520, 776, 1032, 1, "bf16", "f32"),      # K = 16 k-tiles and 8 columns
+    (257, 520, 576, 7, "f32", "bf16"),       # k-halves of 288: a half ends inside a k-tile
+    (512, 512, 640, 15, "bf16", "bf16"),     # whole tiles, k-halves of 320
+]
+
+
+@pytest.mark.parametrize("shape", TILE256_SHAPES, ids=lambda s: "x".join(map(str, s[:4])))
+def test_256_tiles_on_ragged_shapes(shape):
+    """The 256 x 256 tile (64-deep k-tiles, two LDS stages) on shapes ragged in M, N
+    and K: integer inputs stay exact against the oracle under the default policy,
+    with every tile handed over, with early reduce, with early reduce and k-halves,
+    and in the two-kernel baseline."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"256 tiles {shape}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 71, device="cpu")
+    _, want = oracle_rows(A, B, peers, cdt)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    opts = (mk.OPT_TILE_SHAPE, mk.OPT_INPLACE, mk.OPT_EARLY, mk.OPT_KSPLIT)
+    old = [mk.get_option(o) for o in opts]
+    try:
+        mk.set_option(mk.OPT_TILE_SHAPE, 1)
+        for inplace, early, ks in ((-1, -1, -1), (0, 0, 1), (0, 1, 1), (0, 1, 2)):
+            if ks == 2 and K % 64 != 0:
+                continue
+            mk.set_option(mk.OPT_INPLACE, inplace)
+            mk.set_option(mk.OPT_EARLY, early)
+            mk.set_option(mk.OPT_KSPLIT, ks)
+            for mode in ("adaptive", "0", "baseline"):
+                C = run(A, B, peers, cdt, mode)
+                check_exact(c_bits(C), want, f"{shape} inplace {inplace} early {early} ksplit {ks} {mode}")
+    finally:
+        for o, v in zip(opts, old):
+            mk.set_option(o, v)
+
+
 def test_back_to_back_alternating_inputs(inplace_policy):
     """Reducers must never read a partial before its flag: alternate two input sets so
     that any early read would pick up the other set's partial."""
