@@ -395,6 +395,17 @@ def main():
     base_ms = timed(two_kernel, args.steps, cw)
     # stream overlap: per-chunk GEMM kernels, per-chunk reduces on a second stream
     two_stream_ms = timed(two_stream, args.steps, cw)
+    # the same schedule on CU-masked streams: GEMM and reduce kernels on disjoint
+    # compute units, for each split the device allows (multiples of 64 of 256)
+    masked = {}
+    n_cus = mk.num_workgroups()
+    old_split = mk.get_option(mk.OPT_STREAM_CU_SPLIT)
+    try:
+        for split in range(n_cus // 4, n_cus, n_cus // 4):
+            mk.set_option(mk.OPT_STREAM_CU_SPLIT, split)
+            masked[str(split)] = round(timed(two_stream, args.steps, cw), 5)
+    finally:
+        mk.set_option(mk.OPT_STREAM_CU_SPLIT, old_split)
     rs_base_ms = timed(rs_baseline, args.steps, cw)
     rs_ms = timed(rs_fused, args.steps, cw)
     ag_base_ms = timed(ag_baseline, args.steps, cw)
@@ -437,6 +448,8 @@ def main():
         "speedup_vs_two_kernel": round(base_ms / fused_ms, 4),
         "two_stream_ms": round(two_stream_ms, 5),
         "speedup_vs_two_stream": round(two_stream_ms / fused_ms, 4),
+        "two_stream_cu_masked_ms": {"by_reduce_cus": masked,
+                                    "best": min(masked.values()) if masked else None},
         "handover_all_ms": round(handover_ms, 5),
         "reduce_scatter": {"owned_rows": [o0, o1], "fused_ms": round(rs_ms, 5),
                            "baseline_ms": round(rs_base_ms, 5),

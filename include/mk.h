@@ -166,6 +166,11 @@ mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const voi
  * the (device, stream) workspace. The call is ordered on `stream` like the
  * others: every reduce waits for an event recorded on `stream` after its
  * chunk's GEMM, and `stream` waits for the last reduce.
+ * With MK_OPT_STREAM_CU_SPLIT = R > 0 the two streams partition the chip
+ * instead of sharing it (AMD CU-masked streams, the static counterpart of the
+ * role split): the GEMM kernels run on a library stream masked to all but R
+ * compute units and the reduce kernels on one masked to the other R; the GEMM
+ * stream first waits for an event recorded on `stream`.
  *   n_chunks : 0 = automatic (4), else 1..MK_MAX_CHUNKS; at most the number of
  *              tile rows (the tile shape is chosen as for the fused kernel).
  * Other arguments and result as mk_gemm_ar_local (bitwise: the same GEMM tile
@@ -320,13 +325,21 @@ typedef enum {
                                    few-tile decode shapes; the grid then holds one workgroup per
                                    tile plus one per unit, and tiles are handed over rather than
                                    reduced in place), 0 = off, 1 = on. Peer counts 1-4, 7, 8, 15. */
-  MK_OPT_KSPLIT = 8             /* with early reduce and every tile handed over: each tile computed
+  MK_OPT_KSPLIT = 8,            /* with early reduce and every tile handed over: each tile computed
                                    as two k-halves (two workgroups, two fp32 partials, a flag each;
                                    the reducer adds P0 + P1 to the peer sum). -1 = automatic (on
                                    when K is a multiple of 64, at least 512, and two items per tile
                                    plus the reduce units fit one round), 1 = off, 2 = on (K a
                                    multiple of 64). The fp32 rounding of P0 + P1 differs from one
                                    k-loop, so C can differ from the baseline in the last bit. */
+  MK_OPT_STREAM_CU_SPLIT = 9    /* mk_gemm_ar_two_stream: compute units given to the reduce stream
+                                   when the two streams are CU-masked; the GEMM stream gets the
+                                   rest. 0 = no masks (default: both streams share the chip). R > 0
+                                   must be below the device's compute units and a multiple of 8
+                                   per 32-unit mask word (64 on a 256-unit MI355X), so that every
+                                   word, whichever XCD its units sit on, gives the reduce stream
+                                   the same share; checked at the call (MK_ERR_INVALID_ARG). Each
+                                   word's top R/words bits go to the reduce stream. */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

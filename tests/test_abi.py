@@ -240,3 +240,20 @@ def test_ksplit_option_accepts_only_auto_off_and_two():
             assert mk.get_option(mk.OPT_KSPLIT) == v
     finally:
         mk.set_option(mk.OPT_KSPLIT, old)
+
+
+def test_stream_cu_split_option_takes_multiples_of_eight():
+    """The two-stream CU split is 0 (no masks) or a multiple of 8 compute units;
+    whether it fits the device (below its unit count, 8 per mask word) is checked
+    at the call."""
+    old = mk.get_option(mk.OPT_STREAM_CU_SPLIT)
+    assert old == 0
+    try:
+        for v in (-8, 7, 60, 4104):
+            with pytest.raises(mk.MkError):
+                mk.set_option(mk.OPT_STREAM_CU_SPLIT, v)
+        for v in (0, 64, 128, 192, 72):
+            mk.set_option(mk.OPT_STREAM_CU_SPLIT, v)
+            assert mk.get_option(mk.OPT_STREAM_CU_SPLIT) == v
+    finally:
+        mk.set_option(mk.OPT_STREAM_CU_SPLIT, old)

@@ -427,6 +427,41 @@ def test_two_stream_schedule_matches_baseline(shape):
         check_exact(c_bits(C, rows), want, f"{chunks} chunks against the oracle")
 
 
+@pytest.mark.parametrize("shape", TWO_STREAM_SHAPES[1:4], ids=lambda s: "x".join(map(str, s)))
+def test_two_stream_cu_masked_matches_baseline(shape):
+    """The two-stream schedule on CU-masked streams (MK_OPT_STREAM_CU_SPLIT: the
+    GEMM and reduce kernels on disjoint sets of compute units) gives the baseline's
+    bits for several splits, switched between calls and back to unmasked streams;
+    integer inputs stay exact against the oracle. A split that does not fit the
+    device is refused at the call."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"two-stream CU-masked {shape}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 83, device="cpu")
+    rows = sample_rows(M)
+    _, want = oracle_rows(A, B, peers, cdt, rows)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    ref = c_bits(run(A, B, peers, cdt, "baseline"))
+    cus = mk.num_workgroups()  # resident 256x256 workgroups: one per compute unit
+    old = mk.get_option(mk.OPT_STREAM_CU_SPLIT)
+    try:
+        for split in (cus // 4, cus // 2, 3 * cus // 4, cus // 4, 0):
+            mk.set_option(mk.OPT_STREAM_CU_SPLIT, split)
+            for chunks in (0, 3):
+                C = new_c(M, N, cdt)
+                mk.gemm_ar_two_stream(A, B, peers, C, n_chunks=chunks)
+                mk.stream_status()
+                check_exact(c_bits(C), ref, f"split {split}, {chunks} chunks against the baseline")
+                check_exact(c_bits(C, rows), want, f"split {split}, {chunks} chunks against the oracle")
+        for bad in (cus // 4 + 8, cus):
+            mk.set_option(mk.OPT_STREAM_CU_SPLIT, bad)
+            C = new_c(M, N, cdt)
+            with pytest.raises(mk.MkError):
+                mk.gemm_ar_two_stream(A, B, peers, C)
+    finally:
+        mk.set_option(mk.OPT_STREAM_CU_SPLIT, old)
+    mk.stream_status()
+
+
 def test_two_stream_then_fused_on_one_stream():
     """The two schedules share the stream's partial buffer: back-to-back calls with
     alternating inputs must each see only their own partials."""

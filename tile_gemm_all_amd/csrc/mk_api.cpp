@@ -9,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <vector>
 #include <string>
 #include <utility>
 
@@ -46,6 +47,7 @@ struct Options {
   int64_t inplace = -1;     // -1: automatic; 0: none; n: the last n tiles of each XCD's queue
   int64_t early = -1;       // reducers sum a unit's peers before its tile is finished: -1 auto
   int64_t ksplit = -1;      // early-reduce tiles computed as two k-halves: -1 auto, 1 off, 2 on
+  int64_t stream_cu_split = 0;  // two-stream schedule: compute units of the reduce stream (0: no masks)
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -122,6 +124,12 @@ struct Workspace {
   // two-stream schedule: the reduce stream and its events (created on first use)
   hipStream_t s2 = nullptr;
   hipEvent_t ev[MK_MAX_CHUNKS + 1] = {};
+  // ... and, with MK_OPT_STREAM_CU_SPLIT, the CU-masked GEMM and reduce streams
+  // for the split they were made for, and the event that orders the GEMM
+  // stream after the caller's stream
+  hipStream_t sg_mask = nullptr, sr_mask = nullptr;
+  int64_t mask_split = 0;
+  hipEvent_t ev_start = nullptr;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
@@ -130,6 +138,9 @@ void free_ws(Workspace* w) {
   for (hipEvent_t e : w->ev)
     if (e) (void)hipEventDestroy(e);
   if (w->s2) (void)hipStreamDestroy(w->s2);
+  if (w->sg_mask) (void)hipStreamDestroy(w->sg_mask);
+  if (w->sr_mask) (void)hipStreamDestroy(w->sr_mask);
+  if (w->ev_start) (void)hipEventDestroy(w->ev_start);
   if (w->P) (void)hipFree(w->P);
   if (w->flags) (void)hipFree(w->flags);
   if (w->ag_landed) (void)hipFree(w->ag_landed);
@@ -651,6 +662,58 @@ mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const voi
   return MK_OK;
 }
 
+// CU-masked GEMM and reduce streams of the two-stream schedule for a split of
+// `split` compute units to the reduce stream, made on first use and again when
+// the split changes. Each 32-unit mask word gives its top split/words bits to
+// the reduce stream and the rest to the GEMM stream. Whether the device numbers
+// its units XCD by XCD or interleaves them over the XCDs, every XCD then holds
+// the same share of each stream (split/words is a multiple of 8, the XCD count).
+// Caller holds g_ws_mu.
+mk_status_t masked_streams(Workspace* w, int cus, int64_t split) {
+  const int words = (cus + 31) / 32;
+  if (cus % 32 != 0 || split >= cus || split % (8 * words) != 0)
+    return fail(MK_ERR_INVALID_ARG,
+                "stream CU split %lld: needs a multiple of %d below %d compute units",
+                (long long)split, 8 * words, cus);
+  if (w->mask_split == split && w->sg_mask && w->sr_mask) return MK_OK;
+  hipError_t e = hipSuccess;
+  for (hipStream_t* p : {&w->sg_mask, &w->sr_mask}) {
+    if (*p) {
+      e = hipStreamSynchronize(*p);  // earlier calls may still run on it
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      (void)hipStreamDestroy(*p);
+      *p = nullptr;
+    }
+  }
+  w->mask_split = 0;
+  const int per = (int)(split / words);
+  std::vector<uint32_t> mg(words), mr(words);
+  for (int i = 0; i < words; ++i) {
+    mr[i] = per >= 32 ? ~0u : (per == 0 ? 0u : ~0u << (32 - per));
+    mg[i] = ~mr[i];
+  }
+  // default priority, like every stream of the library
+  e = hipExtStreamCreateWithCUMask(&w->sg_mask, (uint32_t)words, mg.data());
+  if (e != hipSuccess) {
+    w->sg_mask = nullptr;
+    return hip_fail(e, "CU-masked GEMM stream");
+  }
+  e = hipExtStreamCreateWithCUMask(&w->sr_mask, (uint32_t)words, mr.data());
+  if (e != hipSuccess) {
+    w->sr_mask = nullptr;
+    return hip_fail(e, "CU-masked reduce stream");
+  }
+  if (!w->ev_start) {
+    e = hipEventCreateWithFlags(&w->ev_start, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      w->ev_start = nullptr;
+      return hip_fail(e, "event");
+    }
+  }
+  w->mask_split = split;
+  return MK_OK;
+}
+
 mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peers, int n_peers,
                                   void* C, int64_t M, int64_t N, int64_t K, int peer_dtype,
                                   int c_dtype, void* stream, int n_chunks) {
@@ -683,6 +746,20 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
       }
     }
   }
+  // GEMM kernels on sg, reduce kernels on sr: the caller's stream and the
+  // library's second stream, or two CU-masked streams of the library, the GEMM
+  // one ordered after everything already on the caller's stream.
+  hipStream_t sg = s, sr = w->s2;
+  const int64_t split = options().stream_cu_split;
+  if (split > 0) {
+    st = masked_streams(w, L.info.cus, split);
+    if (st != MK_OK) return st;
+    hipError_t e0 = hipEventRecord(w->ev_start, s);
+    if (e0 == hipSuccess) e0 = hipStreamWaitEvent(w->sg_mask, w->ev_start, 0);
+    if (e0 != hipSuccess) return hip_fail(e0, "two-stream schedule");
+    sg = w->sg_mask;
+    sr = w->sr_mask;
+  }
   // Chunks of whole tile rows: chunk i is tile rows [i*tm/c, (i+1)*tm/c).
   const int tm = (int)L.tiles_m;
   int c = n_chunks == 0 ? 4 : n_chunks;
@@ -690,9 +767,9 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
   const int BM = mk::shape_bm(L.shape);
   const int n_xcd = L.info.cus / 32;
   hipEvent_t* ev = w->ev;
-  // Every reduce waits for an event recorded on the caller's stream after its
-  // chunk's GEMM, hence after all earlier work on that stream (the previous
-  // call's reduces included, see the end): no wait is needed up front.
+  // Every reduce waits for an event recorded on the GEMM stream after its
+  // chunk's GEMM, hence after all earlier work on the caller's stream (the
+  // previous call's reduces included, see the end).
   hipError_t e = hipSuccess;
   for (int i = 0; i < c && e == hipSuccess; ++i) {
     const int64_t r0 = (int64_t)(i * (int64_t)tm / c) * BM;
@@ -709,11 +786,11 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
     g.tiles_n = (int)L.tiles_n;
     g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
     g.pad_ = 0;
-    e = mk::launch_gemm(L.shape, g, s);
+    e = mk::launch_gemm(L.shape, g, sg);
     if (e != hipSuccess) break;
     // the chunk's partial rows are complete when the GEMM kernel ends
-    e = hipEventRecord(ev[i], s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(w->s2, ev[i], 0);
+    e = hipEventRecord(ev[i], sg);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sr, ev[i], 0);
     if (e != hipSuccess) break;
     mk::ReduceArgs r;
     r.P = w->P + r0 * N;
@@ -724,10 +801,11 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
     r.peer_stride = M * N;
     r.n_peers = n_peers;
     r.pad_ = 0;
-    e = mk::launch_reduce(peer_dtype, c_dtype, r, reduce_grid(r.M * N, L.info.cus), w->s2);
+    e = mk::launch_reduce(peer_dtype, c_dtype, r, reduce_grid(r.M * N, L.info.cus), sr);
   }
   // the call ends on the caller's stream when the last reduce has finished
-  if (e == hipSuccess) e = hipEventRecord(ev[c], w->s2);
+  // (which waited for the last GEMM)
+  if (e == hipSuccess) e = hipEventRecord(ev[c], sr);
   if (e == hipSuccess) e = hipStreamWaitEvent(s, ev[c], 0);
   if (e != hipSuccess) return hip_fail(e, "two-stream schedule");
   return MK_OK;
@@ -1174,6 +1252,12 @@ mk_status_t mk_set_option(int option, int64_t value) {
         return fail(MK_ERR_INVALID_ARG, "k-split %lld", (long long)value);
       g_opt.ksplit = value;
       return MK_OK;
+    case MK_OPT_STREAM_CU_SPLIT:
+      // the device-dependent checks happen at the call
+      if (value < 0 || value > 4096 || value % 8 != 0)
+        return fail(MK_ERR_INVALID_ARG, "stream CU split %lld", (long long)value);
+      g_opt.stream_cu_split = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -1190,6 +1274,7 @@ int64_t mk_get_option(int option) {
     case MK_OPT_INPLACE: return g_opt.inplace;
     case MK_OPT_EARLY: return g_opt.early;
     case MK_OPT_KSPLIT: return g_opt.ksplit;
+    case MK_OPT_STREAM_CU_SPLIT: return g_opt.stream_cu_split;
   }
   return -1;
 }
