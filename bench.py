@@ -24,6 +24,8 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
                                           every workload and the host's threads)
        python bench.py --litmus 10000000 (one JSON line: flag hand-off latency and
                                           stale reads per protocol)
+       python bench.py --peaks           (one JSON line: measured bf16 matrix-core
+                                          and copy ceilings against published peaks)
        python bench.py --trace attn --trace-inplace 0
                                          (one JSON line: the controller's trace
                                           and the device-timer role breakdown)
@@ -218,6 +220,54 @@ def trace(name, inplace):
                       "updates": t.n_updates, "trace": pts}), flush=True)
 
 
+def peaks():
+    """Measured ceilings of the chip next to the published ones the rooflines use:
+    bf16 matrix-core throughput of register-only MFMA chains on every compute unit
+    (mk_mfma_peak) and the bandwidth of a plain elementwise copy (read + write)."""
+    import torch
+
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    stream = torch.cuda.current_stream()
+
+    def timed_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    iters = 20000
+    ms = timed_ms(lambda: mk.mfma_peak(iters, cus, out))
+    mk.stream_status()
+    flops = cus * 4 * 8 * iters * 32768
+    tf = flops / (ms * 1e-3) / 1e12
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    cms = timed_ms(lambda: torch.neg(x, out=y), reps=10)
+    gbps = 2 * x.numel() * 4 / (cms * 1e-3) / 1e9
+    print(json.dumps({
+        "mode": "peaks", "device": props.name, "compute_units": cus,
+        "mfma_bf16": {"TFLOPs": round(tf, 1), "published_dense_TFLOPs": BF16_PEAK_TFLOPS,
+                      "frac_of_published": round(tf / BF16_PEAK_TFLOPS, 3),
+                      "workgroups": cus, "iters": iters, "ms": round(ms, 3)},
+        "copy": {"GBps": round(gbps, 1), "published_GBps": HBM_PEAK_GBPS,
+                 "frac_of_published": round(gbps / HBM_PEAK_GBPS, 3),
+                 "bytes_each_way": x.numel() * 4, "ms": round(cms, 3)},
+    }), flush=True)
+
+
 def litmus(n):
     """The tile-flag message-passing litmus (mk_flag_handoff) n times for each
     protocol, on one XCD and across two: ns per hand-off and stale data reads."""
@@ -302,10 +352,12 @@ def main():
                          "thread for tiny and decode)")
     ap.add_argument("--litmus", type=int, metavar="N",
                     help="flag message-passing litmus, N hand-offs per protocol and placement")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measured ceilings: bf16 matrix-core TFLOP/s and copy GB/s")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the fused kernel; runs on more than one "
-              "GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the fused kernel and has no multi-GPU "
+              "mode (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.all_configs:
         all_configs()
@@ -321,6 +373,9 @@ def main():
         return
     if args.cpu_oracle:
         cpu_oracle()
+        return
+    if args.peaks:
+        peaks()
         return
 
     import torch

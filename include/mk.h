@@ -278,6 +278,19 @@ int mk_ag_grid(int64_t Ms, int n_peers, int64_t N, int64_t K, int c_dtype);
  */
 mk_status_t mk_flag_handoff(int iters, int flag_scope, int cross_xcd, void* stream, void* out);
 
+/*
+ * mk_mfma_peak -- the matrix-core ceiling the roofline is read against. Launches
+ * n_workgroups workgroups of 256 threads (one per compute unit at most: 256
+ * registers of accumulators per lane); each wave issues iters rounds of eight
+ * independent bf16 v_mfma_f32_32x32x16 on register operands, 32768 flops each,
+ * and no loads. Work: n_workgroups * 4 * 8 * iters * 32768 flops; the caller
+ * times the call with events on `stream` (no timing inside).
+ *   out : device buffer of n_workgroups * 256 floats (each lane's accumulator
+ *         sum, written so that no product is dead); 4-byte aligned.
+ *   iters 1 .. 2^24, n_workgroups 1 .. 65536, else MK_ERR_INVALID_ARG.
+ */
+mk_status_t mk_mfma_peak(int iters, int n_workgroups, void* out, void* stream);
+
 /* Synchronizes `stream`, then returns and clears the device error word of that
  * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
 mk_status_t mk_stream_status(void* stream);

@@ -257,3 +257,15 @@ def test_stream_cu_split_option_takes_multiples_of_eight():
             assert mk.get_option(mk.OPT_STREAM_CU_SPLIT) == v
     finally:
         mk.set_option(mk.OPT_STREAM_CU_SPLIT, old)
+
+
+@pytest.mark.parametrize("iters,grid,out,status", [
+    (0, 1, A16, mk.MK_ERR_INVALID_ARG),
+    ((1 << 24) + 1, 1, A16, mk.MK_ERR_INVALID_ARG),
+    (1, 0, A16, mk.MK_ERR_INVALID_ARG),
+    (1, (1 << 16) + 1, A16, mk.MK_ERR_INVALID_ARG),
+    (1, 1, None, mk.MK_ERR_INVALID_ARG),
+    (1, 1, A16 + 2, mk.MK_ERR_INVALID_ARG),
+])
+def test_mfma_peak_validates_before_touching_the_device(iters, grid, out, status):
+    assert mk.library().mk_mfma_peak(iters, grid, out, None) == status, mk.last_error()

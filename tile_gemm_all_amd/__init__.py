@@ -36,7 +36,7 @@ OPT_STREAM_CU_SPLIT = 9  # two-stream schedule: compute units of the CU-masked r
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_stream",
            "mk_gemm_rs_local", "mk_gemm_rs_baseline", "mk_gemm_ag_local", "mk_gemm_ag_baseline",
-           "mk_ag_grid", "mk_flag_handoff",
+           "mk_ag_grid", "mk_flag_handoff", "mk_mfma_peak",
            "mk_stream_status",
            "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
            "mk_get_option",
@@ -80,6 +80,8 @@ _lib.mk_ag_grid.argtypes = [_i64, _int, _i64, _i64, _int]
 _lib.mk_ag_grid.restype = _int
 _lib.mk_flag_handoff.argtypes = [_int, _int, _int, _vp, _vp]
 _lib.mk_flag_handoff.restype = _int
+_lib.mk_mfma_peak.argtypes = [_int, _int, _vp, _vp]
+_lib.mk_mfma_peak.restype = _int
 _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
 _lib.mk_workspace_reset.argtypes = [_int]
@@ -307,6 +309,15 @@ def flag_handoff(iters=1000, flag_scope=0, cross_xcd=False, stream=None):
     if vals[1]:
         raise MkError(MK_ERR_TIMEOUT, "flag hand-off timed out")
     return vals[0] * 10.0 / (2 * iters), vals[4], (vals[2], vals[3])
+
+
+def mfma_peak(iters, n_workgroups, out, stream=None):
+    """Launches the matrix-core ceiling kernel (n_workgroups * 4 * 8 * iters bf16
+    MFMAs of 32768 flops); out: float32 GPU tensor of n_workgroups * 256 elements.
+    Does not synchronize; time it with events on the stream."""
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < n_workgroups * 256:
+        raise ValueError("out must be a float32 GPU tensor of n_workgroups * 256 elements")
+    _check(_lib.mk_mfma_peak(int(iters), int(n_workgroups), out.data_ptr(), _stream_ptr(stream)))
 
 
 def stream_status(stream=None):

@@ -1153,6 +1153,19 @@ mk_status_t mk_flag_handoff(int iters, int flag_scope, int cross_xcd, void* stre
   return MK_OK;
 }
 
+mk_status_t mk_mfma_peak(int iters, int n_workgroups, void* out, void* stream) {
+  if (iters < 1 || iters > (1 << 24)) return fail(MK_ERR_INVALID_ARG, "iters=%d outside [1, 2^24]", iters);
+  if (n_workgroups < 1 || n_workgroups > (1 << 16))
+    return fail(MK_ERR_INVALID_ARG, "n_workgroups=%d outside [1, 65536]", n_workgroups);
+  if (!out || ((uintptr_t)out) % 4 != 0) return fail(MK_ERR_INVALID_ARG, "out is NULL or not 4-byte aligned");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  e = mk::launch_mfma_peak(iters, n_workgroups, (float*)out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "matrix-core peak kernel launch");
+  return MK_OK;
+}
+
 mk_status_t mk_stream_status(void* stream) {
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipStreamSynchronize(s);

@@ -195,5 +195,6 @@ hipError_t launch_pingpong(unsigned long long* slots, unsigned call, int iters, 
                            hipStream_t s);
 hipError_t launch_ag_copy(const AgCopyArgs& a, int grid, hipStream_t s);
 hipError_t launch_gemm_c(int shape, int ct, const GemmArgs& a, void* C, hipStream_t s);
+hipError_t launch_mfma_peak(int iters, int grid, float* out, hipStream_t s);
 
 }  // namespace mk

@@ -936,6 +936,37 @@ __global__ void clear_error_kernel(unsigned long long* slots) {
   if (threadIdx.x == 0) slots[(size_t)S_ERROR * kSlotWords] = 0ull;
 }
 
+// ------------------------------------------------------------ matrix-core peak
+
+// Matrix-core ceiling of the chip: every wave issues `iters` rounds of eight
+// independent v_mfma_f32_32x32x16_bf16 on register operands (no memory traffic
+// in the loop), then each lane stores the sum of its accumulators so that no
+// product is dead. 32768 flops per MFMA.
+__global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float* out) {
+  const int tid = threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(float)((tid + i) & 7);
+    b[i] = (__bf16)(float)((tid * 3 + i) & 7);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[j][i];
+  out[(size_t)blockIdx.x * kThreads + tid] = sum;
+}
+
 // ------------------------------------------------------------ host-side launchers
 
 using T256 = TileCfg<256, 256, 64, 2>;  // 64-deep k-tiles, two LDS stages
@@ -952,6 +983,11 @@ static const void* fused_ptr(int pt, int ct) {
 
 const void* fused_kernel_ptr(int shape, int pt, int ct) {
   return shape == SHAPE_256 ? fused_ptr<T256>(pt, ct) : fused_ptr<T128>(pt, ct);
+}
+
+hipError_t launch_mfma_peak(int iters, int grid, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(grid), dim3(kThreads), 0, s, iters, out);
+  return hipGetLastError();
 }
 
 const void* ag_kernel_ptr(int shape, int ct) {
