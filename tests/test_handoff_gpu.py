@@ -35,3 +35,22 @@ def test_flag_handoff_workgroup_scope_invalidate_completes():
     ns, stale, _ = mk.flag_handoff(1000, 0, False)
     assert 0.0 < ns < 100_000.0 and 0 <= stale <= 1000
     mk.stream_status()
+
+
+@pytest.mark.gpu
+def test_mfma_peak_runs_every_chain():
+    """The matrix-core ceiling kernel does the work it is timed for: each lane's sum
+    of its eight accumulators after n rounds is exactly n times the sum after one
+    (small integer operands, exact in fp32), and no lane's sum is zero."""
+    import torch
+    print("\n[case] mfma peak linearity", flush=True)
+    grid = 4
+    outs = {}
+    for n in (1, 3):
+        out = torch.full((grid * 256,), float("nan"), dtype=torch.float32, device="cuda")
+        mk.mfma_peak(n, grid, out)
+        mk.stream_status()
+        outs[n] = out.cpu()
+    assert torch.isfinite(outs[1]).all()
+    assert (outs[1] != 0).all()
+    assert torch.equal(outs[3], 3 * outs[1])
