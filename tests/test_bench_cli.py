@@ -1,0 +1,31 @@
+"""CPU: bench.py's command-line contract that needs no GPU. A request for more
+than one GPU is refused with a message and exit status 2 before anything touches
+a device, and the committed counter figures are read back as bench.py reports
+them."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_taken_on():
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    got = bench.measured_traffic(rec["workload"])
+    if rec["kernel_sha"] == bench.kernel_sha():
+        assert got == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    else:
+        assert got is None
+    assert bench.measured_traffic("no-such-workload") is None
