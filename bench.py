@@ -519,6 +519,9 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, peers)
     print(json.dumps(out), flush=True)
+    # free the library's workspaces (and the streams they own, CU-masked ones
+    # included) before the process exits
+    mk.workspace_reset()
 
 
 if __name__ == "__main__":
