@@ -292,12 +292,32 @@ mk_status_t mk_flag_handoff(int iters, int flag_scope, int cross_xcd, void* stre
 mk_status_t mk_mfma_peak(int iters, int n_workgroups, void* out, void* stream);
 
 /* Synchronizes `stream`, then returns and clears the device error word of that
- * stream's workspace: MK_OK or MK_ERR_TIMEOUT (or MK_ERR_HIP if the sync fails). */
+ * stream's workspace: MK_OK, MK_ERR_TIMEOUT, MK_ERR_UNSUPPORTED or
+ * MK_ERR_INTERNAL (or MK_ERR_HIP if the sync fails). */
 mk_status_t mk_stream_status(void* stream);
 
 /* Synchronizes the device and frees every workspace of `device`; the next call
  * recreates them zeroed. Use after an error. */
 mk_status_t mk_workspace_reset(int device);
+
+/*
+ * mk_queue_plan -- how a persistent launch of `grid` workgroups on a device of
+ * `cus` compute units queues its tiles, and the flag protocol that allows. A
+ * kernel takes its queue from the hardware XCD id modulo the queue count. Tiles
+ * are queued per XCD (cus / 32 queues on gfx950, 32 compute units per XCD) only
+ * when cus is a multiple of 32 and grid a multiple of cus / 32 (at most 16
+ * queues); then a tile is produced and consumed behind one L2 and the
+ * requested protocol holds. Otherwise there is one queue, and flags use
+ * agent-scope release and acquire (scope 1), which is correct across XCDs. The
+ * kernels also check at run time that each queue is served by one XCD under
+ * scope 0 (else MK_ERR_UNSUPPORTED from mk_stream_status). The same rule serves
+ * mk_gemm_ar_local, mk_gemm_rs_local and mk_gemm_ag_local.
+ *   flag_scope : the requested scope, 0 or 1 (MK_OPT_FLAG_SCOPE).
+ *   n_xcd      : out, the number of queues.
+ * Returns the scope used (0 or 1), or a negative mk_status_t for bad arguments.
+ * Touches no GPU.
+ */
+int mk_queue_plan(int cus, int grid, int flag_scope, int* n_xcd);
 
 /* G: workgroups of the fused kernel's persistent grid on `device` with its
  * large (256x256) tiles: one per compute unit. Returns a negative mk_status_t on

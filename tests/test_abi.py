@@ -269,3 +269,28 @@ def test_stream_cu_split_option_takes_multiples_of_eight():
 ])
 def test_mfma_peak_validates_before_touching_the_device(iters, grid, out, status):
     assert mk.library().mk_mfma_peak(iters, grid, out, None) == status, mk.last_error()
+
+
+@pytest.mark.parametrize("cus,grid,scope,want", [
+    (256, 256, 0, (8, 0)),    # MI355X: eight XCDs of 32 compute units, one queue each
+    (256, 512, 0, (8, 0)),
+    (256, 256, 1, (8, 1)),
+    (256, 100, 0, (1, 1)),    # grid not a multiple of the XCD count: one queue, agent scope
+    (240, 240, 0, (1, 1)),    # compute units not whole XCDs of 32: layout unknown
+    (32, 64, 0, (1, 0)),      # one XCD
+    (128, 64, 0, (4, 0)),
+    (1024, 1024, 0, (1, 1)),  # more than 16 queues: one queue, agent scope
+])
+def test_queue_plan(cus, grid, scope, want):
+    """Tiles are queued per XCD, under the XCD-local flag protocol, only where each
+    queue is served by one XCD; otherwise one queue with agent-scope flags."""
+    assert mk.queue_plan(cus, grid, scope) == want
+
+
+def test_queue_plan_rejects_bad_arguments():
+    n = ctypes.c_int(0)
+    lib = mk.library()
+    assert lib.mk_queue_plan(0, 256, 0, ctypes.byref(n)) == -mk.MK_ERR_INVALID_ARG
+    assert lib.mk_queue_plan(256, 0, 0, ctypes.byref(n)) == -mk.MK_ERR_INVALID_ARG
+    assert lib.mk_queue_plan(256, 256, 2, ctypes.byref(n)) == -mk.MK_ERR_INVALID_ARG
+    assert lib.mk_queue_plan(256, 256, 0, None) == -mk.MK_ERR_INVALID_ARG

@@ -38,7 +38,8 @@ EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_s
            "mk_gemm_rs_local", "mk_gemm_rs_baseline", "mk_gemm_ag_local", "mk_gemm_ag_baseline",
            "mk_ag_grid", "mk_flag_handoff", "mk_mfma_peak",
            "mk_stream_status",
-           "mk_workspace_reset", "mk_num_workgroups", "mk_fused_grid", "mk_set_option",
+           "mk_workspace_reset", "mk_queue_plan", "mk_num_workgroups", "mk_fused_grid",
+           "mk_set_option",
            "mk_get_option",
            "mk_controller_eval", "mk_status_string", "mk_last_error", "mk_version"]
 
@@ -86,6 +87,8 @@ _lib.mk_stream_status.argtypes = [_vp]
 _lib.mk_stream_status.restype = _int
 _lib.mk_workspace_reset.argtypes = [_int]
 _lib.mk_workspace_reset.restype = _int
+_lib.mk_queue_plan.argtypes = [_int, _int, _int, ctypes.POINTER(_int)]
+_lib.mk_queue_plan.restype = _int
 _lib.mk_num_workgroups.argtypes = [_int]
 _lib.mk_num_workgroups.restype = _int
 _lib.mk_fused_grid.argtypes = [_i64, _i64, _i64, _int, _int, _int]
@@ -328,6 +331,17 @@ def stream_status(stream=None):
 def workspace_reset(device=None):
     dev = torch.cuda.current_device() if device is None else int(device)
     _check(_lib.mk_workspace_reset(dev))
+
+
+def queue_plan(cus, grid, flag_scope=0):
+    """(tile queues, flag scope) of a persistent launch of `grid` workgroups on a device
+    of `cus` compute units: one queue per 32-unit XCD with the requested scope, or one
+    queue with agent-scope flags where the device's layout is not known."""
+    n = _int(0)
+    s = _lib.mk_queue_plan(int(cus), int(grid), int(flag_scope), ctypes.byref(n))
+    if s < 0:
+        _check(-s)
+    return n.value, s
 
 
 def num_workgroups(device=None):

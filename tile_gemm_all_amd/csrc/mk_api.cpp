@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -148,6 +149,20 @@ void free_ws(Workspace* w) {
   delete w;
 }
 
+// Every workspace (and the streams and events it owns, CU-masked ones
+// included) is released when the process exits normally, before the HIP
+// runtime's own teardown: the handler is registered after the runtime has
+// initialised, and exit handlers run in reverse order of registration.
+void release_all_workspaces() {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto& kv : g_ws) {
+    (void)hipSetDevice(kv.first.first);
+    free_ws(kv.second);
+  }
+  g_ws.clear();
+}
+std::once_flag g_exit_once;
+
 // Returns the workspace of (dev, stream) with room for P_elems partials and
 // n_tiles flags; caller holds g_ws_mu.
 mk_status_t get_ws(int dev, hipStream_t s, size_t P_elems, int n_tiles, Workspace** out) {
@@ -155,6 +170,7 @@ mk_status_t get_ws(int dev, hipStream_t s, size_t P_elems, int n_tiles, Workspac
   Workspace* w;
   auto it = g_ws.find(key);
   if (it == g_ws.end()) {
+    std::call_once(g_exit_once, [] { std::atexit(release_all_workspaces); });
     w = new Workspace();
     w->device = dev;
     hipError_t e = hipMalloc(&w->slots, sizeof(unsigned long long) * mk::S_COUNT * mk::kSlotWords);
@@ -473,47 +489,84 @@ int ag_grid_size(const DeviceInfo& info, int shape, int c_dtype, int64_t T) {
   return want < full ? (int)want : full / n_xcd * n_xcd;
 }
 
-}  // namespace
 
-extern "C" {
+// ------------------------------------------------------------ fused AllReduce plan
 
-mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, int n_peers, void* C,
-                             int64_t M, int64_t N, int64_t K, int peer_dtype, int c_dtype,
-                             void* stream, int n_reduce_wg, void* telemetry) {
+// Arguments of one fused AllReduce call, checked.
+struct ArCall {
+  const void *A, *B, *peers;
+  void* C;
+  int64_t M, N, K;
+  int n_peers, peer_dtype, c_dtype, n_reduce_wg;
+  void* telemetry;
+  Launch L;
+};
+
+mk_status_t ar_prepare(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                       int64_t M, int64_t N, int64_t K, int peer_dtype, int c_dtype,
+                       int n_reduce_wg, void* telemetry, ArCall& c) {
   mk_status_t st = validate(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype);
   if (st != MK_OK) return st;
   if (n_reduce_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d", n_reduce_wg);
   if (((uintptr_t)telemetry) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "telemetry not 16-byte aligned");
-  Launch L;
-  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, c.L);
   if (st != MK_OK) return st;
-  const int G = fused_grid_size(L, n_peers, peer_dtype, c_dtype);
+  c.A = A;
+  c.B = B;
+  c.peers = peers;
+  c.C = C;
+  c.M = M;
+  c.N = N;
+  c.K = K;
+  c.n_peers = n_peers;
+  c.peer_dtype = peer_dtype;
+  c.c_dtype = c_dtype;
+  c.n_reduce_wg = n_reduce_wg;
+  c.telemetry = telemetry;
+  // the reducer count is checked against the grid of the default plan
+  const int G = fused_grid_size(c.L, n_peers, peer_dtype, c_dtype);
   if (n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
-  if (M == 0 || N == 0) return MK_OK;
-  hipStream_t s = (hipStream_t)stream;
+  return MK_OK;
+}
+
+// Decides the grid, the in-place policy, early reduce, the k-split and the
+// controller's seed and cap of a call, and fills every argument of the fused
+// kernel but the workspace (P, flags, slots, epoch). all_inplace: every tile
+// reduced in place by the workgroup that computed it (no partial in memory, no
+// early reduce or k-split), for peer counts that allow it.
+mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
+  const Launch& L = c.L;
+  const int64_t M = c.M, N = c.N, K = c.K;
+  const int n_peers = c.n_peers, peer_dtype = c.peer_dtype, c_dtype = c.c_dtype;
   const Options opt = options();
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace* w = nullptr;
-  const int T = (int)(L.tiles_m * L.tiles_n);
-  const int ks = ksplit_of(L, n_peers, peer_dtype, c_dtype);  // partial slices and flags per tile
-  st = get_ws(L.dev, s, (size_t)(M * N) * ks, T * ks, &w);
-  if (st != MK_OK) return st;
-  if (++w->epoch >= 0x7FFFFFFF) {  // flags hold old epochs: restart them from zero
-    hipError_t e = mk::launch_ws_init(w->flags, w->flags_cap, nullptr, s);
-    if (e != hipSuccess) return hip_fail(e, "flag reset");
-    w->epoch = 1;
+  const bool inpl_ok =
+      mk::inplace_supported(L.shape == mk::SHAPE_256 ? 1 : 2, dt_size(peer_dtype), n_peers);
+  if (all_inplace && !inpl_ok)
+    return fail(MK_ERR_UNSUPPORTED, "tiles of %d peers of this type cannot be reduced in place",
+                n_peers);
+  const bool early = !all_inplace && early_reduce(L, n_peers, peer_dtype, c_dtype);
+  const int ks = all_inplace ? 1 : ksplit_of(L, n_peers, peer_dtype, c_dtype);
+  int G;
+  {
+    const int full = L.info.cus * L.info.occ[L.shape][peer_dtype][c_dtype];
+    int n_xcd = L.info.cus / 32;
+    if (n_xcd < 1) n_xcd = 1;
+    const int64_t T = L.tiles_m * L.tiles_n;
+    int64_t want = early ? T * (ks + mk::shape_bm(L.shape) / 64) : 2 * T;
+    want = (want + n_xcd - 1) / n_xcd * n_xcd;
+    if (want < n_xcd) want = n_xcd;
+    G = want < full ? (int)want : full;
   }
-  mk::FusedArgs a;
+  if (c.n_reduce_wg > G - 1)
+    return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", c.n_reduce_wg, G - 1);
+  const int T = (int)(L.tiles_m * L.tiles_n);
   memset(&a, 0, sizeof a);
-  a.A = (const uint16_t*)A;
-  a.B = (const uint16_t*)B;
-  a.peers = peers;
-  a.C = C;
-  a.P = w->P;
-  a.flags = w->flags;
-  a.slots = w->slots;
-  a.tel = (mk_telemetry_t*)telemetry;
+  a.A = (const uint16_t*)c.A;
+  a.B = (const uint16_t*)c.B;
+  a.peers = c.peers;
+  a.C = c.C;
+  a.tel = (mk_telemetry_t*)c.telemetry;
   a.M = M;
   a.N = N;
   a.K = K;
@@ -522,24 +575,20 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   a.tiles_n = (int)L.tiles_n;
   a.T = T;
   a.G = G;
-  a.epoch = w->epoch;
   a.seed_x = seed_share(M, N, K, n_peers, peer_dtype, c_dtype);
-  if (n_reduce_wg == MK_ADAPTIVE) {
+  if (c.n_reduce_wg == MK_ADAPTIVE) {
     a.adaptive = 1;
     int t0 = (int)lrintf(a.seed_x * (float)G);
     a.init_target = t0 < 1 ? 1 : (t0 > G - 1 ? G - 1 : t0);
   } else {
     a.adaptive = 0;
-    a.init_target = n_reduce_wg;
+    a.init_target = c.n_reduce_wg;
   }
   a.ctrl_period = opt.ctrl_period < 1 ? 1 : (int)opt.ctrl_period;
   a.withhold_tile = (int)opt.withhold_tile;
   a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
-  // one XCD per 32 compute units on gfx950; tiles are queued per XCD
-  int n_xcd = L.info.cus / 32;
-  a.n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
-  if (G % a.n_xcd != 0) a.n_xcd = 1;
-  a.flag_scope = (int)opt.flag_scope;
+  // tiles are queued per XCD where the device's layout allows it (queue_plan)
+  mk::queue_plan(L.info.cus, G, (int)opt.flag_scope, a.n_xcd, a.flag_scope);
   a.shared_lines = N % 32 != 0 ? 1 : 0;  // partial rows not whole 128-byte lines
   a.reducer_cap = (int)opt.reducer_cap;
   if (a.reducer_cap <= 0) {
@@ -563,8 +612,10 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   //    Those are handed to reducers, so that after the first round half of the
   //    workgroups start their next GEMM while the other half reduce, instead of
   //    every workgroup alternating in step. Longer queues: every tile.
-  a.early = early_reduce(L, n_peers, peer_dtype, c_dtype) ? 1 : 0;
-  if (opt.inplace < 0 && a.early) {
+  a.early = early ? 1 : 0;
+  if (all_inplace) {
+    a.n_inplace = 1 << 30;
+  } else if (opt.inplace < 0 && a.early) {
     a.n_inplace = 0;  // early reduce applies to tiles handed to reducers
   } else if (opt.inplace < 0) {
     const double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -586,8 +637,6 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   // Two k-halves only when every tile is handed to a reducer (an in-place tile
   // would reduce its own half-product).
   a.ksplit = a.early && a.n_inplace == 0 ? ks : 1;
-  const bool inpl_ok =
-      mk::inplace_supported(L.shape == mk::SHAPE_256 ? 1 : 2, dt_size(peer_dtype), n_peers);
   a.T_r = 0;
   for (int xi = 0; xi < a.n_xcd; ++xi) {
     const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
@@ -614,7 +663,39 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
       a.init_target = it;
     }
   }
-  hipError_t e = mk::launch_fused(L.shape, peer_dtype, c_dtype, a, s);
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, int n_peers, void* C,
+                             int64_t M, int64_t N, int64_t K, int peer_dtype, int c_dtype,
+                             void* stream, int n_reduce_wg, void* telemetry) {
+  ArCall c;
+  mk_status_t st = ar_prepare(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype, n_reduce_wg,
+                              telemetry, c);
+  if (st != MK_OK || M == 0 || N == 0) return st;
+  mk::FusedArgs a;
+  st = ar_plan(c, false, a);
+  if (st != MK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  // partial slices and flags per tile
+  st = get_ws(c.L.dev, s, (size_t)(M * N) * a.ksplit, a.T * a.ksplit, &w);
+  if (st != MK_OK) return st;
+  if (++w->epoch >= 0x7FFFFFFF) {  // flags hold old epochs: restart them from zero
+    hipError_t e = mk::launch_ws_init(w->flags, w->flags_cap, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "flag reset");
+    w->epoch = 1;
+  }
+  a.P = w->P;
+  a.flags = w->flags;
+  a.slots = w->slots;
+  a.epoch = w->epoch;
+  hipError_t e = mk::launch_fused(c.L.shape, peer_dtype, c_dtype, a, s);
   if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   return MK_OK;
 }
@@ -838,8 +919,6 @@ mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, in
     if (e != hipSuccess) return hip_fail(e, "flag reset");
     w->epoch = 1;
   }
-  int n_xcd = L.info.cus / 32;
-  n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
   mk::FusedArgs a;
   memset(&a, 0, sizeof a);
   a.A = (const uint16_t*)A;
@@ -862,8 +941,7 @@ mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, in
   a.ctrl_period = opt.ctrl_period < 1 ? 1 : (int)opt.ctrl_period;
   a.withhold_tile = (int)opt.withhold_tile;
   a.spin_limit = (unsigned long long)(opt.spin_timeout_us < 1 ? 1 : opt.spin_timeout_us) * 100ull;
-  a.n_xcd = G % n_xcd == 0 ? n_xcd : 1;
-  a.flag_scope = (int)opt.flag_scope;
+  mk::queue_plan(L.info.cus, G, (int)opt.flag_scope, a.n_xcd, a.flag_scope);
   a.shared_lines = N % 32 != 0 ? 1 : 0;  // partial rows not whole 128-byte lines
   a.early = 0;
   a.rs = 1;
@@ -1015,8 +1093,6 @@ mk_status_t mk_gemm_ag_local(const void* A_local, const void* peers_A, int n_pee
     if (e != hipSuccess) return hip_fail(e, "piece flag init");
     w->ag_cap = cap;
   }
-  int n_xcd = info.cus / 32;
-  n_xcd = n_xcd < 1 ? 1 : (n_xcd > mk::kMaxXcd ? mk::kMaxXcd : n_xcd);
   // Pieces: at most kAgMaxPieces per band, each a whole number of 64-column
   // steps (the deepest k-tile), so that a k-tile never waits for two pieces. A
   // tile may read a piece while the next ones are still landing only if no
@@ -1051,7 +1127,8 @@ mk_status_t mk_gemm_ag_local(const void* A_local, const void* peers_A, int n_pee
   a.tiles_n = (int)tiles_n;
   a.T = (int)(NB * tiles_n);
   a.G = G;
-  a.n_xcd = G % n_xcd == 0 ? n_xcd : 1;
+  // bands are owned per XCD where the device's layout allows it (queue_plan)
+  mk::queue_plan(info.cus, G, (int)opt.flag_scope, a.n_xcd, a.flag_scope);
   // Default: four landing workgroups per XCD (the grid's workgroups beyond the
   // tiles when it has room); the others land pieces only while the first piece
   // of their tile's band is missing.
@@ -1207,6 +1284,14 @@ mk_status_t mk_workspace_reset(int device) {
   (void)hipSetDevice(cur);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   return MK_OK;
+}
+
+int mk_queue_plan(int cus, int grid, int flag_scope, int* n_xcd) {
+  if (cus < 1 || grid < 1 || (flag_scope != 0 && flag_scope != 1) || !n_xcd)
+    return -(int)MK_ERR_INVALID_ARG;
+  int scope = 1;
+  mk::queue_plan(cus, grid, flag_scope, *n_xcd, scope);
+  return scope;
 }
 
 int mk_num_workgroups(int device) {

@@ -26,6 +26,7 @@ enum XcdSlot : int {
   X_RBC,               // reduce units done by workgroups that prefer compute (draining)
   X_CBR,               // tiles computed by workgroups that prefer reducing (helping)
   X_INPLACE,           // tiles reduced in place by the workgroup that computed them
+  X_PHYS,              // 1 + the hardware XCD id of the workgroups serving this queue (0 = none yet)
   kXcdWords
 };
 constexpr int kMaxXcd = 16;
@@ -49,7 +50,24 @@ enum Slot : int {
 constexpr int kSlotWords = 16;
 constexpr int kThreadsHost = 256;  // workgroup size of every kernel
 
+
 enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2 };
+
+// Tile queues and flag protocol of a persistent launch of G workgroups on a
+// device with `cus` compute units. gfx950 groups 32 compute units per XCD, each
+// XCD with its own L2; a kernel takes its queue from the hardware XCD id modulo
+// n_xcd. The XCD-local flag protocol (scope 0: stores complete, relaxed flag,
+// no L2 write-back) is valid only while every queue is served by workgroups of
+// one XCD: the device then has cus/32 XCDs and the grid, dealt to the XCDs in
+// turn, is a multiple of that count. Otherwise every tile goes through one
+// queue with agent-scope release and acquire (scope 1), which is correct across
+// XCDs. scope_opt is the requested scope (MK_OPT_FLAG_SCOPE).
+inline void queue_plan(int cus, int G, int scope_opt, int& n_xcd, int& scope) {
+  const int n = cus > 0 && cus % 32 == 0 ? cus / 32 : 0;
+  const bool per_xcd = n >= 1 && n <= kMaxXcd && G > 0 && G % n == 0;
+  n_xcd = per_xcd ? n : 1;
+  scope = per_xcd ? (scope_opt != 0 ? 1 : 0) : 1;
+}
 
 // Peer counts that have a compile-time reduce ring, and whether that ring fits
 // the register budget of a lane at `occ` workgroups per compute unit (peers of
@@ -163,7 +181,7 @@ struct AgArgs {
   int tiles_n, T;
   int G, n_xcd;
   int n_comm;                  // workgroups that only land pieces while any are left
-  int pad_;
+  int flag_scope;              // 0: pieces landed and read behind one XCD's L2; 1: agent scope
   unsigned long long spin_limit;  // piece-wait limit in 100 MHz ticks
 };
 

@@ -65,6 +65,19 @@ __device__ __forceinline__ void raise_error(unsigned long long* S, int code) {
   __hip_atomic_store(slot32(S, S_ABORT), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The XCD-local flag protocol needs every workgroup of a queue to run on one
+// XCD (the host's queue_plan arranges that for the device's known layout). The
+// first workgroup of queue x records its hardware XCD id; a workgroup of
+// another XCD on the same queue stops the kernel with MK_ERR_UNSUPPORTED
+// instead of exchanging tiles through two L2s. Thread 0 only.
+__device__ __forceinline__ bool same_xcd_queue(unsigned long long* S, int x, int hw_xcd) {
+  const int me = hw_xcd + 1;
+  const int prev = atomicCAS(xslot(S, x, X_PHYS), 0, me);
+  if (prev == 0 || prev == me) return true;
+  raise_error(S, MK_ERR_UNSUPPORTED);
+  return false;
+}
+
 // One controller evaluation (thread 0 of the workgroup that wins the try-lock).
 // Takes its inputs by value: the kernel's argument block must not escape to
 // memory, or every pointer read from it loses its global address space.
@@ -156,7 +169,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   const unsigned long long t_begin = ticks();
 
   // thread 0 state
-  const int x = xcc_id() % a.n_xcd;
+  const int hw_xcd = xcc_id();
+  const int x = hw_xcd % a.n_xcd;
   const int q0 = (int)(((int64_t)x * a.T) / a.n_xcd);
   const int cnt = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd) - q0;
   int rank = -1, last_kind = -1, held = -1;  // held: reserved reduce unit of this XCD
@@ -201,7 +215,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         const int rn = load_relaxed(rnext);  // next reduce unit
         // The arrival rank is taken in the first pass, in the same round trip
         // as the loads above.
-        if (rank < 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+        if (rank < 0) {
+          rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+          if (a.flag_scope == 0 && !same_xcd_queue(S, x, hw_xcd)) break;
+        }
         if (abort) break;
         const int target = (int)(tw >> 32) == a.epoch ? (int)(tw & 0xFFFFFFFFu) : a.init_target;
         const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
@@ -561,6 +578,7 @@ struct AgGate {
   int all;            // 1: wait for every piece at the first k-tile
   int ready;          // pieces [0, ready] have landed
   int kmul;           // 32-column k-steps per k-tile of the GEMM
+  int acq;            // 1: pieces may have landed on another XCD: acquire at agent scope
   // The flag is read by a scalar load that misses the scalar cache (its count
   // is lgkmcnt), so the k-loop's direct loads in flight need not drain first, as
   // they would behind a vector load of the flag.
@@ -585,7 +603,10 @@ struct AgGate {
         __builtin_amdgcn_s_sleep(2);
       }
     }
-    if (kp > ready) ready = kp;
+    if (kp > ready) {
+      if (acq) acquire_fence_agent();
+      ready = kp;
+    }
   }
 };
 
@@ -635,7 +656,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
   __shared__ int s_kind, s_idx, s_last;
   const int tid = threadIdx.x;
   unsigned long long* S = a.slots;
-  const int x = xcc_id() % a.n_xcd;
+  const int hw_xcd = xcc_id();
+  const int x = hw_xcd % a.n_xcd;
   // This XCD's bands: arrival positions x + i*n_xcd for i < nb; the first nl are
   // this GPU's own, the other nbp are landing.
   const int nb = a.NB > x ? (a.NB - x + a.n_xcd - 1) / a.n_xcd : 0;
@@ -656,7 +678,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
         const int abort = load_relaxed(slot32(S, S_ABORT));
         const int cn = load_relaxed(cnext);
         const int ln = load_relaxed(lnext);
-        if (rank < 0) rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+        if (rank < 0) {
+          rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+          if (a.flag_scope == 0 && !same_xcd_queue(S, x, hw_xcd)) break;
+        }
         if (abort) break;
         if (rank < tx && ln < units) {  // a landing workgroup while pieces are left
           const int u = atomicAdd(lnext, 1);
@@ -739,7 +764,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
       wait_stores();    // this wave's stores have reached the L2
       __syncthreads();  // ... and every other wave's
       if (tid == 0) {
-        store_flag(a.landed + gb * kAgMaxPieces + kp, 1);
+        if (a.flag_scope == 0) store_flag(a.landed + gb * kAgMaxPieces + kp, 1);
+        else publish_flag_agent(a.landed + gb * kAgMaxPieces + kp, 1);
         atomicAdd(xslot(S, x, X_REDUCED), 1);
       }
     } else {
@@ -754,7 +780,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void ag_kernel(AgArgs a) {
         g.run(a.A_local, a.B, a.Ms, a.N, a.K, rs, n0, lds);
       } else {
         AgGate gate{a.landed + gb * kAgMaxPieces, S, a.spin_limit, a.ktpp, a.npc, !a.inloop, -1,
-                    Cfg::BK / 32};
+                    Cfg::BK / 32, a.flag_scope};
         g.run(a.A_full, a.B, a.M, a.N, a.K, m0, n0, lds, gate);
       }
       store_tile_c<Cfg, CT>(g, lds, (CT*)a.C, a.M, a.N, m0, n0);
