@@ -103,20 +103,24 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 ]
 
 
-@pytest.fixture(params=[(-1, -1), (0, 0), (0, 1)],
-                ids=["auto", "handover-all", "handover-all-early"])
+@pytest.fixture(params=[(-1, -1, 0), (0, 0, 0), (0, 1, 0), (0, 0, 1)],
+                ids=["auto", "handover-all", "handover-all-early", "handover-all-agent-scope"])
 def inplace_policy(request):
     """Runs a test under the default policies (in place and early reduce automatic),
-    with every tile handed to reducers through its flag (the role-split path), and
-    the same with reducers that sum a unit's peers before its tile is finished (early
-    reduce). Yields the in-place option."""
-    inplace, early = request.param
-    old = mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY)
+    with every tile handed to reducers through its flag (the role-split path), the
+    same with reducers that sum a unit's peers before its tile is finished (early
+    reduce), and every tile handed over under agent-scope release/acquire flags
+    (MK_OPT_FLAG_SCOPE=1). Yields the in-place option."""
+    inplace, early, scope = request.param
+    old = (mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY),
+           mk.get_option(mk.OPT_FLAG_SCOPE))
     mk.set_option(mk.OPT_INPLACE, inplace)
     mk.set_option(mk.OPT_EARLY, early)
+    mk.set_option(mk.OPT_FLAG_SCOPE, scope)
     yield inplace
     mk.set_option(mk.OPT_INPLACE, old[0])
     mk.set_option(mk.OPT_EARLY, old[1])
+    mk.set_option(mk.OPT_FLAG_SCOPE, old[2])
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}-{s[5]}")
@@ -350,6 +354,12 @@ def test_telemetry_and_controller_trace(inplace_policy):
     tel = mk.new_telemetry()
     mk.gemm_ar_local(A, B, peers, C, telemetry=tel)
     mk.stream_status()
+    # the call traced is checked too: bitwise the baseline, and sampled rows within
+    # the tolerance rule against the oracle
+    rows = sample_rows(w.M, seed=w.index)
+    check_exact(c_bits(C), c_bits(run(A, B, peers, "bf16", "baseline")), "traced call vs baseline")
+    C64, _ = oracle_rows(A, B, peers, "bf16", rows)
+    check_tolerance(c_bits(C, rows), C64, "bf16", "traced call vs oracle")
     t = mk.read_telemetry(tel)
     G = mk.fused_grid(A, B, peers, C)
     assert t.tiles in ((w.M // 256) * (w.N // 256), (w.M // 128) * (w.N // 128))
@@ -370,6 +380,44 @@ def test_telemetry_and_controller_trace(inplace_policy):
     assert all(lo <= x <= G for x in targets)
     # once every tile is computed the controller hands all workgroups to the reduce
     assert all(t.trace[i].target == G for i in range(t.n_trace) if computed[i] == t.tiles)
+
+
+@pytest.mark.parametrize("name", ["mlp", "attn"])
+@pytest.mark.parametrize("variant", ["integer", "gaussian"])
+def test_role_split_at_full_size(name, variant):
+    """The role-split path at full size: every tile handed to reducers through its
+    flag (MK_OPT_INPLACE=0), so that reducers wait on flags, hold units, compute when
+    nothing is ready and follow the controller over several rounds of tiles (mlp: two
+    rounds of 256 tiles on 256 workgroups; attn: eight). Adaptive, 0 and 64 reducers,
+    and adaptive under agent-scope flags: sampled rows against the oracle (bit-exact on
+    integer inputs, the tolerance rule on Gaussian ones), every element bitwise
+    against the two-kernel baseline."""
+    w = mk_inputs.BY_NAME[name]
+    A, B, peers = mk_inputs.workload_inputs(w, variant, device=DEV)
+    rows = sample_rows(w.M, seed=w.index)
+    C64, want = oracle_rows(A, B, peers, w.c_dtype, rows)
+    rms = float(np.sqrt(np.mean(C64 * C64)))
+    ref = c_bits(run(A, B, peers, w.c_dtype, "baseline"))
+    opts = (mk.OPT_INPLACE, mk.OPT_FLAG_SCOPE)
+    old = [mk.get_option(o) for o in opts]
+    try:
+        mk.set_option(mk.OPT_INPLACE, 0)
+        for scope, mode in ((0, "adaptive"), (0, "0"), (0, "64"), (1, "adaptive")):
+            announce(f"role split {name} {variant} reducers {mode} flag scope {scope}")
+            mk.set_option(mk.OPT_FLAG_SCOPE, scope)
+            C = run(A, B, peers, w.c_dtype, mode)
+            check_exact(c_bits(C), ref, f"{name} {mode} scope {scope} vs baseline")
+            got = c_bits(C, rows)
+            if variant == "integer":
+                check_exact(got, want, f"{name} {mode} scope {scope} vs oracle")
+            else:
+                check_tolerance(got, C64, w.c_dtype, f"{name} {mode} scope {scope}", rms_ref=rms)
+            del C
+    finally:
+        for o, v in zip(opts, old):
+            mk.set_option(o, v)
+    del A, B, peers
+    torch.cuda.empty_cache()
 
 
 def test_early_reduce_grid_and_parity_on_a_decode_shard():
