@@ -2,20 +2,26 @@
 
 A step is one call of the fused persistent kernel (mk_gemm_ar_local, adaptive
 reducer count, default in-place policy) over one batch of synthetic inputs
-already resident in HBM:
-C = A*B + sum of 15 peer partials for the Llama-70B-like MLP down-projection
-shard (M=4096 tokens, N=8192, K=1792 = 28672/16, P=16; bf16 A/B/peers/C, fp32
-accumulation). The two-kernel baseline (GEMM kernel, then reduce kernel) is timed
-in the same process for the speedup.
+already resident in HBM: C = A*B + the sum of the P-1 peer partials. The headline
+workload is the largest shard (--workload large: M=N=K_local=8192, P=8; bf16
+A/B/peers/C, fp32 accumulation), whose arithmetic intensity (819 flops per
+compulsory byte) puts it on the matrix-core side of MI355X's ridge (about 312).
+The two-kernel baseline (GEMM kernel, then reduce kernel) is timed in the same
+process for the speedup.
 
-Prints ONE JSON line. `value` is effective TFLOP/s = 2*M*N*K / time. The
-roofline object prices the fused kernel against HBM (the workload's arithmetic
-intensity, 107.6 FLOP/byte, is below MI355X's ridge of about 315): achieved =
-compulsory bytes (A + B + peers + C) per launch / average launch time.
-cpu_baseline times the CPU oracle on a bounded sample of rows of the same
+Prints ONE JSON line. `value` is effective TFLOP/s = 2*M*N*K / time of the
+headline call. `roofline` prices that kernel against its bound: matrix cores
+(2.5 PFLOP/s bf16) at or above the ridge, HBM (8 TB/s, compulsory bytes A + B +
+peers + C per launch) below it; achieved = algorithmic work per launch / average
+launch time from HIP events on the launch stream. `workloads` times every other
+workload the same way (fused and baseline, each with its own roofline), the mlp
+shape also under the comparison schedules (two streams, CU-masked streams, every
+tile handed over), and the GEMM+ReduceScatter and AllGather+GEMM shares.
+cpu_baseline times the CPU oracle on a bounded sample of rows of the headline
 workload.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload large]
+                       [--headline-only] [--no-cpu-baseline]
        python bench.py --all-configs     (one JSON line: every workload, fused /
                                           baseline / two-stream, median p10 p90)
        python bench.py --sweep large     (one JSON line: static reducer counts
@@ -47,7 +53,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, vendor figure
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_mlp.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_{}.txt")
 KERNEL_SOURCES = ["tile_gemm_all_amd/csrc/mk_kernels.hip", "tile_gemm_all_amd/csrc/mk_device.h",
                   "tile_gemm_all_amd/csrc/mk_controller.h"]
 
@@ -64,7 +70,7 @@ def measured_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
     on the kernel source as it is now; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -100,7 +106,7 @@ def cpu_baseline(w, A, B, peers, budget_s=12.0):
     t = run_rows(rows)
     flops = 2.0 * len(rows) * w.N * w.K
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{len(rows)} of {w.M} rows of the {w.name} workload (all N={w.N}, "
                       f"K={w.K}, {w.n_peers} peers), fp64, {t:.1f} s"}
 
@@ -333,15 +339,45 @@ def cpu_oracle(budget_s=8.0):
           flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)  # flops per byte, about 312
+
+
+def roofline_of(w, us):
+    """The bound of a workload's fused call (matrix cores at or above the ridge,
+    HBM below it) and the fraction of that peak the call reaches: algorithmic
+    flops or compulsory bytes per launch over the launch time."""
+    if w.flops / w.compulsory_bytes() >= RIDGE:
+        tf = w.flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    gbps = w.compulsory_bytes() / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mlp")
+    ap.add_argument("--workload", default="large",
+                    help="the workload of the headline line (default: the largest, 8192^3)")
     ap.add_argument("--n-reduce-wg", type=int, default=None,
                     help="static reducer count (default: adaptive controller)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload's fused call and its baseline")
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--sweep", metavar="WORKLOAD")
     ap.add_argument("--trace", metavar="WORKLOAD",
@@ -383,50 +419,13 @@ def main():
     import mk_inputs
     import tile_gemm_all_amd as mk
 
-    w = mk_inputs.BY_NAME[args.workload]
     torch.cuda.set_device(0)
-    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
-    C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if w.c_dtype == "bf16" else torch.float32,
-                    device="cuda")
     stream = torch.cuda.current_stream()
+    w = mk_inputs.BY_NAME[args.workload]
 
-    def fused():
-        mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=args.n_reduce_wg)
-
-    def two_kernel():
-        mk.gemm_then_reduce_baseline(A, B, peers, C)
-
-    def two_stream():
-        mk.gemm_ar_two_stream(A, B, peers, C)
-
-    # GEMM+ReduceScatter share of the same GEMM: this GPU owns one P-th of the rows
-    # (slice 3), reduces them with the peers' partials of those rows, publishes the rest
-    o0, o1 = 3 * w.M // w.P, 4 * w.M // w.P
-    rs_peers = peers[:, o0:o1].contiguous()
-    rs_C = torch.empty((o1 - o0, w.N), dtype=C.dtype, device="cuda")
-    rs_send = torch.empty((w.M, w.N), dtype=peers.dtype, device="cuda")
-
-    def rs_fused():
-        mk.gemm_rs_local(A, B, rs_peers, rs_C, rs_send, o0, o1)
-
-    def rs_baseline():
-        mk.gemm_rs_baseline(A, B, rs_peers, rs_C, rs_send, o0, o1)
-
-    # AllGather+GEMM share (gate+up projection, column-parallel): this GPU (rank 5)
-    # holds 256 of the 4096 gathered rows; the other 15 shards land while the GEMM runs
-    aw = mk_inputs.AG_BY_NAME["ag_up"]
-    ag_shards, ag_B = mk_inputs.make_ag_inputs(aw.Ms, aw.P, aw.N, aw.K, "gaussian",
-                                               1000 * aw.index, device="cuda")
-    ag_local, ag_peers = mk_inputs.shard_split(ag_shards, 5)
-    del ag_shards
-    ag_full = torch.empty((aw.M, aw.K), dtype=torch.bfloat16, device="cuda")
-    ag_C = torch.empty((aw.M, aw.N), dtype=torch.bfloat16, device="cuda")
-
-    def ag_fused():
-        mk.gemm_ag_local(ag_local, ag_peers, ag_full, ag_B, ag_C, 5)
-
-    def ag_baseline():
-        mk.gemm_ag_baseline(ag_local, ag_peers, ag_full, ag_B, ag_C, 5)
+    def new_c(wl):
+        return torch.empty((wl.M, wl.N), dtype=torch.bfloat16 if wl.c_dtype == "bf16" else
+                           torch.float32, device="cuda")
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -445,41 +444,117 @@ def main():
     # Comparison legs get at least 50 warmup calls: the first leg timed in a fresh
     # process ran several percent slow after 10 (two-kernel baseline on mlp:
     # 0.336 ms after 10, 0.322 ms after 100, on one box), which would flatter the
-    # fused kernel. The fused leg below keeps --warmup.
+    # fused kernel. The headline's fused leg, timed last, keeps --warmup.
     cw = max(args.warmup, 50)
-    base_ms = timed(two_kernel, args.steps, cw)
-    # stream overlap: per-chunk GEMM kernels, per-chunk reduces on a second stream
-    two_stream_ms = timed(two_stream, args.steps, cw)
-    # the same schedule on CU-masked streams: GEMM and reduce kernels on disjoint
-    # compute units, for each split the device allows (multiples of 64 of 256)
-    masked = {}
-    n_cus = mk.num_workgroups()
-    old_split = mk.get_option(mk.OPT_STREAM_CU_SPLIT)
-    try:
-        for split in range(n_cus // 4, n_cus, n_cus // 4):
-            mk.set_option(mk.OPT_STREAM_CU_SPLIT, split)
-            masked[str(split)] = round(timed(two_stream, args.steps, cw), 5)
-    finally:
-        mk.set_option(mk.OPT_STREAM_CU_SPLIT, old_split)
-    rs_base_ms = timed(rs_baseline, args.steps, cw)
-    rs_ms = timed(rs_fused, args.steps, cw)
-    ag_base_ms = timed(ag_baseline, args.steps, cw)
-    ag_ms = timed(ag_fused, args.steps, cw)
-    # the role-split path alone: every tile handed to reducers through its flag
-    old_inplace = mk.get_option(mk.OPT_INPLACE)
-    mk.set_option(mk.OPT_INPLACE, 0)
-    handover_ms = timed(fused, args.steps, cw)
-    mk.set_option(mk.OPT_INPLACE, old_inplace)
+    out_workloads = {}
+    extras = {}
+    if not args.headline_only:
+        # every other workload: fused (adaptive) and two-kernel baseline, inputs
+        # rotated over enough sets that the peers are not cache-resident
+        for o in mk_inputs.WORKLOADS:
+            if o.name == w.name:
+                continue
+            n_sets = max(1, -(-600_000_000 // o.compulsory_bytes()))
+            base_in = mk_inputs.workload_inputs(o, "gaussian", device="cuda")
+            sets = [base_in] + [tuple(t.clone() for t in base_in) for _ in range(n_sets - 1)]
+            C = new_c(o)
+            it = [0]
+
+            def rot(fn):
+                def call():
+                    fn(*sets[it[0] % n_sets], C)
+                    it[0] += 1
+                return call
+
+            steps = max(args.steps, 20 if o.flops > 1e10 else 200)
+            b_ms = timed(rot(mk.gemm_then_reduce_baseline), steps, cw)
+            f_ms = timed(rot(mk.gemm_ar_local), steps, cw)
+            r = {"M": o.M, "N": o.N, "K_local": o.K, "P": o.P, "input_sets": n_sets,
+                 "fused_us": round(f_ms * 1e3, 2), "baseline_us": round(b_ms * 1e3, 2),
+                 "speedup_vs_two_kernel": round(b_ms / f_ms, 4),
+                 "TFLOPs": round(o.flops / (f_ms * 1e-3) / 1e12, 2),
+                 "GBps": round(o.compulsory_bytes() / (f_ms * 1e-3) / 1e9, 1),
+                 "roofline": roofline_of(o, f_ms * 1e3)}
+            if o.name == "mlp":
+                A, B, peers = base_in
+                # the comparison schedules of the pages' Figure 1 on the mlp shape
+                r["two_stream_us"] = round(timed(lambda: mk.gemm_ar_two_stream(A, B, peers, C),
+                                                 args.steps, cw) * 1e3, 2)
+                masked = {}
+                n_cus = mk.num_workgroups()
+                old_split = mk.get_option(mk.OPT_STREAM_CU_SPLIT)
+                try:
+                    for split in range(n_cus // 4, n_cus, n_cus // 4):
+                        mk.set_option(mk.OPT_STREAM_CU_SPLIT, split)
+                        masked[str(split)] = round(timed(
+                            lambda: mk.gemm_ar_two_stream(A, B, peers, C), args.steps, cw) * 1e3, 1)
+                finally:
+                    mk.set_option(mk.OPT_STREAM_CU_SPLIT, old_split)
+                r["two_stream_cu_masked_us"] = {"by_reduce_cus": masked,
+                                               "best": min(masked.values()) if masked else None}
+                # the role-split path alone: every tile handed to reducers by its flag
+                old_inplace = mk.get_option(mk.OPT_INPLACE)
+                mk.set_option(mk.OPT_INPLACE, 0)
+                try:
+                    r["handover_all_us"] = round(timed(lambda: mk.gemm_ar_local(A, B, peers, C),
+                                                       args.steps, cw) * 1e3, 2)
+                finally:
+                    mk.set_option(mk.OPT_INPLACE, old_inplace)
+                # GEMM+ReduceScatter share of the same GEMM: this GPU owns one P-th of
+                # the rows (slice 3), reduces them with the peers' partials of those
+                # rows and publishes the rest
+                o0, o1 = 3 * o.M // o.P, 4 * o.M // o.P
+                rs_peers = peers[:, o0:o1].contiguous()
+                rs_C = torch.empty((o1 - o0, o.N), dtype=C.dtype, device="cuda")
+                rs_send = torch.empty((o.M, o.N), dtype=peers.dtype, device="cuda")
+                rs_b = timed(lambda: mk.gemm_rs_baseline(A, B, rs_peers, rs_C, rs_send, o0, o1),
+                             args.steps, cw)
+                rs_f = timed(lambda: mk.gemm_rs_local(A, B, rs_peers, rs_C, rs_send, o0, o1),
+                             args.steps, cw)
+                extras["reduce_scatter"] = {"workload": "mlp GEMM", "owned_rows": [o0, o1],
+                                            "fused_us": round(rs_f * 1e3, 2),
+                                            "baseline_us": round(rs_b * 1e3, 2),
+                                            "speedup": round(rs_b / rs_f, 4)}
+                del rs_peers, rs_C, rs_send
+            out_workloads[o.name] = r
+            del sets, base_in, C
+            torch.cuda.empty_cache()
+        # AllGather+GEMM share (gate+up projection, column-parallel): this GPU (rank
+        # 5) holds 256 of the 4096 gathered rows; the other 15 shards land while the
+        # GEMM runs
+        aw = mk_inputs.AG_BY_NAME["ag_up"]
+        ag_shards, ag_B = mk_inputs.make_ag_inputs(aw.Ms, aw.P, aw.N, aw.K, "gaussian",
+                                                   1000 * aw.index, device="cuda")
+        ag_local, ag_peers = mk_inputs.shard_split(ag_shards, 5)
+        del ag_shards
+        ag_full = torch.empty((aw.M, aw.K), dtype=torch.bfloat16, device="cuda")
+        ag_C = torch.empty((aw.M, aw.N), dtype=torch.bfloat16, device="cuda")
+        ag_b = timed(lambda: mk.gemm_ag_baseline(ag_local, ag_peers, ag_full, ag_B, ag_C, 5),
+                     args.steps, cw)
+        ag_f = timed(lambda: mk.gemm_ag_local(ag_local, ag_peers, ag_full, ag_B, ag_C, 5),
+                     args.steps, cw)
+        extras["allgather"] = {"workload": f"{aw.name}: {aw.description}", "Ms": aw.Ms,
+                               "P": aw.P, "N": aw.N, "K": aw.K, "rank": 5,
+                               "fused_us": round(ag_f * 1e3, 2),
+                               "baseline_us": round(ag_b * 1e3, 2),
+                               "speedup": round(ag_b / ag_f, 4),
+                               "fused_TFLOPs": round(aw.flops / (ag_f * 1e-3) / 1e12, 2)}
+        del ag_local, ag_peers, ag_full, ag_B, ag_C
+        torch.cuda.empty_cache()
+
+    # the headline workload, timed last: its fused calls are the last dispatches of
+    # the run
+    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    C = new_c(w)
+    base_ms = timed(lambda: mk.gemm_then_reduce_baseline(A, B, peers, C), args.steps, cw)
     t0 = time.perf_counter()
-    fused_ms = timed(fused, args.steps, args.warmup)
+    fused_ms = timed(lambda: mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=args.n_reduce_wg),
+                     args.steps, args.warmup)
     wall = time.perf_counter() - t0
 
     tflops = w.flops / (fused_ms * 1e-3) / 1e12
-    bytes_ = w.compulsory_bytes()
-    gbps = bytes_ / (fused_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(w.name)}
+    roofline = roofline_of(w, fused_ms * 1e3)
+    roofline["traffic"] = measured_traffic(w.name)
     out = {
         "metric": "fused GEMM+reduce TFLOP/s, % MFMA/HBM roofline, speedup vs 2-kernel baseline",
         "value": round(tflops, 2),
@@ -497,30 +572,19 @@ def main():
                    "P": w.P, "peer_dtype": w.peer_dtype, "c_dtype": w.c_dtype,
                    "reducers": "adaptive" if args.n_reduce_wg is None else args.n_reduce_wg},
         "roofline": roofline,
-        "effective_GBps": round(gbps, 1),
+        "effective_GBps": round(w.compulsory_bytes() / (fused_ms * 1e-3) / 1e9, 1),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "two_kernel_ms": round(base_ms, 5),
         "speedup_vs_two_kernel": round(base_ms / fused_ms, 4),
-        "two_stream_ms": round(two_stream_ms, 5),
-        "speedup_vs_two_stream": round(two_stream_ms / fused_ms, 4),
-        "two_stream_cu_masked_ms": {"by_reduce_cus": masked,
-                                    "best": min(masked.values()) if masked else None},
-        "handover_all_ms": round(handover_ms, 5),
-        "reduce_scatter": {"owned_rows": [o0, o1], "fused_ms": round(rs_ms, 5),
-                           "baseline_ms": round(rs_base_ms, 5),
-                           "speedup": round(rs_base_ms / rs_ms, 4)},
-        "allgather": {"workload": f"{aw.name}: {aw.description}", "Ms": aw.Ms, "P": aw.P,
-                      "N": aw.N, "K": aw.K, "rank": 5, "fused_ms": round(ag_ms, 5),
-                      "baseline_ms": round(ag_base_ms, 5),
-                      "speedup": round(ag_base_ms / ag_ms, 4),
-                      "fused_TFLOPs": round(aw.flops / (ag_ms * 1e-3) / 1e12, 2)},
+        "workloads": out_workloads,
         "timed_wall_s": round(wall, 3),
     }
+    out.update(extras)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, peers)
     print(json.dumps(out), flush=True)
-    # free the library's workspaces (and the streams they own, CU-masked ones
-    # included) before the process exits
+    # free the library's workspaces (and the streams they own) before the process
+    # exits; the library also does this itself at exit
     mk.workspace_reset()
 
 

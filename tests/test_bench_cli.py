@@ -21,11 +21,28 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_is_reported_only_for_the_sources_it_was_taken_on():
-    with open(bench.TRAFFIC_FILE) as f:
-        rec = json.load(f)
-    got = bench.measured_traffic(rec["workload"])
-    if rec["kernel_sha"] == bench.kernel_sha():
-        assert got == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-    else:
-        assert got is None
+    import glob
+
+    files = glob.glob(bench.TRAFFIC_FILE.format("*"))
+    assert files, "no committed counter summary"
+    for path in files:
+        with open(path) as f:
+            rec = json.load(f)
+        assert path == bench.TRAFFIC_FILE.format(rec["workload"])
+        got = bench.measured_traffic(rec["workload"])
+        if rec["kernel_sha"] == bench.kernel_sha():
+            assert got == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        else:
+            assert got is None
     assert bench.measured_traffic("no-such-workload") is None
+
+
+def test_roofline_bound_follows_the_ridge():
+    import mk_inputs
+
+    large = bench.roofline_of(mk_inputs.BY_NAME["large"], 1000.0)
+    assert large["bound"] == "mfma" and large["unit"] == "TFLOP/s"
+    assert abs(large["achieved"] - 2 * 8192 ** 3 / 1e-3 / 1e12) < 0.1
+    mlp = bench.roofline_of(mk_inputs.BY_NAME["mlp"], 1000.0)
+    assert mlp["bound"] == "hbm" and mlp["unit"] == "GB/s"
+    assert abs(mlp["frac"] - mlp["achieved"] / bench.HBM_PEAK_GBPS) < 1e-4
