@@ -153,8 +153,8 @@ class Oracle:
 
     def exact_sum(self, values):
         a = np.ascontiguousarray(values, dtype=np.float64)
-        if a.size > 56:
-            raise ValueError("exact_sum takes at most 56 values")
+        if a.size > 64:
+            raise ValueError("exact_sum takes at most 64 values (the most peers per element)")
         return self.lib.mko_exact_sum(_ptr(a), a.size)
 
     def max_threads(self):

@@ -122,11 +122,15 @@ uint16_t mko_f64_to_bf16_rne(double x) {
   return (uint16_t)(sign | (ebits << 7) | (uint16_t)(mant & 0x7Fu));
 }
 
-/* Exact sum of n doubles, rounded once to nearest-even. Keeps a list of
- * non-overlapping partials whose exact sum equals the running total (each
+/* Exact sum of n doubles (n <= 64), rounded once to nearest-even. Keeps a list
+ * of non-overlapping partials whose exact sum equals the running total (each
  * addition is split into its rounded sum and the exact rounding error by the
- * two-sum transformation), then adds the partials from the largest down and
- * corrects the single case where that last rounding lands on a tie. */
+ * two-sum transformation; Shewchuk 1997, above), then adds the partials from the
+ * largest down and corrects the single case where that last rounding lands on a
+ * tie. The partial list with the final half-way correction is the form of
+ * Raymond Hettinger's "msum" recipe (ActiveState Python Cookbook, recipe
+ * 393090), which CPython's math.fsum also follows. Each input adds at most one
+ * partial, so n <= 64 values never need more than 64 partials. */
 #define MKO_MAX_PARTIALS 64 /* non-overlapping partials of doubles: about 40 at most */
 #define MKO_MAX_PEERS 64    /* peer values held per output element */
 static double exact_sum(const double* x, int n) {

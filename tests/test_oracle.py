@@ -276,6 +276,9 @@ def pin_exact_sum(orc, seed=4):
     lists = [[1e-16, 1.0, 1e16], [1.0, 1e100, 1.0, -1e100], [2.0 ** 53, 1.0, -(2.0 ** 53)],
              [2.0 ** 53, 1.0, 1.0 / 2 ** 30], [1.0, 2.0 ** -53, 2.0 ** -106],
              [1.0, -(2.0 ** -54), -(2.0 ** -120)], [0.1] * 10, []]
+    # 64 values (the most peers), each in its own binade: 64 non-overlapping partials
+    lists.append([(-1.0) ** i * 2.0 ** (16 * i) for i in range(-32, 32)])
+    lists.append(list(rng.standard_normal(64) * np.exp2(rng.integers(-300, 300, size=64))))
     for _ in range(3000):
         n = int(rng.integers(1, 20))
         v = rng.standard_normal(n) * np.exp2(rng.integers(-80, 80, size=n))
