@@ -92,6 +92,9 @@ typedef enum { MK_DT_BF16 = 0, MK_DT_F32 = 1 } mk_dtype_t;
 #define MK_MAX_PEERS 64
 /* Most chunks of mk_gemm_ar_two_stream. */
 #define MK_MAX_CHUNKS 64
+/* Limits of mk_gemm_ar_local_noalloc's fixed workspace (per GPU). */
+#define MK_NOALLOC_PARTIAL_BYTES (32u << 20) /* fp32 partials of tiles handed to reducers */
+#define MK_NOALLOC_MAX_TILE_FLAGS 65536      /* tiles times k-parts per tile */
 
 /* Telemetry written by the fused kernel when the caller passes a device buffer
  * of sizeof(mk_telemetry_t) bytes (else NULL). Times are in ticks of the GPU's
@@ -144,6 +147,33 @@ typedef struct {
 mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, int n_peers,
                              void* C, int64_t M, int64_t N, int64_t K, int peer_dtype,
                              int c_dtype, void* stream, int n_reduce_wg, void* telemetry);
+
+/*
+ * mk_gemm_ar_local_noalloc -- mk_gemm_ar_local for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, kernels and result as mk_gemm_ar_local
+ * (bitwise, with the same exception for tiles computed as two k-halves); it calls
+ * no hipMalloc, hipFree or allocating library routine and no hipMemsetAsync.
+ * Its workspace is a fixed array in device memory, one per GPU the library runs
+ * on, held until the process ends: control words, MK_NOALLOC_MAX_TILE_FLAGS tile
+ * flags and MK_NOALLOC_PARTIAL_BYTES of fp32 partials. The first call on a
+ * device (and the first after mk_workspace_reset) clears its flags and control
+ * words with a fill kernel on `stream`.
+ *   - A call whose default schedule would hand tiles to reducers with more
+ *     partial bytes than that (M * N * 4 per k-part) reduces every tile in place
+ *     instead (same bits); for peer counts that cannot be reduced in place (those
+ *     outside 1-4, 7, 8, 15, or fp32 peers beyond what fits a lane's registers)
+ *     it returns MK_ERR_UNSUPPORTED, as it does for more tiles times k-parts
+ *     than there are flags. Nothing is launched then.
+ *   - Every call on one GPU shares that GPU's workspace. Calls that overlap on
+ *     one GPU (on two streams, or from two threads without ordering) race and
+ *     give undefined results; calls ordered on one stream are safe.
+ *   - Device-side errors are reported by mk_stream_status on the call's stream.
+ */
+mk_status_t mk_gemm_ar_local_noalloc(const void* A, const void* B, const void* peers,
+                                     int n_peers, void* C, int64_t M, int64_t N, int64_t K,
+                                     int peer_dtype, int c_dtype, void* stream, int n_reduce_wg,
+                                     void* telemetry);
 
 /*
  * mk_gemm_then_reduce_baseline -- the unfused schedule of Figure 1 on the
@@ -292,8 +322,9 @@ mk_status_t mk_flag_handoff(int iters, int flag_scope, int cross_xcd, void* stre
 mk_status_t mk_mfma_peak(int iters, int n_workgroups, void* out, void* stream);
 
 /* Synchronizes `stream`, then returns and clears the device error word of that
- * stream's workspace: MK_OK, MK_ERR_TIMEOUT, MK_ERR_UNSUPPORTED or
- * MK_ERR_INTERNAL (or MK_ERR_HIP if the sync fails). */
+ * stream's workspace and of the device's allocation-free workspace: MK_OK,
+ * MK_ERR_TIMEOUT, MK_ERR_UNSUPPORTED or MK_ERR_INTERNAL (or MK_ERR_HIP if the
+ * sync fails). */
 mk_status_t mk_stream_status(void* stream);
 
 /* Synchronizes the device and frees every workspace of `device`; the next call

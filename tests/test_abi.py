@@ -45,6 +45,11 @@ def call(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt
                                          None)
 
 
+def noalloc(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt=0, nr=-1):
+    return mk.library().mk_gemm_ar_local_noalloc(A, B, peers, n_peers, C, M, N, K, pdt, cdt, None,
+                                                 nr, None)
+
+
 def base(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt=0):
     return mk.library().mk_gemm_then_reduce_baseline(A, B, peers, n_peers, C, M, N, K, pdt, cdt,
                                                      None)
@@ -77,6 +82,7 @@ def two(A=A16, B=B16, peers=P16, n_peers=3, C=C16, M=64, N=64, K=64, pdt=0, cdt=
 ])
 def test_validation_rejects(kw, status):
     assert call(**kw) == status, mk.last_error()
+    assert noalloc(**kw) == status, mk.last_error()
     assert base(**kw) == status, mk.last_error()
     assert two(**kw) == status, mk.last_error()
     assert mk.last_error()
@@ -89,6 +95,7 @@ def test_chunk_count_outside_range_is_rejected():
 
 def test_reducer_count_below_adaptive_is_rejected():
     assert call(nr=-2) == mk.MK_ERR_INVALID_ARG
+    assert noalloc(nr=-2) == mk.MK_ERR_INVALID_ARG
 
 
 def test_peers_may_be_null_without_peers_and_inputs_without_size():

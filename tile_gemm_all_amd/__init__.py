@@ -34,7 +34,8 @@ OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 
 OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY, OPT_KSPLIT = 4, 5, 6, 7, 8
 OPT_STREAM_CU_SPLIT = 9  # two-stream schedule: compute units of the CU-masked reduce stream
 
-EXPORTS = ["mk_gemm_ar_local", "mk_gemm_then_reduce_baseline", "mk_gemm_ar_two_stream",
+EXPORTS = ["mk_gemm_ar_local", "mk_gemm_ar_local_noalloc", "mk_gemm_then_reduce_baseline",
+           "mk_gemm_ar_two_stream",
            "mk_gemm_rs_local", "mk_gemm_rs_baseline", "mk_gemm_ag_local", "mk_gemm_ag_baseline",
            "mk_ag_grid", "mk_flag_handoff", "mk_mfma_peak",
            "mk_stream_status",
@@ -59,6 +60,9 @@ _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _lib.mk_gemm_ar_local.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _int, _vp,
                                   _int, _vp]
 _lib.mk_gemm_ar_local.restype = _int
+_lib.mk_gemm_ar_local_noalloc.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int, _int,
+                                          _vp, _int, _vp]
+_lib.mk_gemm_ar_local_noalloc.restype = _int
 _lib.mk_gemm_then_reduce_baseline.argtypes = [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _int,
                                               _int, _vp]
 _lib.mk_gemm_then_reduce_baseline.restype = _int
@@ -189,6 +193,20 @@ def gemm_ar_local(A, B, peers, C, n_reduce_wg=None, telemetry=None, stream=None)
             raise ValueError("telemetry buffer too small")
         tel = telemetry.data_ptr()
     _check(_lib.mk_gemm_ar_local(*a[:10], _stream_ptr(stream), nr, tel))
+    return C
+
+
+def gemm_ar_local_noalloc(A, B, peers, C, n_reduce_wg=None, telemetry=None, stream=None):
+    """gemm_ar_local with the library's fixed per-GPU workspace: no device memory is
+    allocated. Calls that overlap on one GPU race."""
+    a = _args(A, B, peers, C)
+    nr = MK_ADAPTIVE if n_reduce_wg is None else int(n_reduce_wg)
+    tel = None
+    if telemetry is not None:
+        if telemetry.numel() * telemetry.element_size() < TELEMETRY_BYTES or not telemetry.is_cuda:
+            raise ValueError("telemetry buffer too small")
+        tel = telemetry.data_ptr()
+    _check(_lib.mk_gemm_ar_local_noalloc(*a[:10], _stream_ptr(stream), nr, tel))
     return C
 
 

@@ -666,6 +666,38 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   return MK_OK;
 }
 
+// ------------------------------------------------------------ allocation-free workspace
+
+// Per-device state of the fixed workspace: its device address (looked up once
+// per device, with that device current), whether its flags and control words
+// have been cleared, and the epoch of the last call.
+struct Scratch {
+  unsigned char* base = nullptr;
+  bool ready = false;
+  int epoch = 0;
+};
+std::mutex g_scratch_mu;
+std::map<int, Scratch> g_scratch;
+
+unsigned long long* scratch_slots(const Scratch& s) { return (unsigned long long*)s.base; }
+int* scratch_flags(const Scratch& s) { return (int*)(s.base + mk::kScratchSlotBytes); }
+float* scratch_partial(const Scratch& s) {
+  return (float*)(s.base + mk::kScratchSlotBytes + mk::kScratchFlags * 4);
+}
+
+// Caller holds g_scratch_mu; `dev` is current.
+mk_status_t scratch_of(int dev, Scratch** out) {
+  Scratch& s = g_scratch[dev];
+  if (!s.base) {
+    void* p = nullptr;
+    hipError_t e = mk::noalloc_scratch_address(&p);
+    if (e != hipSuccess || !p) return hip_fail(e, "address of the allocation-free workspace");
+    s.base = (unsigned char*)p;
+  }
+  *out = &s;
+  return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -695,6 +727,53 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   a.flags = w->flags;
   a.slots = w->slots;
   a.epoch = w->epoch;
+  hipError_t e = mk::launch_fused(c.L.shape, peer_dtype, c_dtype, a, s);
+  if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}
+
+mk_status_t mk_gemm_ar_local_noalloc(const void* A, const void* B, const void* peers,
+                                     int n_peers, void* C, int64_t M, int64_t N, int64_t K,
+                                     int peer_dtype, int c_dtype, void* stream, int n_reduce_wg,
+                                     void* telemetry) {
+  ArCall c;
+  mk_status_t st = ar_prepare(A, B, peers, n_peers, C, M, N, K, peer_dtype, c_dtype, n_reduce_wg,
+                              telemetry, c);
+  if (st != MK_OK || M == 0 || N == 0) return st;
+  mk::FusedArgs a;
+  st = ar_plan(c, false, a);
+  if (st != MK_OK) return st;
+  // The default plan needs the partial of every handed-over tile ([M, N] fp32 per
+  // k-part); beyond the fixed partial region every tile is reduced in place.
+  const size_t part_bytes = a.T_r > 0 ? (size_t)(M * N) * a.ksplit * 4 : 0;
+  if (part_bytes > mk::kScratchPartialBytes) {
+    st = ar_plan(c, true, a);
+    if (st != MK_OK)
+      return fail(MK_ERR_UNSUPPORTED,
+                  "the partial of this call needs %zu bytes, more than the %zu of the "
+                  "allocation-free workspace, and %s", part_bytes,
+                  (size_t)mk::kScratchPartialBytes, mk_last_error());
+  }
+  if ((size_t)a.T * a.ksplit > mk::kScratchFlags)
+    return fail(MK_ERR_UNSUPPORTED, "%d tiles x %d k-parts exceed the %zu tile flags of the "
+                "allocation-free workspace", a.T, a.ksplit, (size_t)mk::kScratchFlags);
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  Scratch* sc = nullptr;
+  st = scratch_of(c.L.dev, &sc);
+  if (st != MK_OK) return st;
+  if (!sc->ready || sc->epoch >= 0x7FFFFFFE) {
+    // flags to zero and control words to their reset values, by a fill kernel
+    hipError_t e = mk::launch_ws_init(scratch_flags(*sc), (int)mk::kScratchFlags,
+                                      scratch_slots(*sc), s);
+    if (e != hipSuccess) return hip_fail(e, "clearing the allocation-free workspace");
+    sc->ready = true;
+    sc->epoch = 0;
+  }
+  a.P = scratch_partial(*sc);
+  a.flags = scratch_flags(*sc);
+  a.slots = scratch_slots(*sc);
+  a.epoch = ++sc->epoch;
   hipError_t e = mk::launch_fused(c.L.shape, peer_dtype, c_dtype, a, s);
   if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   return MK_OK;
@@ -1250,19 +1329,33 @@ mk_status_t mk_stream_status(void* stream) {
   int dev = 0;
   e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  auto it = g_ws.find(std::make_pair(dev, s));
-  if (it == g_ws.end()) return MK_OK;
-  unsigned long long word = 0;
-  e = hipMemcpy(&word, it->second->slots + (size_t)mk::S_ERROR * mk::kSlotWords, sizeof word,
-                hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
-  if (word == 0) return MK_OK;
-  e = mk::launch_clear_error(it->second->slots, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
-  int code = (int)(word & 0xFFFFFFFFu);
-  return fail((mk_status_t)code, "device reported error %d (%s)", code, mk_status_string(code));
+  // the error words of the stream's workspace and of the device's
+  // allocation-free workspace (if calls used it)
+  unsigned long long* slots[2] = {nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws.find(std::make_pair(dev, s));
+    if (it != g_ws.end()) slots[0] = it->second->slots;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end() && it->second.ready) slots[1] = scratch_slots(it->second);
+  }
+  for (unsigned long long* sl : slots) {
+    if (!sl) continue;
+    unsigned long long word = 0;
+    e = hipMemcpy(&word, sl + (size_t)mk::S_ERROR * mk::kSlotWords, sizeof word,
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+    if (word == 0) continue;
+    e = mk::launch_clear_error(sl, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
+    int code = (int)(word & 0xFFFFFFFFu);
+    return fail((mk_status_t)code, "device reported error %d (%s)", code, mk_status_string(code));
+  }
+  return MK_OK;
 }
 
 mk_status_t mk_workspace_reset(int device) {
@@ -1282,6 +1375,11 @@ mk_status_t mk_workspace_reset(int device) {
     }
   }
   (void)hipSetDevice(cur);
+  {
+    std::lock_guard<std::mutex> lk2(g_scratch_mu);
+    auto it = g_scratch.find(device);
+    if (it != g_scratch.end()) it->second.ready = false;  // cleared again on next use
+  }
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   return MK_OK;
 }

@@ -50,6 +50,12 @@ enum Slot : int {
 constexpr int kSlotWords = 16;
 constexpr int kThreadsHost = 256;  // workgroup size of every kernel
 
+// Fixed device-memory workspace of the allocation-free entry point, one per GPU:
+// control words, then tile flags, then fp32 partials (sizes in mk.h).
+constexpr size_t kScratchSlotBytes = ((size_t)S_COUNT * kSlotWords * 8 + 255) / 256 * 256;
+constexpr size_t kScratchFlags = MK_NOALLOC_MAX_TILE_FLAGS;
+constexpr size_t kScratchPartialBytes = MK_NOALLOC_PARTIAL_BYTES;
+constexpr size_t kScratchBytes = kScratchSlotBytes + kScratchFlags * 4 + kScratchPartialBytes;
 
 enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2 };
 
@@ -203,6 +209,9 @@ int shape_bm(int shape);
 int shape_bn(int shape);
 
 hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s);
+// Device address of the allocation-free workspace on the current device (looked
+// up from its symbol; the caller keeps it per device).
+hipError_t noalloc_scratch_address(void** p);
 hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s);
 hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s);
 hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s);

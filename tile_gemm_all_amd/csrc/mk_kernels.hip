@@ -947,6 +947,16 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   }
 }
 
+// Workspace of mk_gemm_ar_local_noalloc: every GPU the library runs on holds
+// its own copy of this array until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// it looks up each device's address with hipGetSymbolAddress and passes that.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t noalloc_scratch_address(void** p) {
+  return hipGetSymbolAddress(p, HIP_SYMBOL(scratch));
+}
+
 // Workspace initialisation: flags to 0, slots to their reset values.
 __global__ void ws_init_kernel(int* flags, int n_flags, unsigned long long* slots) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_flags; i += gridDim.x * blockDim.x)
