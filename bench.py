@@ -166,6 +166,13 @@ def all_configs():
 
 
 def sweep(name):
+    """Static settings of the reducer target against the adaptive controller (the
+    pages' Figure 3 style: each setting's time over the best static one), under
+    dynamic hand-over (MK_OPT_INPLACE = -2): the target is the number of workgroups
+    streaming a reduce at once, a tile is reduced in place by its workgroup while a
+    slot is free and handed over otherwise. The default policy (every tile in place,
+    or early reduce for few-tile shapes) and every tile handed over are timed beside
+    it."""
     import torch
 
     import mk_inputs
@@ -174,19 +181,44 @@ def sweep(name):
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     w = mk_inputs.BY_NAME[name]
-    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    n_sets = max(1, -(-600_000_000 // w.compulsory_bytes()))
+    base_in = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    sets = [base_in] + [tuple(t.clone() for t in base_in) for _ in range(n_sets - 1)]
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if w.c_dtype == "bf16" else torch.float32,
                     device="cuda")
-    G = mk.fused_grid(A, B, peers, C)
-    res = {"workload": name, "G": G}
-    for nr in [0, 4, 8, 12, 16, 24, 32, 48, 64]:
-        if nr < G:
-            res[str(nr)] = _batched(lambda i: mk.gemm_ar_local(A, B, peers, C, n_reduce_wg=nr), 1,
-                                    stream, batches=5, per_batch=10, warmup=3)
-    res["adaptive"] = _batched(lambda i: mk.gemm_ar_local(A, B, peers, C), 1, stream, batches=5,
-                               per_batch=10, warmup=3)
+    G = mk.fused_grid(*sets[0], C)
+    per = 10 if w.flops > 1e10 else 100
+
+    def t(nr):
+        return _batched(lambda i: mk.gemm_ar_local(*sets[i], C, n_reduce_wg=nr), n_sets, stream,
+                        batches=5, per_batch=per, warmup=3 * per)["median_us"]
+
+    # the knob: the reducer target under dynamic hand-over (MK_OPT_INPLACE = -2;
+    # shapes with early reduce keep their schedule and sweep their reducer target)
+    old = mk.get_option(mk.OPT_INPLACE)
+    mk.set_option(mk.OPT_INPLACE, -2)
+    static = {}
+    try:
+        for nr in sorted({0, 8, 16, 32, 64, 96, 128, 160, 192, 224, G - 1}):
+            if nr < G:
+                static[str(nr)] = t(nr)
+        adaptive = t(None)
+    finally:
+        mk.set_option(mk.OPT_INPLACE, old)
+    best = min(static.values())
+    res = {"workload": name, "G": G, "unit": "us per call (median of 5 batches)",
+           "static": static, "adaptive": adaptive, "best_static": best,
+           "adaptive_over_best_static": round(adaptive / best, 4),
+           "normalised": {k: round(v / best, 3) for k, v in static.items()}}
+    res["default_policy_us"] = t(None)  # every tile in place (or early reduce)
+    res["handover_all_us"] = None
+    try:
+        mk.set_option(mk.OPT_INPLACE, 0)
+        res["handover_all_us"] = t(None)
+    finally:
+        mk.set_option(mk.OPT_INPLACE, old)
     mk.stream_status()
-    print(json.dumps({"mode": "sweep", "unit": "us per call", "results": res}), flush=True)
+    print(json.dumps({"mode": "sweep", "results": res}), flush=True)
 
 
 def trace(name, inplace):
@@ -216,7 +248,8 @@ def trace(name, inplace):
     span = (t.t_end - t.t_start) / 100.0  # us (100 MHz ticks)
     slots = t.grid * span
     pts = [{"t_us": round((t.trace[i].t - t.t_start) / 100.0, 1), "computed": t.trace[i].computed,
-            "reduced": t.trace[i].reduced, "target": t.trace[i].target} for i in range(t.n_trace)]
+            "reduced": t.trace[i].reduced, "target": t.trace[i].target,
+            "streaming": t.trace[i].spare} for i in range(t.n_trace)]
     print(json.dumps({"mode": "trace", "workload": name, "inplace_option": inplace,
                       "span_us": round(span, 1), "grid": t.grid, "tiles": t.tiles,
                       "busy_compute_frac": round(t.busy_compute / 100.0 / slots, 3),

@@ -106,7 +106,7 @@ typedef struct {
   int32_t computed;   /* tiles whose partial was published */
   int32_t reduced;    /* tiles whose C was written */
   int32_t target;     /* published reducer target */
-  int32_t spare;
+  int32_t spare;      /* workgroups streaming a reduce at the update (dynamic hand-over) */
 } mk_trace_entry_t;
 
 typedef struct {
@@ -377,11 +377,13 @@ typedef enum {
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */
   MK_OPT_INPLACE = 6,           /* tiles per XCD reduced in place by the workgroup that computed them
                                    (the last ones of the XCD's queue; the others are handed to
-                                   reducers through flags): -1 = automatic (default: none with early
-                                   reduce; all of them for shapes at or above 315 flops per
-                                   compulsory byte or with queues of more than four rounds;
-                                   otherwise all but the first min(queue/4, workgroups per
-                                   XCD/2)), 0 = none */
+                                   reducers through flags): -1 = automatic (default: every tile,
+                                   or none with early reduce), 0 = none, n = the last n of each
+                                   queue; -2 = dynamic hand-over: a tile is reduced in place when
+                                   its GEMM ends if fewer workgroups than the reducer target are
+                                   streaming a reduce on its XCD (or no GEMM tile is left), else
+                                   published for reducers; the target (n_reduce_wg, or the
+                                   controller's with MK_ADAPTIVE) counts streaming workgroups */
   MK_OPT_EARLY = 7,             /* early reduce: a reducer may take a unit whose tile is still being
                                    computed and sums that unit's peers (into LDS) while it waits for
                                    the tile's flag. -1 = automatic (default: on when every tile and

@@ -121,9 +121,11 @@ def test_options_roundtrip():
     assert old == -1
     mk.set_option(mk.OPT_INPLACE, 0)
     assert mk.get_option(mk.OPT_INPLACE) == 0
+    mk.set_option(mk.OPT_INPLACE, -2)  # dynamic hand-over
+    assert mk.get_option(mk.OPT_INPLACE) == -2
     mk.set_option(mk.OPT_INPLACE, old)
     with pytest.raises(mk.MkError):
-        mk.set_option(mk.OPT_INPLACE, -2)
+        mk.set_option(mk.OPT_INPLACE, -3)
     assert mk.get_option(mk.OPT_EARLY) == -1
     mk.set_option(mk.OPT_EARLY, 1)
     assert mk.get_option(mk.OPT_EARLY) == 1

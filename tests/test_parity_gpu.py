@@ -103,14 +103,17 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 ]
 
 
-@pytest.fixture(params=[(-1, -1, 0), (0, 0, 0), (0, 1, 0), (0, 0, 1)],
-                ids=["auto", "handover-all", "handover-all-early", "handover-all-agent-scope"])
+@pytest.fixture(params=[(-1, -1, 0), (0, 0, 0), (0, 1, 0), (0, 0, 1), (-2, 0, 0)],
+                ids=["auto", "handover-all", "handover-all-early", "handover-all-agent-scope",
+                     "dynamic"])
 def inplace_policy(request):
     """Runs a test under the default policies (in place and early reduce automatic),
     with every tile handed to reducers through its flag (the role-split path), the
     same with reducers that sum a unit's peers before its tile is finished (early
-    reduce), and every tile handed over under agent-scope release/acquire flags
-    (MK_OPT_FLAG_SCOPE=1). Yields the in-place option."""
+    reduce), every tile handed over under agent-scope release/acquire flags
+    (MK_OPT_FLAG_SCOPE=1), and with each tile reduced in place or published when its
+    GEMM ends by the free streaming slots (dynamic hand-over, -2). Yields the
+    in-place option."""
     inplace, early, scope = request.param
     old = (mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY),
            mk.get_option(mk.OPT_FLAG_SCOPE))
@@ -368,12 +371,15 @@ def test_telemetry_and_controller_trace(inplace_policy):
     # with tiles reduced in place the derived cap keeps every workgroup computing
     # (target 0) while GEMM tiles remain; with every tile handed over, at least one
     # workgroup reduces
-    lo = 0 if inplace_policy != 0 else 1
+    lo = 0 if inplace_policy == -1 else 1
     assert lo <= t.initial_target <= G - 1
     assert lo <= t.final_target <= G
     assert 0 < t.n_trace <= mk.MK_TRACE_CAP
     assert t.t_end > t.t_start
-    assert t.busy_compute > 0 and t.busy_reduce > 0
+    assert t.busy_compute > 0
+    # every tile reduced in place counts as compute work; tiles handed over (or
+    # reduced in place under dynamic hand-over) count as reduce work
+    assert t.busy_reduce > 0 or inplace_policy == -1
     targets = [t.trace[i].target for i in range(t.n_trace)]
     computed = [t.trace[i].computed for i in range(t.n_trace)]
     assert all(a <= b for a, b in zip(computed, computed[1:]))
@@ -402,9 +408,12 @@ def test_role_split_at_full_size(name, variant):
     old = [mk.get_option(o) for o in opts]
     try:
         mk.set_option(mk.OPT_INPLACE, 0)
-        for scope, mode in ((0, "adaptive"), (0, "0"), (0, "64"), (1, "adaptive")):
-            announce(f"role split {name} {variant} reducers {mode} flag scope {scope}")
+        for scope, mode, policy in ((0, "adaptive", 0), (0, "0", 0), (0, "64", 0),
+                                    (1, "adaptive", 0), (0, "adaptive", -2), (0, "64", -2)):
+            announce(f"role split {name} {variant} reducers {mode} flag scope {scope} "
+                     f"policy {policy}")
             mk.set_option(mk.OPT_FLAG_SCOPE, scope)
+            mk.set_option(mk.OPT_INPLACE, policy)
             C = run(A, B, peers, w.c_dtype, mode)
             check_exact(c_bits(C), ref, f"{name} {mode} scope {scope} vs baseline")
             got = c_bits(C, rows)

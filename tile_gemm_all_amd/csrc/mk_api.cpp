@@ -63,7 +63,7 @@ Options options() {
 struct DeviceInfo {
   bool ok = false;
   int cus = 0;
-  int occ[3][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU)
+  int occ[3][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU), both variants
   int ag_occ[3][2] = {};  // AllGather+GEMM kernel occupancy per [shape][ct]
 };
 std::mutex g_dev_mu;
@@ -87,11 +87,17 @@ mk_status_t device_info(int dev, DeviceInfo& out) {
   for (int s = 1; s <= 2; ++s)
     for (int pt = 0; pt < 2; ++pt)
       for (int ct = 0; ct < 2; ++ct) {
-        int n = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mk::fused_kernel_ptr(s, pt, ct),
-                                                         mk::kThreadsHost, 0);
-        if (e != hipSuccess || n < 1)
-          return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        // the persistent grid is sized from this count, so it holds for both
+        // variants of the kernel (the lower of the two)
+        int n = 1 << 30;
+        for (int dyn = 0; dyn < 2; ++dyn) {
+          int m = 0;
+          e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &m, mk::fused_kernel_ptr(s, pt, ct, dyn), mk::kThreadsHost, 0);
+          if (e != hipSuccess || m < 1)
+            return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+          n = m < n ? m : n;
+        }
         d.occ[s][pt][ct] = n;
       }
   for (int s = 1; s <= 2; ++s)
@@ -602,45 +608,41 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
     a.reducer_cap = cap < G - 1 ? cap : G - 1;
   }
   if (a.adaptive && a.init_target > a.reducer_cap) a.init_target = a.reducer_cap < 1 ? 1 : a.reducer_cap;
-  // In-place tiles per XCD, counted from the end of the XCD's queue. Automatic:
-  //  - compute-bound shapes (at or above the ridge of about 315 flops per
-  //    compulsory byte): every tile. Workgroups drift apart over the rounds, so
-  //    one's reduce overlaps another's GEMM, and no partial makes the round trip
-  //    through memory.
-  //  - memory-bound shapes whose queues hold at most four rounds: all but the
-  //    first min(cnt/4, W/2) tiles of each queue (W = workgroups per XCD).
-  //    Those are handed to reducers, so that after the first round half of the
-  //    workgroups start their next GEMM while the other half reduce, instead of
-  //    every workgroup alternating in step. Longer queues: every tile.
+  // In-place tiles per XCD, counted from the end of the XCD's queue. Automatic
+  // (-1): every tile, unless the call has early reduce (then every tile is handed
+  // over). Measured on one MI355X (bench.py --sweep, 256 workgroups), a tile
+  // handed to another workgroup only adds its partial's round trip through
+  // memory: every tile in place took 315 us on 4096x8192x1792 with 15 peers
+  // (against 320-326 us handing over the first quarter of each queue's first
+  // round), 972 us on 16384x8192x512 and 1107 us on 8192^3 with 7 peers.
+  // MK_OPT_INPLACE = -2 decides per tile instead (dynamic hand-over, below).
   a.early = early ? 1 : 0;
   if (all_inplace) {
     a.n_inplace = 1 << 30;
   } else if (opt.inplace < 0 && a.early) {
     a.n_inplace = 0;  // early reduce applies to tiles handed to reducers
   } else if (opt.inplace < 0) {
-    const double flops = 2.0 * (double)M * (double)N * (double)K;
-    const double bytes = 2.0 * (double)M * (double)K + 2.0 * (double)K * (double)N +
-                         (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype));
-    const int cnt0 = a.T / a.n_xcd;  // shortest queue
-    int hand = 0;
-    const int w = G / a.n_xcd;
-    // Only queues of at most four rounds: with more, the workgroups drift apart
-    // on their own (16384x8192x512, eight rounds: 965-973 us all in place,
-    // 982-986 us with handed-over first tiles; 4096x8192x1792, two rounds:
-    // 313-314 us against 316 us).
-    if (bytes > 0 && flops / bytes < 315.0 && cnt0 <= 4 * w)
-      hand = cnt0 / 4 < w / 2 ? cnt0 / 4 : w / 2;
-    a.n_inplace = cnt0 - hand;
+    a.n_inplace = 1 << 30;
   } else {
     a.n_inplace = (int)opt.inplace;
   }
   // Two k-halves only when every tile is handed to a reducer (an in-place tile
   // would reduce its own half-product).
   a.ksplit = a.early && a.n_inplace == 0 ? ks : 1;
+  // Dynamic hand-over (MK_OPT_INPLACE = -2, without early reduce): every tile is
+  // reduced in place or handed over when its GEMM ends, by the streaming slots
+  // free then. The controller's target counts workgroups streaming a reduce, in
+  // place or handed over, so all reduce work is its reducers' (T_r = T).
+  a.dyn = opt.inplace == -2 && !all_inplace && !a.early && inpl_ok ? 1 : 0;
   a.T_r = 0;
-  for (int xi = 0; xi < a.n_xcd; ++xi) {
-    const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
-    a.T_r += cnt - mk::xcd_inplace(cnt, a.n_inplace, inpl_ok);
+  if (a.dyn) {
+    a.n_inplace = 0;
+    a.T_r = T;
+  } else {
+    for (int xi = 0; xi < a.n_xcd; ++xi) {
+      const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
+      a.T_r += cnt - mk::xcd_inplace(cnt, a.n_inplace, inpl_ok);
+    }
   }
   // With tiles reduced in place, compute workgroups do most of the reduce
   // themselves; a dedicated reducer takes a compute unit away from the GEMM and
@@ -648,7 +650,17 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // shape: 0 reducers 324 us, one per XCD 351 us, 64 348 us). The derived cap
   // is then zero: the adaptive controller keeps every workgroup computing while
   // GEMM tiles remain, and all of them drain the handed-over tiles.
-  if (opt.reducer_cap <= 0 && a.T_r < a.T) a.reducer_cap = 0;
+  if (opt.reducer_cap <= 0 && a.T_r < a.T && !a.dyn) a.reducer_cap = 0;
+  // With dynamic hand-over a tile beyond the streaming slots makes the partial's
+  // round trip through memory; the target is left to the measured split of the
+  // work rather than held under the HBM cap.
+  if (opt.reducer_cap <= 0 && a.dyn) {
+    a.reducer_cap = G - 1;
+    if (a.adaptive) {
+      int t0 = (int)lrintf(a.seed_x * (float)G);
+      a.init_target = t0 < 1 ? 1 : (t0 > G - 1 ? G - 1 : t0);
+    }
+  }
   // The seed share counts the in-place tiles' reduce as compute-side work.
   if (a.T > 0 && a.T_r < a.T) {
     double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -664,6 +676,16 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
     }
   }
   return MK_OK;
+}
+
+// 32-bit words of tile flags a call needs: its flags (tiles times k-parts), then,
+// 8-byte aligned, one 64-bit publication slot per tile for dynamic hand-over.
+int ar_flag_words(const mk::FusedArgs& a) {
+  const int f = a.T * a.ksplit;
+  return a.dyn ? (f + 1) / 2 * 2 + 2 * a.T : f;
+}
+unsigned long long* ar_pub_slots(const mk::FusedArgs& a, int* flags) {
+  return a.dyn ? (unsigned long long*)(flags + (a.T * a.ksplit + 1) / 2 * 2) : nullptr;
 }
 
 // ------------------------------------------------------------ allocation-free workspace
@@ -715,8 +737,9 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   hipStream_t s = (hipStream_t)stream;
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace* w = nullptr;
-  // partial slices and flags per tile
-  st = get_ws(c.L.dev, s, (size_t)(M * N) * a.ksplit, a.T * a.ksplit, &w);
+  // partial slices and flags per tile, and the publication slots (8 bytes per
+  // tile, after the flags) of dynamic hand-over
+  st = get_ws(c.L.dev, s, (size_t)(M * N) * a.ksplit, ar_flag_words(a), &w);
   if (st != MK_OK) return st;
   if (++w->epoch >= 0x7FFFFFFF) {  // flags hold old epochs: restart them from zero
     hipError_t e = mk::launch_ws_init(w->flags, w->flags_cap, nullptr, s);
@@ -725,6 +748,7 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
   }
   a.P = w->P;
   a.flags = w->flags;
+  a.pub = ar_pub_slots(a, w->flags);
   a.slots = w->slots;
   a.epoch = w->epoch;
   hipError_t e = mk::launch_fused(c.L.shape, peer_dtype, c_dtype, a, s);
@@ -754,7 +778,7 @@ mk_status_t mk_gemm_ar_local_noalloc(const void* A, const void* B, const void* p
                   "allocation-free workspace, and %s", part_bytes,
                   (size_t)mk::kScratchPartialBytes, mk_last_error());
   }
-  if ((size_t)a.T * a.ksplit > mk::kScratchFlags)
+  if ((size_t)ar_flag_words(a) > mk::kScratchFlags)
     return fail(MK_ERR_UNSUPPORTED, "%d tiles x %d k-parts exceed the %zu tile flags of the "
                 "allocation-free workspace", a.T, a.ksplit, (size_t)mk::kScratchFlags);
   hipStream_t s = (hipStream_t)stream;
@@ -772,6 +796,7 @@ mk_status_t mk_gemm_ar_local_noalloc(const void* A, const void* B, const void* p
   }
   a.P = scratch_partial(*sc);
   a.flags = scratch_flags(*sc);
+  a.pub = ar_pub_slots(a, a.flags);
   a.slots = scratch_slots(*sc);
   a.epoch = ++sc->epoch;
   hipError_t e = mk::launch_fused(c.L.shape, peer_dtype, c_dtype, a, s);
@@ -1046,7 +1071,7 @@ mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, in
     // reducer takes a compute unit from the GEMM (on the 4096x8192x1792 shape one
     // reducer per XCD leaves a third round of tiles: 175 -> 211 us); the derived
     // cap is then zero and every workgroup drains the handed-over units.
-    if (opt.reducer_cap <= 0 && a.T_r < a.T) a.reducer_cap = 0;
+    if (opt.reducer_cap <= 0 && a.T_r < a.T && !a.dyn) a.reducer_cap = 0;
     const double rows_h = (double)(a.tmo1 - a.tmo0) * BM;
     const double own = (double)(own_m1 - own_m0);
     const double t_r = (rows_h * N * 4.0 + own * N * (n_peers * (double)dt_size(peer_dtype) +
@@ -1436,7 +1461,7 @@ mk_status_t mk_set_option(int option, int64_t value) {
       g_opt.reducer_cap = value;
       return MK_OK;
     case MK_OPT_INPLACE:
-      if (value < -1 || value > (1 << 30)) return fail(MK_ERR_INVALID_ARG, "in-place tiles %lld", (long long)value);
+      if (value < -2 || value > (1 << 30)) return fail(MK_ERR_INVALID_ARG, "in-place tiles %lld", (long long)value);
       g_opt.inplace = value;
       return MK_OK;
     case MK_OPT_EARLY:

@@ -27,6 +27,8 @@ enum XcdSlot : int {
   X_CBR,               // tiles computed by workgroups that prefer reducing (helping)
   X_INPLACE,           // tiles reduced in place by the workgroup that computed them
   X_PHYS,              // 1 + the hardware XCD id of the workgroups serving this queue (0 = none yet)
+  X_STREAM,            // workgroups streaming a reduce now (in place or a handed-over unit)
+  X_PUB,               // dynamic hand-over: tiles of the queue published for reducers
   kXcdWords
 };
 constexpr int kMaxXcd = 16;
@@ -106,6 +108,8 @@ struct FusedArgs {
   void* C;
   float* P;                    // fp32 partial tiles, [M][N]
   int* flags;                  // one per tile, holds the epoch of the call that published it
+  unsigned long long* pub;     // dynamic hand-over: slot q0 + s of XCD x's queue holds
+                               // (epoch << 32) | tile of the s-th tile it published
   unsigned long long* slots;   // S_COUNT * kSlotWords words
   mk_telemetry_t* tel;         // optional
   int64_t M, N, K;
@@ -127,6 +131,10 @@ struct FusedArgs {
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
   int early;                   // 1: a reducer may take a unit whose tile is still being
                                // computed, and sums its peers while it waits
+  int dyn;                     // 1: each tile is reduced in place or handed over when its GEMM
+                               // ends, by the streaming slots free at that moment (the
+                               // controller's target counts streaming workgroups); 0: the
+                               // last n_inplace tiles of each queue are in place
   int ksplit;                  // 1, or 2 (early reduce only): a tile is computed as two
                                // k-halves, each its own compute item, partial slice
                                // (P + half*M*N) and flag (flags[2*tile + half])
@@ -201,7 +209,7 @@ struct AgCopyArgs {
   int P, rank;
 };
 
-const void* fused_kernel_ptr(int shape, int pt, int ct);
+const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn);
 const void* ag_kernel_ptr(int shape, int ct);
 const void* gemm_kernel_ptr(int shape);
 const void* reduce_kernel_ptr(int pt, int ct);

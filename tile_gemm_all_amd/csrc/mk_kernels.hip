@@ -80,14 +80,17 @@ __device__ __forceinline__ bool same_xcd_queue(unsigned long long* S, int x, int
 
 // One controller evaluation (thread 0 of the workgroup that wins the try-lock).
 // Takes its inputs by value: the kernel's argument block must not escape to
-// memory, or every pointer read from it loses its global address space.
-__device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry_t* tel, int G,
+// memory, or every pointer read from it loses its global address space. Inlined:
+// a call would make the kernel save its live registers around every call site.
+__device__ __forceinline__ void controller_step(unsigned long long* S, mk_telemetry_t* tel, int G,
                                              int T, int T_r, int epoch, int init_target,
-                                             float seed_x, int cap, int rsplit, int n_xcd) {
+                                             float seed_x, int cap, int rsplit, int n_xcd,
+                                             int dyn) {
   if (atomicCAS(slot32(S, S_LOCK), 0, 1) != 0) return;
   int c = sum_xcd32(S, n_xcd, X_COMPUTED);
-  // handed-over tiles reduced: reduce units -> tiles, minus those done in place
-  int r = sum_xcd32(S, n_xcd, X_REDUCED) / rsplit - sum_xcd32(S, n_xcd, X_INPLACE);
+  // tiles reduced (reduce units -> tiles): every one when the target counts
+  // streaming workgroups, else the handed-over ones (less those done in place)
+  int r = sum_xcd32(S, n_xcd, X_REDUCED) / rsplit - (dyn ? 0 : sum_xcd32(S, n_xcd, X_INPLACE));
   unsigned long long bc = sum_xcd64(S, n_xcd, X_BUSY_C);
   unsigned long long br = sum_xcd64(S, n_xcd, X_BUSY_R);
   int cur = current_target(S, epoch, init_target);
@@ -105,7 +108,7 @@ __device__ __noinline__ void controller_step(unsigned long long* S, mk_telemetry
       e.computed = c;
       e.reduced = r;
       e.target = nt;
-      e.spare = 0;
+      e.spare = sum_xcd32(S, n_xcd, X_STREAM);
       tel->trace[i] = e;
     }
   }
@@ -158,10 +161,12 @@ __device__ __forceinline__ void rs_band(const FusedArgs& a, const char* band, in
 // GEMM tile is left) and computes a tile otherwise; a reserved unit whose tile
 // nobody has claimed yet makes its holder compute that far. Compute workgroups
 // reserve units once no GEMM tile is left (draining).
-template <class Cfg, typename PT, typename CT>
+// DYN: dynamic hand-over (a compile-time variant, so that the default schedule's
+// code is not shaped by it).
+template <class Cfg, typename PT, typename CT, bool DYN>
 __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) {
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
-  __shared__ int s_kind, s_tile, s_part, s_ok, s_last;
+  __shared__ int s_kind, s_tile, s_part, s_ok, s_last, s_inpl;
   const int tid = threadIdx.x;
   unsigned long long* S = a.slots;
   const PT* peers = (const PT*)a.peers;
@@ -195,9 +200,123 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   // tile counts as claimed once all of its items are.
   const int KS = a.ksplit > 1 ? a.ksplit : 1;
   const int items = cnt * KS;
+  // Dynamic hand-over: every tile of the queue may be handed over, so its reduce
+  // units are indexed over the whole queue; a tile reduced in place has its flag
+  // set to -epoch, and its units are skipped.
+  const bool inpl_ok = inplace_supported(Cfg::OCC, (int)sizeof(PT), a.n_peers);
+  unsigned long long w_start = 0;  // thread 0: start of a wait for an undecided tile
 
   for (;;) {
-    if (tid == 0) {
+    if constexpr (DYN) if (tid == 0) {
+      // The reducer target counts workgroups streaming a reduce (in place or a
+      // handed-over unit). A tile is handed over only when its GEMM ends with
+      // every streaming slot of the XCD taken; it then gets the next slot of the
+      // XCD's publication list. A workgroup takes a published unit when a
+      // streaming slot is free, computes a GEMM tile otherwise, and drains the
+      // published units once no GEMM tile is left; it leaves when every tile of
+      // the queue is done and every published unit is taken.
+      int kind = K_EXIT, tile = -1;
+      int* rnext = xslot(S, x, X_REDUCE_NEXT);
+      int* cnext = xslot(S, x, X_COMPUTE_NEXT);
+      flag_seen = false;
+      for (;;) {
+        const int abort = load_relaxed(slot32(S, S_ABORT));
+        const unsigned long long tw =
+            __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int cn = load_relaxed(cnext);
+        const int rn = load_relaxed(rnext);
+        const int st = load_relaxed(xslot(S, x, X_STREAM));
+        const int done = load_relaxed(xslot(S, x, X_COMPUTED));
+        int np = load_relaxed(xslot(S, x, X_PUB));
+        // Once every tile is computed the list is final, but the load above may
+        // have been served before the one of `done`: load it again, issued after
+        // `done` has returned (the branch waits for it).
+        if (done >= cnt) np = load_relaxed(xslot(S, x, X_PUB));
+        if (rank < 0) {
+          rank = atomicAdd(xslot(S, x, X_ARRIVE), 1);
+          if (a.flag_scope == 0 && !same_xcd_queue(S, x, hw_xcd)) break;
+        }
+        if (abort) break;
+        const int target = (int)(tw >> 32) == a.epoch ? (int)(tw & 0xFFFFFFFFu) : a.init_target;
+        const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
+        const int avail = np * Cfg::RSPLIT;  // units of the published tiles
+        if (held >= 0) {
+          const int s = held / Cfg::RSPLIT;
+          if (s < np) {
+            const unsigned long long wd = __hip_atomic_load(a.pub + q0 + s, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+            if ((int)(wd >> 32) == a.epoch) {
+              kind = K_REDUCE;
+              tile = (int)(wd & 0xFFFFFFFFu);
+              s_part = held % Cfg::RSPLIT;
+              flag_seen = true;
+              held = -1;
+              w_start = 0;
+              break;
+            }
+          } else if (done >= cnt) {
+            held = -1;  // every tile is done and this unit was never published
+            break;
+          } else if (cn < cnt) {
+            const int i = atomicAdd(cnext, 1);  // compute while the unit is not published
+            if (i < cnt) {
+              kind = K_COMPUTE;
+              tile = q0 + i;
+              break;
+            }
+          }
+          // the slot is taken but its word not yet written, or the last tiles
+          // are still computing: wait (bounded)
+          if (w_start == 0) w_start = ticks();
+          if (ticks() - w_start > a.spin_limit) {
+            raise_error(S, MK_ERR_TIMEOUT);
+            break;
+          }
+          backoff_sleep(1);
+          continue;
+        }
+        w_start = 0;
+        if (rn < avail && (st < tx || cn >= cnt)) {
+          held = atomicAdd(rnext, 1);
+          continue;
+        }
+        if (cn < cnt) {
+          const int i = atomicAdd(cnext, 1);
+          if (i < cnt) {
+            kind = K_COMPUTE;
+            tile = q0 + i;
+            break;
+          }
+          continue;
+        }
+        if (done < cnt) {  // no GEMM left to start; tiles still computing may be published
+          if (rn < avail) {
+            held = atomicAdd(rnext, 1);
+            continue;
+          }
+          if (w_start == 0) w_start = ticks();
+          if (ticks() - w_start > a.spin_limit) {
+            raise_error(S, MK_ERR_TIMEOUT);
+            break;
+          }
+          backoff_sleep(2);
+          continue;
+        }
+        if (rn < avail) {
+          held = atomicAdd(rnext, 1);
+          continue;
+        }
+        break;
+      }
+      if (kind != K_EXIT) {
+        if (last_kind >= 0 && kind != last_kind) atomicAdd(xslot(S, x, X_SWITCHES), 1);
+        last_kind = kind;
+      }
+      s_kind = kind;
+      s_tile = tile;
+      if (kind == K_COMPUTE) s_part = 0;
+    }
+    if (!DYN && tid == 0) {
       int kind = K_EXIT, tile = -1, part = 0;
       bool off_role = false;
       const int units = published * Cfg::RSPLIT;  // unit r: slab r % RSPLIT of tile r / RSPLIT
@@ -340,7 +459,25 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       } else {
         g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
       }
-      if (tile - q0 >= published) {
+      const unsigned long long t_gemm = DYN ? ticks() : 0;
+      if constexpr (DYN) {
+        // In place while a streaming slot of the XCD is free or no GEMM tile is
+        // left to start; otherwise hand the tile over and compute the next one.
+        if (tid == 0) {
+          const unsigned long long tw = __hip_atomic_load(slot64(S, S_TARGET), __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+          const int target =
+              (int)(tw >> 32) == a.epoch ? (int)(tw & 0xFFFFFFFFu) : a.init_target;
+          const int tx = target / a.n_xcd + (x < target % a.n_xcd ? 1 : 0);
+          const int st = load_relaxed(xslot(S, x, X_STREAM));
+          const int cn = load_relaxed(xslot(S, x, X_COMPUTE_NEXT));
+          const int inpl = inpl_ok && (cn >= cnt || st < tx) && tile != a.withhold_tile;
+          if (inpl) atomicAdd(xslot(S, x, X_STREAM), 1);
+          s_inpl = inpl;
+        }
+        __syncthreads();
+      }
+      if (DYN ? s_inpl != 0 : tile - q0 >= published) {
         // In place: the partial goes through LDS (freed by the GEMM's last
         // barrier) in passes, each summed in the same order as a reducer would.
         const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
@@ -365,11 +502,28 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         pass(std::integral_constant<int, 0>{});
         if constexpr (GemmTile<Cfg>::NPASS > 1) pass(std::integral_constant<int, 1>{});
         if (tid == 0) {
-          // the whole tile counts as compute work for the controller
-          atomicAdd(xslot(S, x, X_COMPUTED), 1);
-          atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
-          atomicAdd(xslot(S, x, X_REDUCED), Cfg::RSPLIT);
-          atomicAdd(xslot(S, x, X_INPLACE), 1);
+          const unsigned long long t1 = ticks();
+          if constexpr (DYN) {
+            // the GEMM counts as compute work, the reduce as streaming work
+            atomicAdd(xslot(S, x, X_STREAM), -1);
+            int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;
+            atomicAdd(xslot64(S, x, X_BUSY_C), t_gemm - t0);
+            atomicAdd(xslot64(S, x, X_BUSY_R), t1 - t_gemm);
+            atomicAdd(xslot(S, x, X_REDUCED), Cfg::RSPLIT);
+            atomicAdd(xslot(S, x, X_INPLACE), 1);
+            if (a.adaptive && (done % a.ctrl_period) == 0)
+              controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x,
+                              a.reducer_cap, Cfg::RSPLIT, a.n_xcd, 1);
+          } else {
+            // the whole tile counts as compute work for the controller
+            int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;
+            atomicAdd(xslot64(S, x, X_BUSY_C), t1 - t0);
+            atomicAdd(xslot(S, x, X_REDUCED), Cfg::RSPLIT);
+            atomicAdd(xslot(S, x, X_INPLACE), 1);
+            if (a.adaptive && KS == 1 && (done % a.ctrl_period) == 0)
+              controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x,
+                              a.reducer_cap, Cfg::RSPLIT, a.n_xcd, 0);
+          }
         }
         __syncthreads();
         continue;
@@ -378,7 +532,20 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       wait_stores();    // this wave's partial stores have reached the L2
       __syncthreads();  // ... and so have every other wave's
       if (tid == 0) {
-        if (tile != a.withhold_tile) {
+        if constexpr (DYN) {
+          // the next slot of the XCD's publication list; the slot count is raised
+          // before the computed count, so a queue whose tiles are all computed
+          // has its final list
+          const int s = atomicAdd(xslot(S, x, X_PUB), 1);
+          const unsigned long long wd = ((unsigned long long)(unsigned)a.epoch << 32) | (unsigned)tile;
+          unsigned long long* wp = a.pub + q0 + s;
+          if (tile == a.withhold_tile) {
+          } else if (a.flag_scope == 0) {
+            __hip_atomic_store(wp, wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            __hip_atomic_store(wp, wd, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        } else if (tile != a.withhold_tile) {
           int* fp = a.flags + tile * KS + part;
           if (a.flag_scope == 0) store_flag(fp, a.epoch);
           else publish_flag_agent(fp, a.epoch);
@@ -386,7 +553,9 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;  // this XCD's count
         atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
         // (with a k-split the call fits one round of workgroups: no controller)
-        if (a.adaptive && KS == 1 && (done % a.ctrl_period) == 0) controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x, a.reducer_cap, Cfg::RSPLIT, a.n_xcd);
+        if (a.adaptive && KS == 1 && (done % a.ctrl_period) == 0)
+          controller_step(S, a.tel, a.G, a.T, a.T_r, a.epoch, a.init_target, a.seed_x,
+                          a.reducer_cap, Cfg::RSPLIT, a.n_xcd, DYN ? 1 : 0);
       }
     } else {
       constexpr int SLAB = Cfg::BM / Cfg::RSPLIT;
@@ -394,6 +563,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
       const int rows = (int)(a.M - r0 < SLAB ? a.M - r0 : SLAB);  // <= 0 past a ragged edge
       const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
       const unsigned long long t0 = ticks();
+      if (DYN && tid == 0) atomicAdd(xslot(S, x, X_STREAM), 1);
       if (early) {
         // phase 1: the peers need no flag
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load of the last task in flight
@@ -448,6 +618,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         // completions, the only phase in which its target matters.
         atomicAdd(xslot(S, x, X_REDUCED), 1);
         atomicAdd(xslot64(S, x, X_BUSY_R), t_busy + ticks());
+        if (DYN) atomicAdd(xslot(S, x, X_STREAM), -1);
       }
     }
     __syncthreads();  // s_kind/s_tile/s_ok and LDS are reused by the next task
@@ -1008,17 +1179,18 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 using T256 = TileCfg<256, 256, 64, 2>;  // 64-deep k-tiles, two LDS stages
 using T128 = TileCfg<128, 128>;
 
-template <class Cfg>
+template <class Cfg, bool DYN>
 static const void* fused_ptr(int pt, int ct) {
   if (pt == MK_DT_BF16 && ct == MK_DT_BF16)
-    return (const void*)fused_kernel<Cfg, uint16_t, uint16_t>;
-  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)fused_kernel<Cfg, uint16_t, float>;
-  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)fused_kernel<Cfg, float, uint16_t>;
-  return (const void*)fused_kernel<Cfg, float, float>;
+    return (const void*)fused_kernel<Cfg, uint16_t, uint16_t, DYN>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)fused_kernel<Cfg, uint16_t, float, DYN>;
+  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)fused_kernel<Cfg, float, uint16_t, DYN>;
+  return (const void*)fused_kernel<Cfg, float, float, DYN>;
 }
 
-const void* fused_kernel_ptr(int shape, int pt, int ct) {
-  return shape == SHAPE_256 ? fused_ptr<T256>(pt, ct) : fused_ptr<T128>(pt, ct);
+const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn) {
+  if (dyn) return shape == SHAPE_256 ? fused_ptr<T256, true>(pt, ct) : fused_ptr<T128, true>(pt, ct);
+  return shape == SHAPE_256 ? fused_ptr<T256, false>(pt, ct) : fused_ptr<T128, false>(pt, ct);
 }
 
 hipError_t launch_mfma_peak(int iters, int grid, float* out, hipStream_t s) {
@@ -1057,7 +1229,7 @@ hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s) {
 }
 
 hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s) {
-  const void* f = fused_kernel_ptr(shape, pt, ct);
+  const void* f = fused_kernel_ptr(shape, pt, ct, a.dyn);
   void* args[] = {(void*)&a};
   return hipLaunchKernel(f, dim3(a.G), dim3(kThreads), args, 0, s);
 }
