@@ -371,7 +371,9 @@ typedef enum {
   MK_OPT_SPIN_TIMEOUT_US = 0,   /* reducer flag-wait limit, microseconds (default 2000000) */
   MK_OPT_WITHHOLD_TILE = 1,     /* debug: compute skips publishing this tile (-1 = off) */
   MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
-  MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128 */
+  MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128, 3 = 64x64 (AllReduce
+                                   only: each tile reduced in place by the workgroup that computed
+                                   it; automatic for shapes with fewer 128x128 tiles than CUs) */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default: stores complete + relaxed flag store,
                                    agent-scope acquire), 1 = agent-scope release/acquire */
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */

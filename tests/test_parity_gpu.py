@@ -103,27 +103,30 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 ]
 
 
-@pytest.fixture(params=[(-1, -1, 0), (0, 0, 0), (0, 1, 0), (0, 0, 1), (-2, 0, 0)],
+@pytest.fixture(params=[(-1, -1, 0, 0), (0, 0, 0, 0), (0, 1, 0, 2), (0, 0, 1, 0), (-2, 0, 0, 0)],
                 ids=["auto", "handover-all", "handover-all-early", "handover-all-agent-scope",
                      "dynamic"])
 def inplace_policy(request):
     """Runs a test under the default policies (in place and early reduce automatic),
     with every tile handed to reducers through its flag (the role-split path), the
     same with reducers that sum a unit's peers before its tile is finished (early
-    reduce), every tile handed over under agent-scope release/acquire flags
+    reduce; with 128x128 tiles, since 64x64 tiles are always reduced in place),
+    every tile handed over under agent-scope release/acquire flags
     (MK_OPT_FLAG_SCOPE=1), and with each tile reduced in place or published when its
     GEMM ends by the free streaming slots (dynamic hand-over, -2). Yields the
     in-place option."""
-    inplace, early, scope = request.param
+    inplace, early, scope, shape = request.param
     old = (mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY),
-           mk.get_option(mk.OPT_FLAG_SCOPE))
+           mk.get_option(mk.OPT_FLAG_SCOPE), mk.get_option(mk.OPT_TILE_SHAPE))
     mk.set_option(mk.OPT_INPLACE, inplace)
     mk.set_option(mk.OPT_EARLY, early)
     mk.set_option(mk.OPT_FLAG_SCOPE, scope)
+    mk.set_option(mk.OPT_TILE_SHAPE, shape)
     yield inplace
     mk.set_option(mk.OPT_INPLACE, old[0])
     mk.set_option(mk.OPT_EARLY, old[1])
     mk.set_option(mk.OPT_FLAG_SCOPE, old[2])
+    mk.set_option(mk.OPT_TILE_SHAPE, old[3])
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}-{s[5]}")
@@ -430,9 +433,10 @@ def test_role_split_at_full_size(name, variant):
 
 
 def test_early_reduce_grid_and_parity_on_a_decode_shard():
-    """A shard whose tiles and reduce units fit one round of workgroups gets early
-    reduce automatically: one workgroup per tile plus one per 64-row reduce unit. The
-    result is the same bits as with early reduce off and as the baseline."""
+    """With 128x128 tiles, a shard whose tiles and reduce units fit one round of
+    workgroups gets early reduce automatically: one workgroup per tile plus one per
+    64-row reduce unit. The result is the same bits as with early reduce off and as
+    the baseline."""
     announce("early reduce on a decode-sized shard")
     M, N, K, npeer = 128, 2048, 448, 15
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, "bf16", "integer", 71, device="cpu")
@@ -440,18 +444,58 @@ def test_early_reduce_grid_and_parity_on_a_decode_shard():
     A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
     C = new_c(M, N, "bf16")
     tiles = (M // 128) * (N // 128)
-    assert mk.fused_grid(A, B, peers, C) == tiles * 3  # 128x128 tiles, 2 units each
-    old = mk.get_option(mk.OPT_EARLY)
+    old = mk.get_option(mk.OPT_EARLY), mk.get_option(mk.OPT_TILE_SHAPE)
     try:
+        mk.set_option(mk.OPT_TILE_SHAPE, 2)
+        assert mk.fused_grid(A, B, peers, C) == tiles * 3  # 128x128 tiles, 2 units each
         mk.set_option(mk.OPT_EARLY, 0)
         assert mk.fused_grid(A, B, peers, C) == tiles * 2
         off = c_bits(run(A, B, peers, "bf16", "adaptive"))
+        mk.set_option(mk.OPT_EARLY, old[0])
+        for mode in ["adaptive", "0", str(tiles * 2), "baseline"]:
+            got = c_bits(run(A, B, peers, "bf16", mode))
+            check_exact(got, want, f"early reduce {mode}")
+            check_exact(got, off, f"early reduce {mode} against early off")
     finally:
-        mk.set_option(mk.OPT_EARLY, old)
-    for mode in ["adaptive", "0", str(tiles * 2), "baseline"]:
-        got = c_bits(run(A, B, peers, "bf16", mode))
-        check_exact(got, want, f"early reduce {mode}")
-        check_exact(got, off, f"early reduce {mode} against early off")
+        mk.set_option(mk.OPT_EARLY, old[0])
+        mk.set_option(mk.OPT_TILE_SHAPE, old[1])
+
+
+@pytest.mark.parametrize("shape", [(128, 8192, 1792, 15, "bf16", "bf16"),
+                                   (256, 512, 512, 3, "f32", "f32"),
+                                   (200, 4104, 136, 7, "bf16", "f32"),
+                                   (64, 64, 64, 1, "bf16", "bf16")],
+                         ids=lambda s: "x".join(map(str, s[:4])))
+def test_few_tile_shapes_take_64_tiles_in_place(shape):
+    """Shapes with fewer 128x128 tiles than compute units take 64x64 tiles, each
+    computed and reduced in place by one workgroup (the grid is one workgroup per
+    tile): integer inputs bit-exact against the oracle, and bitwise equal to the
+    baseline, to 128x128 tiles with early reduce and k-halves (exact on integers),
+    and to the same call with telemetry (which takes the persistent loop)."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"64x64 tiles in place {shape}")
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 91, device="cpu")
+    rows = sample_rows(M)
+    _, want = oracle_rows(A, B, peers, cdt, rows)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    C = new_c(M, N, cdt)
+    tiles = ((M + 63) // 64) * ((N + 63) // 64)
+    assert mk.fused_grid(A, B, peers, C) == min(max(tiles, 8), 2 * mk.num_workgroups())
+    ref = c_bits(run(A, B, peers, cdt, "adaptive"))
+    check_exact(ref[rows], want, "64x64 tiles against the oracle")
+    check_exact(c_bits(run(A, B, peers, cdt, "baseline")), ref, "baseline")
+    tel = mk.new_telemetry()
+    C2 = new_c(M, N, cdt)
+    mk.gemm_ar_local(A, B, peers, C2, telemetry=tel)
+    mk.stream_status()
+    check_exact(c_bits(C2), ref, "with telemetry (persistent loop)")
+    assert mk.read_telemetry(tel).tiles == tiles
+    old = mk.get_option(mk.OPT_TILE_SHAPE)
+    try:
+        mk.set_option(mk.OPT_TILE_SHAPE, 2)
+        check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, "128x128 tiles")
+    finally:
+        mk.set_option(mk.OPT_TILE_SHAPE, old)
 
 
 TWO_STREAM_SHAPES = [
@@ -742,8 +786,9 @@ def test_ksplit_on_a_decode_shard(variant):
     C64, want = oracle_rows(A, B, peers, "bf16")
     A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
     tiles = (M // 128) * (N // 128)
-    old = mk.get_option(mk.OPT_KSPLIT)
+    old = mk.get_option(mk.OPT_KSPLIT), mk.get_option(mk.OPT_TILE_SHAPE)
     try:
+        mk.set_option(mk.OPT_TILE_SHAPE, 2)  # early reduce and k-halves are for 128x128 tiles
         outs = {}
         for ks, grid in ((-1, tiles * 4), (2, tiles * 4), (1, tiles * 3)):
             mk.set_option(mk.OPT_KSPLIT, ks)
@@ -752,7 +797,8 @@ def test_ksplit_on_a_decode_shard(variant):
                 outs[(ks, mode)] = c_bits(run(A, B, peers, "bf16", mode))
         outs["baseline"] = c_bits(run(A, B, peers, "bf16", "baseline"))
     finally:
-        mk.set_option(mk.OPT_KSPLIT, old)
+        mk.set_option(mk.OPT_KSPLIT, old[0])
+        mk.set_option(mk.OPT_TILE_SHAPE, old[1])
     for key, got in outs.items():
         if variant == "integer":
             check_exact(got, want, f"k-split {key}")

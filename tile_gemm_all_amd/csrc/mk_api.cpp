@@ -63,7 +63,7 @@ Options options() {
 struct DeviceInfo {
   bool ok = false;
   int cus = 0;
-  int occ[3][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU), both variants
+  int occ[4][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU), both variants
   int ag_occ[3][2] = {};  // AllGather+GEMM kernel occupancy per [shape][ct]
 };
 std::mutex g_dev_mu;
@@ -84,13 +84,13 @@ mk_status_t device_info(int dev, DeviceInfo& out) {
                 p.gcnArchName);
   DeviceInfo d;
   d.cus = p.multiProcessorCount;
-  for (int s = 1; s <= 2; ++s)
+  for (int s = 1; s <= 3; ++s)
     for (int pt = 0; pt < 2; ++pt)
       for (int ct = 0; ct < 2; ++ct) {
         // the persistent grid is sized from this count, so it holds for both
-        // variants of the kernel (the lower of the two)
+        // variants of the kernel (the lower of the two; 64-wide tiles have one)
         int n = 1 << 30;
-        for (int dyn = 0; dyn < 2; ++dyn) {
+        for (int dyn = 0; dyn < (s == mk::SHAPE_64 ? 1 : 2); ++dyn) {
           int m = 0;
           e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
               &m, mk::fused_kernel_ptr(s, pt, ct, dyn), mk::kThreadsHost, 0);
@@ -301,15 +301,24 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
 
 // 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile:
 // they need half the L2 traffic per flop of 128x128 tiles. Otherwise 128x128
-// tiles (two workgroups per CU), so that shapes with fewer 256-tiles than CUs
-// still occupy the chip. Measured on the 16384x8192x512 shape with 15 peers
-// (interleaved runs on one box): 256-tiles 969-979 us, 128-tiles 1073-1081 us.
-int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
+// tiles (two workgroups per CU) while those still give every CU a tile. Measured
+// on the 16384x8192x512 shape with 15 peers (interleaved runs on one box):
+// 256-tiles 969-979 us, 128-tiles 1073-1081 us. Shapes with fewer 128-tiles than
+// CUs take 64x64 tiles, each reduced in place by the one workgroup that computes
+// it (allow64: the AllReduce paths; ReduceScatter keeps 128 and up). Measured on
+// the 128x8192x1792 shard with 15 peers: 19.5 us against 33.6 us for 128-tiles
+// with early reduce and k-halves (baselines 22.7 and 34.6 us); 256x512x512 with 3
+// fp32 peers: 9.2 against 19.4 us (baselines 11.6 and 13.6 us).
+int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus,
+               bool allow64) {
   (void)K; (void)n_peers; (void)peer_dtype; (void)c_dtype;
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
-  int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= cus ? mk::SHAPE_256 : mk::SHAPE_128;
+  if (forced == mk::SHAPE_64) return allow64 ? mk::SHAPE_64 : mk::SHAPE_128;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= cus) return mk::SHAPE_256;
+  return t128 >= cus || !allow64 ? mk::SHAPE_128 : mk::SHAPE_64;
 }
 
 // Host roofline seed for the controller: the reducers' share of the work when
@@ -339,7 +348,9 @@ struct Launch {
 bool early_reduce(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   const int64_t opt = options().early;
   const int occ = L.shape == mk::SHAPE_256 ? 1 : 2;
-  if (opt == 0 || n_peers < 1 || !mk::inplace_supported(occ, (int)dt_size(peer_dtype), n_peers))
+  // 64-wide tiles are always reduced in place
+  if (opt == 0 || n_peers < 1 || L.shape == mk::SHAPE_64 ||
+      !mk::inplace_supported(occ, (int)dt_size(peer_dtype), n_peers))
     return false;
   if (opt > 0) return true;
   const int64_t T = L.tiles_m * L.tiles_n;
@@ -375,6 +386,12 @@ int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   int n_xcd = L.info.cus / 32;
   if (n_xcd < 1) n_xcd = 1;
   const int64_t T = L.tiles_m * L.tiles_n;
+  // 64-wide tiles are all reduced in place: one workgroup per tile (at least one
+  // per XCD, as for every shape)
+  if (L.shape == mk::SHAPE_64) {
+    const int64_t g = T < n_xcd ? n_xcd : T;
+    return g < full ? (int)g : full;
+  }
   int64_t want = early_reduce(L, n_peers, peer_dtype, c_dtype)
                      ? T * (ksplit_of(L, n_peers, peer_dtype, c_dtype) + mk::shape_bm(L.shape) / 64)
                      : 2 * T;
@@ -407,7 +424,7 @@ int rs_grid_size(const Launch& L, int peer_dtype, int c_dtype) {
 }
 
 mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype,
-                    Launch& L) {
+                    Launch& L, bool allow64 = true) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
@@ -415,7 +432,7 @@ mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype
   if (st != MK_OK) return st;
   L.dev = dev;
   L.K = K;
-  L.shape = pick_shape(M, N, K, n_peers, peer_dtype, c_dtype, L.info.cus);
+  L.shape = pick_shape(M, N, K, n_peers, peer_dtype, c_dtype, L.info.cus, allow64);
   L.tiles_m = (M + mk::shape_bm(L.shape) - 1) / mk::shape_bm(L.shape);
   L.tiles_n = (N + mk::shape_bn(L.shape) - 1) / mk::shape_bn(L.shape);
   if (L.tiles_m * L.tiles_n > (1 << 30)) return fail(MK_ERR_UNSUPPORTED, "too many tiles");
@@ -536,6 +553,16 @@ mk_status_t ar_prepare(const void* A, const void* B, const void* peers, int n_pe
   return MK_OK;
 }
 
+// Whether every tile of every XCD queue is reduced in place.
+bool T_inplace_all(const mk::FusedArgs& a, bool inpl_ok) {
+  if (!inpl_ok) return false;
+  for (int xi = 0; xi < a.n_xcd; ++xi) {
+    const int cnt = mk::xcd_tiles(a.T, a.n_xcd, xi);
+    if (mk::xcd_inplace(cnt, a.n_inplace, inpl_ok) != cnt) return false;
+  }
+  return true;
+}
+
 // Decides the grid, the in-place policy, early reduce, the k-split and the
 // controller's seed and cap of a call, and fills every argument of the fused
 // kernel but the workspace (P, flags, slots, epoch). all_inplace: every tile
@@ -563,6 +590,12 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
     want = (want + n_xcd - 1) / n_xcd * n_xcd;
     if (want < n_xcd) want = n_xcd;
     G = want < full ? (int)want : full;
+    // 64-wide tiles are all reduced in place: one workgroup per tile (at least one
+    // per XCD, as for every shape)
+    if (L.shape == mk::SHAPE_64) {
+      const int64_t g = T < n_xcd ? n_xcd : T;
+      G = g < full ? (int)g : full;
+    }
   }
   if (c.n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", c.n_reduce_wg, G - 1);
@@ -633,7 +666,7 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // reduced in place or handed over when its GEMM ends, by the streaming slots
   // free then. The controller's target counts workgroups streaming a reduce, in
   // place or handed over, so all reduce work is its reducers' (T_r = T).
-  a.dyn = opt.inplace == -2 && !all_inplace && !a.early && inpl_ok ? 1 : 0;
+  a.dyn = opt.inplace == -2 && !all_inplace && !a.early && inpl_ok && L.shape != mk::SHAPE_64 ? 1 : 0;
   a.T_r = 0;
   if (a.dyn) {
     a.n_inplace = 0;
@@ -661,6 +694,9 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
       a.init_target = t0 < 1 ? 1 : (t0 > G - 1 ? G - 1 : t0);
     }
   }
+  // One workgroup per tile with every tile in place: no claims or counters (no
+  // telemetry either, which is what a telemetry buffer asks for).
+  a.one_tile = !a.dyn && !a.early && T_inplace_all(a, inpl_ok) && T <= G && !c.telemetry ? 1 : 0;
   // The seed share counts the in-place tiles' reduce as compute-side work.
   if (a.T > 0 && a.T_r < a.T) {
     double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -1005,7 +1041,7 @@ mk_status_t mk_gemm_rs_local(const void* A, const void* B, const void* peers, in
   if (st != MK_OK) return st;
   if (n_reduce_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d", n_reduce_wg);
   Launch L;
-  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L, false);
   if (st != MK_OK) return st;
   const int G = rs_grid_size(L, peer_dtype, c_dtype);
   if (n_reduce_wg > G - 1)
@@ -1101,7 +1137,7 @@ mk_status_t mk_gemm_rs_baseline(const void* A, const void* B, const void* peers,
                                c_dtype);
   if (st != MK_OK) return st;
   Launch L;
-  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L, false);
   if (st != MK_OK) return st;
   if (M == 0 || N == 0) return MK_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -1449,7 +1485,7 @@ mk_status_t mk_set_option(int option, int64_t value) {
       g_opt.ctrl_period = value;
       return MK_OK;
     case MK_OPT_TILE_SHAPE:
-      if (value < 0 || value > 2) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
+      if (value < 0 || value > 3) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
       g_opt.tile_shape = value;
       return MK_OK;
     case MK_OPT_FLAG_SCOPE:

@@ -137,9 +137,10 @@ __device__ __forceinline__ void dma16(const void* g, const char* lds) {
 //   A tile [BM][BK]: 64-byte rows (BK 32), chunk c of row r stored at
 //     c ^ ((r >> 2) & 3), or 128-byte rows (BK 64) at c ^ ((r >> 1) & 7);
 //     a 16-lane phase of ds_read_b128 covers rows r..r+15 of one chunk column.
-//   B tile [BK][BN]: chunk c of row k stored at c ^ (4 * (k & 3)); the gfx950
-//     transposing read (ds_read_b64_tr_b16) has 16 lanes read a 4(k) x 16(n) block,
-//     so 32 lanes touch 4 rows x 4 chunks = all 64 banks once.
+//   B tile [BK][BN]: chunk c of row k stored at c ^ (4 * (k & 3)) (2 * (k & 3)
+//     for 64-wide tiles, whose rows hold 8 chunks); the gfx950 transposing read
+//     (ds_read_b64_tr_b16) has 16 lanes read a 4(k) x 16(n) block, so 32 lanes
+//     touch 4 rows x 4 chunks = all 64 banks once.
 // Default gate of GemmTile::run: every k-tile's inputs are already in memory.
 struct NoGate {
   __device__ __forceinline__ void operator()(int) const {}
@@ -153,6 +154,13 @@ struct TileCfg {
   static constexpr int A_CPR = BK * 2 / 16;  // 16-byte chunks per A row (4 or 8)
   __device__ __forceinline__ static int a_swz(int row) {
     return A_CPR == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
+  }
+  // B tile rows are BN*2 bytes: chunk c of row k is stored at c ^ b_swz(k), which
+  // stays inside the row (16 or more chunks: 4 * (k & 3); 8 chunks, 64-wide
+  // tiles: 2 * (k & 3))
+  static constexpr int B_CPR = BN * 2 / 16;
+  __device__ __forceinline__ static int b_swz(int row) {
+    return B_CPR >= 16 ? 4 * (row & 3) : 2 * (row & 3);
   }
   // fused kernel: workgroups per CU
   static constexpr int OCC = BM * BN >= 256 * 256 ? 1 : 2;
@@ -272,7 +280,7 @@ struct GemmTile {
       int byte = lane * 16;
       int row = blk * Cfg::B_ROWS_PER_LD + byte / Cfg::B_ROW;
       int p = (byte % Cfg::B_ROW) / 16;
-      int c = p ^ (4 * (row & 3));
+      int c = p ^ Cfg::b_swz(row);
       int64_t gn = n0 + c * 8 < N ? n0 + c * 8 : N - 8;
       s.b[i] = (int64_t)row * N + gn;
     }
@@ -338,7 +346,7 @@ struct GemmTile {
 #pragma unroll
     for (int fn = 0; fn < Cfg::FN; ++fn) {
       int c = (wn * Cfg::WN + fn * 32) / 8 + (g & 1) * 2 + ((r & 3) >> 1);
-      int p = c ^ (4 * (brow & 3));
+      int p = c ^ Cfg::b_swz(brow);
       f.b[fn] = Cfg::A_BYTES + brow * Cfg::B_ROW + p * 16 + (r & 1) * 8;
     }
   }
@@ -396,11 +404,16 @@ struct GemmTile {
     }
   }
 
-  // Wait until at most n of this wave's loads are outstanding (n is 0 .. 2*LD).
+  // Wait until at most n of this wave's loads are outstanding (n is a multiple of
+  // LD, 0 .. (NS-2)*LD: the direct loads of the later stages in flight).
+  template <int I = Cfg::NS - 2>
   __device__ __forceinline__ static void wait_loads(int n) {
-    if (n >= 2 * Cfg::LD) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * Cfg::LD) : "memory");
-    else if (n >= Cfg::LD) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(Cfg::LD) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (I <= 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (n >= I * Cfg::LD) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(I * Cfg::LD) : "memory");
+      else wait_loads<I - 1>(n);
+    }
   }
 
   // Full K loop of one tile. Stage kt lives in LDS slot kt % NS; loads for
@@ -414,7 +427,7 @@ struct GemmTile {
                                       const uint16_t* __restrict__ B, int64_t M, int64_t N,
                                       int64_t K, int64_t m0, int64_t n0, char* lds,
                                       Gate gate = Gate(), int64_t lda = 0) {
-    static_assert(Cfg::NS == 4 || Cfg::NS == 2, "wait_loads assumes up to two later stages in flight");
+    static_assert(Cfg::NS >= 2 && (Cfg::NS - 2) * Cfg::LD <= 63, "vmcnt counts at most 63 loads");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int fm = 0; fm < Cfg::FM; ++fm)
@@ -487,10 +500,12 @@ struct GemmTile {
   // after the other in LDS. Blocks of later passes stay in registers meanwhile
   // (at most half of them), so the reduce that follows has room.
   static constexpr int LDS_ROWS = Cfg::LDS_BYTES / (Cfg::BN * 4);
-  static constexpr int NPASS = Cfg::BM / LDS_ROWS;
+  // one pass when the whole fp32 tile fits the LDS (small tiles)
+  static constexpr int NPASS = Cfg::BM <= LDS_ROWS ? 1 : Cfg::BM / LDS_ROWS;
   static constexpr int BAND = Cfg::WM / NPASS;
-  static_assert(NPASS >= 1 && Cfg::BM % LDS_ROWS == 0 && Cfg::FM % NPASS == 0, "LDS passes");
-  static_assert(2 * BAND == LDS_ROWS, "two bands of wave rows per pass");
+  static_assert(NPASS >= 1 && (NPASS == 1 || Cfg::BM % LDS_ROWS == 0) && Cfg::FM % NPASS == 0,
+                "LDS passes");
+  static_assert(2 * BAND <= LDS_ROWS, "two bands of wave rows per pass");
 
   // Lanes 0-31 and 32-63 each write 128 contiguous bytes per store, which
   // touches every bank once.

@@ -59,7 +59,7 @@ constexpr size_t kScratchFlags = MK_NOALLOC_MAX_TILE_FLAGS;
 constexpr size_t kScratchPartialBytes = MK_NOALLOC_PARTIAL_BYTES;
 constexpr size_t kScratchBytes = kScratchSlotBytes + kScratchFlags * 4 + kScratchPartialBytes;
 
-enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2 };
+enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2, SHAPE_64 = 3 };
 
 // Tile queues and flag protocol of a persistent launch of G workgroups on a
 // device with `cus` compute units. gfx950 groups 32 compute units per XCD, each
@@ -131,6 +131,8 @@ struct FusedArgs {
   int T_r;                     // tiles handed to reducers (T minus the in-place ones)
   int early;                   // 1: a reducer may take a unit whose tile is still being
                                // computed, and sums its peers while it waits
+  int one_tile;                // 1: every tile reduced in place and one workgroup per tile: the
+                               // tile is the workgroup's index, no claim or counter is used
   int dyn;                     // 1: each tile is reduced in place or handed over when its GEMM
                                // ends, by the streaming slots free at that moment (the
                                // controller's target counts streaming workgroups); 0: the

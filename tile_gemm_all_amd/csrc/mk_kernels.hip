@@ -161,6 +161,37 @@ __device__ __forceinline__ void rs_band(const FusedArgs& a, const char* band, in
 // GEMM tile is left) and computes a tile otherwise; a reserved unit whose tile
 // nobody has claimed yet makes its holder compute that far. Compute workgroups
 // reserve units once no GEMM tile is left (draining).
+// A tile reduced in place, straight from the accumulators of the workgroup that
+// computed it: the fp32 tile goes through LDS (free after the GEMM's last barrier)
+// in passes, each summed in the order of every other path. All threads.
+template <class Cfg, typename PT, typename CT>
+__device__ __forceinline__ void inplace_tile(const GemmTile<Cfg>& g, char* lds, const PT* peers,
+                                             int n_peers, CT* C, int64_t M, int64_t N, int64_t m0,
+                                             int64_t n0) {
+  const int cols = (int)(N - n0 < Cfg::BN ? N - n0 : Cfg::BN);
+  constexpr int BAND = GemmTile<Cfg>::BAND;
+  auto pass = [&](auto pass_c) {
+    constexpr int PASS = decltype(pass_c)::value;
+    g.template stage_pass_lds<PASS>(lds);
+    __syncthreads();
+    if constexpr (GemmTile<Cfg>::NPASS == 1 && 2 * BAND == Cfg::BM) {
+      const int rows = (int)(M - m0 < Cfg::BM ? M - m0 : Cfg::BM);
+      reduce_region_lds<Cfg::OCC, PT, CT>(lds, Cfg::BN, peers, n_peers, C, M, N, m0, n0, rows, cols);
+    } else {
+#pragma unroll
+      for (int wm = 0; wm < 2; ++wm) {
+        const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
+        const int rows = (int)(M - r0 < BAND ? M - r0 : BAND);  // <= 0 past the edge
+        reduce_region_lds<Cfg::OCC, PT, CT>(lds + wm * BAND * Cfg::BN * 4, Cfg::BN, peers,
+                                            n_peers, C, M, N, r0, n0, rows, cols);
+      }
+    }
+    __syncthreads();
+  };
+  pass(std::integral_constant<int, 0>{});
+  if constexpr (GemmTile<Cfg>::NPASS > 1) pass(std::integral_constant<int, 1>{});
+}
+
 // DYN: dynamic hand-over (a compile-time variant, so that the default schedule's
 // code is not shaped by it).
 template <class Cfg, typename PT, typename CT, bool DYN>
@@ -171,6 +202,23 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
   unsigned long long* S = a.slots;
   const PT* peers = (const PT*)a.peers;
   CT* C = (CT*)a.C;
+  if (a.one_tile) {
+    // Every tile reduced in place, at least one workgroup per tile: the tile
+    // comes from the workgroup index (XCD-aware like the baseline GEMM kernel),
+    // and no claim, counter, flag or controller is involved.
+    const int b = blockIdx.x;
+    if (b >= a.T) return;  // workgroups beyond the tiles (a grid of at least one per XCD)
+    const int t = a.G == a.T && a.n_xcd > 1 && a.T % a.n_xcd == 0
+                      ? (b % a.n_xcd) * (a.T / a.n_xcd) + b / a.n_xcd
+                      : b;
+    int tm, tn;
+    fused_tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * Cfg::BM, n0 = (int64_t)tn * Cfg::BN;
+    GemmTile<Cfg> g;
+    g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);
+    inplace_tile<Cfg, PT, CT>(g, lds, peers, a.n_peers, C, a.M, a.N, m0, n0);
+    return;
+  }
   const unsigned long long t_begin = ticks();
 
   // thread 0 state
@@ -486,16 +534,26 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           constexpr int BAND = GemmTile<Cfg>::BAND;
           g.template stage_pass_lds<PASS>(lds);
           __syncthreads();
-#pragma unroll
-          for (int wm = 0; wm < 2; ++wm) {
-            const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
-            const int rows = (int)(a.M - r0 < BAND ? a.M - r0 : BAND);  // <= 0 past the edge
-            const char* band = lds + wm * BAND * Cfg::BN * 4;
+          if constexpr (GemmTile<Cfg>::NPASS == 1 && 2 * BAND == Cfg::BM) {
+            // the whole tile is in LDS, its rows in order: one region
+            const int rows = (int)(a.M - m0 < Cfg::BM ? a.M - m0 : Cfg::BM);
             if (a.rs)
-              rs_band<PT>(a, band, Cfg::BN, r0, n0, rows, cols);
+              rs_band<PT>(a, lds, Cfg::BN, m0, n0, rows, cols);
             else
-              reduce_region_lds<Cfg::OCC, PT, CT>(band, Cfg::BN, peers, a.n_peers, C, a.M, a.N,
-                                                  r0, n0, rows, cols);
+              reduce_region_lds<Cfg::OCC, PT, CT>(lds, Cfg::BN, peers, a.n_peers, C, a.M, a.N,
+                                                  m0, n0, rows, cols);
+          } else {
+#pragma unroll
+            for (int wm = 0; wm < 2; ++wm) {
+              const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
+              const int rows = (int)(a.M - r0 < BAND ? a.M - r0 : BAND);  // <= 0 past the edge
+              const char* band = lds + wm * BAND * Cfg::BN * 4;
+              if (a.rs)
+                rs_band<PT>(a, band, Cfg::BN, r0, n0, rows, cols);
+              else
+                reduce_region_lds<Cfg::OCC, PT, CT>(band, Cfg::BN, peers, a.n_peers, C, a.M, a.N,
+                                                    r0, n0, rows, cols);
+            }
           }
           __syncthreads();
         };
@@ -1178,6 +1236,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 
 using T256 = TileCfg<256, 256, 64, 2>;  // 64-deep k-tiles, two LDS stages
 using T128 = TileCfg<128, 128>;
+// Few-tile shapes: every tile reduced in place; 64-deep k-tiles in four stages
+// (eight stages measured slower on the 128x8192x1792 shard: 31.9 against 30.0 us).
+using T64 = TileCfg<64, 64, 64, 4>;
 
 template <class Cfg, bool DYN>
 static const void* fused_ptr(int pt, int ct) {
@@ -1189,6 +1250,7 @@ static const void* fused_ptr(int pt, int ct) {
 }
 
 const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn) {
+  if (shape == SHAPE_64) return fused_ptr<T64, false>(pt, ct);  // no dynamic variant
   if (dyn) return shape == SHAPE_256 ? fused_ptr<T256, true>(pt, ct) : fused_ptr<T128, true>(pt, ct);
   return shape == SHAPE_256 ? fused_ptr<T256, false>(pt, ct) : fused_ptr<T128, false>(pt, ct);
 }
@@ -1205,6 +1267,7 @@ const void* ag_kernel_ptr(int shape, int ct) {
 }
 
 const void* gemm_kernel_ptr(int shape) {
+  if (shape == SHAPE_64) return (const void*)gemm_kernel<T64>;
   return shape == SHAPE_256 ? (const void*)gemm_kernel<T256> : (const void*)gemm_kernel<T128>;
 }
 
@@ -1215,8 +1278,8 @@ const void* reduce_kernel_ptr(int pt, int ct) {
   return (const void*)reduce_kernel<float, float>;
 }
 
-int shape_bm(int shape) { return shape == SHAPE_256 ? 256 : 128; }
-int shape_bn(int shape) { return shape == SHAPE_256 ? 256 : 128; }
+int shape_bm(int shape) { return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128); }
+int shape_bn(int shape) { return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128); }
 
 hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s) {
   hipLaunchKernelGGL(ws_init_kernel, dim3(64), dim3(256), 0, s, flags, n_flags, slots);
