@@ -140,8 +140,13 @@ typedef struct {
  *   n_reduce_wg    : 0 .. G-1 dedicated reducer workgroups (G =
  *                    mk_fused_grid() of these arguments), or MK_ADAPTIVE. With 0, compute
  *                    workgroups reduce the tiles once no GEMM tile is left;
- *                    the same draining applies in every mode.
- *   telemetry      : NULL or a device buffer of sizeof(mk_telemetry_t).
+ *                    the same draining applies in every mode. MK_ADAPTIVE also
+ *                    lets the library take the wave-specialised schedule
+ *                    (MK_OPT_TILE_SHAPE); forced by that option, it ignores
+ *                    n_reduce_wg (it has no reducer workgroups: each workgroup
+ *                    reduces its own tiles with eight of its waves).
+ *   telemetry      : NULL or a device buffer of sizeof(mk_telemetry_t); a call with
+ *                    telemetry never takes the wave-specialised schedule.
  * Returns MK_OK once the kernel is enqueued.
  */
 mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, int n_peers,
@@ -373,7 +378,16 @@ typedef enum {
   MK_OPT_CTRL_PERIOD = 2,       /* controller runs every this many completed tiles (default 8) */
   MK_OPT_TILE_SHAPE = 3,        /* 0 = automatic, 1 = 256x256, 2 = 128x128, 3 = 64x64 (AllReduce
                                    only: each tile reduced in place by the workgroup that computed
-                                   it; automatic for shapes with fewer 128x128 tiles than CUs) */
+                                   it; automatic for shapes with fewer 128x128 tiles than CUs),
+                                   4 = wave-specialised (fused AllReduce only, without telemetry:
+                                   64x256 tiles, one 768-thread workgroup per CU whose first four
+                                   waves compute a tile while the other eight reduce the tile
+                                   before from LDS; peer counts 1-4, 7, 8 and 15 of bfloat16, 1-4,
+                                   7 and 8 of float32; otherwise as 0). Automatic, with no
+                                   reducer count, in-place policy, early reduce or k-split set,
+                                   when the peer stream at HBM peak takes at least four times the
+                                   GEMM at matrix-core peak and there are as many 64x256 tiles
+                                   as CUs */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default: stores complete + relaxed flag store,
                                    agent-scope acquire), 1 = agent-scope release/acquire */
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */

@@ -113,8 +113,13 @@ def test_options_roundtrip():
     mk.set_option(mk.OPT_CTRL_PERIOD, old)
     with pytest.raises(mk.MkError):
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 0)
-    with pytest.raises(mk.MkError):
-        mk.set_option(mk.OPT_TILE_SHAPE, 7)
+    for shape in range(5):  # automatic, 256, 128, 64 and the wave-specialised schedule
+        mk.set_option(mk.OPT_TILE_SHAPE, shape)
+        assert mk.get_option(mk.OPT_TILE_SHAPE) == shape
+    mk.set_option(mk.OPT_TILE_SHAPE, 0)
+    for bad in (-1, 5, 7):
+        with pytest.raises(mk.MkError):
+            mk.set_option(mk.OPT_TILE_SHAPE, bad)
     with pytest.raises(mk.MkError):
         mk.set_option(99, 1)
     old = mk.get_option(mk.OPT_INPLACE)

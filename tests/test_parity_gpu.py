@@ -103,18 +103,22 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 ]
 
 
-@pytest.fixture(params=[(-1, -1, 0, 0), (0, 0, 0, 0), (0, 1, 0, 2), (0, 0, 1, 0), (-2, 0, 0, 0)],
+@pytest.fixture(params=[(-1, -1, 0, 0), (0, 0, 0, 0), (0, 1, 0, 2), (0, 0, 1, 0), (-2, 0, 0, 0),
+                        (-1, -1, 0, 4)],
                 ids=["auto", "handover-all", "handover-all-early", "handover-all-agent-scope",
-                     "dynamic"])
+                     "dynamic", "wave-specialised"])
 def inplace_policy(request):
     """Runs a test under the default policies (in place and early reduce automatic),
     with every tile handed to reducers through its flag (the role-split path), the
     same with reducers that sum a unit's peers before its tile is finished (early
     reduce; with 128x128 tiles, since 64x64 tiles are always reduced in place),
     every tile handed over under agent-scope release/acquire flags
-    (MK_OPT_FLAG_SCOPE=1), and with each tile reduced in place or published when its
-    GEMM ends by the free streaming slots (dynamic hand-over, -2). Yields the
-    in-place option."""
+    (MK_OPT_FLAG_SCOPE=1), with each tile reduced in place or published when its
+    GEMM ends by the free streaming slots (dynamic hand-over, -2), and under the
+    wave-specialised schedule (MK_OPT_TILE_SHAPE=4: four waves of each workgroup
+    compute a 64x256 tile while eight reduce the one before; peer counts without a
+    compile-time ring, or a call with telemetry, fall back to the automatic
+    choice). Yields the in-place option."""
     inplace, early, scope, shape = request.param
     old = (mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY),
            mk.get_option(mk.OPT_FLAG_SCOPE), mk.get_option(mk.OPT_TILE_SHAPE))
@@ -494,6 +498,49 @@ def test_few_tile_shapes_take_64_tiles_in_place(shape):
     try:
         mk.set_option(mk.OPT_TILE_SHAPE, 2)
         check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, "128x128 tiles")
+    finally:
+        mk.set_option(mk.OPT_TILE_SHAPE, old)
+
+
+WS_SHAPES = [  # several rounds per workgroup, ragged edges, every ring peer count
+    (2100, 2056, 136, 15, "bf16", "bf16"),
+    (2176, 2048, 64, 8, "f32", "f32"),
+    (1000, 1032, 1000, 1, "bf16", "bf16"),
+    (4224, 4096, 40, 4, "bf16", "f32"),
+    (4160, 2312, 104, 7, "f32", "bf16"),
+    (1088, 4160, 96, 2, "bf16", "bf16"),
+    (2112, 2304, 72, 3, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", WS_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
+def test_wave_specialised_schedule(shape):
+    """The wave-specialised kernel (MK_OPT_TILE_SHAPE=4) on shapes where each of the
+    256 workgroups runs several rounds (the GEMM of one 64x256 tile while the tile
+    before is reduced from LDS): integer inputs bit-exact against the oracle on
+    sampled rows and bitwise equal to the two-kernel baseline and to the default
+    schedule over the whole output, twice in a row (the LDS hand-over starts clean
+    in every call); Gaussian inputs within tolerance."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"wave-specialised {shape}")
+    rows = sample_rows(M, band=128, seed=M)
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 17, device="cpu")
+    _, want = oracle_rows(A, B, peers, cdt, rows)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    ref = c_bits(run(A, B, peers, cdt, "baseline"))
+    check_exact(ref[rows], want, "baseline against the oracle")
+    check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, "default schedule")
+    old = mk.get_option(mk.OPT_TILE_SHAPE)
+    try:
+        mk.set_option(mk.OPT_TILE_SHAPE, 4)
+        for rep in range(2):
+            check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, f"wave-specialised {rep}")
+        A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "gaussian", 18, device="cpu")
+        C64, _ = oracle_rows(A, B, peers, cdt, rows)
+        A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+        got = c_bits(run(A, B, peers, cdt, "adaptive"), rows)
+        check_tolerance(got, C64, cdt, "wave-specialised gaussian",
+                        rms_ref=float(np.sqrt(np.mean(C64 * C64))))
     finally:
         mk.set_option(mk.OPT_TILE_SHAPE, old)
 

@@ -63,7 +63,8 @@ Options options() {
 struct DeviceInfo {
   bool ok = false;
   int cus = 0;
-  int occ[4][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU), both variants
+  int occ[mk::kShapes][2][2] = {};  // fused occupancy per [shape][pt][ct] (workgroups per CU),
+                                    // both variants
   int ag_occ[3][2] = {};  // AllGather+GEMM kernel occupancy per [shape][ct]
 };
 std::mutex g_dev_mu;
@@ -84,16 +85,18 @@ mk_status_t device_info(int dev, DeviceInfo& out) {
                 p.gcnArchName);
   DeviceInfo d;
   d.cus = p.multiProcessorCount;
-  for (int s = 1; s <= 3; ++s)
+  for (int s = 1; s < mk::kShapes; ++s)
     for (int pt = 0; pt < 2; ++pt)
       for (int ct = 0; ct < 2; ++ct) {
         // the persistent grid is sized from this count, so it holds for both
-        // variants of the kernel (the lower of the two; 64-wide tiles have one)
+        // variants of the kernel (the lower of the two; 64-wide tiles and the
+        // wave-specialised kernel have one)
         int n = 1 << 30;
-        for (int dyn = 0; dyn < (s == mk::SHAPE_64 ? 1 : 2); ++dyn) {
+        const int variants = s == mk::SHAPE_256 || s == mk::SHAPE_128 ? 2 : 1;
+        for (int dyn = 0; dyn < variants; ++dyn) {
           int m = 0;
           e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &m, mk::fused_kernel_ptr(s, pt, ct, dyn), mk::kThreadsHost, 0);
+              &m, mk::fused_kernel_ptr(s, pt, ct, dyn), mk::shape_threads(s), 0);
           if (e != hipSuccess || m < 1)
             return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
           n = m < n ? m : n;
@@ -299,6 +302,23 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
   return MK_OK;
 }
 
+// Whether the wave-specialised kernel is the automatic choice: for shapes whose
+// peer stream (at HBM peak) takes at least four times their GEMM (at matrix-core
+// peak), with a 64x256 tile for every compute unit. There the GEMM hides under
+// the stream; where the two are closer its 64x256 tiles, which load more bytes
+// per flop than 256x256 ones, cost more than the overlap gains. Measured on
+// MI355X (ratio 9.8) 16384x8192x512 with 15 peers: 835 us against 975 us with
+// every 256x256 tile reduced in place (two-kernel baseline 1360 us); on
+// 4096x8192x1792 (ratio 2.8) 320-360 against 322-342 us, and on 8192^3 with 7
+// peers (0.3) 1680 against 1091 us.
+bool ws_pays(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
+  const double t_stream =
+      (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype)) / 8.0e12;
+  const double t_gemm = 2.0 * (double)M * (double)N * (double)K / 2.5e15;
+  const int64_t tiles = ((M + 63) / 64) * ((N + 255) / 256);
+  return tiles >= cus && t_stream >= 4.0 * t_gemm;
+}
+
 // 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile:
 // they need half the L2 traffic per flop of 128x128 tiles. Otherwise 128x128
 // tiles (two workgroups per CU) while those still give every CU a tile. Measured
@@ -309,14 +329,23 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
 // the 128x8192x1792 shard with 15 peers: 19.5 us against 33.6 us for 128-tiles
 // with early reduce and k-halves (baselines 22.7 and 34.6 us); 256x512x512 with 3
 // fp32 peers: 9.2 against 19.4 us (baselines 11.6 and 13.6 us).
+//
+// ws: the call may run the wave-specialised kernel (SHAPE_WS: the fused
+// AllReduce without telemetry, K > 0, a peer count whose tiles can be reduced in
+// place at two waves per SIMD); auto_ws: the automatic choice may take it (no
+// explicit reducer count, in-place policy or early reduce).
 int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus,
-               bool allow64) {
-  (void)K; (void)n_peers; (void)peer_dtype; (void)c_dtype;
+               bool allow64, bool ws, bool auto_ws) {
+  (void)c_dtype;
+  ws = ws && allow64 && K > 0 && mk::inplace_supported(2, (int)dt_size(peer_dtype), n_peers);
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
   if (forced == mk::SHAPE_64) return allow64 ? mk::SHAPE_64 : mk::SHAPE_128;
+  if (forced == mk::SHAPE_WS && ws) return mk::SHAPE_WS;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (forced == mk::SHAPE_AUTO && ws && auto_ws && ws_pays(M, N, K, n_peers, peer_dtype, c_dtype, cus))
+    return mk::SHAPE_WS;
   if (t256 >= cus) return mk::SHAPE_256;
   return t128 >= cus || !allow64 ? mk::SHAPE_128 : mk::SHAPE_64;
 }
@@ -349,7 +378,7 @@ bool early_reduce(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   const int64_t opt = options().early;
   const int occ = L.shape == mk::SHAPE_256 ? 1 : 2;
   // 64-wide tiles are always reduced in place
-  if (opt == 0 || n_peers < 1 || L.shape == mk::SHAPE_64 ||
+  if (opt == 0 || n_peers < 1 || L.shape == mk::SHAPE_64 || L.shape == mk::SHAPE_WS ||
       !mk::inplace_supported(occ, (int)dt_size(peer_dtype), n_peers))
     return false;
   if (opt > 0) return true;
@@ -392,6 +421,8 @@ int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
     const int64_t g = T < n_xcd ? n_xcd : T;
     return g < full ? (int)g : full;
   }
+  // wave-specialised: one workgroup per compute unit, at most one per tile
+  if (L.shape == mk::SHAPE_WS) return T < full ? (int)(T > 0 ? T : 1) : full;
   int64_t want = early_reduce(L, n_peers, peer_dtype, c_dtype)
                      ? T * (ksplit_of(L, n_peers, peer_dtype, c_dtype) + mk::shape_bm(L.shape) / 64)
                      : 2 * T;
@@ -424,7 +455,7 @@ int rs_grid_size(const Launch& L, int peer_dtype, int c_dtype) {
 }
 
 mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype,
-                    Launch& L, bool allow64 = true) {
+                    Launch& L, bool allow64 = true, bool ws = false, bool auto_ws = false) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MK_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
@@ -432,7 +463,7 @@ mk_status_t prepare(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype
   if (st != MK_OK) return st;
   L.dev = dev;
   L.K = K;
-  L.shape = pick_shape(M, N, K, n_peers, peer_dtype, c_dtype, L.info.cus, allow64);
+  L.shape = pick_shape(M, N, K, n_peers, peer_dtype, c_dtype, L.info.cus, allow64, ws, auto_ws);
   L.tiles_m = (M + mk::shape_bm(L.shape) - 1) / mk::shape_bm(L.shape);
   L.tiles_n = (N + mk::shape_bn(L.shape) - 1) / mk::shape_bn(L.shape);
   if (L.tiles_m * L.tiles_n > (1 << 30)) return fail(MK_ERR_UNSUPPORTED, "too many tiles");
@@ -525,6 +556,13 @@ struct ArCall {
   Launch L;
 };
 
+// The automatic choice of the wave-specialised kernel leaves a call alone that
+// names its schedule: a reducer count, an in-place policy, early reduce or a k-split.
+bool ws_auto_allowed(int n_reduce_wg) {
+  const Options o = options();
+  return n_reduce_wg == MK_ADAPTIVE && o.inplace == -1 && o.early == -1 && o.ksplit == -1;
+}
+
 mk_status_t ar_prepare(const void* A, const void* B, const void* peers, int n_peers, void* C,
                        int64_t M, int64_t N, int64_t K, int peer_dtype, int c_dtype,
                        int n_reduce_wg, void* telemetry, ArCall& c) {
@@ -532,7 +570,8 @@ mk_status_t ar_prepare(const void* A, const void* B, const void* peers, int n_pe
   if (st != MK_OK) return st;
   if (n_reduce_wg < MK_ADAPTIVE) return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d", n_reduce_wg);
   if (((uintptr_t)telemetry) % 16 != 0) return fail(MK_ERR_INVALID_ARG, "telemetry not 16-byte aligned");
-  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, c.L);
+  st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, c.L, true, telemetry == nullptr,
+               ws_auto_allowed(n_reduce_wg));
   if (st != MK_OK) return st;
   c.A = A;
   c.B = B;
@@ -546,9 +585,10 @@ mk_status_t ar_prepare(const void* A, const void* B, const void* peers, int n_pe
   c.c_dtype = c_dtype;
   c.n_reduce_wg = n_reduce_wg;
   c.telemetry = telemetry;
-  // the reducer count is checked against the grid of the default plan
+  // the reducer count is checked against the grid of the default plan (the
+  // wave-specialised kernel has no reducer workgroups and ignores it)
   const int G = fused_grid_size(c.L, n_peers, peer_dtype, c_dtype);
-  if (n_reduce_wg > G - 1)
+  if (c.L.shape != mk::SHAPE_WS && n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
   return MK_OK;
 }
@@ -596,8 +636,9 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
       const int64_t g = T < n_xcd ? n_xcd : T;
       G = g < full ? (int)g : full;
     }
+    if (L.shape == mk::SHAPE_WS) G = T < full ? (int)(T > 0 ? T : 1) : full;
   }
-  if (c.n_reduce_wg > G - 1)
+  if (L.shape != mk::SHAPE_WS && c.n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", c.n_reduce_wg, G - 1);
   const int T = (int)(L.tiles_m * L.tiles_n);
   memset(&a, 0, sizeof a);
@@ -650,7 +691,7 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // round), 972 us on 16384x8192x512 and 1107 us on 8192^3 with 7 peers.
   // MK_OPT_INPLACE = -2 decides per tile instead (dynamic hand-over, below).
   a.early = early ? 1 : 0;
-  if (all_inplace) {
+  if (all_inplace || L.shape == mk::SHAPE_WS) {
     a.n_inplace = 1 << 30;
   } else if (opt.inplace < 0 && a.early) {
     a.n_inplace = 0;  // early reduce applies to tiles handed to reducers
@@ -666,7 +707,10 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // reduced in place or handed over when its GEMM ends, by the streaming slots
   // free then. The controller's target counts workgroups streaming a reduce, in
   // place or handed over, so all reduce work is its reducers' (T_r = T).
-  a.dyn = opt.inplace == -2 && !all_inplace && !a.early && inpl_ok && L.shape != mk::SHAPE_64 ? 1 : 0;
+  a.dyn = opt.inplace == -2 && !all_inplace && !a.early && inpl_ok && L.shape != mk::SHAPE_64 &&
+                  L.shape != mk::SHAPE_WS
+              ? 1
+              : 0;
   a.T_r = 0;
   if (a.dyn) {
     a.n_inplace = 0;
@@ -696,7 +740,10 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   }
   // One workgroup per tile with every tile in place: no claims or counters (no
   // telemetry either, which is what a telemetry buffer asks for).
-  a.one_tile = !a.dyn && !a.early && T_inplace_all(a, inpl_ok) && T <= G && !c.telemetry ? 1 : 0;
+  a.one_tile = !a.dyn && !a.early && T_inplace_all(a, inpl_ok) && T <= G && !c.telemetry &&
+                       L.shape != mk::SHAPE_WS
+                   ? 1
+                   : 0;
   // The seed share counts the in-place tiles' reduce as compute-side work.
   if (a.T > 0 && a.T_r < a.T) {
     double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -1465,7 +1512,8 @@ int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, 
   if (c_dtype != MK_DT_BF16 && c_dtype != MK_DT_F32) return -(int)MK_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0 || n_peers < 0) return -(int)MK_ERR_INVALID_ARG;
   Launch L;
-  mk_status_t st = prepare(M, N, K, n_peers, peer_dtype, c_dtype, L);
+  mk_status_t st =
+      prepare(M, N, K, n_peers, peer_dtype, c_dtype, L, true, true, ws_auto_allowed(MK_ADAPTIVE));
   if (st != MK_OK) return -(int)st;
   return fused_grid_size(L, n_peers, peer_dtype, c_dtype);
 }
@@ -1485,7 +1533,7 @@ mk_status_t mk_set_option(int option, int64_t value) {
       g_opt.ctrl_period = value;
       return MK_OK;
     case MK_OPT_TILE_SHAPE:
-      if (value < 0 || value > 3) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
+      if (value < 0 || value > 4) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
       g_opt.tile_shape = value;
       return MK_OK;
     case MK_OPT_FLAG_SCOPE:

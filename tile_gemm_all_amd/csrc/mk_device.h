@@ -673,7 +673,7 @@ __device__ __forceinline__ void reduce_chunks(const float* __restrict__ P,
 // (a tile reduced in place by the workgroup that computed it), or nowhere (peers
 // summed ahead of their tile's partial). The first two give the same bits.
 struct PartialGlobal {
-  static constexpr bool kHas = true;
+  static constexpr bool kHas = true, kLate = false;
   const float* __restrict__ P;  // region base
   __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t off, uint32_t) const {
     const uint32_t op = off * 4u;
@@ -686,7 +686,7 @@ struct PartialGlobal {
 // the tile's partial; it is formed before anything is added to it).
 template <int NP>
 struct PartialGlobalN {
-  static constexpr bool kHas = true;
+  static constexpr bool kHas = true, kLate = false;
   const float* __restrict__ P;  // region base of part 0
   uint32_t stride_bytes;        // bytes between two parts' region bases
   __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t off, uint32_t) const {
@@ -711,15 +711,21 @@ struct PartialGlobalN {
 };
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 struct PartialLds {
-  static constexpr bool kHas = true;
+  static constexpr bool kHas = true, kLate = false;
   const lds_char* base;  // region base in LDS, rows of the LDS pitch
   __device__ __forceinline__ void load(f32x4& a, f32x4& b, uint32_t, uint32_t loff) const {
     a = *(const lds_f32x4*)(base + loff * 4u);
     b = *(const lds_f32x4*)(base + loff * 4u + 16u);
   }
 };
+// The same, read when the chunk is summed rather than with its peers' loads: a
+// chunk in flight then holds only its peers' registers (the LDS read's latency
+// hides behind the peer additions, which come first).
+struct PartialLdsLate : PartialLds {
+  static constexpr bool kLate = true;
+};
 struct NoPartial {
-  static constexpr bool kHas = false;
+  static constexpr bool kHas = false, kLate = false;
   __device__ __forceinline__ void load(f32x4&, f32x4&, uint32_t, uint32_t) const {}
 };
 
@@ -755,13 +761,15 @@ struct SumOp {
   // Byte offsets are formed in 32 bits, so each load is a scalar base plus a
   // 32-bit vector offset.
   __device__ __forceinline__ void load(Chunk& k, uint32_t off, uint32_t loff) const {
-    ps.load(k.pa, k.pb, off, loff);
+    if constexpr (!PS::kLate) ps.load(k.pa, k.pb, off, loff);
     const uint32_t ov = off * (uint32_t)sizeof(PT);
 #pragma unroll
     for (int s = 0; s < NP; ++s) k.v[s].load((const PT*)((const char*)peer[s] + ov));
     __builtin_amdgcn_sched_barrier(0);  // keep the group where the ring puts it
   }
   __device__ __forceinline__ void finish(const Chunk& k, uint32_t off, uint32_t loff) const {
+    f32x4 pa = k.pa, pb = k.pb;
+    if constexpr (PS::kLate) ps.load(pa, pb, off, loff);
     float acc[8];
     k.v[0].set(acc);
 #pragma unroll
@@ -769,8 +777,8 @@ struct SumOp {
     if constexpr (PS::kHas) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i] += k.pa[i];
-        acc[4 + i] += k.pb[i];
+        acc[i] += pa[i];
+        acc[4 + i] += pb[i];
       }
     }
     out.store(off, loff, acc);
@@ -827,18 +835,22 @@ struct CopyLdsOp {
   }
 };
 
-// Walks chunk indices q = q0, q0+256, ... of a region of `cpr` chunks per row,
-// giving each one's element offset for two row pitches (N for device memory, LP
-// for a region in LDS), clamped to the last chunk past the end.
+// Walks chunk indices q = q0, q0+stride, ... (stride: the threads that share the
+// region, 256 unless given) of a region of `cpr` chunks per row, giving each
+// one's element offset for two row pitches (N for device memory, LP for a region
+// in LDS), clamped to the last chunk past the end.
 struct ChunkCursor {
   int q, c;                 // chunk index and its column chunk
+  int stride;
   uint32_t off, loff;       // element offsets of chunk q (unclamped)
   int total, cpr;
   uint32_t last, llast;     // element offsets of the last chunk
   uint32_t step_off, step_loff;  // advance for 256 chunks without a row wrap
   int step_c;               // column-chunk advance for 256 chunks (256 % cpr)
   uint32_t wrap_off, wrap_loff;  // extra advance when the column wraps: pitch - 8 * cpr
-  __device__ __forceinline__ void init(int q0, int total_, int cpr_, int64_t N, int64_t LP) {
+  __device__ __forceinline__ void init(int q0, int total_, int cpr_, int64_t N, int64_t LP,
+                                       int stride_ = kThreads) {
+    stride = stride_;
     total = total_;
     cpr = cpr_;
     const int r = q0 / cpr_;
@@ -849,8 +861,8 @@ struct ChunkCursor {
     const int rows = total_ / cpr_;
     last = (uint32_t)((rows - 1) * N + (cpr_ - 1) * 8);
     llast = (uint32_t)((rows - 1) * LP + (cpr_ - 1) * 8);
-    const int a = kThreads / cpr_;
-    step_c = kThreads - a * cpr_;
+    const int a = stride_ / cpr_;
+    step_c = stride_ - a * cpr_;
     step_off = (uint32_t)(a * N + step_c * 8);
     step_loff = (uint32_t)(a * LP + step_c * 8);
     wrap_off = (uint32_t)(N - 8 * cpr_);
@@ -859,7 +871,7 @@ struct ChunkCursor {
   __device__ __forceinline__ uint32_t get() const { return q < total ? off : last; }
   __device__ __forceinline__ uint32_t lget() const { return q < total ? loff : llast; }
   __device__ __forceinline__ void advance() {
-    q += kThreads;
+    q += stride;
     c += step_c;
     off += step_off;
     loff += step_loff;
@@ -900,6 +912,48 @@ struct ReduceRing {
     } while (w0 + k < total);
     // The last pass issued loads of clamped chunks that are never summed (L2
     // hits); the compute path waits for them before its GEMM loop.
+  }
+};
+
+// The ring of the streaming waves of a wave-specialised workgroup (STRIDE
+// threads, t = 0..STRIDE-1 among them). It walks the chunks like ReduceRing and
+// takes part in nb workgroup barriers on the way, spread evenly over its steps
+// and all passed by its last step: the GEMM waves run a k-loop with one barrier
+// per k-tile meanwhile, and every wave of the workgroup has to reach each
+// barrier. Loads in flight stay in flight across a barrier.
+template <int DEPTH, typename OP, int STRIDE>
+struct PacedRing {
+  __device__ __forceinline__ static void run(const OP& op, int t, int total, int cpr, int64_t N,
+                                             int64_t LP, int nb) {
+    const int w0 = __builtin_amdgcn_readfirstlane(t & ~63);
+    constexpr int per = DEPTH * STRIDE;
+    // steps of this wave: whole passes of DEPTH chunks, at least one (as ReduceRing)
+    const int steps = DEPTH * (total > w0 ? (total - w0 + per - 1) / per : 1);
+    ChunkCursor ld, st;
+    ld.init(t, total, cpr, N, LP, STRIDE);
+    st = ld;
+    typename OP::Chunk b[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i) {
+      op.load(b[i], ld.get(), ld.lget());
+      ld.advance();
+    }
+    int s = 0, done = 0;
+    do {
+#pragma unroll
+      for (int i = 0; i < DEPTH; ++i) {
+        op.load(b[(i + DEPTH - 1) % DEPTH], ld.get(), ld.lget());
+        ld.advance();
+        op.finish(b[i], st.get(), st.lget());
+        st.advance();
+        ++s;
+        const int due = s * nb / steps;
+        while (done < due) {
+          __syncthreads();
+          ++done;
+        }
+      }
+    } while (s < steps);
   }
 };
 
@@ -1005,6 +1059,63 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
     default: return;
   }
 #undef MK_RING
+}
+
+// Ring depth of the streaming waves of a wave-specialised workgroup: three waves
+// share each SIMD (168 registers per lane each); chunks in flight hold only their
+// peers' registers (the partial is read from LDS when the chunk is summed),
+// within about 120 registers, between 2 and 4 chunks.
+template <typename PT, int NP>
+__host__ __device__ constexpr int ws_ring_depth() {
+  constexpr int regs = NP * (sizeof(PT) == 2 ? 4 : 8);
+  constexpr int d = 120 / regs;
+  return d < 2 ? 2 : (d > 4 ? 4 : d);
+}
+
+// The same sum by the STRIDE streaming threads of a wave-specialised workgroup
+// (thread t among them), taking part in nb workgroup barriers on the way
+// (PacedRing). With no peers the partial is rounded and stored. Only peer counts
+// for which inplace_supported(2, ...) holds; another count passes its barriers
+// without touching C.
+template <int STRIDE, typename PT, typename CT>
+__device__ __forceinline__ void stream_region_lds(const char* lds, int64_t LP,
+                                                  const PT* __restrict__ peers, int n_peers,
+                                                  CT* __restrict__ C, int64_t M, int64_t N,
+                                                  int64_t m0, int64_t n0, int rows, int cols, int t,
+                                                  int nb) {
+  const int cpr = __builtin_amdgcn_readfirstlane(cols >> 3);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  const int total = rows * cpr;
+  const int64_t stride = M * N;
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
+                       __builtin_amdgcn_readfirstlane((int)n0);
+  PartialLdsLate ps;
+  ps.base = (const lds_char*)lds;
+  if (total > 0) {
+    if (n_peers == 0) {
+      typedef CopyLdsOp<CT> Op;
+      PacedRing<4, Op, STRIDE>::run(Op{(const lds_char*)lds, OutC<CT>{C + base}}, t, total, cpr,
+                                    N, LP, nb);
+      return;
+    }
+#define MK_RING(NPV)                                                                     \
+  case NPV:                                                                              \
+    if constexpr (ring_fits<2, PT, NPV>()) {                                             \
+      const PT* pr[NPV];                                                                 \
+      _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base;   \
+      typedef SumOp<PT, NPV, PartialLdsLate, OutC<CT>> Op;                               \
+      PacedRing<ws_ring_depth<PT, NPV>(), Op, STRIDE>::run(Op{ps, pr, OutC<CT>{C + base}}, t,  \
+                                                           total, cpr, N, LP, nb);       \
+      return;                                                                            \
+    }                                                                                    \
+    break;
+    switch (n_peers) {
+      MK_RING_PEER_COUNTS(MK_RING)
+      default: break;
+    }
+#undef MK_RING
+  }
+  for (int i = 0; i < nb; ++i) __syncthreads();
 }
 
 // Rounds the fp32 partial of a region in LDS (row pitch LP) to OT and stores it

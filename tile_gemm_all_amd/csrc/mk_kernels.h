@@ -59,7 +59,10 @@ constexpr size_t kScratchFlags = MK_NOALLOC_MAX_TILE_FLAGS;
 constexpr size_t kScratchPartialBytes = MK_NOALLOC_PARTIAL_BYTES;
 constexpr size_t kScratchBytes = kScratchSlotBytes + kScratchFlags * 4 + kScratchPartialBytes;
 
-enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2, SHAPE_64 = 3 };
+// SHAPE_WS: 64x256 tiles in the wave-specialised kernel (768 threads, the GEMM
+// of one tile overlapping the reduce of the one before, every tile in place)
+enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2, SHAPE_64 = 3, SHAPE_WS = 4 };
+constexpr int kShapes = 5;
 
 // Tile queues and flag protocol of a persistent launch of G workgroups on a
 // device with `cus` compute units. gfx950 groups 32 compute units per XCD, each
@@ -216,6 +219,7 @@ const void* ag_kernel_ptr(int shape, int ct);
 const void* gemm_kernel_ptr(int shape);
 const void* reduce_kernel_ptr(int pt, int ct);
 int shape_bm(int shape);
+int shape_threads(int shape);  // workgroup size of the fused kernel of a shape
 int shape_bn(int shape);
 
 hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s);

@@ -1232,6 +1232,98 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
   out[(size_t)blockIdx.x * kThreads + tid] = sum;
 }
 
+// ------------------------------------------------------------ wave-specialised AllReduce
+
+// Persistent fused GEMM+AllReduce in which the GEMM and the reduce overlap inside
+// each workgroup: one workgroup of 768 threads per compute unit. Waves 0-3 run
+// the GEMM of the workgroup's tiles one after another (the fp32 accumulators in
+// their registers); waves 4-11 meanwhile reduce the tile before: its partial
+// waits in LDS, where the GEMM waves staged it when their k-loop ended, and the
+// streaming waves add it to the sum of the peers' slices and write C. The
+// matrix cores thus work while the peers stream from HBM, and no partial goes
+// through device memory. Three waves per SIMD leave 168 registers per lane,
+// which the GEMM of 32-deep k-tiles fits (64-deep ones spill).
+//
+// Tiles are 64 x 256: a tile row is 512 contiguous bytes of every bfloat16 peer
+// (128 x 128 tiles read 256-byte pieces, which streamed about 15% slower from
+// HBM on MI355X), and the fp32 partial (64 KiB) plus four k-stages (80 KiB) fit
+// the LDS. They are dealt statically: XCD x owns a contiguous range of the tile
+// order, served by its workgroups in turn.
+//
+// Both groups pass the same workgroup barriers in each round: the GEMM's k-loop
+// holds one per k-tile and a last one after it; the streaming waves spread as
+// many as the k-loop has over their chunks and meet the last one when their
+// reads of the partial are done. After that barrier the GEMM waves stage the new
+// partial, and one more barrier hands it over. The round after the last GEMM
+// only streams.
+constexpr int kWsStream = 2 * kThreads;  // streaming threads
+constexpr int kWsThreads = kThreads + kWsStream;
+using TWs = TileCfg<64, 256>;
+constexpr int kWsPartialBytes = TWs::BM * TWs::BN * 4;
+
+template <typename PT, typename CT>
+__global__ __launch_bounds__(kWsThreads, 1) void ws_kernel(FusedArgs a) {
+  using Cfg = TWs;
+  static_assert(GemmTile<Cfg>::NPASS == 1, "the whole fp32 tile is staged in one pass");
+  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES + kWsPartialBytes];
+  char* const part = lds + Cfg::LDS_BYTES;
+  const int b = blockIdx.x, G = gridDim.x;
+  // this workgroup's tiles: q0 + s, q0 + s + per, ... below q1
+  int q0 = 0, q1 = a.T, s = b, per = G;
+  if (a.n_xcd > 1 && G % a.n_xcd == 0) {
+    const int x = b % a.n_xcd;  // workgroups are dealt to the XCDs in turn
+    q0 = (int)(((int64_t)x * a.T) / a.n_xcd);
+    q1 = (int)(((int64_t)(x + 1) * a.T) / a.n_xcd);
+    s = b / a.n_xcd;
+    per = G / a.n_xcd;
+  }
+  const int n_my = q1 - q0 > s ? (q1 - q0 - s + per - 1) / per : 0;
+  const int KT = (int)((a.K + Cfg::BK - 1) / Cfg::BK);
+  auto origin = [&](int j, int64_t& m0, int64_t& n0) {
+    int tm, tn;
+    fused_tile_coords(q0 + s + j * per, a.tiles_m, a.tiles_n, tm, tn);
+    m0 = (int64_t)tm * Cfg::BM;
+    n0 = (int64_t)tn * Cfg::BN;
+  };
+  // Each group runs its own loop over the rounds (what one keeps in registers
+  // across rounds is not live in the other's code).
+  if (threadIdx.x < kThreads) {
+    for (int j = 0; j <= n_my; ++j) {
+      if (j < n_my) {
+        int64_t m0, n0;
+        origin(j, m0, n0);
+        GemmTile<Cfg> g;
+        g.run(a.A, a.B, a.M, a.N, a.K, m0, n0, lds);  // KT + 1 barriers (none when K = 0)
+        if (KT == 0) __syncthreads();
+        g.template stage_pass_lds<0>(part);
+      } else {
+        __syncthreads();  // stands for the k-loop's last barrier
+      }
+      __syncthreads();  // the new partial is staged
+    }
+  } else {
+    const PT* peers = (const PT*)a.peers;
+    CT* C = (CT*)a.C;
+    const int t = threadIdx.x - kThreads;
+    for (int j = 0; j <= n_my; ++j) {
+      // barriers of this round's k-loop before its last one
+      const int nb = j < n_my ? KT : 0;
+      if (j > 0) {
+        int64_t m0, n0;  // the tile whose partial is staged
+        origin(j - 1, m0, n0);
+        const int rows = (int)(a.M - m0 < Cfg::BM ? a.M - m0 : Cfg::BM);
+        const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
+        stream_region_lds<kWsStream, PT, CT>(part, Cfg::BN, peers, a.n_peers, C, a.M, a.N, m0,
+                                             n0, rows, cols, t, nb);
+      } else {
+        for (int i = 0; i < nb; ++i) __syncthreads();
+      }
+      __syncthreads();  // the k-loop's last barrier: the staged partial is consumed
+      __syncthreads();  // the new partial is staged
+    }
+  }
+}
+
 // ------------------------------------------------------------ host-side launchers
 
 using T256 = TileCfg<256, 256, 64, 2>;  // 64-deep k-tiles, two LDS stages
@@ -1249,7 +1341,15 @@ static const void* fused_ptr(int pt, int ct) {
   return (const void*)fused_kernel<Cfg, float, float, DYN>;
 }
 
+static const void* ws_ptr(int pt, int ct) {
+  if (pt == MK_DT_BF16 && ct == MK_DT_BF16) return (const void*)ws_kernel<uint16_t, uint16_t>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)ws_kernel<uint16_t, float>;
+  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)ws_kernel<float, uint16_t>;
+  return (const void*)ws_kernel<float, float>;
+}
+
 const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn) {
+  if (shape == SHAPE_WS) return ws_ptr(pt, ct);
   if (shape == SHAPE_64) return fused_ptr<T64, false>(pt, ct);  // no dynamic variant
   if (dyn) return shape == SHAPE_256 ? fused_ptr<T256, true>(pt, ct) : fused_ptr<T128, true>(pt, ct);
   return shape == SHAPE_256 ? fused_ptr<T256, false>(pt, ct) : fused_ptr<T128, false>(pt, ct);
@@ -1278,8 +1378,15 @@ const void* reduce_kernel_ptr(int pt, int ct) {
   return (const void*)reduce_kernel<float, float>;
 }
 
-int shape_bm(int shape) { return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128); }
-int shape_bn(int shape) { return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128); }
+int shape_threads(int shape) { return shape == SHAPE_WS ? kWsThreads : kThreads; }
+int shape_bm(int shape) {
+  if (shape == SHAPE_WS) return TWs::BM;
+  return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128);
+}
+int shape_bn(int shape) {
+  if (shape == SHAPE_WS) return TWs::BN;
+  return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128);
+}
 
 hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s) {
   hipLaunchKernelGGL(ws_init_kernel, dim3(64), dim3(256), 0, s, flags, n_flags, slots);
@@ -1294,7 +1401,7 @@ hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s) {
 hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s) {
   const void* f = fused_kernel_ptr(shape, pt, ct, a.dyn);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel(f, dim3(a.G), dim3(kThreads), args, 0, s);
+  return hipLaunchKernel(f, dim3(a.G), dim3(shape_threads(shape)), args, 0, s);
 }
 
 hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s) {
