@@ -35,6 +35,9 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload large]
        python bench.py --trace attn --trace-inplace 0
                                          (one JSON line: the controller's trace
                                           and the device-timer role breakdown)
+       python bench.py --flag-overhead decode
+                                         (one JSON line per flag scope: device
+                                          timers of the tile-flag hand-over)
 
 --all-configs times batches of calls between two HIP events (10 batches of 20
 calls after warmup; median, p10 and p90 of the per-call averages). Workloads
@@ -259,6 +262,70 @@ def trace(name, inplace):
                       "updates": t.n_updates, "trace": pts}), flush=True)
 
 
+def flag_overhead(name):
+    """Tile-flag overhead inside the fused kernel, from its device timers: every tile
+    handed to reducers through its flag (MK_OPT_INPLACE=0; 128x128 tiles on shapes
+    that would otherwise take 64x64 ones, which never publish), under XCD-local
+    flags (scope 0) and agent-scope release/acquire (scope 1). Per published tile:
+    ticks from its partial's store-complete wait to its flag store; per reduce
+    unit: ticks from the poll that sees the flag to the end of the acquire. One
+    JSON line per scope, with the call's time without telemetry next to it."""
+    import torch
+
+    import mk_inputs
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    w = mk_inputs.BY_NAME[name]
+    A, B, peers = mk_inputs.workload_inputs(w, "gaussian", device="cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16 if w.c_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    tel = torch.zeros(mk.TELEMETRY_BYTES, dtype=torch.uint8, device="cuda")
+    opts = (mk.OPT_INPLACE, mk.OPT_FLAG_SCOPE, mk.OPT_TILE_SHAPE)
+    old = [mk.get_option(o) for o in opts]
+    tiles128 = -(-w.M // 128) * -(-w.N // 128)
+    shape = 2 if tiles128 < torch.cuda.get_device_properties(0).multi_processor_count else 0
+    try:
+        for scope in (0, 1):
+            mk.set_option(mk.OPT_INPLACE, 0)
+            mk.set_option(mk.OPT_FLAG_SCOPE, scope)
+            mk.set_option(mk.OPT_TILE_SHAPE, shape)
+            for _ in range(3):
+                mk.gemm_ar_local(A, B, peers, C, telemetry=tel)
+            mk.stream_status()
+            t = mk.Telemetry.from_buffer_copy(bytes(tel.cpu().numpy()))
+            reps = 50 if w.flops < 1e10 else 10
+            for _ in range(3):
+                mk.gemm_ar_local(A, B, peers, C)
+            torch.cuda.synchronize()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                mk.gemm_ar_local(A, B, peers, C)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            mk.stream_status()
+            span = (t.t_end - t.t_start) / 100.0  # us (100 MHz ticks)
+            slots = t.grid * span
+            print(json.dumps({
+                "mode": "flag_overhead", "workload": name, "flag_scope": scope,
+                "tile": "128x128" if shape == 2 else "auto", "tiles": t.tiles, "grid": t.grid,
+                "call_us": round(ev0.elapsed_time(ev1) / reps * 1e3, 2),
+                "span_us_with_telemetry": round(span, 2),
+                "published": t.published,
+                "publish_us_per_tile": round(t.publish_ticks / 100.0 / max(t.published, 1), 3),
+                "acquired": t.acquired,
+                "acquire_us_per_unit": round(t.acquire_ticks / 100.0 / max(t.acquired, 1), 3),
+                "publish_frac_of_workgroup_time": round(t.publish_ticks / 100.0 / slots, 4),
+                "acquire_frac_of_workgroup_time": round(t.acquire_ticks / 100.0 / slots, 4),
+                "wait_reduce_frac": round(t.wait_reduce / 100.0 / slots, 4)}), flush=True)
+    finally:
+        for o, v in zip(opts, old):
+            mk.set_option(o, v)
+
+
 def peaks():
     """Measured ceilings of the chip next to the published ones the rooflines use:
     bf16 matrix-core throughput of register-only MFMA chains on every compute unit
@@ -416,6 +483,9 @@ def main():
     ap.add_argument("--trace", metavar="WORKLOAD",
                     help="one call with telemetry; --trace-inplace 0 hands every tile over")
     ap.add_argument("--trace-inplace", type=int, default=-1)
+    ap.add_argument("--flag-overhead", metavar="WORKLOAD",
+                    help="device timers of the tile-flag hand-over (publish and acquire) "
+                         "with every tile handed over, under both flag scopes")
     ap.add_argument("--cpu-oracle", action="store_true",
                     help="the CPU oracle's GFLOP/s on every workload (all threads; one "
                          "thread for tiny and decode)")
@@ -436,6 +506,9 @@ def main():
         return
     if args.trace:
         trace(args.trace, args.trace_inplace)
+        return
+    if args.flag_overhead:
+        flag_overhead(args.flag_overhead)
         return
     if args.litmus:
         litmus(args.litmus)

@@ -125,6 +125,17 @@ typedef struct {
   int32_t reduced_by_compute;/* tiles reduced by compute-role workgroups (draining) */
   int32_t computed_by_reducers; /* tiles computed by reducer-role workgroups with nothing to reduce */
   int32_t n_xcd;             /* XCDs; each XCD computes and reduces its own share of tiles */
+  /* Tile-flag overhead (the two halves of a hand-over that Table 2's caption of the
+   * thelatestinai.com page separates: a write completing, then becoming visible):
+   * publish_ticks sums, over the tiles handed to reducers, the ticks from the
+   * computing workgroup's wait for its partial stores to complete to its flag
+   * store; acquire_ticks sums, over reduce units, the ticks from the poll that
+   * sees the flag to the end of the acquire (wait_reduce, which also counts the
+   * time spent waiting for the tile to be computed, includes it). */
+  uint64_t publish_ticks;
+  uint64_t acquire_ticks;
+  int32_t published;         /* tiles handed over through a flag */
+  int32_t acquired;          /* reduce units that acquired a flag */
   mk_trace_entry_t trace[MK_TRACE_CAP];
 } mk_telemetry_t;
 

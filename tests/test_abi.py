@@ -141,8 +141,9 @@ def test_options_roundtrip():
 
 
 def test_telemetry_struct_size():
-    # 5 u64 + 10 i32 + MK_TRACE_CAP entries of 24 bytes
-    assert mk.TELEMETRY_BYTES == 5 * 8 + 10 * 4 + mk.MK_TRACE_CAP * 24
+    # 5 u64 + 10 i32, 2 u64 + 2 i32 of flag overhead, MK_TRACE_CAP entries of 24 bytes
+    assert mk.TELEMETRY_BYTES == 5 * 8 + 10 * 4 + 2 * 8 + 2 * 4 + mk.MK_TRACE_CAP * 24
+    assert mk.Telemetry.trace.offset == 104
 
 
 S16 = 0xC0000000

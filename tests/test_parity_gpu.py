@@ -393,6 +393,19 @@ def test_telemetry_and_controller_trace(inplace_policy):
     assert all(lo <= x <= G for x in targets)
     # once every tile is computed the controller hands all workgroups to the reduce
     assert all(t.trace[i].target == G for i in range(t.n_trace) if computed[i] == t.tiles)
+    # flag-overhead timers: every tile handed over is published once and each of its
+    # reduce units (64-row slabs) acquires once; tiles reduced in place use no flag
+    rsplit = 4 if t.tiles == (w.M // 256) * (w.N // 256) else 2
+    if inplace_policy == -1:
+        assert t.published == 0 and t.acquired == 0
+        assert t.publish_ticks == 0 and t.acquire_ticks == 0
+    elif inplace_policy == 0:
+        assert t.published == t.tiles and t.acquired == t.tiles * rsplit
+        assert t.publish_ticks > 0
+    else:
+        assert 0 <= t.published <= t.tiles and 0 <= t.acquired <= t.tiles * rsplit
+    # an acquire ends after its poll, within the call
+    assert t.acquire_ticks <= t.wait_reduce
 
 
 @pytest.mark.parametrize("name", ["mlp", "attn"])

@@ -125,7 +125,9 @@ class Telemetry(ctypes.Structure):
                 ("final_target", ctypes.c_int32), ("n_updates", ctypes.c_int32),
                 ("n_trace", ctypes.c_int32), ("role_switches", ctypes.c_int32),
                 ("reduced_by_compute", ctypes.c_int32), ("computed_by_reducers", ctypes.c_int32),
-                ("n_xcd", ctypes.c_int32), ("trace", TraceEntry * MK_TRACE_CAP)]
+                ("n_xcd", ctypes.c_int32), ("publish_ticks", ctypes.c_uint64),
+                ("acquire_ticks", ctypes.c_uint64), ("published", ctypes.c_int32),
+                ("acquired", ctypes.c_int32), ("trace", TraceEntry * MK_TRACE_CAP)]
 
 
 TELEMETRY_BYTES = ctypes.sizeof(Telemetry)

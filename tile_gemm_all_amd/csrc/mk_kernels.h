@@ -29,6 +29,10 @@ enum XcdSlot : int {
   X_PHYS,              // 1 + the hardware XCD id of the workgroups serving this queue (0 = none yet)
   X_STREAM,            // workgroups streaming a reduce now (in place or a handed-over unit)
   X_PUB,               // dynamic hand-over: tiles of the queue published for reducers
+  X_PUB_T,             // summed ticks from a partial's store-complete wait to its flag store
+  X_ACQ_T,             // summed ticks from a flag seen set to the end of its acquire
+  X_NPUB,              // tiles published through a flag
+  X_NACQ,              // reduce units that acquired a flag
   kXcdWords
 };
 constexpr int kMaxXcd = 16;

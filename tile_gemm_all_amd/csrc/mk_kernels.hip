@@ -587,6 +587,8 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         continue;
       }
       g.store_partial(a.P + (KS > 1 ? part * a.M * a.N : 0), a.M, a.N, m0, n0);
+      // with telemetry: ticks from here (stores issued) to the flag store
+      const unsigned long long tp0 = a.tel && tid == 0 ? ticks() : 0ull;
       wait_stores();    // this wave's partial stores have reached the L2
       __syncthreads();  // ... and so have every other wave's
       if (tid == 0) {
@@ -607,6 +609,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
           int* fp = a.flags + tile * KS + part;
           if (a.flag_scope == 0) store_flag(fp, a.epoch);
           else publish_flag_agent(fp, a.epoch);
+        }
+        if (a.tel) {
+          atomicAdd(xslot64(S, x, X_PUB_T), ticks() - tp0);
+          atomicAdd(xslot(S, x, X_NPUB), 1);
         }
         int done = atomicAdd(xslot(S, x, X_COMPUTED), 1) + 1;  // this XCD's count
         atomicAdd(xslot64(S, x, X_BUSY_C), ticks() - t0);
@@ -647,6 +653,7 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
             backoff = backoff < 4 ? backoff * 2 : 4;
           }
         }
+        const unsigned long long ws = ticks();  // every flag of the unit seen set
         // The partial must not come from a stale L1 copy: with lines that can
         // hold two units' rows (or agent-scope flags) acquire at agent scope;
         // otherwise this compute unit has never read the unit's lines in this
@@ -654,6 +661,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         if (a.flag_scope != 0 || a.shared_lines) acquire_fence_agent();
         const unsigned long long w1 = ticks();
         atomicAdd(xslot64(S, x, X_WAIT_R), w1 - w0);
+        if (a.tel && ok) {
+          atomicAdd(xslot64(S, x, X_ACQ_T), w1 - ws);
+          atomicAdd(xslot(S, x, X_NACQ), 1);
+        }
         s_ok = ok;
         // busy time: phase 1 plus what follows the wait
         t_busy = (w0 - t0) - w1;
@@ -721,6 +732,10 @@ __global__ __launch_bounds__(kThreads, Cfg::OCC) void fused_kernel(FusedArgs a) 
         t->reduced_by_compute = sum_xcd32(S, a.n_xcd, X_RBC) / Cfg::RSPLIT;  // units -> tiles
         t->computed_by_reducers = sum_xcd32(S, a.n_xcd, X_CBR);
         t->n_xcd = a.n_xcd;
+        t->publish_ticks = sum_xcd64(S, a.n_xcd, X_PUB_T);
+        t->acquire_ticks = sum_xcd64(S, a.n_xcd, X_ACQ_T);
+        t->published = sum_xcd32(S, a.n_xcd, X_NPUB);
+        t->acquired = sum_xcd32(S, a.n_xcd, X_NACQ);
       }
     }
   }
