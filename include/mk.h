@@ -391,12 +391,12 @@ typedef enum {
                                    only: each tile reduced in place by the workgroup that computed
                                    it; automatic for shapes with fewer 128x128 tiles than CUs),
                                    4 = wave-specialised (fused AllReduce only, without telemetry:
-                                   64x256 tiles, one 768-thread workgroup per CU whose first four
-                                   waves compute a tile while the other eight reduce the tile
+                                   64x256 tiles, one 384-thread workgroup per CU whose first four
+                                   waves compute a tile while the other two reduce the tile
                                    before from LDS; peer counts 1-4, 7, 8 and 15 of bfloat16, 1-4,
                                    7 and 8 of float32; otherwise as 0). Automatic, with no
                                    reducer count, in-place policy, early reduce or k-split set,
-                                   when the peer stream at HBM peak takes at least four times the
+                                   when the peer stream at HBM peak takes at least twice the
                                    GEMM at matrix-core peak and there are as many 64x256 tiles
                                    as CUs */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default: stores complete + relaxed flag store,

@@ -303,20 +303,21 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
 }
 
 // Whether the wave-specialised kernel is the automatic choice: for shapes whose
-// peer stream (at HBM peak) takes at least four times their GEMM (at matrix-core
+// peer stream (at HBM peak) takes at least twice their GEMM (at matrix-core
 // peak), with a 64x256 tile for every compute unit. There the GEMM hides under
-// the stream; where the two are closer its 64x256 tiles, which load more bytes
-// per flop than 256x256 ones, cost more than the overlap gains. Measured on
-// MI355X (ratio 9.8) 16384x8192x512 with 15 peers: 835 us against 975 us with
-// every 256x256 tile reduced in place (two-kernel baseline 1360 us); on
-// 4096x8192x1792 (ratio 2.8) 320-360 against 322-342 us, and on 8192^3 with 7
-// peers (0.3) 1680 against 1091 us.
+// the stream; where the GEMM weighs more, its 64x256 tiles, which load more
+// bytes per flop than 256x256 ones, cost more than the overlap gains. Measured
+// on MI355X against every 256x256 tile reduced in place (stream/GEMM ratio in
+// brackets), us per call: 16384x8192x512 P=16 (9.8) 821 against 963;
+// 16384x8192x1024 P=16 (4.9) 918 / 1057; 4096x8192x1792 P=16 (2.8) 308 / 322;
+// 8192x16384x1024 P=8 (2.4) 633 / 660; 4096x8192x3584 P=16 (1.4) 480 / 424;
+// 8192x8192x2048 P=8 (1.2) 519 / 466; 8192x8192x4096 P=8 (0.6) 903 / 677.
 bool ws_pays(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   const double t_stream =
       (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype)) / 8.0e12;
   const double t_gemm = 2.0 * (double)M * (double)N * (double)K / 2.5e15;
   const int64_t tiles = ((M + 63) / 64) * ((N + 255) / 256);
-  return tiles >= cus && t_stream >= 4.0 * t_gemm;
+  return tiles >= cus && t_stream >= 2.0 * t_gemm;
 }
 
 // 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile:

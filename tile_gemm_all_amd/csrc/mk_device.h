@@ -1061,10 +1061,11 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
 #undef MK_RING
 }
 
-// Ring depth of the streaming waves of a wave-specialised workgroup: three waves
-// share each SIMD (168 registers per lane each); chunks in flight hold only their
-// peers' registers (the partial is read from LDS when the chunk is summed),
-// within about 120 registers, between 2 and 4 chunks.
+// Ring depth of the streaming waves of a wave-specialised workgroup: chunks in
+// flight hold only their peers' registers (the partial is read from LDS when the
+// chunk is summed), within about 120 registers, between 2 and 4 chunks (a third
+// chunk of 15 bfloat16 peers in flight streamed about 5% slower on MI355X: more
+// concurrent peer streams per wave).
 template <typename PT, int NP>
 __host__ __device__ constexpr int ws_ring_depth() {
   constexpr int regs = NP * (sizeof(PT) == 2 ? 4 : 8);

@@ -1250,14 +1250,17 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 // ------------------------------------------------------------ wave-specialised AllReduce
 
 // Persistent fused GEMM+AllReduce in which the GEMM and the reduce overlap inside
-// each workgroup: one workgroup of 768 threads per compute unit. Waves 0-3 run
+// each workgroup: one workgroup of 384 threads per compute unit. Waves 0-3 run
 // the GEMM of the workgroup's tiles one after another (the fp32 accumulators in
-// their registers); waves 4-11 meanwhile reduce the tile before: its partial
+// their registers); waves 4-5 meanwhile reduce the tile before: its partial
 // waits in LDS, where the GEMM waves staged it when their k-loop ended, and the
 // streaming waves add it to the sum of the peers' slices and write C. The
 // matrix cores thus work while the peers stream from HBM, and no partial goes
-// through device memory. Three waves per SIMD leave 168 registers per lane,
-// which the GEMM of 32-deep k-tiles fits (64-deep ones spill).
+// through device memory. Two streaming waves streamed as fast as four or eight
+// on MI355X (16384x8192x512 with 15 peers: 817, 817 and 838 us) and left more
+// of each CU's memory pipeline to the GEMM's loads (4096x8192x1792: 301, 311 and
+// 316 us); deeper rings were slower (859 us). 32-deep k-tiles: 64-deep ones
+// spill.
 //
 // Tiles are 64 x 256: a tile row is 512 contiguous bytes of every bfloat16 peer
 // (128 x 128 tiles read 256-byte pieces, which streamed about 15% slower from
@@ -1271,7 +1274,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 // reads of the partial are done. After that barrier the GEMM waves stage the new
 // partial, and one more barrier hands it over. The round after the last GEMM
 // only streams.
-constexpr int kWsStream = 2 * kThreads;  // streaming threads
+constexpr int kWsStream = 128;  // streaming threads (two waves)
 constexpr int kWsThreads = kThreads + kWsStream;
 using TWs = TileCfg<64, 256>;
 constexpr int kWsPartialBytes = TWs::BM * TWs::BN * 4;
