@@ -580,7 +580,8 @@ def main():
                  "speedup_vs_two_kernel": round(b_ms / f_ms, 4),
                  "TFLOPs": round(o.flops / (f_ms * 1e-3) / 1e12, 2),
                  "GBps": round(o.compulsory_bytes() / (f_ms * 1e-3) / 1e9, 1),
-                 "roofline": roofline_of(o, f_ms * 1e3)}
+                 "roofline": roofline_of(o, f_ms * 1e3),
+                 "schedule": mk.SCHEDULES[mk.fused_schedule(*sets[0], C)]}
             if o.name == "mlp":
                 A, B, peers = base_in
                 # the comparison schedules of the pages' Figure 1 on the mlp shape
@@ -676,7 +677,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "M": w.M, "N": w.N, "K_local": w.K,
                    "P": w.P, "peer_dtype": w.peer_dtype, "c_dtype": w.c_dtype,
-                   "reducers": "adaptive" if args.n_reduce_wg is None else args.n_reduce_wg},
+                   "reducers": "adaptive" if args.n_reduce_wg is None else args.n_reduce_wg,
+                   # the adaptive call's schedule: with every tile reduced in place the
+                   # controller keeps no dedicated reducers (a static count takes the
+                   # role split instead)
+                   "schedule": (mk.SCHEDULES[mk.fused_schedule(A, B, peers, C)]
+                                if args.n_reduce_wg is None
+                                else f"persistent kernel, {args.n_reduce_wg} workgroups prefer "
+                                     "reducing")},
         "roofline": roofline,
         "effective_GBps": round(w.compulsory_bytes() / (fused_ms * 1e-3) / 1e9, 1),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),

@@ -382,6 +382,15 @@ int mk_num_workgroups(int device);
  * failure. */
 int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype);
 
+/* The schedule that mk_gemm_ar_local with these sizes, MK_ADAPTIVE and no
+ * telemetry takes under the options in force: its tile shape as an
+ * MK_OPT_TILE_SHAPE value, 1 = 256x256 and 2 = 128x128 (the persistent kernel;
+ * with the default MK_OPT_INPLACE every tile reduced in place by the workgroup
+ * that computed it, unless early reduce applies), 3 = 64x64 (one workgroup per
+ * tile, in place), 4 = the wave-specialised kernel. Returns a negative
+ * mk_status_t on failure (no device included). */
+int mk_fused_schedule(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype);
+
 /* Tunables and debug switches (process-wide; read at each call). */
 typedef enum {
   MK_OPT_SPIN_TIMEOUT_US = 0,   /* reducer flag-wait limit, microseconds (default 2000000) */

@@ -309,3 +309,13 @@ def test_queue_plan_rejects_bad_arguments():
     assert lib.mk_queue_plan(256, 0, 0, ctypes.byref(n)) == -mk.MK_ERR_INVALID_ARG
     assert lib.mk_queue_plan(256, 256, 2, ctypes.byref(n)) == -mk.MK_ERR_INVALID_ARG
     assert lib.mk_queue_plan(256, 256, 0, None) == -mk.MK_ERR_INVALID_ARG
+
+
+def test_fused_schedule_validates_before_touching_the_device():
+    lib = mk.library()
+    for args in ((64, 64, 64, 1, 7, 0), (64, 64, 64, 1, 0, 7), (-1, 64, 64, 1, 0, 0),
+                 (64, 64, 64, -1, 0, 0)):
+        assert lib.mk_fused_schedule(*args) == -mk.MK_ERR_INVALID_ARG
+    # valid arguments need the device (its compute-unit count): a schedule or an error
+    v = lib.mk_fused_schedule(4096, 8192, 1792, 15, 0, 0)
+    assert v in (1, 2, 3, 4) or -v in (mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP)

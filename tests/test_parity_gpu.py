@@ -558,6 +558,32 @@ def test_wave_specialised_schedule(shape):
         mk.set_option(mk.OPT_TILE_SHAPE, old)
 
 
+def test_automatic_schedule_per_workload():
+    """The automatic choice on MI355X (256 CUs): few-tile shapes take 64x64 tiles
+    in place, stream-dominated ones the wave-specialised kernel, the compute-bound
+    shard 256x256 tiles in place; an explicit schedule option or a forced shape
+    is honoured."""
+    want = {"tiny": 3, "decode": 3, "mlp": 4, "attn": 4, "large": 1}
+    for w in mk_inputs.WORKLOADS:
+        A = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=DEV)
+        B = torch.empty((w.K, w.N), dtype=torch.bfloat16, device=DEV)
+        peers = torch.empty((w.n_peers, w.M, w.N), dtype=TORCH_DT[w.peer_dtype], device=DEV)
+        C = torch.empty((w.M, w.N), dtype=TORCH_DT[w.c_dtype], device=DEV)
+        assert mk.fused_schedule(A, B, peers, C) == want[w.name], w.name
+        if w.name == "attn":
+            old = mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_TILE_SHAPE)
+            try:
+                mk.set_option(mk.OPT_INPLACE, 0)  # an explicit schedule keeps the role split
+                assert mk.fused_schedule(A, B, peers, C) == 1
+                mk.set_option(mk.OPT_INPLACE, -1)
+                mk.set_option(mk.OPT_TILE_SHAPE, 2)
+                assert mk.fused_schedule(A, B, peers, C) == 2
+            finally:
+                mk.set_option(mk.OPT_INPLACE, old[0])
+                mk.set_option(mk.OPT_TILE_SHAPE, old[1])
+        del A, B, peers, C
+
+
 TWO_STREAM_SHAPES = [
     # M, N, K, n_peers, peer dtype, C dtype: one tile row, ragged rows, 256x256 tiles
     (256, 512, 512, 3, "f32", "f32"),

@@ -40,6 +40,7 @@ EXPORTS = ["mk_gemm_ar_local", "mk_gemm_ar_local_noalloc", "mk_gemm_then_reduce_
            "mk_ag_grid", "mk_flag_handoff", "mk_mfma_peak",
            "mk_stream_status",
            "mk_workspace_reset", "mk_queue_plan", "mk_num_workgroups", "mk_fused_grid",
+           "mk_fused_schedule",
            "mk_set_option",
            "mk_get_option",
            "mk_controller_eval", "mk_status_string", "mk_last_error", "mk_version"]
@@ -97,6 +98,8 @@ _lib.mk_num_workgroups.argtypes = [_int]
 _lib.mk_num_workgroups.restype = _int
 _lib.mk_fused_grid.argtypes = [_i64, _i64, _i64, _int, _int, _int]
 _lib.mk_fused_grid.restype = _int
+_lib.mk_fused_schedule.argtypes = [_i64, _i64, _i64, _int, _int, _int]
+_lib.mk_fused_schedule.restype = _int
 _lib.mk_set_option.argtypes = [_int, _i64]
 _lib.mk_set_option.restype = _int
 _lib.mk_get_option.argtypes = [_int]
@@ -379,6 +382,21 @@ def fused_grid(A, B, peers, C):
     if g < 0:
         _check(-g)
     return g
+
+
+SCHEDULES = {1: "256x256 tiles, every tile in place", 2: "128x128 tiles, every tile in place",
+             3: "64x64 tiles, one workgroup per tile, in place",
+             4: "wave-specialised, 64x256 tiles"}
+
+
+def fused_schedule(A, B, peers, C):
+    """Tile shape (MK_OPT_TILE_SHAPE value, 1-4) of the schedule gemm_ar_local takes
+    for these tensors with the adaptive default and no telemetry."""
+    a = _args(A, B, peers, C)
+    v = _lib.mk_fused_schedule(a[5], a[6], a[7], a[3], a[8], a[9])
+    if v < 0:
+        _check(-v)
+    return v
 
 
 def set_option(option, value):

@@ -1519,6 +1519,17 @@ int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, 
   return fused_grid_size(L, n_peers, peer_dtype, c_dtype);
 }
 
+int mk_fused_schedule(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype) {
+  if (peer_dtype != MK_DT_BF16 && peer_dtype != MK_DT_F32) return -(int)MK_ERR_INVALID_ARG;
+  if (c_dtype != MK_DT_BF16 && c_dtype != MK_DT_F32) return -(int)MK_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0 || n_peers < 0) return -(int)MK_ERR_INVALID_ARG;
+  Launch L;
+  mk_status_t st =
+      prepare(M, N, K, n_peers, peer_dtype, c_dtype, L, true, true, ws_auto_allowed(MK_ADAPTIVE));
+  if (st != MK_OK) return -(int)st;
+  return L.shape;
+}
+
 mk_status_t mk_set_option(int option, int64_t value) {
   std::lock_guard<std::mutex> lk(g_opt_mu);
   switch (option) {
