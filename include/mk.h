@@ -155,7 +155,7 @@ typedef struct {
  *                    lets the library take the wave-specialised schedule
  *                    (MK_OPT_TILE_SHAPE); forced by that option, it ignores
  *                    n_reduce_wg (it has no reducer workgroups: each workgroup
- *                    reduces its own tiles with eight of its waves).
+ *                    reduces its own tiles with two of its waves).
  *   telemetry      : NULL or a device buffer of sizeof(mk_telemetry_t); a call with
  *                    telemetry never takes the wave-specialised schedule.
  * Returns MK_OK once the kernel is enqueued.

@@ -947,7 +947,7 @@ struct PacedRing {
         op.finish(b[i], st.get(), st.lget());
         st.advance();
         ++s;
-        const int due = s * nb / steps;
+        const int due = (int)((int64_t)s * nb / steps);  // nb (k-tiles) can exceed 2^25
         while (done < due) {
           __syncthreads();
           ++done;
