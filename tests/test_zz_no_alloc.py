@@ -50,8 +50,9 @@ def abi_call(fn, A, B, peers, C, n_reduce_wg=-1):
 
 # pairs of calls: the second smaller than the first
 PAIRS = [
-    # a shape whose handed-over partial (64 MiB) exceeds the fixed region: every tile
-    # in place, then a few-tile shape with early reduce and k-halves
+    # a shape whose handed-over partial (64 MiB) would exceed the fixed region (the
+    # adaptive call takes the wave-specialised kernel, a static count every
+    # 256x256 tile in place), then a few-tile shape (64x64 tiles)
     ((4096, 4096, 256, 3, "bf16", "bf16"), (128, 2048, 448, 15, "bf16", "bf16")),
     # handed-over and in-place tiles with the partial in the fixed region, then fp32
     ((1024, 2048, 576, 7, "bf16", "bf16"), (256, 512, 512, 3, "f32", "f32")),
