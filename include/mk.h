@@ -387,7 +387,8 @@ int mk_fused_grid(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, 
  * MK_OPT_TILE_SHAPE value, 1 = 256x256 and 2 = 128x128 (the persistent kernel;
  * with the default MK_OPT_INPLACE every tile reduced in place by the workgroup
  * that computed it, unless early reduce applies), 3 = 64x64 (one workgroup per
- * tile, in place), 4 = the wave-specialised kernel. Returns a negative
+ * tile, in place), 4 and 5 = the wave-specialised kernel with 64x256 and 128x128
+ * tiles. Returns a negative
  * mk_status_t on failure (no device included). */
 int mk_fused_schedule(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype);
 
@@ -402,12 +403,14 @@ typedef enum {
                                    4 = wave-specialised (fused AllReduce only, without telemetry:
                                    64x256 tiles, one 384-thread workgroup per CU whose first four
                                    waves compute a tile while the other two reduce the tile
-                                   before from LDS; peer counts 1-4, 7, 8 and 15 of bfloat16, 1-4,
-                                   7 and 8 of float32; otherwise as 0). Automatic, with no
-                                   reducer count, in-place policy, early reduce or k-split set,
-                                   when the peer stream at HBM peak takes at least twice the
-                                   GEMM at matrix-core peak and there are as many 64x256 tiles
-                                   as CUs */
+                                   before from LDS), 5 = the same with 128x128 tiles (4 and 5:
+                                   peer counts 1-4, 7, 8 and 15 of bfloat16, 1-4, 7 and 8 of
+                                   float32; otherwise as 0). Automatic, with no reducer count,
+                                   in-place policy, early reduce or k-split set, when the peer
+                                   stream at HBM peak takes at least twice the GEMM at
+                                   matrix-core peak and there are as many 64x256 tiles as CUs:
+                                   64x256 tiles where the stream weighs most (see
+                                   mk_fused_schedule), 128x128 otherwise */
   MK_OPT_FLAG_SCOPE = 4,        /* 0 = XCD-local flags (default: stores complete + relaxed flag store,
                                    agent-scope acquire), 1 = agent-scope release/acquire */
   MK_OPT_REDUCER_CAP = 5,       /* adaptive mode: most reducers while GEMM tiles remain (0 = derived) */

@@ -113,11 +113,11 @@ def test_options_roundtrip():
     mk.set_option(mk.OPT_CTRL_PERIOD, old)
     with pytest.raises(mk.MkError):
         mk.set_option(mk.OPT_SPIN_TIMEOUT_US, 0)
-    for shape in range(5):  # automatic, 256, 128, 64 and the wave-specialised schedule
+    for shape in range(6):  # automatic, 256, 128, 64 and the two wave-specialised tiles
         mk.set_option(mk.OPT_TILE_SHAPE, shape)
         assert mk.get_option(mk.OPT_TILE_SHAPE) == shape
     mk.set_option(mk.OPT_TILE_SHAPE, 0)
-    for bad in (-1, 5, 7):
+    for bad in (-1, 6, 7):
         with pytest.raises(mk.MkError):
             mk.set_option(mk.OPT_TILE_SHAPE, bad)
     with pytest.raises(mk.MkError):
@@ -318,4 +318,4 @@ def test_fused_schedule_validates_before_touching_the_device():
         assert lib.mk_fused_schedule(*args) == -mk.MK_ERR_INVALID_ARG
     # valid arguments need the device (its compute-unit count): a schedule or an error
     v = lib.mk_fused_schedule(4096, 8192, 1792, 15, 0, 0)
-    assert v in (1, 2, 3, 4) or -v in (mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP)
+    assert v in (1, 2, 3, 4, 5) or -v in (mk.MK_ERR_NO_DEVICE, mk.MK_ERR_HIP)

@@ -104,9 +104,9 @@ SMALL = [  # M, N, K, n_peers, peer dtype, c dtype
 
 
 @pytest.fixture(params=[(-1, -1, 0, 0), (0, 0, 0, 0), (0, 1, 0, 2), (0, 0, 1, 0), (-2, 0, 0, 0),
-                        (-1, -1, 0, 4)],
+                        (-1, -1, 0, 4), (-1, -1, 0, 5)],
                 ids=["auto", "handover-all", "handover-all-early", "handover-all-agent-scope",
-                     "dynamic", "wave-specialised"])
+                     "dynamic", "wave-specialised", "wave-specialised-128"])
 def inplace_policy(request):
     """Runs a test under the default policies (in place and early reduce automatic),
     with every tile handed to reducers through its flag (the role-split path), the
@@ -115,10 +115,10 @@ def inplace_policy(request):
     every tile handed over under agent-scope release/acquire flags
     (MK_OPT_FLAG_SCOPE=1), with each tile reduced in place or published when its
     GEMM ends by the free streaming slots (dynamic hand-over, -2), and under the
-    wave-specialised schedule (MK_OPT_TILE_SHAPE=4: four waves of each workgroup
-    compute a 64x256 tile while eight reduce the one before; peer counts without a
-    compile-time ring, or a call with telemetry, fall back to the automatic
-    choice). Yields the in-place option."""
+    wave-specialised schedule (MK_OPT_TILE_SHAPE=4 and 5: four waves of each
+    workgroup compute a 64x256 or 128x128 tile while two reduce the one before;
+    peer counts without a compile-time ring, or a call with telemetry, fall back to
+    the automatic choice). Yields the in-place option."""
     inplace, early, scope, shape = request.param
     old = (mk.get_option(mk.OPT_INPLACE), mk.get_option(mk.OPT_EARLY),
            mk.get_option(mk.OPT_FLAG_SCOPE), mk.get_option(mk.OPT_TILE_SHAPE))
@@ -526,16 +526,17 @@ WS_SHAPES = [  # several rounds per workgroup, ragged edges, every ring peer cou
 ]
 
 
+@pytest.mark.parametrize("tile", [4, 5], ids=["64x256", "128x128"])
 @pytest.mark.parametrize("shape", WS_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
-def test_wave_specialised_schedule(shape):
-    """The wave-specialised kernel (MK_OPT_TILE_SHAPE=4) on shapes where each of the
-    256 workgroups runs several rounds (the GEMM of one 64x256 tile while the tile
-    before is reduced from LDS): integer inputs bit-exact against the oracle on
+def test_wave_specialised_schedule(shape, tile):
+    """The wave-specialised kernel (MK_OPT_TILE_SHAPE=4: 64x256 tiles, 5: 128x128) on
+    shapes where each of the 256 workgroups runs several rounds (the GEMM of one
+    tile while the tile before is reduced from LDS): integer inputs bit-exact against the oracle on
     sampled rows and bitwise equal to the two-kernel baseline and to the default
     schedule over the whole output, twice in a row (the LDS hand-over starts clean
     in every call); Gaussian inputs within tolerance."""
     M, N, K, npeer, pdt, cdt = shape
-    announce(f"wave-specialised {shape}")
+    announce(f"wave-specialised {shape} tile option {tile}")
     rows = sample_rows(M, band=128, seed=M)
     A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 17, device="cpu")
     _, want = oracle_rows(A, B, peers, cdt, rows)
@@ -545,7 +546,7 @@ def test_wave_specialised_schedule(shape):
     check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, "default schedule")
     old = mk.get_option(mk.OPT_TILE_SHAPE)
     try:
-        mk.set_option(mk.OPT_TILE_SHAPE, 4)
+        mk.set_option(mk.OPT_TILE_SHAPE, tile)
         for rep in range(2):
             check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, f"wave-specialised {rep}")
         A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "gaussian", 18, device="cpu")
@@ -560,10 +561,10 @@ def test_wave_specialised_schedule(shape):
 
 def test_automatic_schedule_per_workload():
     """The automatic choice on MI355X (256 CUs): few-tile shapes take 64x64 tiles
-    in place, stream-dominated ones the wave-specialised kernel, the compute-bound
-    shard 256x256 tiles in place; an explicit schedule option or a forced shape
-    is honoured."""
-    want = {"tiny": 3, "decode": 3, "mlp": 4, "attn": 4, "large": 1}
+    in place, stream-dominated ones the wave-specialised kernel (64x256 tiles for
+    attn, 128x128 for mlp), the compute-bound shard 256x256 tiles in place; an
+    explicit schedule option or a forced shape is honoured."""
+    want = {"tiny": 3, "decode": 3, "mlp": 5, "attn": 4, "large": 1}
     for w in mk_inputs.WORKLOADS:
         A = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=DEV)
         B = torch.empty((w.K, w.N), dtype=torch.bfloat16, device=DEV)

@@ -386,7 +386,7 @@ def fused_grid(A, B, peers, C):
 
 SCHEDULES = {1: "256x256 tiles, every tile in place", 2: "128x128 tiles, every tile in place",
              3: "64x64 tiles, one workgroup per tile, in place",
-             4: "wave-specialised, 64x256 tiles"}
+             4: "wave-specialised, 64x256 tiles", 5: "wave-specialised, 128x128 tiles"}
 
 
 def fused_schedule(A, B, peers, C):

@@ -302,22 +302,25 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
   return MK_OK;
 }
 
-// Whether the wave-specialised kernel is the automatic choice: for shapes whose
-// peer stream (at HBM peak) takes at least twice their GEMM (at matrix-core
-// peak), with a 64x256 tile for every compute unit. There the GEMM hides under
-// the stream; where the GEMM weighs more, its 64x256 tiles, which load more
-// bytes per flop than 256x256 ones, cost more than the overlap gains. Measured
-// on MI355X against every 256x256 tile reduced in place (stream/GEMM ratio in
-// brackets), us per call: 16384x8192x512 P=16 (9.8) 821 against 963;
-// 16384x8192x1024 P=16 (4.9) 918 / 1057; 4096x8192x1792 P=16 (2.8) 308 / 322;
-// 8192x16384x1024 P=8 (2.4) 633 / 660; 4096x8192x3584 P=16 (1.4) 480 / 424;
-// 8192x8192x2048 P=8 (1.2) 519 / 466; 8192x8192x4096 P=8 (0.6) 903 / 677.
-bool ws_pays(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
+// The wave-specialised kernel's automatic choice: for shapes whose peer stream
+// (at HBM peak) takes at least twice their GEMM (at matrix-core peak), with a
+// 64x256 tile for every compute unit; 64x256 tiles (512-byte pieces of peer rows)
+// from four times on, 128x128 tiles (fewer A and B bytes per output) below.
+// Returns the shape, or 0 for the other schedules. Where the GEMM weighs more,
+// the overlap gains less than the smaller tiles cost. Measured on MI355X, us
+// per call (stream/GEMM ratio; 256x256 tiles in place / 64x256 / 128x128):
+//   16384x8192x512 P=16 (9.8)   976 / 812 / 929     8192x8192x512 P=16 (9.8)  498 / 417 / 470
+//   16384x8192x1024 P=16 (4.9) 1051 / 936 / 1000    4096x8192x1024 P=16 (4.9) 288 / 250 / 239
+//   4096x8192x1792 P=16 (2.8)   324 / 314 / 292     8192x8192x1024 P=8 (2.4)  356 / 332 / 318
+//   8192x16384x1024 P=8 (2.4)   676 / 636 / 606     4096x8192x2560 P=16 (1.95) 367 / 384 / 360
+//   4096x8192x3584 P=16 (1.4)   419 / 480 / 442     8192x8192x2048 P=8 (1.2)  469 / 521 / 485
+int ws_pays(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   const double t_stream =
       (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype)) / 8.0e12;
   const double t_gemm = 2.0 * (double)M * (double)N * (double)K / 2.5e15;
   const int64_t tiles = ((M + 63) / 64) * ((N + 255) / 256);
-  return tiles >= cus && t_stream >= 2.0 * t_gemm;
+  if (tiles < cus || t_stream < 2.0 * t_gemm) return 0;
+  return t_stream >= 4.0 * t_gemm ? mk::SHAPE_WS : mk::SHAPE_WS128;
 }
 
 // 256x256 tiles (one workgroup per CU) whenever they still give every CU a tile:
@@ -342,11 +345,11 @@ int pick_shape(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int
   int64_t forced = options().tile_shape;
   if (forced == mk::SHAPE_256 || forced == mk::SHAPE_128) return (int)forced;
   if (forced == mk::SHAPE_64) return allow64 ? mk::SHAPE_64 : mk::SHAPE_128;
-  if (forced == mk::SHAPE_WS && ws) return mk::SHAPE_WS;
+  if ((forced == mk::SHAPE_WS || forced == mk::SHAPE_WS128) && ws) return (int)forced;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (forced == mk::SHAPE_AUTO && ws && auto_ws && ws_pays(M, N, K, n_peers, peer_dtype, c_dtype, cus))
-    return mk::SHAPE_WS;
+  if (forced == mk::SHAPE_AUTO && ws && auto_ws)
+    if (int s = ws_pays(M, N, K, n_peers, peer_dtype, c_dtype, cus)) return s;
   if (t256 >= cus) return mk::SHAPE_256;
   return t128 >= cus || !allow64 ? mk::SHAPE_128 : mk::SHAPE_64;
 }
@@ -379,7 +382,7 @@ bool early_reduce(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   const int64_t opt = options().early;
   const int occ = L.shape == mk::SHAPE_256 ? 1 : 2;
   // 64-wide tiles are always reduced in place
-  if (opt == 0 || n_peers < 1 || L.shape == mk::SHAPE_64 || L.shape == mk::SHAPE_WS ||
+  if (opt == 0 || n_peers < 1 || L.shape == mk::SHAPE_64 || mk::is_ws(L.shape) ||
       !mk::inplace_supported(occ, (int)dt_size(peer_dtype), n_peers))
     return false;
   if (opt > 0) return true;
@@ -423,7 +426,7 @@ int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
     return g < full ? (int)g : full;
   }
   // wave-specialised: one workgroup per compute unit, at most one per tile
-  if (L.shape == mk::SHAPE_WS) return T < full ? (int)(T > 0 ? T : 1) : full;
+  if (mk::is_ws(L.shape)) return T < full ? (int)(T > 0 ? T : 1) : full;
   int64_t want = early_reduce(L, n_peers, peer_dtype, c_dtype)
                      ? T * (ksplit_of(L, n_peers, peer_dtype, c_dtype) + mk::shape_bm(L.shape) / 64)
                      : 2 * T;
@@ -589,7 +592,7 @@ mk_status_t ar_prepare(const void* A, const void* B, const void* peers, int n_pe
   // the reducer count is checked against the grid of the default plan (the
   // wave-specialised kernel has no reducer workgroups and ignores it)
   const int G = fused_grid_size(c.L, n_peers, peer_dtype, c_dtype);
-  if (c.L.shape != mk::SHAPE_WS && n_reduce_wg > G - 1)
+  if (!mk::is_ws(c.L.shape) && n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", n_reduce_wg, G - 1);
   return MK_OK;
 }
@@ -637,9 +640,9 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
       const int64_t g = T < n_xcd ? n_xcd : T;
       G = g < full ? (int)g : full;
     }
-    if (L.shape == mk::SHAPE_WS) G = T < full ? (int)(T > 0 ? T : 1) : full;
+    if (mk::is_ws(L.shape)) G = T < full ? (int)(T > 0 ? T : 1) : full;
   }
-  if (L.shape != mk::SHAPE_WS && c.n_reduce_wg > G - 1)
+  if (!mk::is_ws(L.shape) && c.n_reduce_wg > G - 1)
     return fail(MK_ERR_INVALID_ARG, "n_reduce_wg=%d outside [0, %d]", c.n_reduce_wg, G - 1);
   const int T = (int)(L.tiles_m * L.tiles_n);
   memset(&a, 0, sizeof a);
@@ -692,7 +695,7 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // round), 972 us on 16384x8192x512 and 1107 us on 8192^3 with 7 peers.
   // MK_OPT_INPLACE = -2 decides per tile instead (dynamic hand-over, below).
   a.early = early ? 1 : 0;
-  if (all_inplace || L.shape == mk::SHAPE_WS) {
+  if (all_inplace || mk::is_ws(L.shape)) {
     a.n_inplace = 1 << 30;
   } else if (opt.inplace < 0 && a.early) {
     a.n_inplace = 0;  // early reduce applies to tiles handed to reducers
@@ -709,7 +712,7 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // free then. The controller's target counts workgroups streaming a reduce, in
   // place or handed over, so all reduce work is its reducers' (T_r = T).
   a.dyn = opt.inplace == -2 && !all_inplace && !a.early && inpl_ok && L.shape != mk::SHAPE_64 &&
-                  L.shape != mk::SHAPE_WS
+                  !mk::is_ws(L.shape)
               ? 1
               : 0;
   a.T_r = 0;
@@ -742,7 +745,7 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // One workgroup per tile with every tile in place: no claims or counters (no
   // telemetry either, which is what a telemetry buffer asks for).
   a.one_tile = !a.dyn && !a.early && T_inplace_all(a, inpl_ok) && T <= G && !c.telemetry &&
-                       L.shape != mk::SHAPE_WS
+                       !mk::is_ws(L.shape)
                    ? 1
                    : 0;
   // The seed share counts the in-place tiles' reduce as compute-side work.
@@ -1545,7 +1548,7 @@ mk_status_t mk_set_option(int option, int64_t value) {
       g_opt.ctrl_period = value;
       return MK_OK;
     case MK_OPT_TILE_SHAPE:
-      if (value < 0 || value > 4) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
+      if (value < 0 || value > 5) return fail(MK_ERR_INVALID_ARG, "tile shape %lld", (long long)value);
       g_opt.tile_shape = value;
       return MK_OK;
     case MK_OPT_FLAG_SCOPE:

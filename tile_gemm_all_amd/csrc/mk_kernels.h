@@ -63,10 +63,14 @@ constexpr size_t kScratchFlags = MK_NOALLOC_MAX_TILE_FLAGS;
 constexpr size_t kScratchPartialBytes = MK_NOALLOC_PARTIAL_BYTES;
 constexpr size_t kScratchBytes = kScratchSlotBytes + kScratchFlags * 4 + kScratchPartialBytes;
 
-// SHAPE_WS: 64x256 tiles in the wave-specialised kernel (768 threads, the GEMM
-// of one tile overlapping the reduce of the one before, every tile in place)
-enum TileShape : int { SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2, SHAPE_64 = 3, SHAPE_WS = 4 };
-constexpr int kShapes = 5;
+// SHAPE_WS, SHAPE_WS128: 64x256 or 128x128 tiles in the wave-specialised kernel
+// (384 threads, the GEMM of one tile overlapping the reduce of the one before,
+// every tile in place)
+enum TileShape : int {
+  SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2, SHAPE_64 = 3, SHAPE_WS = 4, SHAPE_WS128 = 5
+};
+constexpr int kShapes = 6;
+constexpr bool is_ws(int shape) { return shape == SHAPE_WS || shape == SHAPE_WS128; }
 
 // Tile queues and flag protocol of a persistent launch of G workgroups on a
 // device with `cus` compute units. gfx950 groups 32 compute units per XCD, each

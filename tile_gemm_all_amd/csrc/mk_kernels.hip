@@ -1277,13 +1277,15 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 constexpr int kWsStream = 128;  // streaming threads (two waves)
 constexpr int kWsThreads = kThreads + kWsStream;
 using TWs = TileCfg<64, 256>;
-constexpr int kWsPartialBytes = TWs::BM * TWs::BN * 4;
+// 128x128 tiles: fewer A and B bytes per output (256 rows and columns per 16 K
+// outputs against 320), 256-byte pieces of peer rows; they pay where the GEMM
+// weighs more against the stream
+using TWs128 = TileCfg<128, 128>;
 
-template <typename PT, typename CT>
+template <class Cfg, typename PT, typename CT>
 __global__ __launch_bounds__(kWsThreads, 1) void ws_kernel(FusedArgs a) {
-  using Cfg = TWs;
   static_assert(GemmTile<Cfg>::NPASS == 1, "the whole fp32 tile is staged in one pass");
-  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES + kWsPartialBytes];
+  __shared__ __align__(1024) char lds[Cfg::LDS_BYTES + Cfg::BM * Cfg::BN * 4];
   char* const part = lds + Cfg::LDS_BYTES;
   const int b = blockIdx.x, G = gridDim.x;
   // this workgroup's tiles: q0 + s, q0 + s + per, ... below q1
@@ -1359,15 +1361,17 @@ static const void* fused_ptr(int pt, int ct) {
   return (const void*)fused_kernel<Cfg, float, float, DYN>;
 }
 
+template <class Cfg>
 static const void* ws_ptr(int pt, int ct) {
-  if (pt == MK_DT_BF16 && ct == MK_DT_BF16) return (const void*)ws_kernel<uint16_t, uint16_t>;
-  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)ws_kernel<uint16_t, float>;
-  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)ws_kernel<float, uint16_t>;
-  return (const void*)ws_kernel<float, float>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_BF16) return (const void*)ws_kernel<Cfg, uint16_t, uint16_t>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)ws_kernel<Cfg, uint16_t, float>;
+  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)ws_kernel<Cfg, float, uint16_t>;
+  return (const void*)ws_kernel<Cfg, float, float>;
 }
 
 const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn) {
-  if (shape == SHAPE_WS) return ws_ptr(pt, ct);
+  if (shape == SHAPE_WS) return ws_ptr<TWs>(pt, ct);
+  if (shape == SHAPE_WS128) return ws_ptr<TWs128>(pt, ct);
   if (shape == SHAPE_64) return fused_ptr<T64, false>(pt, ct);  // no dynamic variant
   if (dyn) return shape == SHAPE_256 ? fused_ptr<T256, true>(pt, ct) : fused_ptr<T128, true>(pt, ct);
   return shape == SHAPE_256 ? fused_ptr<T256, false>(pt, ct) : fused_ptr<T128, false>(pt, ct);
@@ -1396,13 +1400,15 @@ const void* reduce_kernel_ptr(int pt, int ct) {
   return (const void*)reduce_kernel<float, float>;
 }
 
-int shape_threads(int shape) { return shape == SHAPE_WS ? kWsThreads : kThreads; }
+int shape_threads(int shape) { return is_ws(shape) ? kWsThreads : kThreads; }
 int shape_bm(int shape) {
   if (shape == SHAPE_WS) return TWs::BM;
+  if (shape == SHAPE_WS128) return TWs128::BM;
   return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128);
 }
 int shape_bn(int shape) {
   if (shape == SHAPE_WS) return TWs::BN;
+  if (shape == SHAPE_WS128) return TWs128::BN;
   return shape == SHAPE_256 ? 256 : (shape == SHAPE_64 ? 64 : 128);
 }
 
