@@ -1076,10 +1076,10 @@ __host__ __device__ constexpr int ws_ring_depth() {
 // The same sum by the STRIDE streaming threads of a wave-specialised workgroup
 // (thread t among them), taking part in nb workgroup barriers on the way
 // (PacedRing). With no peers the partial is rounded and stored. Only peer counts
-// for which inplace_supported(2, ...) holds; another count passes its barriers
-// without touching C.
+// for which inplace_supported(2, ...) holds: another count passes its barriers
+// without touching C and returns false.
 template <int STRIDE, typename PT, typename CT>
-__device__ __forceinline__ void stream_region_lds(const char* lds, int64_t LP,
+__device__ __forceinline__ bool stream_region_lds(const char* lds, int64_t LP,
                                                   const PT* __restrict__ peers, int n_peers,
                                                   CT* __restrict__ C, int64_t M, int64_t N,
                                                   int64_t m0, int64_t n0, int rows, int cols, int t,
@@ -1097,7 +1097,7 @@ __device__ __forceinline__ void stream_region_lds(const char* lds, int64_t LP,
       typedef CopyLdsOp<CT> Op;
       PacedRing<4, Op, STRIDE>::run(Op{(const lds_char*)lds, OutC<CT>{C + base}}, t, total, cpr,
                                     N, LP, nb);
-      return;
+      return true;
     }
 #define MK_RING(NPV)                                                                     \
   case NPV:                                                                              \
@@ -1107,7 +1107,7 @@ __device__ __forceinline__ void stream_region_lds(const char* lds, int64_t LP,
       typedef SumOp<PT, NPV, PartialLdsLate, OutC<CT>> Op;                               \
       PacedRing<ws_ring_depth<PT, NPV>(), Op, STRIDE>::run(Op{ps, pr, OutC<CT>{C + base}}, t,  \
                                                            total, cpr, N, LP, nb);       \
-      return;                                                                            \
+      return true;                                                                       \
     }                                                                                    \
     break;
     switch (n_peers) {
@@ -1117,6 +1117,7 @@ __device__ __forceinline__ void stream_region_lds(const char* lds, int64_t LP,
 #undef MK_RING
   }
   for (int i = 0; i < nb; ++i) __syncthreads();
+  return total <= 0;
 }
 
 // Rounds the fp32 partial of a region in LDS (row pitch LP) to OT and stores it

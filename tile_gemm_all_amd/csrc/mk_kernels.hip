@@ -1333,8 +1333,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void ws_kernel(FusedArgs a) {
         origin(j - 1, m0, n0);
         const int rows = (int)(a.M - m0 < Cfg::BM ? a.M - m0 : Cfg::BM);
         const int cols = (int)(a.N - n0 < Cfg::BN ? a.N - n0 : Cfg::BN);
-        stream_region_lds<kWsStream, PT, CT>(part, Cfg::BN, peers, a.n_peers, C, a.M, a.N, m0,
-                                             n0, rows, cols, t, nb);
+        // a peer count without a ring is never launched here (the host checks);
+        // were it, C would be left unwritten: report it
+        if (!stream_region_lds<kWsStream, PT, CT>(part, Cfg::BN, peers, a.n_peers, C, a.M, a.N,
+                                                  m0, n0, rows, cols, t, nb) &&
+            t == 0)
+          atomicCAS(slot32(a.slots, S_ERROR), 0, MK_ERR_INTERNAL);  // (no abort: nothing waits)
       } else {
         for (int i = 0; i < nb; ++i) __syncthreads();
       }
