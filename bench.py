@@ -47,6 +47,7 @@ so that repeated calls do not find their peers in the 256 MB Infinity Cache.
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -61,11 +62,22 @@ KERNEL_SOURCES = ["tile_gemm_all_amd/csrc/mk_kernels.hip", "tile_gemm_all_amd/cs
                   "tile_gemm_all_amd/csrc/mk_controller.h"]
 
 
+def code_only(text):
+    """C/C++/HIP source without its comments and with runs of whitespace folded:
+    what the compiler reads (string literals in these sources hold no comment
+    markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sha():
+    """Hash of the device sources' code (comments and layout left out), which the
+    committed traffic counters are tied to."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -46,3 +46,12 @@ def test_roofline_bound_follows_the_ridge():
     mlp = bench.roofline_of(mk_inputs.BY_NAME["mlp"], 1000.0)
     assert mlp["bound"] == "hbm" and mlp["unit"] == "GB/s"
     assert abs(mlp["frac"] - mlp["achieved"] / bench.HBM_PEAK_GBPS) < 1e-4
+
+
+def test_kernel_hash_ignores_comments_and_layout():
+    a = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    b = "int f(int x) { return x + 1; }"
+    c = "int f(int x) { return x + 2; }"
+    assert bench.code_only(a) == bench.code_only(b)
+    assert bench.code_only(a) != bench.code_only(c)
+    assert len(bench.kernel_sha()) == 16

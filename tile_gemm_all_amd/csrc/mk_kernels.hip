@@ -1259,14 +1259,16 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 // through device memory. Two streaming waves streamed as fast as four or eight
 // on MI355X (16384x8192x512 with 15 peers: 817, 817 and 838 us) and left more
 // of each CU's memory pipeline to the GEMM's loads (4096x8192x1792: 301, 311 and
-// 316 us); deeper rings were slower (859 us). 32-deep k-tiles: 64-deep ones
-// spill.
+// 316 us); deeper rings were slower (859 us). 32-deep k-tiles (64-deep ones
+// measured slower).
 //
-// Tiles are 64 x 256: a tile row is 512 contiguous bytes of every bfloat16 peer
-// (128 x 128 tiles read 256-byte pieces, which streamed about 15% slower from
-// HBM on MI355X), and the fp32 partial (64 KiB) plus four k-stages (80 KiB) fit
-// the LDS. They are dealt statically: XCD x owns a contiguous range of the tile
-// order, served by its workgroups in turn.
+// Two tile shapes, each with its fp32 partial (64 KiB) and four k-stages in the
+// LDS: 64 x 256, whose rows are 512 contiguous bytes of every bfloat16 peer (the
+// 256-byte pieces of 128 x 128 tiles streamed about 15% slower from HBM on
+// MI355X), for shapes where the stream dominates; 128 x 128, which load fewer A
+// and B bytes per output, where the GEMM weighs more. Tiles are dealt
+// statically: XCD x owns a contiguous range of the tile order, served by its
+// workgroups in turn.
 //
 // Both groups pass the same workgroup barriers in each round: the GEMM's k-loop
 // holds one per k-tile and a last one after it; the streaming waves spread as
@@ -1276,11 +1278,8 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 // only streams.
 constexpr int kWsStream = 128;  // streaming threads (two waves)
 constexpr int kWsThreads = kThreads + kWsStream;
-using TWs = TileCfg<64, 256>;
-// 128x128 tiles: fewer A and B bytes per output (256 rows and columns per 16 K
-// outputs against 320), 256-byte pieces of peer rows; they pay where the GEMM
-// weighs more against the stream
-using TWs128 = TileCfg<128, 128>;
+using TWs = TileCfg<64, 256>;     // 320 rows and columns of A and B per 16 K outputs
+using TWs128 = TileCfg<128, 128>;  // 256 per 16 K outputs
 
 template <class Cfg, typename PT, typename CT>
 __global__ __launch_bounds__(kWsThreads, 1) void ws_kernel(FusedArgs a) {
