@@ -188,8 +188,8 @@ struct TileCfg {
 
 // Tile index -> (tile row, tile column), grouped so that consecutive tiles share
 // A row-panels (GROUP rows of tiles sweep the columns together).
+template <int GROUP = 8>
 __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP = 8;
   int group_size = GROUP * tiles_n;
   int g = t / group_size;
   int first = g * GROUP;
@@ -205,9 +205,10 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // L2 reuse, but its tiles no longer sit side by side in memory: concurrent
 // streams spread over the whole row of every operand, which measured 10-25%
 // more reduce bandwidth than compact blocks of tiles per XCD.
+template <int GROUP = 8>
 __device__ __forceinline__ void fused_tile_coords(int t, int tiles_m, int tiles_n, int& tm,
                                                   int& tn) {
-  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  tile_coords<GROUP>(t, tiles_m, tiles_n, tm, tn);
   constexpr int S = 4;
   if (tiles_n >= 2 * S && tiles_n % S == 0) {
     const int w = tiles_n / S;
