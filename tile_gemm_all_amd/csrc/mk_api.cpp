@@ -435,13 +435,26 @@ int fused_grid_size(const Launch& L, int n_peers, int peer_dtype, int c_dtype) {
   return want < full ? (int)want : full;
 }
 
-// Grid of the reduce kernel for `elems` output elements: two 8-element chunks
-// per thread, at most 8 workgroups per compute unit (grid-stride beyond).
-int reduce_grid(int64_t elems, int cus) {
+// Grid of the AllGather landing copy for `elems` elements: two 8-element
+// chunks per thread, at most 8 workgroups per compute unit (grid-stride beyond).
+int copy_grid(int64_t elems, int cus) {
   const int64_t chunks = elems / 8;
   int64_t grid = (chunks + 2 * 256 - 1) / (2 * 256);
   const int64_t cap = (int64_t)cus * 8;
   if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  return (int)grid;
+}
+
+// Grid of the reduce kernel for `elems` output elements: one workgroup per
+// compute unit, fewer when there are fewer than 256 chunks of 8 elements per
+// workgroup. Each thread keeps its next chunk's loads in flight while it sums
+// one; on MI355X one such workgroup per compute unit streamed the attention
+// shape's 15 peers at 6.2 TB/s, against 5.6-5.8 TB/s with 4 or 8 per unit.
+int reduce_grid(int64_t elems, int cus) {
+  const int64_t chunks = elems / 8;
+  int64_t grid = (chunks + 256 - 1) / 256;
+  if (grid > cus) grid = cus;
   if (grid < 1) grid = 1;
   return (int)grid;
 }
@@ -1354,7 +1367,7 @@ mk_status_t mk_gemm_ag_baseline(const void* A_local, const void* peers_A, int n_
     c.K = K;
     c.P = P;
     c.rank = rank;
-    e = mk::launch_ag_copy(c, reduce_grid(M * K, info.cus), s);
+    e = mk::launch_ag_copy(c, copy_grid(M * K, info.cus), s);
     if (e != hipSuccess) return hip_fail(e, "gather kernel launch");
   }
   if (N == 0) return MK_OK;

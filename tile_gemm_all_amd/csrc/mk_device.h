@@ -885,12 +885,19 @@ struct ChunkCursor {
 
 template <int DEPTH, typename OP>
 struct ReduceRing {
+  // The workgroup's 256 threads walk the region's chunks together.
   __device__ __forceinline__ static void run(const OP& op, int total, int cpr, int64_t N,
                                              int64_t LP) {
+    run_strided(op, total, cpr, N, LP, (int)threadIdx.x, kThreads);
+  }
+  // Thread t takes chunks t, t + stride, ... (stride a multiple of 64; the 64
+  // lanes of a wave hold consecutive t).
+  __device__ __forceinline__ static void run_strided(const OP& op, int total, int cpr, int64_t N,
+                                                     int64_t LP, int t, int stride) {
     // loop bound on the wave's first chunk: a uniform (scalar) loop
-    const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
+    const int w0 = __builtin_amdgcn_readfirstlane(t & ~63);
     ChunkCursor ld, st;  // the chunk loaded next, the chunk summed next
-    ld.init(threadIdx.x, total, cpr, N, LP);
+    ld.init(t, total, cpr, N, LP, stride);
     st = ld;
     typename OP::Chunk b[DEPTH];
 #pragma unroll
@@ -909,7 +916,7 @@ struct ReduceRing {
         op.finish(b[i], st.get(), st.lget());
         st.advance();
       }
-      k += DEPTH * kThreads;
+      k += DEPTH * stride;
     } while (w0 + k < total);
     // The last pass issued loads of clamped chunks that are never summed (L2
     // hits); the compute path waits for them before its GEMM loop.
