@@ -437,7 +437,7 @@ typedef enum {
                                    plus the reduce units fit one round), 1 = off, 2 = on (K a
                                    multiple of 64). The fp32 rounding of P0 + P1 differs from one
                                    k-loop, so C can differ from the baseline in the last bit. */
-  MK_OPT_STREAM_CU_SPLIT = 9    /* mk_gemm_ar_two_stream: compute units given to the reduce stream
+  MK_OPT_STREAM_CU_SPLIT = 9,   /* mk_gemm_ar_two_stream: compute units given to the reduce stream
                                    when the two streams are CU-masked; the GEMM stream gets the
                                    rest. 0 = no masks (default: both streams share the chip). R > 0
                                    must be below the device's compute units and a multiple of 8
@@ -445,6 +445,12 @@ typedef enum {
                                    word, whichever XCD its units sit on, gives the reduce stream
                                    the same share; checked at the call (MK_ERR_INVALID_ARG). Each
                                    word's top R/words bits go to the reduce stream. */
+  MK_OPT_STATIC_TILES = 10      /* 256x256 tiles all reduced in place with more tiles than one round
+                                   of workgroups (the default schedule of compute-bound shapes,
+                                   without telemetry): 1 = the in-place kernel, which deals each
+                                   XCD's range of tiles to its workgroups in a fixed order and
+                                   keeps no claim, flag or counter (default); 0 = the persistent
+                                   kernel with per-XCD tile claims. Both give the same bits. */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

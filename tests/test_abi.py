@@ -274,6 +274,23 @@ def test_stream_cu_split_option_takes_multiples_of_eight():
         mk.set_option(mk.OPT_STREAM_CU_SPLIT, old)
 
 
+def test_static_tiles_option_range():
+    """The in-place kernel's switch: 1 (default) or 0 (the claim-queue kernel);
+    anything else is rejected without changing the setting."""
+    old = mk.get_option(mk.OPT_STATIC_TILES)
+    assert old == 1
+    try:
+        for v in (-1, 2, 7):
+            with pytest.raises(mk.MkError):
+                mk.set_option(mk.OPT_STATIC_TILES, v)
+            assert mk.get_option(mk.OPT_STATIC_TILES) == old
+        for v in (0, 1):
+            mk.set_option(mk.OPT_STATIC_TILES, v)
+            assert mk.get_option(mk.OPT_STATIC_TILES) == v
+    finally:
+        mk.set_option(mk.OPT_STATIC_TILES, old)
+
+
 @pytest.mark.parametrize("iters,grid,out,status", [
     (0, 1, A16, mk.MK_ERR_INVALID_ARG),
     ((1 << 24) + 1, 1, A16, mk.MK_ERR_INVALID_ARG),

@@ -559,6 +559,50 @@ def test_wave_specialised_schedule(shape, tile):
         mk.set_option(mk.OPT_TILE_SHAPE, old)
 
 
+STATIC_SHAPES = [  # M, N, K, n_peers, peer dtype, C dtype: more 256x256 tiles than workgroups
+    (4608, 4096, 2176, 7, "bf16", "bf16"),   # 288 tiles: 256 workgroups, a second round for 32
+    (4600, 4104, 2120, 3, "bf16", "f32"),    # ragged M, N and K
+    (4608, 4096, 1024, 15, "bf16", "bf16"),  # 15 peers
+    (4608, 4096, 1024, 7, "f32", "bf16"),    # float32 peers
+    (8448, 8192, 64, 1, "bf16", "bf16"),     # 1056 tiles (five rounds), one k-tile
+]
+
+
+@pytest.mark.parametrize("shape", STATIC_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
+def test_inplace_kernel_matches_claim_queues(shape):
+    """256x256 tiles all reduced in place with more tiles than workgroups: the
+    in-place kernel (each XCD's tiles dealt to its workgroups in a fixed order,
+    MK_OPT_STATIC_TILES=1, the default) and the persistent kernel's per-XCD claim
+    queues (0). Integer inputs bit-exact against the oracle on sampled rows and
+    bitwise equal to the two-kernel baseline over the whole output, twice in a
+    row; Gaussian inputs within tolerance."""
+    M, N, K, npeer, pdt, cdt = shape
+    announce(f"in-place kernel {shape}")
+    rows = sample_rows(M, band=256, seed=M + K)
+    A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "integer", 27, device="cpu")
+    _, want = oracle_rows(A, B, peers, cdt, rows)
+    A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+    ref = c_bits(run(A, B, peers, cdt, "baseline"))
+    check_exact(ref[rows], want, "baseline against the oracle")
+    opts = (mk.OPT_TILE_SHAPE, mk.OPT_STATIC_TILES)
+    old = [mk.get_option(o) for o in opts]
+    try:
+        mk.set_option(mk.OPT_TILE_SHAPE, 1)
+        for static in (1, 0, 1):
+            mk.set_option(mk.OPT_STATIC_TILES, static)
+            for rep in range(2):
+                check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, f"static tiles {static} call {rep}")
+        A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "gaussian", 28, device="cpu")
+        C64, _ = oracle_rows(A, B, peers, cdt, rows)
+        A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
+        got = c_bits(run(A, B, peers, cdt, "adaptive"), rows)
+        check_tolerance(got, C64, cdt, "in-place kernel gaussian",
+                        rms_ref=float(np.sqrt(np.mean(C64 * C64))))
+    finally:
+        for o, v in zip(opts, old):
+            mk.set_option(o, v)
+
+
 def test_automatic_schedule_per_workload():
     """The automatic choice on MI355X (256 CUs): few-tile shapes take 64x64 tiles
     in place, stream-dominated ones the wave-specialised kernel (64x256 tiles for

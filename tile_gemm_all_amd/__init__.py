@@ -33,6 +33,7 @@ MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
 OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY, OPT_KSPLIT = 4, 5, 6, 7, 8
 OPT_STREAM_CU_SPLIT = 9  # two-stream schedule: compute units of the CU-masked reduce stream
+OPT_STATIC_TILES = 10  # all-in-place 256x256 tiles: 1 the in-place kernel (fixed tile order), 0 claim queues
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_ar_local_noalloc", "mk_gemm_then_reduce_baseline",
            "mk_gemm_ar_two_stream",
@@ -390,7 +391,7 @@ SCHEDULES = {1: "256x256 tiles, every tile in place", 2: "128x128 tiles, every t
 
 
 def fused_schedule(A, B, peers, C):
-    """Tile shape (MK_OPT_TILE_SHAPE value, 1-4) of the schedule gemm_ar_local takes
+    """Tile shape (MK_OPT_TILE_SHAPE value, 1-5) of the schedule gemm_ar_local takes
     for these tensors with the adaptive default and no telemetry."""
     a = _args(A, B, peers, C)
     v = _lib.mk_fused_schedule(a[5], a[6], a[7], a[3], a[8], a[9])

@@ -49,6 +49,7 @@ struct Options {
   int64_t early = -1;       // reducers sum a unit's peers before its tile is finished: -1 auto
   int64_t ksplit = -1;      // early-reduce tiles computed as two k-halves: -1 auto, 1 off, 2 on
   int64_t stream_cu_split = 0;  // two-stream schedule: compute units of the reduce stream (0: no masks)
+  int64_t static_tiles = 1;  // all-in-place 256x256 tiles: 1 the in-place kernel, 0 claim queues
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -761,6 +762,14 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
                        !mk::is_ws(L.shape)
                    ? 1
                    : 0;
+  // Every tile in place with more tiles than one round of workgroups, 256x256
+  // tiles: the in-place kernel, which deals the tiles in a fixed order and keeps
+  // no claim or flag state (MK_OPT_STATIC_TILES).
+  a.static_tiles = !a.one_tile && !a.dyn && !a.early && a.ksplit == 1 &&
+                           T_inplace_all(a, inpl_ok) && !c.telemetry &&
+                           L.shape == mk::SHAPE_256 && opt.static_tiles == 1
+                       ? 1
+                       : 0;
   // The seed share counts the in-place tiles' reduce as compute-side work.
   if (a.T > 0 && a.T_r < a.T) {
     double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -1591,6 +1600,10 @@ mk_status_t mk_set_option(int option, int64_t value) {
         return fail(MK_ERR_INVALID_ARG, "stream CU split %lld", (long long)value);
       g_opt.stream_cu_split = value;
       return MK_OK;
+    case MK_OPT_STATIC_TILES:
+      if (value < 0 || value > 1) return fail(MK_ERR_INVALID_ARG, "static tiles %lld", (long long)value);
+      g_opt.static_tiles = value;
+      return MK_OK;
   }
   return fail(MK_ERR_INVALID_ARG, "unknown option %d", option);
 }
@@ -1608,6 +1621,7 @@ int64_t mk_get_option(int option) {
     case MK_OPT_EARLY: return g_opt.early;
     case MK_OPT_KSPLIT: return g_opt.ksplit;
     case MK_OPT_STREAM_CU_SPLIT: return g_opt.stream_cu_split;
+    case MK_OPT_STATIC_TILES: return g_opt.static_tiles;
   }
   return -1;
 }

@@ -160,6 +160,8 @@ struct FusedArgs {
   int64_t own0, own1;
   void* send;
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
+  int static_tiles;            // 1: every tile reduced in place, tiles dealt to the workgroups
+                               // in a fixed order (inplace_kernel): no claim, flag or counter
 };
 
 struct GemmArgs {
