@@ -178,7 +178,7 @@ mk_status_t mk_gemm_ar_local(const void* A, const void* B, const void* peers, in
  *   - A call whose default schedule would hand tiles to reducers with more
  *     partial bytes than that (M * N * 4 per k-part) reduces every tile in place
  *     instead (same bits); for peer counts that cannot be reduced in place (those
- *     outside 1-4, 7, 8, 15, or fp32 peers beyond what fits a lane's registers)
+ *     outside 0-4, 7, 8, 15, or fp32 peers beyond what fits a lane's registers)
  *     it returns MK_ERR_UNSUPPORTED, as it does for more tiles times k-parts
  *     than there are flags. Nothing is launched then.
  *   - Every call on one GPU shares that GPU's workspace. Calls that overlap on
@@ -404,7 +404,7 @@ typedef enum {
                                    64x256 tiles, one 384-thread workgroup per CU whose first four
                                    waves compute a tile while the other two reduce the tile
                                    before from LDS), 5 = the same with 128x128 tiles (4 and 5:
-                                   peer counts 1-4, 7, 8 and 15 of bfloat16, 1-4, 7 and 8 of
+                                   peer counts 0-4, 7, 8 and 15 of bfloat16, 0-4, 7 and 8 of
                                    float32; otherwise as 0). Automatic, with no reducer count,
                                    in-place policy, early reduce or k-split set, when the peer
                                    stream at HBM peak takes at least twice the GEMM at

@@ -603,6 +603,38 @@ def test_inplace_kernel_matches_claim_queues(shape):
             mk.set_option(o, v)
 
 
+ZERO_PEER_CASES = [  # M, N, K, C dtype, MK_OPT_TILE_SHAPE: no peers (C = round(A*B)), every in-place path
+    (4608, 4096, 256, "bf16", 1),   # 288 tiles of 256x256: the in-place kernel
+    (4608, 4096, 256, "f32", 0),    # automatic
+    (2100, 2056, 136, "bf16", 4),   # wave-specialised, 64x256 (rounded partial streamed from LDS)
+    (2100, 2056, 136, "f32", 5),    # wave-specialised, 128x128
+    (1000, 1032, 1000, "bf16", 2),  # 128x128 tiles in place
+    (300, 264, 200, "f32", 3),      # 64x64 tiles, one per workgroup
+]
+
+
+@pytest.mark.parametrize("case", ZERO_PEER_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_zero_peers_reduced_in_place(case):
+    """A call with no peers (one GPU: C = round(A*B)) reduces its tiles in place
+    like any other peer count: integer inputs bit-exact against the oracle on
+    sampled rows and bitwise equal to the two-kernel baseline, twice in a row."""
+    M, N, K, cdt, shape = case
+    announce(f"zero peers {case}")
+    rows = sample_rows(M, band=256, seed=M + N)
+    A, B, peers = mk_inputs.make_inputs(M, N, K, 0, "bf16", "integer", 37, device="cpu")
+    _, want = oracle_rows(A, B, None, cdt, rows)
+    A, B = A.to(DEV), B.to(DEV)
+    ref = c_bits(run(A, B, None, cdt, "baseline"))
+    check_exact(ref[rows], want, "baseline against the oracle")
+    old = mk.get_option(mk.OPT_TILE_SHAPE)
+    try:
+        mk.set_option(mk.OPT_TILE_SHAPE, shape)
+        for rep in range(2):
+            check_exact(c_bits(run(A, B, None, cdt, "adaptive")), ref, f"tile option {shape} call {rep}")
+    finally:
+        mk.set_option(mk.OPT_TILE_SHAPE, old)
+
+
 def test_automatic_schedule_per_workload():
     """The automatic choice on MI355X (256 CUs): few-tile shapes take 64x64 tiles
     in place, stream-dominated ones the wave-specialised kernel (64x256 tiles for

@@ -1052,6 +1052,11 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
   const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane((int)m0) * N +
                        __builtin_amdgcn_readfirstlane((int)n0);
   const PartialLds ps{(const lds_char*)lds};
+  if (n_peers == 0) {  // C = round(partial)
+    typedef CopyLdsOp<CT> Op;
+    ReduceRing<4, Op>::run(Op{(const lds_char*)lds, OutC<CT>{C + base}}, total, cpr, N, LP);
+    return;
+  }
 #define MK_RING(NPV)                                                                   \
   case NPV:                                                                            \
     if constexpr (ring_fits<OCC, PT, NPV>()) {                                         \

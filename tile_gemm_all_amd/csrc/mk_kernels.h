@@ -88,13 +88,14 @@ inline void queue_plan(int cus, int G, int scope_opt, int& n_xcd, int& scope) {
   scope = per_xcd ? (scope_opt != 0 ? 1 : 0) : 1;
 }
 
-// Peer counts that have a compile-time reduce ring, and whether that ring fits
-// the register budget of a lane at `occ` workgroups per compute unit (peers of
-// peer_bytes bytes: 8 registers of partial plus 4 or 8 per peer per chunk, two
-// chunks at least). A tile can be reduced in place (partial in LDS) only then.
-// Shared by the host (which counts the tiles handed to reducers) and the kernels.
+// Peer counts that have a compile-time reduce ring (0: the partial rounded and
+// stored), and whether that ring fits the register budget of a lane at `occ`
+// workgroups per compute unit (peers of peer_bytes bytes: 8 registers of
+// partial plus 4 or 8 per peer per chunk, two chunks at least). A tile can be
+// reduced in place (partial in LDS) only then. Shared by the host (which counts
+// the tiles handed to reducers) and the kernels.
 constexpr bool ring_peer_count(int np) {
-  return np == 1 || np == 2 || np == 3 || np == 4 || np == 7 || np == 8 || np == 15;
+  return np == 0 || np == 1 || np == 2 || np == 3 || np == 4 || np == 7 || np == 8 || np == 15;
 }
 constexpr bool ring_fits_regs(int occ, int peer_bytes, int np) {
   return 2 * (8 + np * (peer_bytes == 2 ? 4 : 8)) <= (occ == 1 ? 320 : 160);
