@@ -407,7 +407,7 @@ typedef enum {
                                    peer counts 0-4, 7, 8 and 15 of bfloat16, 0-4, 7 and 8 of
                                    float32; otherwise as 0). Automatic, with no reducer count,
                                    in-place policy, early reduce or k-split set, when the peer
-                                   stream at HBM peak takes at least twice the GEMM at
+                                   stream at HBM peak takes at least 1.8 times the GEMM at
                                    matrix-core peak and there are as many 64x256 tiles as CUs:
                                    64x256 tiles where the stream weighs most (see
                                    mk_fused_schedule), 128x128 otherwise */

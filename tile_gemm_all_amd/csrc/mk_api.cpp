@@ -304,23 +304,24 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
 }
 
 // The wave-specialised kernel's automatic choice: for shapes whose peer stream
-// (at HBM peak) takes at least twice their GEMM (at matrix-core peak), with a
-// 64x256 tile for every compute unit; 64x256 tiles (512-byte pieces of peer rows)
-// from four times on, 128x128 tiles (fewer A and B bytes per output) below.
-// Returns the shape, or 0 for the other schedules. Where the GEMM weighs more,
-// the overlap gains less than the smaller tiles cost. Measured on MI355X, us
-// per call (stream/GEMM ratio; 256x256 tiles in place / 64x256 / 128x128):
-//   16384x8192x512 P=16 (9.8)   976 / 812 / 929     8192x8192x512 P=16 (9.8)  498 / 417 / 470
-//   16384x8192x1024 P=16 (4.9) 1051 / 936 / 1000    4096x8192x1024 P=16 (4.9) 288 / 250 / 239
-//   4096x8192x1792 P=16 (2.8)   324 / 314 / 292     8192x8192x1024 P=8 (2.4)  356 / 332 / 318
-//   8192x16384x1024 P=8 (2.4)   676 / 636 / 606     4096x8192x2560 P=16 (1.95) 367 / 384 / 360
-//   4096x8192x3584 P=16 (1.4)   419 / 480 / 442     8192x8192x2048 P=8 (1.2)  469 / 521 / 485
+// (at HBM peak) takes at least 1.8 times their GEMM (at matrix-core peak), with
+// a 64x256 tile for every compute unit; 64x256 tiles (512-byte pieces of peer
+// rows) from four times on, 128x128 tiles (fewer A and B bytes per output)
+// below. Returns the shape, or 0 for the other schedules. Where the GEMM weighs
+// more, the overlap gains less than the smaller tiles cost. Measured on MI355X,
+// us per call (stream/GEMM ratio; 256x256 tiles in place / 64x256 / 128x128
+// with 64-deep k-tiles in three stages; same machine):
+//   16384x8192x512 P=16 (9.8)   934 / 807 / 912     8192x8192x512 P=16 (9.8)  474 / 411 / 455
+//   16384x8192x1024 P=16 (4.9) 1009 / 934 / 946     4096x8192x1024 P=16 (4.9) 269 / 244 / 232
+//   4096x8192x1792 P=16 (2.8)   311 / 311 / 281     8192x8192x1024 P=8 (2.4)  339 / 331 / 291
+//   8192x16384x1024 P=8 (2.4)   624 / 647 / 568     4096x8192x2560 P=16 (1.95) 348 / 388 / 341
+//   4096x8192x3584 P=16 (1.4)   409 / 484 / 419     8192x8192x2048 P=8 (1.2)  441 / 524 / 456
 int ws_pays(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   const double t_stream =
       (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype)) / 8.0e12;
   const double t_gemm = 2.0 * (double)M * (double)N * (double)K / 2.5e15;
   const int64_t tiles = ((M + 63) / 64) * ((N + 255) / 256);
-  if (tiles < cus || t_stream < 2.0 * t_gemm) return 0;
+  if (tiles < cus || t_stream < 1.8 * t_gemm) return 0;
   return t_stream >= 4.0 * t_gemm ? mk::SHAPE_WS : mk::SHAPE_WS128;
 }
 
