@@ -403,7 +403,8 @@ typedef enum {
                                    4 = wave-specialised (fused AllReduce only, without telemetry:
                                    64x256 tiles, one 384-thread workgroup per CU whose first four
                                    waves compute a tile while the other two reduce the tile
-                                   before from LDS), 5 = the same with 128x128 tiles (4 and 5:
+                                   before from LDS), 5 = the same with 128x128 tiles and four
+                                   reducing waves (512 threads) (4 and 5:
                                    peer counts 0-4, 7, 8 and 15 of bfloat16, 0-4, 7 and 8 of
                                    float32; otherwise as 0). Automatic, with no reducer count,
                                    in-place policy, early reduce or k-split set, when the peer

@@ -90,14 +90,16 @@ mk_status_t device_info(int dev, DeviceInfo& out) {
     for (int pt = 0; pt < 2; ++pt)
       for (int ct = 0; ct < 2; ++ct) {
         // the persistent grid is sized from this count, so it holds for both
-        // variants of the kernel (the lower of the two; 64-wide tiles and the
-        // wave-specialised kernel have one)
+        // variants of the kernel (the lower of the two: the dynamic hand-over
+        // kernel, or the 128x128 wave-specialised kernel's four streaming waves;
+        // 64-wide tiles and 64x256 wave-specialised tiles have one)
         int n = 1 << 30;
-        const int variants = s == mk::SHAPE_256 || s == mk::SHAPE_128 ? 2 : 1;
-        for (int dyn = 0; dyn < variants; ++dyn) {
+        const int variants =
+            s == mk::SHAPE_256 || s == mk::SHAPE_128 || s == mk::SHAPE_WS128 ? 2 : 1;
+        for (int v = 0; v < variants; ++v) {
           int m = 0;
           e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &m, mk::fused_kernel_ptr(s, pt, ct, dyn), mk::shape_threads(s), 0);
+              &m, mk::fused_kernel_ptr(s, pt, ct, v), mk::shape_threads(s, v), 0);
           if (e != hipSuccess || m < 1)
             return fail(MK_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
           n = m < n ? m : n;
@@ -766,6 +768,7 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   // Every tile in place with more tiles than one round of workgroups, 256x256
   // tiles: the in-place kernel, which deals the tiles in a fixed order and keeps
   // no claim or flag state (MK_OPT_STATIC_TILES).
+  a.ws_wide = mk::ws_wide(L.shape, (int)dt_size(peer_dtype), n_peers) ? 1 : 0;
   a.static_tiles = !a.one_tile && !a.dyn && !a.early && a.ksplit == 1 &&
                            T_inplace_all(a, inpl_ok) && !c.telemetry &&
                            L.shape == mk::SHAPE_256 && opt.static_tiles == 1

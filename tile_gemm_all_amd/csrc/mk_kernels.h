@@ -64,8 +64,8 @@ constexpr size_t kScratchPartialBytes = MK_NOALLOC_PARTIAL_BYTES;
 constexpr size_t kScratchBytes = kScratchSlotBytes + kScratchFlags * 4 + kScratchPartialBytes;
 
 // SHAPE_WS, SHAPE_WS128: 64x256 or 128x128 tiles in the wave-specialised kernel
-// (384 threads, the GEMM of one tile overlapping the reduce of the one before,
-// every tile in place)
+// (384 or 512 threads, the GEMM of one tile overlapping the reduce of the one
+// before, every tile in place)
 enum TileShape : int {
   SHAPE_AUTO = 0, SHAPE_256 = 1, SHAPE_128 = 2, SHAPE_64 = 3, SHAPE_WS = 4, SHAPE_WS128 = 5
 };
@@ -163,6 +163,7 @@ struct FusedArgs {
   unsigned long long spin_limit;  // flag-wait limit in 100 MHz ticks
   int static_tiles;            // 1: every tile reduced in place, tiles dealt to the workgroups
                                // in a fixed order (inplace_kernel): no claim, flag or counter
+  int ws_wide;                 // wave-specialised 128x128 tiles: 1 = four streaming waves
 };
 
 struct GemmArgs {
@@ -225,12 +226,20 @@ struct AgCopyArgs {
   int P, rank;
 };
 
-const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn);
+// variant: the dynamic hand-over kernel (256x256 and 128x128 tiles), or four
+// streaming waves instead of two (wave-specialised 128x128 tiles)
+const void* fused_kernel_ptr(int shape, int pt, int ct, int variant);
 const void* ag_kernel_ptr(int shape, int ct);
 const void* gemm_kernel_ptr(int shape);
 const void* reduce_kernel_ptr(int pt, int ct);
 int shape_bm(int shape);
-int shape_threads(int shape);  // workgroup size of the fused kernel of a shape
+int shape_threads(int shape, int variant);  // workgroup size of the fused kernel of a shape
+// Whether a wave-specialised call with 128x128 tiles streams with four waves:
+// when each streaming lane holds one chunk in flight while it sums another (the
+// ring depth of its peer count, 120 registers over the chunk's, is at most 2).
+constexpr bool ws_wide(int shape, int peer_bytes, int n_peers) {
+  return shape == SHAPE_WS128 && n_peers > 0 && 120 / (n_peers * (peer_bytes == 2 ? 4 : 8)) <= 2;
+}
 int shape_bn(int shape);
 
 hipError_t launch_ws_init(int* flags, int n_flags, unsigned long long* slots, hipStream_t s);

@@ -1312,19 +1312,19 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 // ------------------------------------------------------------ wave-specialised AllReduce
 
 // Persistent fused GEMM+AllReduce in which the GEMM and the reduce overlap inside
-// each workgroup: one workgroup of 384 threads per compute unit. Waves 0-3 run
-// the GEMM of the workgroup's tiles one after another (the fp32 accumulators in
-// their registers); waves 4-5 meanwhile reduce the tile before: its partial
+// each workgroup: one workgroup per compute unit. Waves 0-3 run the GEMM of the
+// workgroup's tiles one after another (the fp32 accumulators in their
+// registers); the streaming waves (two or four, ws_stream) meanwhile reduce the
+// tile before: its partial
 // waits in LDS, where the GEMM waves staged it when their k-loop ended, and the
 // streaming waves add it to the sum of the peers' slices and write C. The
 // matrix cores thus work while the peers stream from HBM, and no partial goes
-// through device memory. Two streaming waves streamed as fast as four or eight
-// on MI355X (16384x8192x512 with 15 peers: 817, 817 and 838 us) and left more
-// of each CU's memory pipeline to the GEMM's loads (4096x8192x1792: 301, 311 and
-// 316 us); deeper rings were slower (859 us). 32-deep k-tiles (64-deep ones
-// measured slower).
+// through device memory. With 64x256 tiles two streaming waves streamed as fast
+// as four or eight on MI355X (16384x8192x512 with 15 peers: 817, 817 and 838 us)
+// and left more of each CU's memory pipeline to the GEMM's loads; deeper rings
+// were slower (859 us). 32-deep k-tiles there (64-deep ones measured slower).
 //
-// Two tile shapes, each with its fp32 partial (64 KiB) and four k-stages in the
+// Two tile shapes, each with its fp32 partial (64 KiB) and its k-stages in the
 // LDS: 64 x 256, whose rows are 512 contiguous bytes of every bfloat16 peer (the
 // 256-byte pieces of 128 x 128 tiles streamed about 15% slower from HBM on
 // MI355X), for shapes where the stream dominates; 128 x 128, which load fewer A
@@ -1338,16 +1338,22 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_peak_kernel(int iters, float
 // reads of the partial are done. After that barrier the GEMM waves stage the new
 // partial, and one more barrier hands it over. The round after the last GEMM
 // only streams.
-constexpr int kWsStream = 128;  // streaming threads (two waves)
-constexpr int kWsThreads = kThreads + kWsStream;
 using TWs = TileCfg<64, 256>;     // 320 rows and columns of A and B per 16 K outputs
 // 256 per 16 K outputs; 64-deep k-tiles in three stages, which with the 64 KiB
 // partial fill the 160 KiB of LDS (mlp 284-285 us against 292-296 us with 32-deep
 // k-tiles in four stages, and 3-9% faster on every shape of the rule's table)
 using TWs128 = TileCfg<128, 128, 64, 3>;
-
-template <class Cfg, typename PT, typename CT>
-__global__ __launch_bounds__(kWsThreads, 1) void ws_kernel(FusedArgs a) {
+// Streaming threads per workgroup (STREAM): two waves, or four beside the
+// 128x128 GEMM when each streaming lane has one chunk in flight (ring depth 2:
+// 15 bfloat16 peers, say; the host's ws_wide). Measured on MI355X, same
+// machine: 16384x8192x512 with 15 peers (64x256 tiles) 807-810 us with two
+// waves, 891-893 with three, 818-821 with four; 4096x8192x1792 with 15 peers
+// (128x128) 282-284 us with two, 285-287 with three, 276 with four; 8192x8192x
+// 1024 with 7 peers (128x128, three chunks in flight) 291 us with two, 314 with
+// four.
+template <class Cfg, typename PT, typename CT, int STREAM>
+__global__ __launch_bounds__(kThreads + STREAM, 1) void ws_kernel(FusedArgs a) {
+  constexpr int kWsStream = STREAM;
   static_assert(GemmTile<Cfg>::NPASS == 1, "the whole fp32 tile is staged in one pass");
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES + Cfg::BM * Cfg::BN * 4];
   char* const part = lds + Cfg::LDS_BYTES;
@@ -1463,12 +1469,12 @@ static const void* fused_ptr(int pt, int ct) {
   return (const void*)fused_kernel<Cfg, float, float, DYN>;
 }
 
-template <class Cfg>
+template <class Cfg, int STREAM>
 static const void* ws_ptr(int pt, int ct) {
-  if (pt == MK_DT_BF16 && ct == MK_DT_BF16) return (const void*)ws_kernel<Cfg, uint16_t, uint16_t>;
-  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)ws_kernel<Cfg, uint16_t, float>;
-  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)ws_kernel<Cfg, float, uint16_t>;
-  return (const void*)ws_kernel<Cfg, float, float>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_BF16) return (const void*)ws_kernel<Cfg, uint16_t, uint16_t, STREAM>;
+  if (pt == MK_DT_BF16 && ct == MK_DT_F32) return (const void*)ws_kernel<Cfg, uint16_t, float, STREAM>;
+  if (pt == MK_DT_F32 && ct == MK_DT_BF16) return (const void*)ws_kernel<Cfg, float, uint16_t, STREAM>;
+  return (const void*)ws_kernel<Cfg, float, float, STREAM>;
 }
 
 template <class Cfg>
@@ -1479,9 +1485,10 @@ static const void* inplace_ptr(int pt, int ct) {
   return (const void*)inplace_kernel<Cfg, float, float>;
 }
 
-const void* fused_kernel_ptr(int shape, int pt, int ct, int dyn) {
-  if (shape == SHAPE_WS) return ws_ptr<TWs>(pt, ct);
-  if (shape == SHAPE_WS128) return ws_ptr<TWs128>(pt, ct);
+const void* fused_kernel_ptr(int shape, int pt, int ct, int variant) {
+  const int dyn = variant;
+  if (shape == SHAPE_WS) return ws_ptr<TWs, 128>(pt, ct);
+  if (shape == SHAPE_WS128) return variant ? ws_ptr<TWs128, 256>(pt, ct) : ws_ptr<TWs128, 128>(pt, ct);
   if (shape == SHAPE_64) return fused_ptr<T64, false>(pt, ct);  // no dynamic variant
   if (dyn) return shape == SHAPE_256 ? fused_ptr<T256, true>(pt, ct) : fused_ptr<T128, true>(pt, ct);
   return shape == SHAPE_256 ? fused_ptr<T256, false>(pt, ct) : fused_ptr<T128, false>(pt, ct);
@@ -1510,7 +1517,11 @@ const void* reduce_kernel_ptr(int pt, int ct) {
   return (const void*)reduce_kernel<float, float>;
 }
 
-int shape_threads(int shape) { return is_ws(shape) ? kWsThreads : kThreads; }
+int shape_threads(int shape, int variant) {
+  if (shape == SHAPE_WS) return kThreads + 128;
+  if (shape == SHAPE_WS128) return kThreads + (variant ? 256 : 128);
+  return kThreads;
+}
 int shape_bm(int shape) {
   if (shape == SHAPE_WS) return TWs::BM;
   if (shape == SHAPE_WS128) return TWs128::BM;
@@ -1534,10 +1545,11 @@ hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s) {
 
 hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s) {
   // the host sets static_tiles for 256x256 tiles only
+  const int variant = is_ws(shape) ? a.ws_wide : a.dyn;
   const void* f = a.static_tiles && shape == SHAPE_256 ? inplace_ptr<T256>(pt, ct)
-                                                       : fused_kernel_ptr(shape, pt, ct, a.dyn);
+                                                       : fused_kernel_ptr(shape, pt, ct, variant);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel(f, dim3(a.G), dim3(shape_threads(shape)), args, 0, s);
+  return hipLaunchKernel(f, dim3(a.G), dim3(shape_threads(shape, variant)), args, 0, s);
 }
 
 hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s) {
