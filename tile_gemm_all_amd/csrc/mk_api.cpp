@@ -312,12 +312,13 @@ mk_status_t validate_rs(const void* A, const void* B, const void* peers, int n_p
 // below. Returns the shape, or 0 for the other schedules. Where the GEMM weighs
 // more, the overlap gains less than the smaller tiles cost. Measured on MI355X,
 // us per call (stream/GEMM ratio; 256x256 tiles in place / 64x256 / 128x128
-// with 64-deep k-tiles in three stages; same machine):
-//   16384x8192x512 P=16 (9.8)   934 / 807 / 912     8192x8192x512 P=16 (9.8)  474 / 411 / 455
-//   16384x8192x1024 P=16 (4.9) 1009 / 934 / 946     4096x8192x1024 P=16 (4.9) 269 / 244 / 232
-//   4096x8192x1792 P=16 (2.8)   311 / 311 / 281     8192x8192x1024 P=8 (2.4)  339 / 331 / 291
-//   8192x16384x1024 P=8 (2.4)   624 / 647 / 568     4096x8192x2560 P=16 (1.95) 348 / 388 / 341
-//   4096x8192x3584 P=16 (1.4)   409 / 484 / 419     8192x8192x2048 P=8 (1.2)  441 / 524 / 456
+// with 64-deep k-tiles in three stages and, with 15 peers, four streaming
+// waves; same machine):
+//   16384x8192x512 P=16 (9.8)   928 / 802 / 902     8192x8192x512 P=16 (9.8)  501 / 412 / 446
+//   16384x8192x1024 P=16 (4.9) 1010 / 923 / 989     4096x8192x1024 P=16 (4.9) 273 / 245 / 234
+//   4096x8192x1792 P=16 (2.8)   311 / 313 / 273     8192x8192x1024 P=8 (2.4)  336 / 328 / 291
+//   8192x16384x1024 P=8 (2.4)   608 / 648 / 571     4096x8192x2560 P=16 (1.95) 356 / 387 / 334
+//   4096x8192x3584 P=16 (1.4)   399 / 483 / 403     8192x8192x2048 P=8 (1.2)  435 / 516 / 442
 int ws_pays(int64_t M, int64_t N, int64_t K, int n_peers, int peer_dtype, int c_dtype, int cus) {
   const double t_stream =
       (double)M * (double)N * (n_peers * (double)dt_size(peer_dtype) + dt_size(c_dtype)) / 8.0e12;
