@@ -448,10 +448,14 @@ typedef enum {
                                    word's top R/words bits go to the reduce stream. */
   MK_OPT_STATIC_TILES = 10      /* 256x256 tiles all reduced in place with more tiles than one round
                                    of workgroups (the default schedule of compute-bound shapes,
-                                   without telemetry): 1 = the in-place kernel, which deals each
+                                   without telemetry): 2 = the in-place kernel, which deals each
                                    XCD's range of tiles to its workgroups in a fixed order and
-                                   keeps no claim, flag or counter (default); 0 = the persistent
-                                   kernel with per-XCD tile claims. Both give the same bits. */
+                                   keeps no claim, flag or counter, with eight waves per
+                                   workgroup where the tile-end reduce fits two waves per SIMD
+                                   (bfloat16 peer counts 0-4, 7, 8, 15; float32 0-4, 7), else
+                                   four (default); 1 = the in-place kernel with four waves; 0 =
+                                   the persistent kernel with per-XCD tile claims. All give the
+                                   same bits. */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

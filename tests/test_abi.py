@@ -275,16 +275,17 @@ def test_stream_cu_split_option_takes_multiples_of_eight():
 
 
 def test_static_tiles_option_range():
-    """The in-place kernel's switch: 1 (default) or 0 (the claim-queue kernel);
-    anything else is rejected without changing the setting."""
+    """The in-place kernel's switch: 2 (default: eight waves where they fit), 1
+    (four waves) or 0 (the claim-queue kernel); anything else is rejected without
+    changing the setting."""
     old = mk.get_option(mk.OPT_STATIC_TILES)
-    assert old == 1
+    assert old == 2
     try:
-        for v in (-1, 2, 7):
+        for v in (-1, 3, 7):
             with pytest.raises(mk.MkError):
                 mk.set_option(mk.OPT_STATIC_TILES, v)
             assert mk.get_option(mk.OPT_STATIC_TILES) == old
-        for v in (0, 1):
+        for v in (0, 1, 2):
             mk.set_option(mk.OPT_STATIC_TILES, v)
             assert mk.get_option(mk.OPT_STATIC_TILES) == v
     finally:

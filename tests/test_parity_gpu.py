@@ -571,9 +571,9 @@ STATIC_SHAPES = [  # M, N, K, n_peers, peer dtype, C dtype: more 256x256 tiles t
 @pytest.mark.parametrize("shape", STATIC_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
 def test_inplace_kernel_matches_claim_queues(shape):
     """256x256 tiles all reduced in place with more tiles than workgroups: the
-    in-place kernel (each XCD's tiles dealt to its workgroups in a fixed order,
-    MK_OPT_STATIC_TILES=1, the default) and the persistent kernel's per-XCD claim
-    queues (0). Integer inputs bit-exact against the oracle on sampled rows and
+    in-place kernel (each XCD's tiles dealt to its workgroups in a fixed order)
+    with eight waves where they fit (MK_OPT_STATIC_TILES=2, the default) and with
+    four (1), and the persistent kernel's per-XCD claim queues (0). Integer inputs bit-exact against the oracle on sampled rows and
     bitwise equal to the two-kernel baseline over the whole output, twice in a
     row; Gaussian inputs within tolerance."""
     M, N, K, npeer, pdt, cdt = shape
@@ -588,7 +588,7 @@ def test_inplace_kernel_matches_claim_queues(shape):
     old = [mk.get_option(o) for o in opts]
     try:
         mk.set_option(mk.OPT_TILE_SHAPE, 1)
-        for static in (1, 0, 1):
+        for static in (2, 1, 0, 2):
             mk.set_option(mk.OPT_STATIC_TILES, static)
             for rep in range(2):
                 check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, f"static tiles {static} call {rep}")

@@ -33,7 +33,7 @@ MK_TRACE_CAP = 512
 OPT_SPIN_TIMEOUT_US, OPT_WITHHOLD_TILE, OPT_CTRL_PERIOD, OPT_TILE_SHAPE = 0, 1, 2, 3
 OPT_FLAG_SCOPE, OPT_REDUCER_CAP, OPT_INPLACE, OPT_EARLY, OPT_KSPLIT = 4, 5, 6, 7, 8
 OPT_STREAM_CU_SPLIT = 9  # two-stream schedule: compute units of the CU-masked reduce stream
-OPT_STATIC_TILES = 10  # all-in-place 256x256 tiles: 1 the in-place kernel (fixed tile order), 0 claim queues
+OPT_STATIC_TILES = 10  # all-in-place 256x256 tiles: 2 in-place kernel, 8 waves where they fit; 1 four; 0 claim queues
 
 EXPORTS = ["mk_gemm_ar_local", "mk_gemm_ar_local_noalloc", "mk_gemm_then_reduce_baseline",
            "mk_gemm_ar_two_stream",

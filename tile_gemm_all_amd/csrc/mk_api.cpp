@@ -49,7 +49,8 @@ struct Options {
   int64_t early = -1;       // reducers sum a unit's peers before its tile is finished: -1 auto
   int64_t ksplit = -1;      // early-reduce tiles computed as two k-halves: -1 auto, 1 off, 2 on
   int64_t stream_cu_split = 0;  // two-stream schedule: compute units of the reduce stream (0: no masks)
-  int64_t static_tiles = 1;  // all-in-place 256x256 tiles: 1 the in-place kernel, 0 claim queues
+  int64_t static_tiles = 2;  // all-in-place 256x256 tiles: 2 the in-place kernel with eight waves
+                             // where its rings fit, 1 with four, 0 claim queues
 };
 std::mutex g_opt_mu;
 Options g_opt;
@@ -772,9 +773,14 @@ mk_status_t ar_plan(const ArCall& c, bool all_inplace, mk::FusedArgs& a) {
   a.ws_wide = mk::ws_wide(L.shape, (int)dt_size(peer_dtype), n_peers) ? 1 : 0;
   a.static_tiles = !a.one_tile && !a.dyn && !a.early && a.ksplit == 1 &&
                            T_inplace_all(a, inpl_ok) && !c.telemetry &&
-                           L.shape == mk::SHAPE_256 && opt.static_tiles == 1
+                           L.shape == mk::SHAPE_256 && opt.static_tiles >= 1
                        ? 1
                        : 0;
+  // ... with eight waves where the tile-end rings fit two waves per SIMD
+  a.waves8 = a.static_tiles && opt.static_tiles == 2 &&
+                     mk::inplace_supported(2, (int)dt_size(peer_dtype), n_peers)
+                 ? 1
+                 : 0;
   // The seed share counts the in-place tiles' reduce as compute-side work.
   if (a.T > 0 && a.T_r < a.T) {
     double flops = 2.0 * (double)M * (double)N * (double)K;
@@ -1606,7 +1612,7 @@ mk_status_t mk_set_option(int option, int64_t value) {
       g_opt.stream_cu_split = value;
       return MK_OK;
     case MK_OPT_STATIC_TILES:
-      if (value < 0 || value > 1) return fail(MK_ERR_INVALID_ARG, "static tiles %lld", (long long)value);
+      if (value < 0 || value > 2) return fail(MK_ERR_INVALID_ARG, "static tiles %lld", (long long)value);
       g_opt.static_tiles = value;
       return MK_OK;
   }

@@ -146,9 +146,12 @@ struct NoGate {
   __device__ __forceinline__ void operator()(int) const {}
 };
 
-template <int BM_, int BN_, int BK_ = 32, int NS_ = 4>
+// NW waves per workgroup, WGN of them along N (4 and 2: a 2 x 2 grid of wave
+// tiles; 8 and 4: a 2 x 4 grid)
+template <int BM_, int BN_, int BK_ = 32, int NS_ = 4, int NW_ = 4, int WGN_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  static constexpr int NW = NW_, WGN = WGN_;
   // A tile rows are BK*2 bytes: chunk c of row r is stored at c ^ a_swz(r), so
   // that 16 consecutive rows of one chunk column hit distinct 16-byte bank groups
   static constexpr int A_CPR = BK * 2 / 16;  // 16-byte chunks per A row (4 or 8)
@@ -168,7 +171,7 @@ struct TileCfg {
   // on its own, so that the last reduces spread over every idle workgroup
   static constexpr int RSPLIT = BM / 64;
   static constexpr int KSTEPS = BK / 16;
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WM = BM / (NW / WGN), WN = BN / WGN;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_ROW = BK * 2;              // bytes per A row
   static constexpr int A_BYTES = BM * A_ROW;
@@ -176,13 +179,14 @@ struct TileCfg {
   static constexpr int B_BYTES = BK * B_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;   // bytes per stage
   static constexpr int LDS_BYTES = NS * STAGE;
-  static constexpr int A_LD = A_BYTES / 1024 / 4;   // 1 KiB direct loads per wave
-  static constexpr int B_LD = B_BYTES / 1024 / 4;
+  static constexpr int A_LD = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave
+  static constexpr int B_LD = B_BYTES / 1024 / NW;
   static constexpr int LD = A_LD + B_LD;            // direct loads per wave per stage
   static constexpr int A_ROWS_PER_LD = 1024 / A_ROW;
   static constexpr int B_ROWS_PER_LD = 1024 / B_ROW;
   static_assert(FM >= 1 && FN >= 1 && FN <= 4, "tile shape");
-  static_assert(A_LD >= 1 && B_LD >= 1 && B_ROW <= 1024, "tile too small for 4 waves");
+  static_assert(A_LD >= 1 && B_LD >= 1 && B_ROW <= 1024, "tile too small for its waves");
+  static_assert(NW / WGN == 2, "two rows of wave tiles");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -335,7 +339,7 @@ struct GemmTile {
   };
 
   __device__ __forceinline__ static void frag_offsets(Frag& f, int wave, int lane) {
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
     const int arow = wm * Cfg::WM + (lane & 31);  // + 32*fm keeps a_swz(row)
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
@@ -479,7 +483,7 @@ struct GemmTile {
   __device__ __forceinline__ void store_partial(float* __restrict__ P, int64_t M, int64_t N,
                                                 int64_t m0, int64_t n0) const {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int fm = 0; fm < Cfg::FM; ++fm)
 #pragma unroll
@@ -514,7 +518,7 @@ struct GemmTile {
   __device__ __forceinline__ void stage_pass_lds(char* lds) const {
     typedef __attribute__((address_space(3))) float lds_float;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
     lds_float* f = (lds_float*)(lds_char*)lds;
     constexpr int F0 = PASS * Cfg::FM / NPASS, F1 = (PASS + 1) * Cfg::FM / NPASS;
 #pragma unroll
@@ -1037,9 +1041,14 @@ __device__ __forceinline__ void reduce_region(const float* __restrict__ P,
 }
 
 // The same for a region whose fp32 partial sits in LDS (row pitch LP elements,
-// first row and column of the region at lds). Only peer counts for which
-// inplace_supported() holds.
-template <int OCC, typename PT, typename CT>
+// first row and column of the region at lds), by the THREADS threads of the
+// workgroup (ring depths for OCC waves per SIMD). With more than 256 threads
+// each lane keeps one chunk in flight: the same bytes in flight per compute
+// unit as four waves at their depth, since every CU streams its tile ends at
+// once (8192^3 with 7 peers, eight waves: 1080-1091 us with depth 2 against
+// 1099-1105 us with depth 3). Only peer counts for which inplace_supported()
+// holds.
+template <int OCC, typename PT, typename CT, int THREADS = kThreads>
 __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
                                                   const PT* __restrict__ peers, int n_peers,
                                                   CT* __restrict__ C, int64_t M, int64_t N,
@@ -1054,7 +1063,8 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
   const PartialLds ps{(const lds_char*)lds};
   if (n_peers == 0) {  // C = round(partial)
     typedef CopyLdsOp<CT> Op;
-    ReduceRing<4, Op>::run(Op{(const lds_char*)lds, OutC<CT>{C + base}}, total, cpr, N, LP);
+    ReduceRing<4, Op>::run_strided(Op{(const lds_char*)lds, OutC<CT>{C + base}}, total, cpr, N,
+                                   LP, (int)threadIdx.x, THREADS);
     return;
   }
 #define MK_RING(NPV)                                                                   \
@@ -1063,8 +1073,9 @@ __device__ __forceinline__ void reduce_region_lds(const char* lds, int64_t LP,
       const PT* pr[NPV];                                                               \
       _Pragma("unroll") for (int s = 0; s < NPV; ++s) pr[s] = peers + s * stride + base; \
       typedef SumOp<PT, NPV, PartialLds, OutC<CT>> Op;                                 \
-      ReduceRing<ring_depth<OCC, PT, NPV>(), Op>::run(Op{ps, pr, OutC<CT>{C + base}},  \
-                                                      total, cpr, N, LP);              \
+      constexpr int D = THREADS > kThreads ? 2 : ring_depth<OCC, PT, NPV>();           \
+      ReduceRing<D, Op>::run_strided(Op{ps, pr, OutC<CT>{C + base}}, total, cpr, N, LP,  \
+                                     (int)threadIdx.x, THREADS);                       \
     }                                                                                  \
     return;
   switch (n_peers) {

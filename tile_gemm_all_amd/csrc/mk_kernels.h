@@ -164,6 +164,7 @@ struct FusedArgs {
   int static_tiles;            // 1: every tile reduced in place, tiles dealt to the workgroups
                                // in a fixed order (inplace_kernel): no claim, flag or counter
   int ws_wide;                 // wave-specialised 128x128 tiles: 1 = four streaming waves
+  int waves8;                  // in-place kernel (static_tiles, 256x256): eight waves
 };
 
 struct GemmArgs {

@@ -163,7 +163,13 @@ __device__ __forceinline__ void rs_band(const FusedArgs& a, const char* band, in
 // reserve units once no GEMM tile is left (draining).
 // A tile reduced in place, straight from the accumulators of the workgroup that
 // computed it: the fp32 tile goes through LDS (free after the GEMM's last barrier)
-// in passes, each summed in the order of every other path. All threads.
+// in passes, each summed in the order of every other path. All threads (NW
+// waves); with eight waves two share a SIMD, and the reduce rings take the
+// register budget of two workgroups per compute unit.
+template <class Cfg>
+constexpr int ring_occ() {
+  return Cfg::NW == 8 ? 2 : Cfg::OCC;
+}
 template <class Cfg, typename PT, typename CT>
 __device__ __forceinline__ void inplace_tile(const GemmTile<Cfg>& g, char* lds, const PT* peers,
                                              int n_peers, CT* C, int64_t M, int64_t N, int64_t m0,
@@ -176,14 +182,15 @@ __device__ __forceinline__ void inplace_tile(const GemmTile<Cfg>& g, char* lds, 
     __syncthreads();
     if constexpr (GemmTile<Cfg>::NPASS == 1 && 2 * BAND == Cfg::BM) {
       const int rows = (int)(M - m0 < Cfg::BM ? M - m0 : Cfg::BM);
-      reduce_region_lds<Cfg::OCC, PT, CT>(lds, Cfg::BN, peers, n_peers, C, M, N, m0, n0, rows, cols);
+      reduce_region_lds<ring_occ<Cfg>(), PT, CT, Cfg::NW * 64>(lds, Cfg::BN, peers, n_peers, C, M,
+                                                               N, m0, n0, rows, cols);
     } else {
 #pragma unroll
       for (int wm = 0; wm < 2; ++wm) {
         const int64_t r0 = m0 + wm * Cfg::WM + PASS * BAND;
         const int rows = (int)(M - r0 < BAND ? M - r0 : BAND);  // <= 0 past the edge
-        reduce_region_lds<Cfg::OCC, PT, CT>(lds + wm * BAND * Cfg::BN * 4, Cfg::BN, peers,
-                                            n_peers, C, M, N, r0, n0, rows, cols);
+        reduce_region_lds<ring_occ<Cfg>(), PT, CT, Cfg::NW * 64>(
+            lds + wm * BAND * Cfg::BN * 4, Cfg::BN, peers, n_peers, C, M, N, r0, n0, rows, cols);
       }
     }
     __syncthreads();
@@ -1429,7 +1436,7 @@ __global__ __launch_bounds__(kThreads + STREAM, 1) void ws_kernel(FusedArgs a) {
 // registers (on MI355X, 8192^3 with 7 peers: 1087-1096 us against 1113-1121 us
 // for the claim-queue kernel in the same run).
 template <class Cfg, typename PT, typename CT>
-__global__ __launch_bounds__(kThreads, 1) void inplace_kernel(FusedArgs a) {
+__global__ __launch_bounds__(Cfg::NW * 64, 1) void inplace_kernel(FusedArgs a) {
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
   const int b = blockIdx.x, G = gridDim.x;
   int q0 = 0, q1 = a.T, s = b, per = G;
@@ -1455,6 +1462,11 @@ __global__ __launch_bounds__(kThreads, 1) void inplace_kernel(FusedArgs a) {
 // ------------------------------------------------------------ host-side launchers
 
 using T256 = TileCfg<256, 256, 64, 2>;  // 64-deep k-tiles, two LDS stages
+// The same tile computed by eight waves in a 2 x 4 grid (128 x 64 each, two
+// waves per SIMD) for the in-place kernel: bitwise the same products; on MI355X
+// 8192^3 ran 895-900 us against 919-951 us with four waves (GEMM alone), and the
+// fused call on 8192^3 with 7 peers 1024-1028 us against 1039-1045 us.
+using T256w8 = TileCfg<256, 256, 64, 2, 8, 4>;
 using T128 = TileCfg<128, 128>;
 // Few-tile shapes: every tile reduced in place; 64-deep k-tiles in four stages
 // (eight stages measured slower on the 128x8192x1792 shard: 31.9 against 30.0 us).
@@ -1546,8 +1558,12 @@ hipError_t launch_clear_error(unsigned long long* slots, hipStream_t s) {
 hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream_t s) {
   // the host sets static_tiles for 256x256 tiles only
   const int variant = is_ws(shape) ? a.ws_wide : a.dyn;
-  const void* f = a.static_tiles && shape == SHAPE_256 ? inplace_ptr<T256>(pt, ct)
-                                                       : fused_kernel_ptr(shape, pt, ct, variant);
+  if (a.static_tiles && shape == SHAPE_256) {
+    const void* f = a.waves8 ? inplace_ptr<T256w8>(pt, ct) : inplace_ptr<T256>(pt, ct);
+    void* args[] = {(void*)&a};
+    return hipLaunchKernel(f, dim3(a.G), dim3(a.waves8 ? 512 : kThreads), args, 0, s);
+  }
+  const void* f = fused_kernel_ptr(shape, pt, ct, variant);
   void* args[] = {(void*)&a};
   return hipLaunchKernel(f, dim3(a.G), dim3(shape_threads(shape, variant)), args, 0, s);
 }
