@@ -48,6 +48,7 @@ import argparse
 import hashlib
 import json
 import re
+import statistics
 import os
 import sys
 import time
@@ -559,6 +560,21 @@ def main():
         mk.stream_status()
         return start.elapsed_time(stop) / steps  # ms per launch
 
+    def timed_pair(fb, ff, steps, warmup, rounds=4):
+        """Baseline and fused legs of one comparison, timed in alternating blocks
+        (b f f b b f f b): the clock of a power-limited chip drifts over a run, and
+        two legs timed one after the other would carry that drift into their ratio.
+        Returns the median block time of each leg, ms per launch."""
+        for _ in range(warmup):
+            fb()
+            ff()
+        per = max(1, -(-steps // rounds))
+        tb, tf = [], []
+        for r in range(rounds):
+            for leg in ((0, 1) if r % 2 == 0 else (1, 0)):
+                (tb if leg == 0 else tf).append(timed(fb if leg == 0 else ff, per, 0))
+        return statistics.median(tb), statistics.median(tf)
+
     # Comparison legs get at least 50 warmup calls: the first leg timed in a fresh
     # process ran several percent slow after 10 (two-kernel baseline on mlp:
     # 0.336 ms after 10, 0.322 ms after 100, on one box), which would flatter the
@@ -585,8 +601,8 @@ def main():
                 return call
 
             steps = max(args.steps, 20 if o.flops > 1e10 else 200)
-            b_ms = timed(rot(mk.gemm_then_reduce_baseline), steps, cw)
-            f_ms = timed(rot(mk.gemm_ar_local), steps, cw)
+            b_ms, f_ms = timed_pair(rot(mk.gemm_then_reduce_baseline), rot(mk.gemm_ar_local),
+                                    steps, cw)
             r = {"M": o.M, "N": o.N, "K_local": o.K, "P": o.P, "input_sets": n_sets,
                  "fused_us": round(f_ms * 1e3, 2), "baseline_us": round(b_ms * 1e3, 2),
                  "speedup_vs_two_kernel": round(b_ms / f_ms, 4),
@@ -626,10 +642,10 @@ def main():
                 rs_peers = peers[:, o0:o1].contiguous()
                 rs_C = torch.empty((o1 - o0, o.N), dtype=C.dtype, device="cuda")
                 rs_send = torch.empty((o.M, o.N), dtype=peers.dtype, device="cuda")
-                rs_b = timed(lambda: mk.gemm_rs_baseline(A, B, rs_peers, rs_C, rs_send, o0, o1),
-                             args.steps, cw)
-                rs_f = timed(lambda: mk.gemm_rs_local(A, B, rs_peers, rs_C, rs_send, o0, o1),
-                             args.steps, cw)
+                rs_b, rs_f = timed_pair(
+                    lambda: mk.gemm_rs_baseline(A, B, rs_peers, rs_C, rs_send, o0, o1),
+                    lambda: mk.gemm_rs_local(A, B, rs_peers, rs_C, rs_send, o0, o1),
+                    args.steps, cw)
                 extras["reduce_scatter"] = {"workload": "mlp GEMM", "owned_rows": [o0, o1],
                                             "fused_us": round(rs_f * 1e3, 2),
                                             "baseline_us": round(rs_b * 1e3, 2),
@@ -648,10 +664,10 @@ def main():
         del ag_shards
         ag_full = torch.empty((aw.M, aw.K), dtype=torch.bfloat16, device="cuda")
         ag_C = torch.empty((aw.M, aw.N), dtype=torch.bfloat16, device="cuda")
-        ag_b = timed(lambda: mk.gemm_ag_baseline(ag_local, ag_peers, ag_full, ag_B, ag_C, 5),
-                     args.steps, cw)
-        ag_f = timed(lambda: mk.gemm_ag_local(ag_local, ag_peers, ag_full, ag_B, ag_C, 5),
-                     args.steps, cw)
+        ag_b, ag_f = timed_pair(
+            lambda: mk.gemm_ag_baseline(ag_local, ag_peers, ag_full, ag_B, ag_C, 5),
+            lambda: mk.gemm_ag_local(ag_local, ag_peers, ag_full, ag_B, ag_C, 5),
+            args.steps, cw)
         extras["allgather"] = {"workload": f"{aw.name}: {aw.description}", "Ms": aw.Ms,
                                "P": aw.P, "N": aw.N, "K": aw.K, "rank": 5,
                                "fused_us": round(ag_f * 1e3, 2),

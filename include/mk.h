@@ -455,7 +455,9 @@ typedef enum {
                                    (bfloat16 peer counts 0-4, 7, 8, 15; float32 0-4, 7), else
                                    four (default); 1 = the in-place kernel with four waves; 0 =
                                    the persistent kernel with per-XCD tile claims. All give the
-                                   same bits. */
+                                   same bits. With 2, the baselines' GEMM kernel also takes the
+                                   eight-wave 256x256 tile when there are more tiles than
+                                   compute units. */
 } mk_option_t;
 mk_status_t mk_set_option(int option, int64_t value);
 int64_t mk_get_option(int option);

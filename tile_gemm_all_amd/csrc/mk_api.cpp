@@ -924,6 +924,17 @@ mk_status_t mk_gemm_ar_local_noalloc(const void* A, const void* B, const void* p
   return MK_OK;
 }
 
+// GEMM kernels of the baselines: 256x256 tiles take the in-place kernel's
+// eight-wave layout under its option (MK_OPT_STATIC_TILES = 2) when there are
+// more tiles than compute units, where it is the faster GEMM (8192 x 8192 x 8192:
+// 895-900 us against 919-951 us with four waves, bitwise the same).
+int gemm_waves8(const Launch& L, const mk::GemmArgs& g) {
+  return L.shape == mk::SHAPE_256 && options().static_tiles == 2 &&
+                 (int64_t)g.tiles_m * g.tiles_n > L.info.cus
+             ? 1
+             : 0;
+}
+
 mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const void* peers,
                                          int n_peers, void* C, int64_t M, int64_t N, int64_t K,
                                          int peer_dtype, int c_dtype, void* stream) {
@@ -950,7 +961,7 @@ mk_status_t mk_gemm_then_reduce_baseline(const void* A, const void* B, const voi
   g.tiles_n = (int)L.tiles_n;
   const int n_xcd = L.info.cus / 32;  // 32 compute units per XCD on gfx950
   g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
-  g.pad_ = 0;
+  g.waves8 = gemm_waves8(L, g);
   hipError_t e = mk::launch_gemm(L.shape, g, s);
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
   mk::ReduceArgs r;
@@ -1090,7 +1101,7 @@ mk_status_t mk_gemm_ar_two_stream(const void* A, const void* B, const void* peer
     g.tiles_m = (int)((r1 - r0 + BM - 1) / BM);
     g.tiles_n = (int)L.tiles_n;
     g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
-    g.pad_ = 0;
+    g.waves8 = gemm_waves8(L, g);
     e = mk::launch_gemm(L.shape, g, sg);
     if (e != hipSuccess) break;
     // the chunk's partial rows are complete when the GEMM kernel ends
@@ -1241,7 +1252,7 @@ mk_status_t mk_gemm_rs_baseline(const void* A, const void* B, const void* peers,
   g.tiles_n = (int)L.tiles_n;
   const int n_xcd = L.info.cus / 32;
   g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
-  g.pad_ = 0;
+  g.waves8 = gemm_waves8(L, g);
   hipError_t e = mk::launch_gemm(L.shape, g, s);
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
   const int64_t own = own_m1 - own_m0;
@@ -1403,7 +1414,7 @@ mk_status_t mk_gemm_ag_baseline(const void* A_local, const void* peers_A, int n_
   g.tiles_n = (int)((N + mk::shape_bn(shape) - 1) / mk::shape_bn(shape));
   const int n_xcd = info.cus / 32;
   g.n_xcd = n_xcd >= 1 && n_xcd <= mk::kMaxXcd ? n_xcd : 1;
-  g.pad_ = 0;
+  g.waves8 = 0;
   e = mk::launch_gemm_c(shape, c_dtype, g, C, s);
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
   return MK_OK;

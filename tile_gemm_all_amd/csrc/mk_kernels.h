@@ -174,7 +174,7 @@ struct GemmArgs {
   int64_t M, N, K;
   int tiles_m, tiles_n;
   int n_xcd;  // workgroup b runs on XCD b % n_xcd; 1 = no XCD-aware mapping
-  int pad_;
+  int waves8;  // 256x256 tiles: eight waves per workgroup (512 threads), else four
 };
 
 struct ReduceArgs {
@@ -231,7 +231,7 @@ struct AgCopyArgs {
 // streaming waves instead of two (wave-specialised 128x128 tiles)
 const void* fused_kernel_ptr(int shape, int pt, int ct, int variant);
 const void* ag_kernel_ptr(int shape, int ct);
-const void* gemm_kernel_ptr(int shape);
+const void* gemm_kernel_ptr(int shape, int waves8);
 const void* reduce_kernel_ptr(int pt, int ct);
 int shape_bm(int shape);
 int shape_threads(int shape, int variant);  // workgroup size of the fused kernel of a shape

@@ -1174,7 +1174,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_c_kernel(GemmArgs a, CT* C) 
 // ------------------------------------------------------------ baseline kernels
 
 template <class Cfg>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(Cfg::NW * 64, 1) void gemm_kernel(GemmArgs a) {
   __shared__ __align__(1024) char lds[Cfg::LDS_BYTES];
   // The dispatcher deals workgroups to XCDs in turn (workgroup b on XCD
   // b % n_xcd). Giving each XCD a contiguous range of the tile order, mapped as
@@ -1517,8 +1517,9 @@ const void* ag_kernel_ptr(int shape, int ct) {
   return ct == MK_DT_BF16 ? (const void*)ag_kernel<T128, uint16_t> : (const void*)ag_kernel<T128, float>;
 }
 
-const void* gemm_kernel_ptr(int shape) {
+const void* gemm_kernel_ptr(int shape, int waves8) {
   if (shape == SHAPE_64) return (const void*)gemm_kernel<T64>;
+  if (shape == SHAPE_256 && waves8) return (const void*)gemm_kernel<T256w8>;
   return shape == SHAPE_256 ? (const void*)gemm_kernel<T256> : (const void*)gemm_kernel<T128>;
 }
 
@@ -1569,9 +1570,10 @@ hipError_t launch_fused(int shape, int pt, int ct, const FusedArgs& a, hipStream
 }
 
 hipError_t launch_gemm(int shape, const GemmArgs& a, hipStream_t s) {
-  const void* f = gemm_kernel_ptr(shape);
+  const bool w8 = shape == SHAPE_256 && a.waves8;
+  const void* f = gemm_kernel_ptr(shape, w8);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel(f, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), args, 0, s);
+  return hipLaunchKernel(f, dim3(a.tiles_m * a.tiles_n), dim3(w8 ? 512 : kThreads), args, 0, s);
 }
 
 hipError_t launch_reduce(int pt, int ct, const ReduceArgs& a, int grid, hipStream_t s) {
