@@ -40,7 +40,8 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload large]
                                           timers of the tile-flag hand-over)
 
 --all-configs times batches of calls between two HIP events (10 batches of 20
-calls after warmup; median, p10 and p90 of the per-call averages). Workloads
+calls after warmup, the fused, baseline and two-stream batches alternating;
+median, p10 and p90 of the per-call averages). Workloads
 whose inputs are under 600 MB rotate through enough input sets to exceed 600 MB,
 so that repeated calls do not find their peers in the 256 MB Infinity Cache.
 """
@@ -127,29 +128,40 @@ def cpu_baseline(w, A, B, peers, budget_s=12.0):
                       f"K={w.K}, {w.n_peers} peers), fp64, {t:.1f} s"}
 
 
-def _batched(fn_of_set, n_sets, stream, batches=10, per_batch=20, warmup=10):
-    """Per-call averages of `batches` batches of `per_batch` calls (call i uses
-    input set i % n_sets), each batch between two events on `stream`."""
+def _batched(legs, n_sets, stream, batches=10, per_batch=20, warmup=10):
+    """Per-call averages of `batches` batches of `per_batch` calls for each leg
+    (a name -> fn(input set) dict; call i of a leg uses input set i % n_sets),
+    each batch between two events on `stream`. The legs' batches alternate, in
+    an order rotated every batch, so that clock drift over the run falls on all
+    legs alike."""
     import torch
 
-    for i in range(warmup):
-        fn_of_set(i % n_sets)
+    names = list(legs)
+    for name in names:
+        for i in range(warmup):
+            legs[name](i % n_sets)
     torch.cuda.synchronize()
-    out, i = [], 0
-    for _ in range(batches):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(per_batch):
-            fn_of_set(i % n_sets)
-            i += 1
-        b.record(stream)
-        torch.cuda.synchronize()
-        out.append(a.elapsed_time(b) / per_batch * 1e3)  # us per call
-    out.sort()
-    pick = lambda q: out[min(len(out) - 1, int(q * (len(out) - 1) + 0.5))]
-    return {"median_us": round(pick(0.5), 1), "p10_us": round(pick(0.1), 1),
-            "p90_us": round(pick(0.9), 1)}
+    times = {name: [] for name in names}
+    i = 0
+    for bi in range(batches):
+        for j in range(len(names)):
+            name = names[(bi + j) % len(names)]
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for k in range(per_batch):
+                legs[name]((i + k) % n_sets)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times[name].append(a.elapsed_time(b) / per_batch * 1e3)  # us per call
+        i += per_batch
+    out = {}
+    for name in names:
+        v = sorted(times[name])
+        pick = lambda q: v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+        out[name] = {"median_us": round(pick(0.5), 1), "p10_us": round(pick(0.1), 1),
+                     "p90_us": round(pick(0.9), 1)}
+    return out
 
 
 def all_configs():
@@ -168,9 +180,10 @@ def all_configs():
         cdt = torch.bfloat16 if w.c_dtype == "bf16" else torch.float32
         C = torch.empty((w.M, w.N), dtype=cdt, device="cuda")
         r = {"n_input_sets": n_sets}
-        r["fused"] = _batched(lambda i: mk.gemm_ar_local(*sets[i], C), n_sets, stream)
-        r["baseline"] = _batched(lambda i: mk.gemm_then_reduce_baseline(*sets[i], C), n_sets, stream)
-        r["two_stream"] = _batched(lambda i: mk.gemm_ar_two_stream(*sets[i], C), n_sets, stream)
+        r.update(_batched({"fused": lambda i: mk.gemm_ar_local(*sets[i], C),
+                           "baseline": lambda i: mk.gemm_then_reduce_baseline(*sets[i], C),
+                           "two_stream": lambda i: mk.gemm_ar_two_stream(*sets[i], C)},
+                          n_sets, stream))
         mk.stream_status()
         r["speedup_vs_baseline"] = round(r["baseline"]["median_us"] / r["fused"]["median_us"], 3)
         r["fused_TFLOPs"] = round(w.flops / (r["fused"]["median_us"] * 1e-6) / 1e12, 1)
@@ -206,8 +219,9 @@ def sweep(name):
     per = 10 if w.flops > 1e10 else 100
 
     def t(nr):
-        return _batched(lambda i: mk.gemm_ar_local(*sets[i], C, n_reduce_wg=nr), n_sets, stream,
-                        batches=5, per_batch=per, warmup=3 * per)["median_us"]
+        return _batched({"fused": lambda i: mk.gemm_ar_local(*sets[i], C, n_reduce_wg=nr)},
+                        n_sets, stream, batches=5, per_batch=per,
+                        warmup=3 * per)["fused"]["median_us"]
 
     # the knob: the reducer target under dynamic hand-over (MK_OPT_INPLACE = -2;
     # shapes with early reduce keep their schedule and sweep their reducer target)
