@@ -575,7 +575,9 @@ def test_inplace_kernel_matches_claim_queues(shape):
     with eight waves where they fit (MK_OPT_STATIC_TILES=2, the default) and with
     four (1), and the persistent kernel's per-XCD claim queues (0). Integer inputs bit-exact against the oracle on sampled rows and
     bitwise equal to the two-kernel baseline over the whole output, twice in a
-    row; Gaussian inputs within tolerance."""
+    row; the baseline itself with its GEMM on the 256x256 tile of eight waves
+    (option 2) and of four (1, 0) gives the same bits. Gaussian inputs within
+    tolerance."""
     M, N, K, npeer, pdt, cdt = shape
     announce(f"in-place kernel {shape}")
     rows = sample_rows(M, band=256, seed=M + K)
@@ -592,6 +594,8 @@ def test_inplace_kernel_matches_claim_queues(shape):
             mk.set_option(mk.OPT_STATIC_TILES, static)
             for rep in range(2):
                 check_exact(c_bits(run(A, B, peers, cdt, "adaptive")), ref, f"static tiles {static} call {rep}")
+            check_exact(c_bits(run(A, B, peers, cdt, "baseline")), ref,
+                        f"baseline, 256x256 GEMM tiles, static tiles {static}")
         A, B, peers = mk_inputs.make_inputs(M, N, K, npeer, pdt, "gaussian", 28, device="cpu")
         C64, _ = oracle_rows(A, B, peers, cdt, rows)
         A, B, peers = A.to(DEV), B.to(DEV), peers.to(DEV)
