@@ -22,6 +22,7 @@ workload.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload large]
                        [--headline-only] [--no-cpu-baseline]
+       python bench.py --allgather       (the AllGather+GEMM share alone)
        python bench.py --all-configs     (one JSON line: every workload, fused /
                                           baseline / two-stream, median p10 p90)
        python bench.py --sweep large     (one JSON line: static reducer counts
@@ -162,6 +163,33 @@ def _batched(legs, n_sets, stream, batches=10, per_batch=20, warmup=10):
         out[name] = {"median_us": round(pick(0.5), 1), "p10_us": round(pick(0.1), 1),
                      "p90_us": round(pick(0.9), 1)}
     return out
+
+
+def allgather(steps, warmup):
+    """The AllGather+GEMM share on ag_up (rank 5) alone: baseline (gather kernel,
+    then the GEMM kernel) and fused kernel in alternating batches; one JSON line.
+    Short runs of it serve the kernels' counter passes."""
+    import torch
+
+    import mk_inputs
+    import tile_gemm_all_amd as mk
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    aw = mk_inputs.AG_BY_NAME["ag_up"]
+    shards, B = mk_inputs.make_ag_inputs(aw.Ms, aw.P, aw.N, aw.K, "gaussian", 1000 * aw.index,
+                                         device="cuda")
+    loc, peers = mk_inputs.shard_split(shards, 5)
+    full = torch.empty((aw.M, aw.K), dtype=torch.bfloat16, device="cuda")
+    C = torch.empty((aw.M, aw.N), dtype=torch.bfloat16, device="cuda")
+    r = _batched({"baseline": lambda i: mk.gemm_ag_baseline(loc, peers, full, B, C, 5),
+                  "fused": lambda i: mk.gemm_ag_local(loc, peers, full, B, C, 5)},
+                 1, stream, batches=4, per_batch=max(1, steps), warmup=warmup)
+    mk.stream_status()
+    print(json.dumps({"mode": "allgather", "workload": aw.name, "Ms": aw.Ms, "P": aw.P,
+                      "N": aw.N, "K": aw.K, "rank": 5, **r,
+                      "speedup": round(r["baseline"]["median_us"] / r["fused"]["median_us"], 4)}),
+          flush=True)
 
 
 def all_configs():
@@ -506,6 +534,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload's fused call and its baseline")
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--allgather", action="store_true",
+                    help="the AllGather+GEMM share alone (baseline and fused, alternating)")
     ap.add_argument("--sweep", metavar="WORKLOAD")
     ap.add_argument("--trace", metavar="WORKLOAD",
                     help="one call with telemetry; --trace-inplace 0 hands every tile over")
@@ -527,6 +557,9 @@ def main():
         sys.exit(2)
     if args.all_configs:
         all_configs()
+        return
+    if args.allgather:
+        allgather(args.steps, args.warmup)
         return
     if args.sweep:
         sweep(args.sweep)
